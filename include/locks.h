@@ -1,0 +1,208 @@
+/*
+ * locks.h -- C ABI of the LOCKS decode hot path on AMD Instinct MI355X (gfx950).
+ *
+ * LOCKS keeps the whole paged KV cache resident and, per decode step and KV
+ * head, reads only (a) a small spectral summary of every full page and (b) the
+ * full K/V of the pages it selects from those summaries.
+ *
+ * Pages this interface follows (cited by title and section):
+ *   [N] "LOCKS 阅读笔记" (zhongzhuzhou.org reading notes, 2026-07-29) on
+ *       "LOCKS: Page-Local Compact Key Summaries for Efficient Long-Context
+ *       Decoding", arXiv 2607.24555.
+ *   [S] "Resumo Técnico: LOCKS" (gist.science technical summary).
+ *
+ * Conventions shared by every call
+ *   - Pointers are DEVICE pointers unless stated otherwise. Every call is
+ *     asynchronous and ordered on `stream`; none allocates, frees or
+ *     synchronises the host.
+ *   - The caller owns every buffer (pools, tables, outputs, workspace). The
+ *     library keeps no mutable global state; calls on different streams with
+ *     different output/workspace buffers may run concurrently.
+ *   - Errors: arguments known on the host are validated before anything is
+ *     enqueued; a call that returns an error has enqueued nothing. A failed
+ *     kernel launch returns LOCKS_ERR_HIP.
+ *   - Device-resident data (block ids, lengths, budgets, selections) is
+ *     trusted in meaning but never dereferenced out of range: a block id
+ *     outside [0, num_blocks) is treated as a missing page (not scored, not
+ *     attended, its summary not written), lengths are clamped to
+ *     [0, max_pages * page_size] and budgets to [2, max_budget].
+ *   - Layouts (row-major, innermost last):
+ *       K / V pool     bf16 [num_blocks][num_kv_heads][page_size][head_dim]
+ *       summaries      uint8 [num_blocks][num_kv_heads][slot_stride]
+ *       q              bf16 [num_seqs][num_kv_heads * group_size][head_dim];
+ *                      query head h belongs to KV head h / group_size
+ *       block_table    int32 [num_seqs][max_pages], logical page -> block id
+ *       seq_lens       int32 [num_seqs], tokens cached including the current
+ *                      one; the sequence has P = ceil(len / page_size) pages,
+ *                      of which F = floor(len / page_size) are full
+ *   - Supported shapes: head_dim 128, page_size 16, rank 1..16,
+ *     group_size 1, 2 or 4, num_kv_heads >= 1.
+ */
+#ifndef LOCKS_H
+#define LOCKS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Version of the summary slot byte layout described below. */
+#define LOCKS_SLOT_LAYOUT_VERSION 1
+
+typedef struct {
+    int32_t head_dim;     /* d: 128 */
+    int32_t page_size;    /* B: tokens per page, 16 */
+    int32_t rank;         /* r: kept basis vectors per page, 1..16 */
+    int32_t num_kv_heads; /* H_kv >= 1 */
+    int32_t group_size;   /* G: query heads per KV head (GQA), 1, 2 or 4 */
+} locks_dims;
+
+typedef enum {
+    LOCKS_OK = 0,
+    LOCKS_ERR_INVALID_ARG = -1, /* null pointer, negative count, bad shape   */
+    LOCKS_ERR_UNSUPPORTED = -2, /* valid but not implemented shape           */
+    LOCKS_ERR_WORKSPACE = -3,   /* workspace missing or smaller than needed  */
+    LOCKS_ERR_HIP = -4          /* a HIP launch or device query failed       */
+} locks_status;
+
+const char* locks_status_string(locks_status status);
+
+/*
+ * Summary slot of one (block, KV head) page -- [N] §4.1 (storage paragraph)
+ * and Algorithm 1: an int4 basis with one scale per column, int8 coefficients
+ * with one scale per token row, an int8 centroid with one scale; about a
+ * tenth of the page's K+V bytes at r = 8, B = 16.
+ *
+ *   offset 0          Vq   r columns x (d/2) bytes, two's-complement int4.
+ *                          Each little-endian 32-bit word of a column covers
+ *                          dims 8t..8t+7; its four bytes hold the dim pairs
+ *                          (0,1), (4,5), (2,3), (6,7), low nibble first.
+ *   offset r*d/2      Cq   page_size x r int8, row-major (row i = c_i)
+ *   next              muq  d int8 (centroid codes in dim order)
+ *   next              scales, fp16 little-endian: r basis-column scales,
+ *                          page_size coefficient-row scales, 1 centroid scale
+ *   then zero padding up to slot_stride (a multiple of 16 bytes).
+ * Decoded values are code * scale. r = 8: 818 payload bytes, stride 832.
+ */
+size_t locks_summary_slot_bytes(const locks_dims* dims);  /* payload; 0 if dims invalid */
+size_t locks_summary_slot_stride(const locks_dims* dims); /* bytes between slots; 0 if invalid */
+
+/*
+ * Bytes of device workspace that locks_score_select and locks_sparse_attn
+ * need for up to num_seqs sequences of up to max_pages pages and budgets of
+ * up to max_budget pages. One workspace may serve both calls when they are
+ * ordered on one stream. It must be zero-filled once before its first use;
+ * every call leaves its counters at zero again when it completes. Returns 0
+ * for invalid arguments.
+ */
+size_t locks_workspace_bytes(const locks_dims* dims, int32_t num_seqs, int32_t max_pages,
+                             int32_t max_budget);
+
+/*
+ * locks_build -- [N] §4.1 eq. 2-3 and §4.3 Algorithm 1, for n full pages.
+ * For each i < n and each KV head, reads the page_size x head_dim keys of
+ * block block_ids[i] (device int32) and writes that (block, head) slot:
+ * centroid mu = mean of the keys, deviations D = keys - mu, Gram D D^T,
+ * eigendecomposition (Jacobi, descending eigenvalues), basis
+ * V = D^T U_r Sigma_r^{-1} and coefficients C = U_r Sigma_r, then int4/int8
+ * quantisation. Component k is kept only if lambda_k > 1e-6 trace(D D^T) and
+ * lambda_k > 1e-12 sum_i |k_i|^2; otherwise its basis column and
+ * coefficients are zero. Each kept basis vector is signed so that its entry of
+ * largest magnitude (lowest dim on ties) is positive. Quantiser: scale =
+ * fp16(fp32(absmax) / qmax) (qmax 7 for int4, 127 for int8; an overflowing
+ * scale saturates at 65504), code = clamp(rint(x / scale), -qmax, qmax) in
+ * fp32, all-zero when absmax is 0. Block ids outside [0, num_blocks) are
+ * skipped. Errors: INVALID_ARG (null pointers, n < 0, num_blocks < 1, bad
+ * dims), UNSUPPORTED (shape), HIP.
+ */
+locks_status locks_build(const locks_dims* dims, const void* k_pool, int64_t num_blocks,
+                         const int32_t* block_ids, int32_t n, void* summaries,
+                         hipStream_t stream);
+
+/*
+ * locks_build_filled -- the incremental build trigger of [N] §2 and
+ * [S] §2: for every sequence whose length is a positive multiple of
+ * page_size (its newest page has just filled), builds that page
+ * (block_table[s][len/page_size - 1]) for all KV heads exactly as
+ * locks_build does. Sequences whose last page is partial are left alone.
+ * The decision is taken on the device, so the call can sit in a captured
+ * decode step. Errors as for locks_build.
+ */
+locks_status locks_build_filled(const locks_dims* dims, const void* k_pool, int64_t num_blocks,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                int32_t num_seqs, int32_t max_pages, void* summaries,
+                                hipStream_t stream);
+
+/*
+ * locks_append_kv -- writes one new token per sequence into the paged cache
+ * (the decode-step append that precedes scoring, [N] §2 figure 1):
+ * k_new / v_new bf16 [num_seqs][num_kv_heads][head_dim] go to position
+ * seq_lens[s] - 1 (seq_lens already counts the new token) of block
+ * block_table[s][(seq_lens[s]-1) / page_size]. Sequences with length < 1 or
+ * an out-of-range block are skipped. Errors: INVALID_ARG, UNSUPPORTED, HIP.
+ */
+locks_status locks_append_kv(const locks_dims* dims, const void* k_new, const void* v_new,
+                             void* k_pool, void* v_pool, int64_t num_blocks,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             int32_t num_seqs, int32_t max_pages, hipStream_t stream);
+
+/*
+ * locks_score_select -- [N] §4.2 eq. 4-5 and §4.4 Algorithm 2 up to the
+ * selection; reads summaries only, never K or V.
+ *   score: for every full page j < F and query head g of the group,
+ *     s_hat_jg = LSE_i ((q_g . mu_j + (V_j^T q_g) . c_i) / sqrt(d))
+ *     from the decoded summary (natural-log units).
+ *   shares: Z_g = LSE_j s_hat_jg over all F full pages (sink and a full last
+ *     page included); key_j = log((1/G) sum_g exp(s_hat_jg - Z_g)).
+ *   select: S = {0, P-1} plus the k-2 pages of largest key among pages
+ *     1..P-2 (equal keys: lower page first); k = clamp(budgets[s], 2,
+ *     max_budget); every page when k >= P; {0} when P == 1; nothing when
+ *     P == 0. One S per (sequence, KV head) serves its whole GQA group.
+ * Outputs: sel_pages int32 [num_seqs][num_kv_heads][max_budget], the logical
+ *   page ids of S in ascending order, padded with -1; sel_count int32
+ *   [num_seqs][num_kv_heads] = |S|. scores_out (optional, may be NULL):
+ *   float [num_seqs][num_kv_heads][max_pages][group_size] with s_hat for
+ *   j < F and NaN elsewhere.
+ * Errors: INVALID_ARG (null required pointer, num_seqs < 0, max_pages < 1,
+ *   max_budget < 2, num_blocks < 1, bad dims), UNSUPPORTED (shape),
+ *   WORKSPACE (workspace NULL or smaller than locks_workspace_bytes), HIP.
+ */
+locks_status locks_score_select(const locks_dims* dims, const void* q, const void* summaries,
+                                int64_t num_blocks, const int32_t* block_table,
+                                const int32_t* seq_lens, const int32_t* budgets,
+                                int32_t num_seqs, int32_t max_pages, int32_t max_budget,
+                                int32_t* sel_pages, int32_t* sel_count, float* scores_out,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * locks_sparse_attn -- [N] §4.4 Algorithm 2 last steps and §3.1 eq. 1: for
+ * every query head g of KV head h, softmax attention over the tokens of the
+ * selected pages only, renormalised over them:
+ *   o_g = sum_{t in S} exp(l_t) v_t / sum_{t in S} exp(l_t), l_t = q_g.k_t/sqrt(d),
+ * where the last page P-1 contributes its len - (P-1)*page_size valid tokens.
+ * The pages are split across workgroups (split-K flash decoding) and the
+ * partial (max, sum, accumulator) triples are merged by log-sum-exp in a fixed
+ * order, so results do not depend on scheduling.
+ * Outputs: out float [num_seqs][num_kv_heads * group_size][head_dim];
+ *   lse_out (optional) float [num_seqs][num_kv_heads * group_size] =
+ *   log sum_{t in S} exp(l_t); an empty selection gives out = 0, lse = -inf.
+ * Selected ids outside [0, P) or whose block is out of range are ignored.
+ * Errors as for locks_score_select.
+ */
+locks_status locks_sparse_attn(const locks_dims* dims, const void* q, const void* k_pool,
+                               const void* v_pool, int64_t num_blocks,
+                               const int32_t* block_table, const int32_t* seq_lens,
+                               const int32_t* sel_pages, const int32_t* sel_count,
+                               int32_t num_seqs, int32_t max_pages, int32_t max_budget,
+                               float* out, float* lse_out, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOCKS_H */

@@ -1,0 +1,202 @@
+// C ABI of the LOCKS decode path: host-side validation, workspace carving and
+// kernel dispatch. Declarations and the contract of every entry point are in
+// include/locks.h.
+#include "locks.h"
+
+#include <hip/hip_runtime.h>
+
+#include "locks_device.h"
+
+namespace locks {
+hipError_t launch_score(int r, int G, const void* q, const void* summ, const int32_t* table,
+                        const int32_t* lens, float* scores, int64_t nb, int S, int H, int MP,
+                        int fill_nan, hipStream_t st);
+hipError_t launch_select(int G, const float* scores, const int32_t* lens, const int32_t* budgets,
+                         int32_t* sel, int32_t* cnt, uint32_t* keybuf, int S, int H, int MP,
+                         int max_budget, hipStream_t st);
+hipError_t launch_attn(int G, const void* q, const void* kpool, const void* vpool,
+                       const int32_t* table, const int32_t* lens, const int32_t* sel,
+                       const int32_t* cnt, float* part, uint32_t* counters, float* out,
+                       float* lse_out, int64_t nb, int S, int H, int MP, int max_budget,
+                       int nsplit, int ppw, hipStream_t st);
+hipError_t launch_build(int r, const void* kpool, int64_t nb, int H, const int32_t* ids, int n,
+                        const int32_t* table, const int32_t* lens, int MP, void* summ,
+                        hipStream_t st);
+hipError_t launch_append(const void* knew, const void* vnew, void* kpool, void* vpool, int64_t nb,
+                         const int32_t* table, const int32_t* lens, int S, int H, int MP,
+                         hipStream_t st);
+}  // namespace locks
+
+namespace {
+
+constexpr int kMaxPagesSupported = 65536;  // select keeps one 64-bit page mask per thread
+constexpr int kAttnPagesPerWave = 1;
+constexpr int kAttnWaves = 4;
+
+locks_status check_dims(const locks_dims* d) {
+  if (!d) return LOCKS_ERR_INVALID_ARG;
+  if (d->head_dim <= 0 || d->page_size <= 0 || d->rank <= 0 || d->num_kv_heads <= 0 ||
+      d->group_size <= 0)
+    return LOCKS_ERR_INVALID_ARG;
+  if (d->head_dim != locks::kHeadDim || d->page_size != locks::kPage) return LOCKS_ERR_UNSUPPORTED;
+  if (d->rank > locks::kPage) return LOCKS_ERR_UNSUPPORTED;
+  if (d->group_size != 1 && d->group_size != 2 && d->group_size != 4) return LOCKS_ERR_UNSUPPORTED;
+  return LOCKS_OK;
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Workspace {
+  size_t scores, keys, parts, counters, total;
+  int nsplit;
+};
+
+Workspace carve(const locks_dims* d, int32_t S, int32_t MP, int32_t KB) {
+  Workspace w{};
+  const size_t sh = (size_t)S * d->num_kv_heads;
+  const int per_wg = kAttnWaves * kAttnPagesPerWave;
+  w.nsplit = (KB + per_wg - 1) / per_wg;
+  size_t off = 0;
+  w.counters = off;
+  off = align_up(off + sh * sizeof(uint32_t));
+  w.scores = off;
+  off = align_up(off + sh * MP * d->group_size * sizeof(float));
+  w.keys = off;
+  off = align_up(off + sh * MP * sizeof(uint32_t));
+  w.parts = off;
+  off = align_up(off + sh * w.nsplit * d->group_size * (locks::kHeadDim + 2) * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+locks_status hip_status(hipError_t e) { return e == hipSuccess ? LOCKS_OK : LOCKS_ERR_HIP; }
+
+locks_status check_batch(int32_t S, int32_t MP, int32_t KB, int64_t nb) {
+  if (S < 0 || MP < 1 || KB < 2 || nb < 1) return LOCKS_ERR_INVALID_ARG;
+  if (MP > kMaxPagesSupported) return LOCKS_ERR_UNSUPPORTED;
+  if ((int64_t)MP * locks::kPage > INT32_MAX) return LOCKS_ERR_UNSUPPORTED;
+  return LOCKS_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* locks_status_string(locks_status s) {
+  switch (s) {
+    case LOCKS_OK: return "ok";
+    case LOCKS_ERR_INVALID_ARG: return "invalid argument";
+    case LOCKS_ERR_UNSUPPORTED: return "unsupported shape";
+    case LOCKS_ERR_WORKSPACE: return "workspace missing or too small";
+    case LOCKS_ERR_HIP: return "HIP launch or runtime error";
+  }
+  return "unknown status";
+}
+
+size_t locks_summary_slot_bytes(const locks_dims* d) {
+  if (check_dims(d) != LOCKS_OK) return 0;
+  return (size_t)locks::slot_layout(d->rank).payload;
+}
+
+size_t locks_summary_slot_stride(const locks_dims* d) {
+  if (check_dims(d) != LOCKS_OK) return 0;
+  return (size_t)locks::slot_layout(d->rank).stride;
+}
+
+size_t locks_workspace_bytes(const locks_dims* d, int32_t S, int32_t MP, int32_t KB) {
+  if (check_dims(d) != LOCKS_OK || check_batch(S, MP, KB, 1) != LOCKS_OK) return 0;
+  return carve(d, S, MP, KB).total;
+}
+
+locks_status locks_build(const locks_dims* d, const void* k_pool, int64_t nb,
+                         const int32_t* block_ids, int32_t n, void* summaries, hipStream_t st) {
+  locks_status e = check_dims(d);
+  if (e != LOCKS_OK) return e;
+  if (n < 0 || nb < 1) return LOCKS_ERR_INVALID_ARG;
+  if (n == 0) return LOCKS_OK;
+  if (!k_pool || !block_ids || !summaries) return LOCKS_ERR_INVALID_ARG;
+  if (!aligned16(k_pool) || !aligned16(summaries)) return LOCKS_ERR_INVALID_ARG;
+  return hip_status(locks::launch_build(d->rank, k_pool, nb, d->num_kv_heads, block_ids, n,
+                                        nullptr, nullptr, 0, summaries, st));
+}
+
+locks_status locks_build_filled(const locks_dims* d, const void* k_pool, int64_t nb,
+                                const int32_t* block_table, const int32_t* seq_lens, int32_t S,
+                                int32_t MP, void* summaries, hipStream_t st) {
+  locks_status e = check_dims(d);
+  if (e != LOCKS_OK) return e;
+  if (S < 0 || MP < 1 || nb < 1) return LOCKS_ERR_INVALID_ARG;
+  if (S == 0) return LOCKS_OK;
+  if (!k_pool || !block_table || !seq_lens || !summaries) return LOCKS_ERR_INVALID_ARG;
+  if (!aligned16(k_pool) || !aligned16(summaries)) return LOCKS_ERR_INVALID_ARG;
+  return hip_status(locks::launch_build(d->rank, k_pool, nb, d->num_kv_heads, nullptr, S,
+                                        block_table, seq_lens, MP, summaries, st));
+}
+
+locks_status locks_append_kv(const locks_dims* d, const void* k_new, const void* v_new,
+                             void* k_pool, void* v_pool, int64_t nb, const int32_t* block_table,
+                             const int32_t* seq_lens, int32_t S, int32_t MP, hipStream_t st) {
+  locks_status e = check_dims(d);
+  if (e != LOCKS_OK) return e;
+  if (S < 0 || MP < 1 || nb < 1) return LOCKS_ERR_INVALID_ARG;
+  if (S == 0) return LOCKS_OK;
+  if (!k_new || !v_new || !k_pool || !v_pool || !block_table || !seq_lens)
+    return LOCKS_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
+    return LOCKS_ERR_INVALID_ARG;
+  return hip_status(locks::launch_append(k_new, v_new, k_pool, v_pool, nb, block_table, seq_lens,
+                                         S, d->num_kv_heads, MP, st));
+}
+
+locks_status locks_score_select(const locks_dims* d, const void* q, const void* summaries,
+                                int64_t nb, const int32_t* block_table, const int32_t* seq_lens,
+                                const int32_t* budgets, int32_t S, int32_t MP, int32_t KB,
+                                int32_t* sel_pages, int32_t* sel_count, float* scores_out,
+                                void* workspace, size_t ws_bytes, hipStream_t st) {
+  locks_status e = check_dims(d);
+  if (e != LOCKS_OK) return e;
+  e = check_batch(S, MP, KB, nb);
+  if (e != LOCKS_OK) return e;
+  if (S == 0) return LOCKS_OK;
+  if (!q || !summaries || !block_table || !seq_lens || !budgets || !sel_pages || !sel_count)
+    return LOCKS_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(summaries)) return LOCKS_ERR_INVALID_ARG;
+  const Workspace w = carve(d, S, MP, KB);
+  if (!workspace || ws_bytes < w.total) return LOCKS_ERR_WORKSPACE;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* scores = scores_out ? scores_out : reinterpret_cast<float*>(ws + w.scores);
+  const int H = d->num_kv_heads, G = d->group_size;
+  hipError_t he = locks::launch_score(d->rank, G, q, summaries, block_table, seq_lens, scores, nb,
+                                      S, H, MP, scores_out ? 1 : 0, st);
+  if (he != hipSuccess) return LOCKS_ERR_HIP;
+  he = locks::launch_select(G, scores, seq_lens, budgets, sel_pages, sel_count,
+                            reinterpret_cast<uint32_t*>(ws + w.keys), S, H, MP, KB, st);
+  return hip_status(he);
+}
+
+locks_status locks_sparse_attn(const locks_dims* d, const void* q, const void* k_pool,
+                               const void* v_pool, int64_t nb, const int32_t* block_table,
+                               const int32_t* seq_lens, const int32_t* sel_pages,
+                               const int32_t* sel_count, int32_t S, int32_t MP, int32_t KB,
+                               float* out, float* lse_out, void* workspace, size_t ws_bytes,
+                               hipStream_t st) {
+  locks_status e = check_dims(d);
+  if (e != LOCKS_OK) return e;
+  e = check_batch(S, MP, KB, nb);
+  if (e != LOCKS_OK) return e;
+  if (S == 0) return LOCKS_OK;
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !sel_pages || !sel_count || !out)
+    return LOCKS_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool)) return LOCKS_ERR_INVALID_ARG;
+  const Workspace w = carve(d, S, MP, KB);
+  if (!workspace || ws_bytes < w.total) return LOCKS_ERR_WORKSPACE;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  return hip_status(locks::launch_attn(
+      d->group_size, q, k_pool, v_pool, block_table, seq_lens, sel_pages, sel_count,
+      reinterpret_cast<float*>(ws + w.parts), reinterpret_cast<uint32_t*>(ws + w.counters), out,
+      lse_out, nb, S, d->num_kv_heads, MP, KB, w.nsplit, kAttnPagesPerWave, st));
+}
+
+}  // extern "C"

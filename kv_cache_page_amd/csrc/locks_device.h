@@ -1,0 +1,81 @@
+// Internal device helpers of the LOCKS HIP library (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace locks {
+
+constexpr int kHeadDim = 128;
+constexpr int kPage = 16;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// Summary slot byte layout: [Vq r*d/2][Cq B*r][muq d][fp16 scales r+B+1][pad].
+struct SlotLayout {
+  int v, c, mu, sv, sc, smu, payload, stride;
+};
+
+__host__ __device__ constexpr SlotLayout slot_layout(int r) {
+  return SlotLayout{0,
+                    r * (kHeadDim / 2),
+                    r * (kHeadDim / 2) + kPage * r,
+                    r * (kHeadDim / 2) + kPage * r + kHeadDim,
+                    r * (kHeadDim / 2) + kPage * r + kHeadDim + 2 * r,
+                    r * (kHeadDim / 2) + kPage * r + kHeadDim + 2 * (r + kPage),
+                    r * (kHeadDim / 2) + kPage * r + kHeadDim + 2 * (r + kPage + 1),
+                    (r * (kHeadDim / 2) + kPage * r + kHeadDim + 2 * (r + kPage + 1) + 15) / 16 * 16};
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Lane exchanges. DPP quad permutations move data inside groups of 4 lanes;
+// ds_swizzle in bit-mask mode xors the lane id inside groups of 32 lanes.
+__device__ __forceinline__ float quad_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+// Sum over the 4 lanes of a quad. (a+b)+(c+d) is bit-identical on every lane.
+__device__ __forceinline__ float quad_sum(float v) {
+  v += quad_xor1(v);
+  return v + quad_xor2(v);
+}
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, quad_xor1(v));
+  return fmaxf(v, quad_xor2(v));
+}
+
+template <int M>
+__device__ __forceinline__ int swz_xor(int v) {
+  static_assert(M > 0 && M < 32, "xor mask");
+  return __builtin_amdgcn_ds_swizzle(v, 0x1F | (M << 10));
+}
+template <int M>
+__device__ __forceinline__ float swz_xor(float v) {
+  return __int_as_float(swz_xor<M>(__float_as_int(v)));
+}
+template <int M>
+__device__ __forceinline__ double swz_xor(double v) {
+  uint64_t u = __builtin_bit_cast(uint64_t, v);
+  int lo = swz_xor<M>((int)(uint32_t)u);
+  int hi = swz_xor<M>((int)(uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+__device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+
+// Order-preserving map of a float onto uint32 (larger float -> larger uint).
+__device__ __forceinline__ uint32_t float_to_ordered(float f) {
+  uint32_t b = __float_as_uint(f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+}  // namespace locks

@@ -1,0 +1,215 @@
+"""Thin ctypes binding of the LOCKS C ABI (include/locks.h).
+
+Argument marshalling only: tensors are passed as device pointers plus sizes,
+the current torch stream is passed as the HIP stream, and every computation
+runs in the HIP library. Importing this module raises if the library has not
+been built (python -m kv_cache_page_amd.build_lib).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblocks_hip.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(
+        f"LOCKS HIP library not found at {_LIB_PATH}; build it with "
+        "`python -m kv_cache_page_amd.build_lib` (hipcc, gfx950)")
+_lib = ctypes.CDLL(_LIB_PATH)
+
+OK = 0
+ERR_INVALID_ARG = -1
+ERR_UNSUPPORTED = -2
+ERR_WORKSPACE = -3
+ERR_HIP = -4
+
+ENTRY_POINTS = (
+    "locks_status_string", "locks_summary_slot_bytes", "locks_summary_slot_stride",
+    "locks_workspace_bytes", "locks_build", "locks_build_filled", "locks_append_kv",
+    "locks_score_select", "locks_sparse_attn",
+)
+
+
+class Dims(ctypes.Structure):
+    """locks_dims: head_dim, page_size, rank, num_kv_heads, group_size."""
+    _fields_ = [("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("rank", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("group_size", ctypes.c_int32)]
+
+    def __init__(self, num_kv_heads, group_size, rank=8, head_dim=128, page_size=16):
+        super().__init__(head_dim, page_size, rank, num_kv_heads, group_size)
+
+
+class LocksError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+_vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_pd = ctypes.POINTER(Dims)
+
+
+def _sig(name, res, args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = args
+    return f
+
+
+_status_string = _sig("locks_status_string", ctypes.c_char_p, [ctypes.c_int])
+_slot_bytes = _sig("locks_summary_slot_bytes", _sz, [_pd])
+_slot_stride = _sig("locks_summary_slot_stride", _sz, [_pd])
+_ws_bytes = _sig("locks_workspace_bytes", _sz, [_pd, _i32, _i32, _i32])
+_build = _sig("locks_build", ctypes.c_int, [_pd, _vp, _i64, _vp, _i32, _vp, _vp])
+_build_filled = _sig("locks_build_filled", ctypes.c_int,
+                     [_pd, _vp, _i64, _vp, _vp, _i32, _i32, _vp, _vp])
+_append = _sig("locks_append_kv", ctypes.c_int,
+               [_pd, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _i32, _i32, _vp])
+_score_select = _sig("locks_score_select", ctypes.c_int,
+                     [_pd, _vp, _vp, _i64, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp,
+                      _vp, _sz, _vp])
+_sparse_attn = _sig("locks_sparse_attn", ctypes.c_int,
+                    [_pd, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp,
+                     _vp, _sz, _vp])
+
+
+def status_string(status):
+    return _status_string(int(status)).decode()
+
+
+def slot_bytes(dims):
+    return int(_slot_bytes(ctypes.byref(dims)))
+
+
+def slot_stride(dims):
+    return int(_slot_stride(ctypes.byref(dims)))
+
+
+def workspace_bytes(dims, num_seqs, max_pages, max_budget):
+    return int(_ws_bytes(ctypes.byref(dims), num_seqs, max_pages, max_budget))
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _ptr(t, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream)
+
+
+def _check(status, where):
+    if status != OK:
+        raise LocksError(status, where)
+
+
+def alloc_summaries(dims, num_blocks, device):
+    """Zeroed summary pool uint8 [num_blocks][H][slot_stride]."""
+    return torch.zeros(num_blocks, dims.num_kv_heads, slot_stride(dims), dtype=torch.uint8,
+                       device=device)
+
+
+def alloc_workspace(dims, num_seqs, max_pages, max_budget, device):
+    """Zero-filled workspace of locks_workspace_bytes bytes."""
+    return torch.zeros(max(workspace_bytes(dims, num_seqs, max_pages, max_budget), 1),
+                       dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------
+# entry points (names follow include/locks.h)
+# ---------------------------------------------------------------------------
+
+def build(dims, k_pool, block_ids, summaries, stream=None):
+    """locks_build over the int32 block ids in `block_ids` (device)."""
+    st = _build(ctypes.byref(dims), _ptr(k_pool, torch.bfloat16, "k_pool"), k_pool.shape[0],
+                _ptr(block_ids, torch.int32, "block_ids"), block_ids.numel(),
+                _ptr(summaries, torch.uint8, "summaries"), _stream(stream))
+    _check(st, "locks_build")
+
+
+def build_filled(dims, k_pool, block_table, seq_lens, summaries, stream=None):
+    st = _build_filled(ctypes.byref(dims), _ptr(k_pool, torch.bfloat16, "k_pool"),
+                       k_pool.shape[0], _ptr(block_table, torch.int32, "block_table"),
+                       _ptr(seq_lens, torch.int32, "seq_lens"), seq_lens.numel(),
+                       block_table.shape[1], _ptr(summaries, torch.uint8, "summaries"),
+                       _stream(stream))
+    _check(st, "locks_build_filled")
+
+
+def append_kv(dims, k_new, v_new, k_pool, v_pool, block_table, seq_lens, stream=None):
+    st = _append(ctypes.byref(dims), _ptr(k_new, torch.bfloat16, "k_new"),
+                 _ptr(v_new, torch.bfloat16, "v_new"), _ptr(k_pool, torch.bfloat16, "k_pool"),
+                 _ptr(v_pool, torch.bfloat16, "v_pool"), k_pool.shape[0],
+                 _ptr(block_table, torch.int32, "block_table"),
+                 _ptr(seq_lens, torch.int32, "seq_lens"), seq_lens.numel(),
+                 block_table.shape[1], _stream(stream))
+    _check(st, "locks_append_kv")
+
+
+def score_select(dims, q, summaries, block_table, seq_lens, budgets, max_budget, sel_pages,
+                 sel_count, workspace, scores_out=None, num_blocks=None, stream=None):
+    nb = summaries.shape[0] if num_blocks is None else num_blocks
+    st = _score_select(ctypes.byref(dims), _ptr(q, torch.bfloat16, "q"),
+                       _ptr(summaries, torch.uint8, "summaries"), nb,
+                       _ptr(block_table, torch.int32, "block_table"),
+                       _ptr(seq_lens, torch.int32, "seq_lens"), _ptr(budgets, torch.int32, "budgets"),
+                       seq_lens.numel(), block_table.shape[1], max_budget,
+                       _ptr(sel_pages, torch.int32, "sel_pages"),
+                       _ptr(sel_count, torch.int32, "sel_count"),
+                       _ptr(scores_out, torch.float32, "scores_out"),
+                       _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                       _stream(stream))
+    _check(st, "locks_score_select")
+
+
+def sparse_attn(dims, q, k_pool, v_pool, block_table, seq_lens, sel_pages, sel_count, max_budget,
+                out, workspace, lse_out=None, stream=None):
+    st = _sparse_attn(ctypes.byref(dims), _ptr(q, torch.bfloat16, "q"),
+                      _ptr(k_pool, torch.bfloat16, "k_pool"), _ptr(v_pool, torch.bfloat16, "v_pool"),
+                      k_pool.shape[0], _ptr(block_table, torch.int32, "block_table"),
+                      _ptr(seq_lens, torch.int32, "seq_lens"),
+                      _ptr(sel_pages, torch.int32, "sel_pages"),
+                      _ptr(sel_count, torch.int32, "sel_count"), seq_lens.numel(),
+                      block_table.shape[1], max_budget, _ptr(out, torch.float32, "out"),
+                      _ptr(lse_out, torch.float32, "lse_out"),
+                      _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                      _stream(stream))
+    _check(st, "locks_sparse_attn")
+
+
+class Decoder:
+    """Holds the per-layer output buffers and workspace of one decode step and
+    calls score_select then sparse_attn on the current stream."""
+
+    def __init__(self, dims, num_seqs, max_pages, max_budget, device):
+        self.dims, self.max_budget = dims, max_budget
+        H, G = dims.num_kv_heads, dims.group_size
+        self.sel = torch.empty(num_seqs, H, max_budget, dtype=torch.int32, device=device)
+        self.cnt = torch.empty(num_seqs, H, dtype=torch.int32, device=device)
+        self.out = torch.empty(num_seqs, H * G, dims.head_dim, dtype=torch.float32, device=device)
+        self.lse = torch.empty(num_seqs, H * G, dtype=torch.float32, device=device)
+        self.ws = alloc_workspace(dims, num_seqs, max_pages, max_budget, device)
+
+    def step(self, q, summaries, k_pool, v_pool, block_table, seq_lens, budgets, stream=None,
+             scores_out=None):
+        score_select(self.dims, q, summaries, block_table, seq_lens, budgets, self.max_budget,
+                     self.sel, self.cnt, self.ws, scores_out=scores_out, stream=stream)
+        sparse_attn(self.dims, q, k_pool, v_pool, block_table, seq_lens, self.sel, self.cnt,
+                    self.max_budget, self.out, self.ws, lse_out=self.lse, stream=stream)
+        return self.out

@@ -1,0 +1,88 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry point
+that include/locks.h declares, reports the documented slot sizes, and rejects
+invalid arguments before enqueueing anything (no GPU needed: every call here
+returns from host validation)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from kv_cache_page_amd import locks as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "locks.h")).read()
+    return sorted(set(re.findall(r"\b(locks_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert set(names) == set(L.ENTRY_POINTS)
+    lib = ctypes.CDLL(L._LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_slot_sizes():
+    assert L.slot_bytes(L.Dims(8, 4, 8)) == 818 and L.slot_stride(L.Dims(8, 4, 8)) == 832
+    assert L.slot_bytes(L.Dims(8, 4, 4)) == 490 and L.slot_bytes(L.Dims(8, 4, 16)) == 1474
+    for r in range(1, 17):
+        assert L.slot_bytes(L.Dims(8, 4, r)) == 64 * r + 16 * r + 128 + 2 * (r + 17)
+        assert L.slot_stride(L.Dims(8, 4, r)) % 16 == 0
+
+
+def test_invalid_dims_rejected():
+    assert L.slot_bytes(L.Dims(8, 3, 8)) == 0            # group size 3 unsupported
+    assert L.slot_bytes(L.Dims(8, 4, 17)) == 0           # rank > page size
+    assert L.slot_bytes(L.Dims(8, 4, 8, head_dim=64)) == 0
+    assert L.slot_bytes(L.Dims(0, 4, 8)) == 0
+    assert L.workspace_bytes(L.Dims(8, 4, 8), 1, 8192, 1) == 0   # budget < 2
+    assert L.workspace_bytes(L.Dims(8, 4, 8), 1, 1 << 17, 128) == 0  # too many pages
+    assert L.workspace_bytes(L.Dims(8, 4, 8), 1, 8192, 128) > 0
+
+
+def test_status_codes_before_launch():
+    d = L.Dims(8, 4, 8)
+    bd = ctypes.byref(d)
+    bad = L.Dims(8, 3, 8)
+    fake = ctypes.c_void_p(256)  # never dereferenced: every call below fails validation
+    # build: negative count, null pool, bad dims, zero-sized pool
+    assert L._build(bd, fake, 16, fake, -1, fake, None) == L.ERR_INVALID_ARG
+    assert L._build(bd, None, 16, fake, 4, fake, None) == L.ERR_INVALID_ARG
+    assert L._build(ctypes.byref(bad), fake, 16, fake, 4, fake, None) == L.ERR_UNSUPPORTED
+    assert L._build(bd, fake, 0, fake, 4, fake, None) == L.ERR_INVALID_ARG
+    assert L._build(bd, fake, 16, fake, 0, fake, None) == L.OK          # nothing to do
+    assert L._build(bd, ctypes.c_void_p(258), 16, fake, 4, fake, None) == L.ERR_INVALID_ARG
+    # score/select: budget < 2, null outputs, undersized workspace
+    args = [fake, fake, 16, fake, fake, fake, 1, 8, 4, fake, fake, None, fake, 1 << 20, None]
+    a = list(args); a[8] = 1
+    assert L._score_select(bd, *a) == L.ERR_INVALID_ARG
+    a = list(args); a[9] = None
+    assert L._score_select(bd, *a) == L.ERR_INVALID_ARG
+    a = list(args); a[13] = 16
+    assert L._score_select(bd, *a) == L.ERR_WORKSPACE
+    a = list(args); a[12] = None
+    assert L._score_select(bd, *a) == L.ERR_WORKSPACE
+    a = list(args); a[6] = -1
+    assert L._score_select(bd, *a) == L.ERR_INVALID_ARG
+    a = list(args); a[6] = 0
+    assert L._score_select(bd, *a) == L.OK                                # empty batch
+    # attention: null out, undersized workspace
+    aargs = [fake, fake, fake, 16, fake, fake, fake, fake, 1, 8, 4, fake, None, fake, 1 << 20, None]
+    a = list(aargs); a[11] = None
+    assert L._sparse_attn(bd, *a) == L.ERR_INVALID_ARG
+    a = list(aargs); a[14] = 8
+    assert L._sparse_attn(bd, *a) == L.ERR_WORKSPACE
+    # append / build_filled
+    assert L._append(bd, None, fake, fake, fake, 16, fake, fake, 1, 8, None) == L.ERR_INVALID_ARG
+    assert L._build_filled(bd, fake, 16, fake, fake, -2, 8, fake, None) == L.ERR_INVALID_ARG
+
+
+def test_status_strings():
+    for s in (L.OK, L.ERR_INVALID_ARG, L.ERR_UNSUPPORTED, L.ERR_WORKSPACE, L.ERR_HIP):
+        assert L.status_string(s) and L.status_string(s) != "unknown status"
+    with pytest.raises(L.LocksError):
+        L._check(L.ERR_WORKSPACE, "x")

@@ -1,0 +1,354 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Tolerances (scores 1e-3 abs; selections exact except near-ties with a key gap
+below 1e-5 in log-share units; attention 1e-2 relative L2; GPU-built codes
+within +-1 LSB on at most 0.1% of entries) are written in each test.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import locks_oracle as O
+from tests import locks_harness as Hh
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def L():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    from kv_cache_page_amd import locks
+    return locks
+
+
+def _to_dev(b):
+    return synth.DecodeBatch(
+        k_pool=b.k_pool.to(DEV), v_pool=b.v_pool.to(DEV), q=b.q.to(DEV),
+        block_table=b.block_table.to(DEV), seq_lens=b.seq_lens.to(DEV), budgets=b.budgets.to(DEV),
+        needles=b.needles, H=b.H, G=b.G)
+
+
+def _run_decode(L, dims, bd, summ_dev, max_budget, scores=True):
+    S, H, G = bd.num_seqs, bd.H, bd.G
+    MP = bd.max_pages
+    sel = torch.full((S, H, max_budget), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.full((S, H), -7, dtype=torch.int32, device=DEV)
+    sc = torch.full((S, H, MP, G), 123.0, dtype=torch.float32, device=DEV) if scores else None
+    out = torch.full((S, H * G, 128), 7.0, dtype=torch.float32, device=DEV)
+    lse = torch.full((S, H * G), 7.0, dtype=torch.float32, device=DEV)
+    ws = L.alloc_workspace(dims, S, MP, max_budget, DEV)
+    L.score_select(dims, bd.q, summ_dev, bd.block_table, bd.seq_lens, bd.budgets, max_budget, sel,
+                   cnt, ws, scores_out=sc)
+    L.sparse_attn(dims, bd.q, bd.k_pool, bd.v_pool, bd.block_table, bd.seq_lens, sel, cnt,
+                  max_budget, out, ws, lse_out=lse)
+    torch.cuda.synchronize()
+    return dict(sel=sel.cpu().numpy(), cnt=cnt.cpu().numpy(),
+                scores=None if sc is None else sc.cpu().numpy(), out=out.cpu().numpy(),
+                lse=lse.cpu().numpy())
+
+
+def _check_against_oracle(b, summ, res, r, max_budget, heads=None, score_tol=1e-3):
+    """Compare one decode step (every or the listed (seq, head)) with the
+    oracle fed the same summaries. Returns (max score error, mismatched pages,
+    worst attention rel-L2)."""
+    G = b.G
+    worst_s, nmis, worst_o = 0.0, 0, 0.0
+    pairs = heads if heads is not None else [(s, h) for s in range(b.num_seqs) for h in range(b.H)]
+    for (s, h) in pairs:
+        Lq = int(b.seq_lens[s])
+        P, F = (Lq + 15) // 16, Lq // 16
+        ora = Hh.oracle_head(b.q, b.k_pool, b.v_pool, b.block_table, b.seq_lens, b.budgets, summ,
+                             s, h, G, r)
+        if res["scores"] is not None and F:
+            d = np.abs(res["scores"][s, h, :F] - ora["scores"])
+            worst_s = max(worst_s, float(d.max()))
+            assert d.max() <= score_tol, (s, h, float(d.max()))
+            assert np.isnan(res["scores"][s, h, F:]).all()
+        n = int(res["cnt"][s, h])
+        gsel = [int(j) for j in res["sel"][s, h, :n]]
+        assert (res["sel"][s, h, n:] == -1).all()
+        assert gsel == sorted(gsel) and len(set(gsel)) == n
+        k = min(max(int(b.budgets[s]), 2), max_budget)
+        assert n == (min(k, P) if P else 0)
+        if P:
+            nmis += Hh.selection_mismatch(gsel, ora["sel"], ora["key"], P)
+        # attention over the GPU's own selection against the oracle's softmax
+        Kp, Vp = Hh.head_pages(b.k_pool, b.v_pool, b.block_table, Lq, s, h)
+        qq = Hh.np64(b.q[s, h * G:(h + 1) * G])
+        if gsel:
+            toks_k = np.concatenate([Kp[j, :(16 if j < P - 1 else Lq - 16 * (P - 1))] for j in gsel])
+            toks_v = np.concatenate([Vp[j, :(16 if j < P - 1 else Lq - 16 * (P - 1))] for j in gsel])
+            o_ref, lse_ref = O.attend(qq, toks_k, toks_v)
+            e = Hh.rel_l2(res["out"][s, h * G:(h + 1) * G], o_ref)
+            worst_o = max(worst_o, e)
+            assert e <= 1e-2, (s, h, e)
+            np.testing.assert_allclose(res["lse"][s, h * G:(h + 1) * G], lse_ref, atol=1e-3)
+        else:
+            assert (res["out"][s, h * G:(h + 1) * G] == 0).all()
+    return worst_s, nmis, worst_o
+
+
+# ---------------------------------------------------------------------------
+# score + select + attention from oracle-built summaries
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,r", [("tiny", 8), ("ctx32k", 8), ("tiny", 4), ("tiny", 16)])
+def test_decode_from_oracle_summaries(L, name, r):
+    _say(f"[gpu] decode from oracle summaries: {name} r={r}")
+    b = synth.config_batch(name)
+    summ = Hh.oracle_summaries(b.k_pool, b.block_table, b.seq_lens, b.H, r, b.num_blocks)
+    dims = L.Dims(b.H, b.G, r)
+    bd = _to_dev(b)
+    kb = int(b.budgets.max())
+    res = _run_decode(L, dims, bd, torch.from_numpy(summ).to(DEV), kb)
+    ws, nmis, wo = _check_against_oracle(b, summ, res, r, kb)
+    _say(f"    max |score err| {ws:.2e}, near-tie page swaps {nmis}, worst attn rel-L2 {wo:.2e}")
+    # the exact-LSE selector keeps the needles; report LOCKS's own retention
+    kept = sum(1 for (s, h, j, _) in b.needles if j in set(res["sel"][s, h, :res["cnt"][s, h]]))
+    _say(f"    needle pages kept by the GPU selection: {kept}/{len(b.needles)}")
+
+
+@pytest.mark.parametrize("G", [1, 2])
+def test_group_sizes(L, G):
+    _say(f"[gpu] group size {G}")
+    b = synth.make_decode_batch([70 * 16 + 3, 33 * 16], 2, G, [9, 40], seed=40 + G)
+    summ = Hh.oracle_summaries(b.k_pool, b.block_table, b.seq_lens, b.H, 8, b.num_blocks)
+    dims = L.Dims(b.H, G, 8)
+    res = _run_decode(L, dims, _to_dev(b), torch.from_numpy(summ).to(DEV), 40)
+    _check_against_oracle(b, summ, res, 8, 40)
+
+
+def test_ragged_edges(L):
+    """Lengths around page boundaries (1, 16, 17 tokens ...), budgets 2..P+,
+    shuffled blocks with spare blocks in the pool."""
+    _say("[gpu] ragged edge cases")
+    lens = [1, 15, 16, 17, 32, 33, 48, 40 * 16, 40 * 16 + 1, 300 * 16 + 9, 257 * 16]
+    budgets = [2, 2, 3, 2, 2, 5, 2, 2, 7, 64, 1000]
+    b = synth.make_decode_batch(lens, 3, 4, budgets, seed=50, extra_blocks=37)
+    summ = Hh.oracle_summaries(b.k_pool, b.block_table, b.seq_lens, b.H, 8, b.num_blocks)
+    dims = L.Dims(b.H, b.G, 8)
+    res = _run_decode(L, dims, _to_dev(b), torch.from_numpy(summ).to(DEV), 300)
+    _check_against_oracle(b, summ, res, 8, 300)
+
+
+def test_select_all_is_dense(L):
+    _say("[gpu] budget >= pages gives dense attention")
+    b = synth.make_decode_batch([61 * 16 + 11], 2, 4, [64], seed=60)
+    summ = Hh.oracle_summaries(b.k_pool, b.block_table, b.seq_lens, b.H, 8, b.num_blocks)
+    res = _run_decode(L, L.Dims(2, 4, 8), _to_dev(b), torch.from_numpy(summ).to(DEV), 64)
+    Lq = int(b.seq_lens[0])
+    for h in range(2):
+        assert list(res["sel"][0, h, :res["cnt"][0, h]]) == list(range(62))
+        Kp, Vp = Hh.head_pages(b.k_pool, b.v_pool, b.block_table, Lq, 0, h)
+        q = Hh.np64(b.q[0, 4 * h:4 * h + 4])
+        dense, _ = O.attend(q, Kp.reshape(-1, 128)[:Lq], Vp.reshape(-1, 128)[:Lq])
+        assert Hh.rel_l2(res["out"][0, 4 * h:4 * h + 4], dense) <= 1e-2
+
+
+def test_invalid_block_ids_are_skipped(L):
+    _say("[gpu] out-of-range block ids")
+    b = synth.make_decode_batch([50 * 16], 1, 4, [10], seed=70)
+    summ = Hh.oracle_summaries(b.k_pool, b.block_table, b.seq_lens, 1, 8, b.num_blocks)
+    bd = _to_dev(b)
+    bd.block_table[0, 7] = -1
+    bd.block_table[0, 9] = b.num_blocks + 5
+    res = _run_decode(L, L.Dims(1, 4, 8), bd, torch.from_numpy(summ).to(DEV), 10)
+    assert res["scores"][0, 0, 7].max() == -np.inf and res["scores"][0, 0, 9].max() == -np.inf
+    sel = set(res["sel"][0, 0, :res["cnt"][0, 0]].tolist())
+    assert 7 not in sel and 9 not in sel
+
+
+def test_deterministic(L):
+    _say("[gpu] bit-identical reruns")
+    b = synth.config_batch("ctx32k")
+    summ = torch.from_numpy(Hh.oracle_summaries(b.k_pool, b.block_table, b.seq_lens, b.H, 8,
+                                                b.num_blocks)).to(DEV)
+    bd = _to_dev(b)
+    r1 = _run_decode(L, L.Dims(8, 4, 8), bd, summ, 64)
+    r2 = _run_decode(L, L.Dims(8, 4, 8), bd, summ, 64)
+    for k in r1:
+        assert np.array_equal(r1[k], r2[k], equal_nan=True), k
+
+
+# ---------------------------------------------------------------------------
+# build
+# ---------------------------------------------------------------------------
+
+def _compare_codes(gpu_slots, keys, r):
+    """GPU slots vs the oracle's for the same keys. Returns (fraction of code
+    entries that differ, pages excluded as near-degenerate, columns excluded
+    as sign-ambiguous)."""
+    ora_slots, summ, _ = O.build_slots(keys, r)
+    g = O.unpack_slots(gpu_slots, r)
+    o = O.unpack_slots(ora_slots, r)
+    flag = Hh.gap_flags(summ["lam"], r)
+    amb = Hh.sign_ambiguous(summ["V"]) & summ["active"]
+    keep = ~flag
+    colmask = keep[:, None] & ~amb                                  # (n, r)
+    dv = np.abs(g["Vq"] - o["Vq"])[:, :, :]                         # (n, d, r)
+    dv = np.where(colmask[:, None, :], dv, 0)
+    dc = np.abs(g["Cq"] - o["Cq"])                                  # (n, B, r)
+    dc = np.where(colmask[:, None, :], dc, 0)
+    dm = np.abs(g["muq"] - o["muq"])[keep]
+    assert dv.max() <= 1 and dc.max() <= 1 and (dm.max() if dm.size else 0) <= 1, \
+        (dv.max(), dc.max(), dm.max() if dm.size else 0)
+    n_entries = colmask.sum() * (128 + 16) + keep.sum() * 128
+    frac = (np.count_nonzero(dv) + np.count_nonzero(dc) + np.count_nonzero(dm)) / max(n_entries, 1)
+    # scales of comparable pages agree to fp16 rounding of the same absmax
+    for nm in ("sV", "sC"):
+        a = g[nm][keep].astype(np.float64)
+        c = o[nm][keep].astype(np.float64)
+        np.testing.assert_allclose(a, c, rtol=2e-3, atol=1e-7)
+    assert np.array_equal(g["smu"], o["smu"])
+    return frac, int(flag.sum()), int(amb.sum())
+
+
+@pytest.mark.parametrize("r", [4, 8, 16])
+def test_build_codes(L, r):
+    n = 8192
+    _say(f"[gpu] build parity r={r} n={n}")
+    keys = synth.random_pages(n, seed=100 + r)                       # bf16 [n][16][128] on CPU
+    pool = keys.view(n, 1, 16, 128).contiguous().to(DEV)
+    dims = L.Dims(1, 4, r)
+    summ = L.alloc_summaries(dims, n, DEV)
+    ids = torch.arange(n, dtype=torch.int32, device=DEV)
+    L.build(dims, pool, ids, summ)
+    torch.cuda.synchronize()
+    frac, nflag, namb = _compare_codes(summ[:, 0].cpu().numpy(), keys.double().numpy(), r)
+    _say(f"    differing code entries {frac:.2e}; near-degenerate pages {nflag}; "
+         f"sign-ambiguous columns {namb}")
+    assert frac <= 1e-3
+
+
+def test_build_degenerate_pages(L):
+    _say("[gpu] build of degenerate pages")
+    n = 8
+    k = torch.zeros(n, 16, 128)
+    k[1] = 0.375                                          # all keys equal
+    k[2, :, :5] = torch.randn(16, 5)                       # rank <= 5
+    k[3] = torch.randn(1, 128)                             # equal keys, random vector
+    k[4, 0] = 3.0                                          # one outlier token
+    k[5] = torch.randn(16, 128) * 1e-3
+    k[6] = torch.randn(16, 128) * 300
+    k[7, ::2] = 1.0                                        # two distinct keys
+    keys = k.to(torch.bfloat16)
+    for r in (1, 8, 16):
+        dims = L.Dims(1, 4, r)
+        summ = L.alloc_summaries(dims, n, DEV)
+        L.build(dims, keys.view(n, 1, 16, 128).contiguous().to(DEV),
+                torch.arange(n, dtype=torch.int32, device=DEV), summ)
+        torch.cuda.synchronize()
+        got = summ[:, 0].cpu().numpy()
+        ora, s, _ = O.build_slots(keys.double().numpy(), r)
+        for p in (0, 1, 3):                               # exactly degenerate: byte-identical
+            assert np.array_equal(got[p], ora[p]), (r, p)
+        g = O.unpack_slots(got, r)
+        assert not np.isnan(g["sV"].astype(np.float64)).any()
+
+
+def test_build_list_and_filled(L):
+    """locks_build over a shuffled id list (invalid ids skipped), and
+    locks_build_filled picking the page each sequence has just filled."""
+    _say("[gpu] build id list / filled pages")
+    b = synth.make_decode_batch([10 * 16, 7 * 16 + 3, 4 * 16], 2, 4, [4, 4, 4], seed=80,
+                                extra_blocks=5)
+    dims = L.Dims(2, 4, 8)
+    bd = _to_dev(b)
+    summ = L.alloc_summaries(dims, b.num_blocks, DEV)
+    ids = torch.tensor([3, -1, 5, b.num_blocks, 0], dtype=torch.int32, device=DEV)
+    L.build(dims, bd.k_pool, ids, summ)
+    summ2 = L.alloc_summaries(dims, b.num_blocks, DEV)
+    L.build_filled(dims, bd.k_pool, bd.block_table, bd.seq_lens, summ2)
+    torch.cuda.synchronize()
+    got, got2 = summ.cpu().numpy(), summ2.cpu().numpy()
+    for blk in (3, 5, 0):
+        for h in range(2):
+            ora, _, _ = O.build_slots(Hh.np64(b.k_pool[blk, h])[None], 8)
+            assert np.count_nonzero(got[blk, h] != ora[0]) <= 4
+    built = {int(b.block_table[0, 9]), int(b.block_table[2, 3])}   # seqs 0 and 2 just filled
+    for blk in range(b.num_blocks):
+        for h in range(2):
+            if blk in built:
+                ora, _, _ = O.build_slots(Hh.np64(b.k_pool[blk, h])[None], 8)
+                assert np.count_nonzero(got2[blk, h] != ora[0]) <= 4
+            else:
+                assert not got2[blk, h].any()
+
+
+def test_append(L):
+    _say("[gpu] append one token per sequence")
+    b = synth.make_decode_batch([5 * 16 + 2, 3 * 16, 1], 2, 4, [4, 4, 4], seed=90)
+    dims = L.Dims(2, 4, 8)
+    bd = _to_dev(b)
+    kn = torch.randn(3, 2, 128, device=DEV).to(torch.bfloat16)
+    vn = torch.randn(3, 2, 128, device=DEV).to(torch.bfloat16)
+    kp0 = bd.k_pool.clone()
+    L.append_kv(dims, kn, vn, bd.k_pool, bd.v_pool, bd.block_table, bd.seq_lens)
+    torch.cuda.synchronize()
+    for s, Lq in enumerate(b.seq_lens.tolist()):
+        blk = int(b.block_table[s, (Lq - 1) // 16])
+        assert torch.equal(bd.k_pool[blk, :, (Lq - 1) % 16], kn[s])
+        assert torch.equal(bd.v_pool[blk, :, (Lq - 1) % 16], vn[s])
+        kp0[blk, :, (Lq - 1) % 16] = kn[s]
+    assert torch.equal(kp0, bd.k_pool)
+
+
+# ---------------------------------------------------------------------------
+# end to end and full size
+# ---------------------------------------------------------------------------
+
+def test_end_to_end_gpu_build(L):
+    """GPU build -> GPU score/select -> GPU attention, against the oracle run
+    from its own summaries of the same keys."""
+    _say("[gpu] end to end with GPU-built summaries (ctx32k)")
+    b = synth.config_batch("ctx32k")
+    dims = L.Dims(b.H, b.G, 8)
+    bd = _to_dev(b)
+    summ_dev = L.alloc_summaries(dims, b.num_blocks, DEV)
+    F = int(b.seq_lens[0]) // 16
+    L.build(dims, bd.k_pool, bd.block_table[0, :F].contiguous(), summ_dev)
+    res = _run_decode(L, dims, bd, summ_dev, 64)
+    summ = Hh.oracle_summaries(b.k_pool, b.block_table, b.seq_lens, b.H, 8, b.num_blocks)
+    ws, nmis, wo = _check_against_oracle(b, summ, res, 8, 64)
+    _say(f"    max |score err| {ws:.2e}, near-tie swaps {nmis}, worst attn rel-L2 {wo:.2e}")
+
+
+def test_full_size_128k_layer(L):
+    """One layer of the 128K-token, 8-KV-head workload at its real shape,
+    launched as the benchmark launches it: GPU build of all 65536 pages,
+    score/select from oracle-built summaries of every head (full comparison),
+    attention checked on every head."""
+    _say("[gpu] full-size 128K layer")
+    b = synth.config_batch("ctx128k", device=DEV)
+    dims = L.Dims(b.H, b.G, 8)
+    summ_gpu = L.alloc_summaries(dims, b.num_blocks, DEV)
+    L.build(dims, b.k_pool, b.block_table[0].contiguous(), summ_gpu)
+    torch.cuda.synchronize()
+    bc = synth.DecodeBatch(k_pool=b.k_pool.cpu(), v_pool=b.v_pool.cpu(), q=b.q.cpu(),
+                           block_table=b.block_table.cpu(), seq_lens=b.seq_lens.cpu(),
+                           budgets=b.budgets.cpu(), needles=b.needles, H=b.H, G=b.G)
+    _say("    oracle build of 65536 pages")
+    summ = Hh.oracle_summaries(bc.k_pool, bc.block_table, bc.seq_lens, b.H, 8, b.num_blocks)
+    # sampled build parity: 2 heads x 8192 pages
+    for h in (0, 5):
+        blocks = bc.block_table[0].long()
+        frac, nflag, namb = _compare_codes(summ_gpu[blocks.to(DEV), h].cpu().numpy(),
+                                           bc.k_pool[blocks, h].double().numpy(), 8)
+        _say(f"    head {h}: differing codes {frac:.2e}, flagged pages {nflag}, ambiguous cols {namb}")
+        assert frac <= 1e-3
+    res = _run_decode(L, dims, b, torch.from_numpy(summ).to(DEV), 128)
+    ws, nmis, wo = _check_against_oracle(bc, summ, res, 8, 128)
+    _say(f"    max |score err| {ws:.2e}, near-tie swaps {nmis}, worst attn rel-L2 {wo:.2e}")
+    kept = sum(1 for (s, h, j, _) in b.needles if j in set(res["sel"][s, h, :res["cnt"][s, h]]))
+    _say(f"    needle pages kept: {kept}/{len(b.needles)}")
