@@ -179,6 +179,31 @@ locks_status locks_score_select(const locks_dims* dims, const void* q, const voi
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * locks_score_pages -- the scoring half of locks_score_select ([N] §4.2
+ * eq. 4): writes s_hat for every full page j < F of every (sequence, KV head)
+ * into scores float [num_seqs][num_kv_heads][max_pages][group_size]
+ * (entries j >= F are left untouched; an out-of-range block gives -inf).
+ * Needs no workspace. Errors as for locks_score_select.
+ */
+locks_status locks_score_pages(const locks_dims* dims, const void* q, const void* summaries,
+                               int64_t num_blocks, const int32_t* block_table,
+                               const int32_t* seq_lens, int32_t num_seqs, int32_t max_pages,
+                               float* scores, hipStream_t stream);
+
+/*
+ * locks_select_pages -- the selection half of locks_score_select ([N] §4.2
+ * eq. 5 and §4.4 Algorithm 2): from scores laid out as locks_score_pages
+ * writes them, computes the group-averaged shares and writes sel_pages /
+ * sel_count exactly as locks_score_select does. Uses the workspace.
+ * Errors as for locks_score_select.
+ */
+locks_status locks_select_pages(const locks_dims* dims, const float* scores,
+                                const int32_t* seq_lens, const int32_t* budgets,
+                                int32_t num_seqs, int32_t max_pages, int32_t max_budget,
+                                int32_t* sel_pages, int32_t* sel_count, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/*
  * locks_sparse_attn -- [N] §4.4 Algorithm 2 last steps and §3.1 eq. 1: for
  * every query head g of KV head h, softmax attention over the tokens of the
  * selected pages only, renormalised over them:

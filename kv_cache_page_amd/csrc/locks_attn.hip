@@ -23,6 +23,7 @@
 namespace locks {
 
 constexpr int kAttnWaves = 4;
+constexpr int kAttnMaxSplits = 128;  // host raises pages per wave to stay within this
 
 template <int G>
 __global__ __launch_bounds__(256) void attn_kernel(
@@ -36,6 +37,8 @@ __global__ __launch_bounds__(256) void attn_kernel(
   __shared__ float sh_acc[kAttnWaves][G][kHeadDim];
   __shared__ float sh_ml[kAttnWaves][G][2];
   __shared__ int sh_last;
+  __shared__ float sh_f[kAttnMaxSplits * G];  // merge factors of the splits
+  __shared__ float sh_M[2 * G];               // global max and total sum per query
 
   const int s = blockIdx.z, h = blockIdx.y, x = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -53,7 +56,7 @@ __global__ __launch_bounds__(256) void attn_kernel(
     }
     return;
   }
-  if (x >= nact) return;
+  if (x >= nact || nact > kAttnMaxSplits) return;
 
   // ---- query registers for the QK role: dims [32c, 32c+32) as bf16 pairs
   const int t_qk = lane >> 2, c_qk = lane & 3;
@@ -209,23 +212,46 @@ __global__ __launch_bounds__(256) void attn_kernel(
   __syncthreads();
   if (!sh_last) return;
   __threadfence();
+  // Merge the nact split partials in split order. Per-split maxima and sums
+  // go through LDS first so that the accumulator loads below are independent
+  // of each other and can all be in flight at once.
   const float* parts = part + sh_idx * nsplit * kPart;
+  for (int i = tid; i < nact * G; i += blockDim.x) {
+    const int y = i / G, g = i % G;
+    sh_f[i] = __builtin_nontemporal_load(parts + y * kPart + g * (kHeadDim + 2) + kHeadDim);
+  }
+  __syncthreads();
+  if (tid < G) {
+    float M = -__builtin_inff();
+    for (int y = 0; y < nact; ++y) M = fmaxf(M, sh_f[y * G + tid]);
+    sh_M[tid] = M;
+  }
+  __syncthreads();
+  for (int i = tid; i < nact * G; i += blockDim.x) {
+    const int g = i % G;
+    const float M = sh_M[g];
+    sh_f[i] = (M == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(sh_f[i] - M);
+  }
+  __syncthreads();
+  if (tid < G) {
+    float Lsum = 0.f;
+    for (int y = 0; y < nact; ++y)
+      Lsum += sh_f[y * G + tid] *
+              __builtin_nontemporal_load(parts + y * kPart + tid * (kHeadDim + 2) + kHeadDim + 1);
+    sh_M[G + tid] = Lsum;
+  }
+  __syncthreads();
   for (int i = tid; i < G * kHeadDim; i += blockDim.x) {
     const int g = i / kHeadDim, d = i % kHeadDim;
-    float M = -__builtin_inff();
+    float a = 0.f;
+#pragma unroll 8
     for (int y = 0; y < nact; ++y)
-      M = fmaxf(M, __builtin_nontemporal_load(parts + y * kPart + g * (kHeadDim + 2) + kHeadDim));
-    float a = 0.f, L = 0.f;
-    for (int y = 0; y < nact; ++y) {
-      const float* py = parts + y * kPart + g * (kHeadDim + 2);
-      const float My = __builtin_nontemporal_load(py + kHeadDim);
-      const float f = (M == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(My - M);
-      a += f * __builtin_nontemporal_load(py + d);
-      L += f * __builtin_nontemporal_load(py + kHeadDim + 1);
-    }
-    o_base[g * kHeadDim + d] = (L > 0.f) ? a / L : 0.f;
+      a += sh_f[y * G + g] * __builtin_nontemporal_load(parts + y * kPart + g * (kHeadDim + 2) + d);
+    const float Lsum = sh_M[G + g];
+    o_base[g * kHeadDim + d] = (Lsum > 0.f) ? a / Lsum : 0.f;
     if (lse_out && d == 0)
-      lse_out[sh_idx * G + g] = (L > 0.f) ? (M + __builtin_amdgcn_logf(L)) * kLn2 : -__builtin_inff();
+      lse_out[sh_idx * G + g] =
+          (Lsum > 0.f) ? (sh_M[g] + __builtin_amdgcn_logf(Lsum)) * kLn2 : -__builtin_inff();
   }
   if (tid == 0) counters[sh_idx] = 0u;
 }

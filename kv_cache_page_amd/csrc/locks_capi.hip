@@ -30,8 +30,14 @@ hipError_t launch_append(const void* knew, const void* vnew, void* kpool, void* 
 namespace {
 
 constexpr int kMaxPagesSupported = 65536;  // select keeps one 64-bit page mask per thread
-constexpr int kAttnPagesPerWave = 1;
 constexpr int kAttnWaves = 4;
+constexpr int kAttnMaxSplits = 128;
+
+// Pages each attention wave streams: one, unless the budget would need more
+// than kAttnMaxSplits workgroups per (sequence, KV head).
+int attn_pages_per_wave(int32_t KB) {
+  return (KB + kAttnWaves * kAttnMaxSplits - 1) / (kAttnWaves * kAttnMaxSplits);
+}
 
 locks_status check_dims(const locks_dims* d) {
   if (!d) return LOCKS_ERR_INVALID_ARG;
@@ -54,7 +60,7 @@ struct Workspace {
 Workspace carve(const locks_dims* d, int32_t S, int32_t MP, int32_t KB) {
   Workspace w{};
   const size_t sh = (size_t)S * d->num_kv_heads;
-  const int per_wg = kAttnWaves * kAttnPagesPerWave;
+  const int per_wg = kAttnWaves * attn_pages_per_wave(KB);
   w.nsplit = (KB + per_wg - 1) / per_wg;
   size_t off = 0;
   w.counters = off;
@@ -176,6 +182,38 @@ locks_status locks_score_select(const locks_dims* d, const void* q, const void* 
   return hip_status(he);
 }
 
+locks_status locks_score_pages(const locks_dims* d, const void* q, const void* summaries,
+                               int64_t nb, const int32_t* block_table, const int32_t* seq_lens,
+                               int32_t S, int32_t MP, float* scores, hipStream_t st) {
+  locks_status e = check_dims(d);
+  if (e != LOCKS_OK) return e;
+  e = check_batch(S, MP, 2, nb);
+  if (e != LOCKS_OK) return e;
+  if (S == 0) return LOCKS_OK;
+  if (!q || !summaries || !block_table || !seq_lens || !scores) return LOCKS_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(summaries)) return LOCKS_ERR_INVALID_ARG;
+  return hip_status(locks::launch_score(d->rank, d->group_size, q, summaries, block_table,
+                                        seq_lens, scores, nb, S, d->num_kv_heads, MP, 0, st));
+}
+
+locks_status locks_select_pages(const locks_dims* d, const float* scores, const int32_t* seq_lens,
+                                const int32_t* budgets, int32_t S, int32_t MP, int32_t KB,
+                                int32_t* sel_pages, int32_t* sel_count, void* workspace,
+                                size_t ws_bytes, hipStream_t st) {
+  locks_status e = check_dims(d);
+  if (e != LOCKS_OK) return e;
+  e = check_batch(S, MP, KB, 1);
+  if (e != LOCKS_OK) return e;
+  if (S == 0) return LOCKS_OK;
+  if (!scores || !seq_lens || !budgets || !sel_pages || !sel_count) return LOCKS_ERR_INVALID_ARG;
+  const Workspace w = carve(d, S, MP, KB);
+  if (!workspace || ws_bytes < w.total) return LOCKS_ERR_WORKSPACE;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  return hip_status(locks::launch_select(d->group_size, scores, seq_lens, budgets, sel_pages,
+                                         sel_count, reinterpret_cast<uint32_t*>(ws + w.keys), S,
+                                         d->num_kv_heads, MP, KB, st));
+}
+
 locks_status locks_sparse_attn(const locks_dims* d, const void* q, const void* k_pool,
                                const void* v_pool, int64_t nb, const int32_t* block_table,
                                const int32_t* seq_lens, const int32_t* sel_pages,
@@ -196,7 +234,7 @@ locks_status locks_sparse_attn(const locks_dims* d, const void* q, const void* k
   return hip_status(locks::launch_attn(
       d->group_size, q, k_pool, v_pool, block_table, seq_lens, sel_pages, sel_count,
       reinterpret_cast<float*>(ws + w.parts), reinterpret_cast<uint32_t*>(ws + w.counters), out,
-      lse_out, nb, S, d->num_kv_heads, MP, KB, w.nsplit, kAttnPagesPerWave, st));
+      lse_out, nb, S, d->num_kv_heads, MP, KB, w.nsplit, attn_pages_per_wave(KB), st));
 }
 
 }  // extern "C"

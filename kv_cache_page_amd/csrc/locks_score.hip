@@ -266,18 +266,44 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t digit, bool ac
 // ---------------------------------------------------------------------------
 // select: one 1024-thread workgroup per (sequence, KV head)
 // ---------------------------------------------------------------------------
+constexpr int kSelectThreads = 1024;
+constexpr int kSelectLdsPages = 12288;  // keys of up to this many pages live in LDS (48 KB)
+
 template <int G>
-__global__ __launch_bounds__(1024) void select_kernel(
+__device__ __forceinline__ void load_scores(const float* p, float (&v)[G]) {
+  if constexpr (G == 4) {
+    const float4 x = *reinterpret_cast<const float4*>(p);
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  } else if constexpr (G == 2) {
+    const float2 x = *reinterpret_cast<const float2*>(p);
+    v[0] = x.x; v[1] = x.y;
+  } else {
+    v[0] = p[0];
+  }
+}
+
+// Online (max, sum-exp) merge: (m, s) absorbs (m2, s2).
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  const float M = fmaxf(m, m2);
+  if (M == -__builtin_inff()) return;
+  s = s * __expf(m - M) + s2 * __expf(m2 - M);
+  m = M;
+}
+
+template <int G, bool kLdsKeys>
+__global__ __launch_bounds__(kSelectThreads) void select_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ budgets, int32_t* __restrict__ sel_pages,
     int32_t* __restrict__ sel_count, uint32_t* __restrict__ keybuf, int H, int MP,
     int max_budget) {
+  extern __shared__ uint32_t sh_keys[];
   __shared__ uint32_t hist[256];
-  __shared__ float red[16][G];
+  __shared__ float red_m[16][G], red_s[16][G];
   __shared__ int sh_waves[16];
   __shared__ int sh_pick[2];
   const int s = blockIdx.y, h = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nthr = blockDim.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int nthr = kSelectThreads;
   const int len = clampi(seq_lens[s], 0, MP * kPage);
   const int P = (len + kPage - 1) / kPage;
   const int F = len / kPage;
@@ -290,65 +316,73 @@ __global__ __launch_bounds__(1024) void select_kernel(
   }
   // From here P >= 3, k < P and pages 0..P-2 are full (F >= P-1).
   const float* sc = scores + ((int64_t)s * H + h) * MP * G;
-  uint32_t* ukey = keybuf + ((int64_t)s * H + h) * MP;
+  uint32_t* ukey = kLdsKeys ? sh_keys : keybuf + ((int64_t)s * H + h) * MP;
 
-  // ---- Z_g = LSE over the F summarised pages (two passes: max, then sum)
-  float mx[G];
+  // ---- Z_g = LSE over the F summarised pages, one pass, 4 loads in flight
+  float zm[G], zs[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) mx[g] = -__builtin_inff();
-  for (int j = tid; j < F; j += nthr) {
+  for (int g = 0; g < G; ++g) { zm[g] = -__builtin_inff(); zs[g] = 0.f; }
+  for (int j0 = tid; j0 < F; j0 += 4 * nthr) {
+    float v[4][G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) mx[g] = fmaxf(mx[g], sc[(int64_t)j * G + g]);
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + u * nthr;
+      if (j < F) {
+        load_scores<G>(sc + (int64_t)j * G, v[u]);
+      } else {
+#pragma unroll
+        for (int g = 0; g < G; ++g) v[u][g] = -__builtin_inff();
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int g = 0; g < G; ++g) lse_merge(zm[g], zs[g], v[u][g], 1.f);
   }
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const float w = wave_max(mx[g]);
-    if (lane == 0) red[wave][g] = w;
-  }
-  __syncthreads();
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float m = red[0][g];
-    for (int w = 1; w < (nthr >> 6); ++w) m = fmaxf(m, red[w][g]);
-    mx[g] = (m == -__builtin_inff()) ? 0.f : m;
-  }
-  __syncthreads();
-  float sm[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) sm[g] = 0.f;
-  for (int j = tid; j < F; j += nthr) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) sm[g] += __expf(sc[(int64_t)j * G + g] - mx[g]);
-  }
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float w = wave_sum(sm[g]);
-    if (lane == 0) red[wave][g] = w;
+    for (int d = 1; d < 64; d <<= 1) {
+      const float m2 = __shfl_xor(zm[g], d, 64), s2 = __shfl_xor(zs[g], d, 64);
+      lse_merge(zm[g], zs[g], m2, s2);
+    }
+    if (lane == 0) { red_m[wave][g] = zm[g]; red_s[wave][g] = zs[g]; }
   }
   __syncthreads();
   float logZ[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    float t = 0.f;
-    for (int w = 0; w < (nthr >> 6); ++w) t += red[w][g];
-    logZ[g] = mx[g] + __logf(t);
+    float m = red_m[0][g], t = red_s[0][g];
+    for (int w = 1; w < nthr / 64; ++w) lse_merge(m, t, red_m[w][g], red_s[w][g]);
+    logZ[g] = m + __logf(t);
   }
 
   // ---- key_j = log mean_g exp(s_hat_jg - Z_g) for candidates 1..P-2
   const float logG = __logf((float)G);
-  for (int j = 1 + tid; j <= P - 2; j += nthr) {
-    float d[G], m = -__builtin_inff();
+  for (int j0 = 1 + tid; j0 <= P - 2; j0 += 4 * nthr) {
+    float v[4][G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      d[g] = sc[(int64_t)j * G + g] - logZ[g];
-      m = fmaxf(m, d[g]);
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + u * nthr;
+      if (j <= P - 2) load_scores<G>(sc + (int64_t)j * G, v[u]);
     }
-    float t = 0.f;
 #pragma unroll
-    for (int g = 0; g < G; ++g) t += __expf(d[g] - m);
-    float key = m + __logf(t) - logG;
-    if (!(key == key) || m == -__builtin_inff()) key = -__builtin_inff();
-    ukey[j] = float_to_ordered(key);
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + u * nthr;
+      if (j > P - 2) continue;
+      float d[G], m = -__builtin_inff();
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        d[g] = v[u][g] - logZ[g];
+        m = fmaxf(m, d[g]);
+      }
+      float t = 0.f;
+#pragma unroll
+      for (int g = 0; g < G; ++g) t += __expf(d[g] - m);
+      float key = m + __logf(t) - logG;
+      if (!(key == key) || m == -__builtin_inff()) key = -__builtin_inff();
+      ukey[j] = float_to_ordered(key);
+    }
   }
   __syncthreads();
 
@@ -372,7 +406,6 @@ __global__ __launch_bounds__(1024) void select_kernel(
     int incl = 0;
     if (tid < 256) {
       incl = (int)hist[255 - tid];
-      // in-wave inclusive scan over r (waves 0..3 cover r = 0..255)
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) {
         const int y = __shfl_up(incl, d, 64);
@@ -469,25 +502,29 @@ hipError_t launch_score(int r, int G, const void* q, const void* summ, const int
   }
 }
 
+template <int G>
+static void launch_select_g(dim3 grid, int MP, const float* scores, const int32_t* lens,
+                            const int32_t* budgets, int32_t* sel, int32_t* cnt, uint32_t* keybuf,
+                            int H, int max_budget, hipStream_t st) {
+  if (MP <= kSelectLdsPages) {
+    hipLaunchKernelGGL((select_kernel<G, true>), grid, dim3(kSelectThreads),
+                       (size_t)MP * sizeof(uint32_t), st, scores, lens, budgets, sel, cnt, keybuf,
+                       H, MP, max_budget);
+  } else {
+    hipLaunchKernelGGL((select_kernel<G, false>), grid, dim3(kSelectThreads), 0, st, scores, lens,
+                       budgets, sel, cnt, keybuf, H, MP, max_budget);
+  }
+}
+
 hipError_t launch_select(int G, const float* scores, const int32_t* lens, const int32_t* budgets,
                          int32_t* sel, int32_t* cnt, uint32_t* keybuf, int S, int H, int MP,
                          int max_budget, hipStream_t st) {
   dim3 grid(H, S);
   switch (G) {
-    case 1:
-      hipLaunchKernelGGL(select_kernel<1>, grid, dim3(1024), 0, st, scores, lens, budgets, sel, cnt,
-                         keybuf, H, MP, max_budget);
-      break;
-    case 2:
-      hipLaunchKernelGGL(select_kernel<2>, grid, dim3(1024), 0, st, scores, lens, budgets, sel, cnt,
-                         keybuf, H, MP, max_budget);
-      break;
-    case 4:
-      hipLaunchKernelGGL(select_kernel<4>, grid, dim3(1024), 0, st, scores, lens, budgets, sel, cnt,
-                         keybuf, H, MP, max_budget);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case 1: launch_select_g<1>(grid, MP, scores, lens, budgets, sel, cnt, keybuf, H, max_budget, st); break;
+    case 2: launch_select_g<2>(grid, MP, scores, lens, budgets, sel, cnt, keybuf, H, max_budget, st); break;
+    case 4: launch_select_g<4>(grid, MP, scores, lens, budgets, sel, cnt, keybuf, H, max_budget, st); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -28,7 +28,7 @@ ERR_HIP = -4
 ENTRY_POINTS = (
     "locks_status_string", "locks_summary_slot_bytes", "locks_summary_slot_stride",
     "locks_workspace_bytes", "locks_build", "locks_build_filled", "locks_append_kv",
-    "locks_score_select", "locks_sparse_attn",
+    "locks_score_select", "locks_score_pages", "locks_select_pages", "locks_sparse_attn",
 )
 
 
@@ -71,6 +71,10 @@ _append = _sig("locks_append_kv", ctypes.c_int,
 _score_select = _sig("locks_score_select", ctypes.c_int,
                      [_pd, _vp, _vp, _i64, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp,
                       _vp, _sz, _vp])
+_score_pages = _sig("locks_score_pages", ctypes.c_int,
+                    [_pd, _vp, _vp, _i64, _vp, _vp, _i32, _i32, _vp, _vp])
+_select_pages = _sig("locks_select_pages", ctypes.c_int,
+                     [_pd, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp])
 _sparse_attn = _sig("locks_sparse_attn", ctypes.c_int,
                     [_pd, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp,
                      _vp, _sz, _vp])
@@ -176,6 +180,27 @@ def score_select(dims, q, summaries, block_table, seq_lens, budgets, max_budget,
                        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
                        _stream(stream))
     _check(st, "locks_score_select")
+
+
+def score_pages(dims, q, summaries, block_table, seq_lens, scores, num_blocks=None, stream=None):
+    nb = summaries.shape[0] if num_blocks is None else num_blocks
+    st = _score_pages(ctypes.byref(dims), _ptr(q, torch.bfloat16, "q"),
+                      _ptr(summaries, torch.uint8, "summaries"), nb,
+                      _ptr(block_table, torch.int32, "block_table"),
+                      _ptr(seq_lens, torch.int32, "seq_lens"), seq_lens.numel(),
+                      block_table.shape[1], _ptr(scores, torch.float32, "scores"), _stream(stream))
+    _check(st, "locks_score_pages")
+
+
+def select_pages(dims, scores, seq_lens, budgets, max_pages, max_budget, sel_pages, sel_count,
+                 workspace, stream=None):
+    st = _select_pages(ctypes.byref(dims), _ptr(scores, torch.float32, "scores"),
+                       _ptr(seq_lens, torch.int32, "seq_lens"), _ptr(budgets, torch.int32, "budgets"),
+                       seq_lens.numel(), max_pages, max_budget,
+                       _ptr(sel_pages, torch.int32, "sel_pages"),
+                       _ptr(sel_count, torch.int32, "sel_count"),
+                       _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
+    _check(st, "locks_select_pages")
 
 
 def sparse_attn(dims, q, k_pool, v_pool, block_table, seq_lens, sel_pages, sel_count, max_budget,

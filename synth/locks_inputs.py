@@ -19,7 +19,7 @@ QUERY_NOISE = 0.3
 
 __all__ = [
     "SIGMAS", "DecodeBatch", "page_keys", "page_values", "gqa_queries",
-    "make_decode_batch", "config_batch", "random_pages",
+    "make_decode_batch", "config_batch", "random_pages", "LayerStack", "make_layer_stack",
 ]
 
 
@@ -178,3 +178,52 @@ def config_batch(name, device="cpu", seed=None):
         budgets = [max(8, math.ceil(((L + 15) // 16) / 16)) for L in lens]
         return make_decode_batch(lens, 8, 4, budgets, sd, needles_per_head=2, device=device)
     raise ValueError(name)
+
+
+@dataclasses.dataclass
+class LayerStack:
+    """A single long sequence across `layers` layers that share one block
+    table, with every layer's pools filled for `max_len` tokens and queries
+    drawn for every (step, layer). Token t of the sequence lives in block
+    block_table[0, t // B], slot t % B."""
+    k_pools: list               # per layer bf16 [num_blocks][H][B][d]
+    v_pools: list
+    q: torch.Tensor             # bf16 [steps][layers][1][H*G][d]
+    block_table: torch.Tensor   # int32 [1][max_pages]
+    needles: list               # (layer, head, logical page, slot)
+    H: int
+    G: int
+    max_len: int
+    B: int = 16
+    d: int = 128
+
+
+def make_layer_stack(layers, max_len, H, G, steps, seed, needle_pages, device="cpu",
+                     d=128, B=16):
+    """Pools for `layers` layers of one `max_len`-token sequence (blocks
+    shuffled), one needle per (layer, KV head) on a logical page drawn
+    uniformly from 1..needle_pages-2, and fresh query noise for each of
+    `steps` decode steps (one q_dir per (layer, KV head))."""
+    gc = _gen(seed + 7919, "cpu")
+    P = (max_len + B - 1) // B
+    table = torch.randperm(P, generator=gc).to(torch.int32).view(1, P)
+    kps, vps, qs, needles = [], [], [], []
+    for l in range(layers):
+        g = _gen(seed * 1000 + l, device)
+        k = page_keys(P * H, g, B, d, device).view(P, H, B, d)
+        v = page_values(P * H, g, B, d, device).view(P, H, B, d)
+        q_dir = torch.randn(H, d, generator=g, device=device)
+        unit = q_dir / q_dir.norm(dim=1, keepdim=True)
+        for h in range(H):
+            j = 1 + int(torch.randint(max(needle_pages - 2, 1), (1,), generator=gc))
+            slot = int(torch.randint(B, (1,), generator=gc))
+            k[int(table[0, j]), h, slot] = NEEDLE_NORM * unit[h]
+            needles.append((l, h, j, slot))
+        kps.append(k.to(torch.bfloat16))
+        vps.append(v.to(torch.bfloat16))
+        noise = torch.randn(steps, H, G, d, generator=g, device=device)
+        qs.append((q_dir[None, :, None, :] + QUERY_NOISE * noise).reshape(steps, 1, H * G, d))
+        del k, v
+    q = torch.stack(qs, dim=1).to(torch.bfloat16)        # [steps][layers][1][H*G][d]
+    return LayerStack(k_pools=kps, v_pools=vps, q=q, block_table=table.to(device),
+                      needles=needles, H=H, G=G, max_len=max_len, B=B, d=d)

@@ -156,6 +156,20 @@ def test_select_all_is_dense(L):
         assert Hh.rel_l2(res["out"][0, 4 * h:4 * h + 4], dense) <= 1e-2
 
 
+def test_long_table_global_keys(L):
+    """A block table wider than the LDS key buffer takes the global-memory key
+    path of the selection; results must not change."""
+    _say("[gpu] wide block table (global key buffer)")
+    b = synth.make_decode_batch([300 * 16 + 5, 1000 * 16], 2, 4, [20, 64], seed=75)
+    summ = Hh.oracle_summaries(b.k_pool, b.block_table, b.seq_lens, b.H, 8, b.num_blocks)
+    wide = torch.full((2, 13000), -1, dtype=torch.int32)
+    wide[:, :b.max_pages] = b.block_table
+    bw = synth.DecodeBatch(k_pool=b.k_pool, v_pool=b.v_pool, q=b.q, block_table=wide,
+                           seq_lens=b.seq_lens, budgets=b.budgets, needles=b.needles, H=b.H, G=b.G)
+    res = _run_decode(L, L.Dims(2, 4, 8), _to_dev(bw), torch.from_numpy(summ).to(DEV), 64)
+    _check_against_oracle(bw, summ, res, 8, 64)
+
+
 def test_invalid_block_ids_are_skipped(L):
     _say("[gpu] out-of-range block ids")
     b = synth.make_decode_batch([50 * 16], 1, 4, [10], seed=70)
