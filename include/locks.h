@@ -92,12 +92,12 @@ size_t locks_summary_slot_bytes(const locks_dims* dims);  /* payload; 0 if dims 
 size_t locks_summary_slot_stride(const locks_dims* dims); /* bytes between slots; 0 if invalid */
 
 /*
- * Bytes of device workspace that locks_score_select and locks_sparse_attn
- * need for up to num_seqs sequences of up to max_pages pages and budgets of
- * up to max_budget pages. One workspace may serve both calls when they are
- * ordered on one stream. It must be zero-filled once before its first use;
- * every call leaves its counters at zero again when it completes. Returns 0
- * for invalid arguments.
+ * Bytes of device workspace that locks_score_select, locks_select_pages and
+ * locks_sparse_attn need for up to num_seqs sequences of up to max_pages pages
+ * and budgets of up to max_budget pages. One workspace may serve all of them
+ * when the calls are ordered on one stream; its contents need no
+ * initialisation and carry nothing between calls. Returns 0 for invalid
+ * arguments.
  */
 size_t locks_workspace_bytes(const locks_dims* dims, int32_t num_seqs, int32_t max_pages,
                              int32_t max_budget);
@@ -209,9 +209,9 @@ locks_status locks_select_pages(const locks_dims* dims, const float* scores,
  * selected pages only, renormalised over them:
  *   o_g = sum_{t in S} exp(l_t) v_t / sum_{t in S} exp(l_t), l_t = q_g.k_t/sqrt(d),
  * where the last page P-1 contributes its len - (P-1)*page_size valid tokens.
- * The pages are split across workgroups (split-K flash decoding) and the
- * partial (max, sum, accumulator) triples are merged by log-sum-exp in a fixed
- * order, so results do not depend on scheduling.
+ * The pages are split across workgroups (split-K flash decoding) and a second
+ * kernel merges the partial (max, sum, accumulator) triples by log-sum-exp in
+ * split order, so results do not depend on scheduling.
  * Outputs: out float [num_seqs][num_kv_heads * group_size][head_dim];
  *   lse_out (optional) float [num_seqs][num_kv_heads * group_size] =
  *   log sum_{t in S} exp(l_t); an empty selection gives out = 0, lse = -inf.

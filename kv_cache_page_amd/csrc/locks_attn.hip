@@ -7,10 +7,11 @@
 // Split-K flash decoding. A workgroup of 4 waves takes 4 * PPW consecutive
 // entries of the (sequence, KV head) selection list; each wave streams PPW
 // pages with an online softmax, the 4 waves merge in LDS, and the workgroup
-// writes one partial (max, sum, accumulator[G][d]) to the workspace. The last
-// workgroup of the (sequence, KV head) to finish -- found with an atomic
-// counter -- merges all partials in split order, so the result does not depend
-// on scheduling, and resets the counter to zero.
+// writes one partial (max, sum, accumulator[G][d]) to the workspace. A second
+// kernel merges the partials of each (sequence, KV head) in split order, so
+// the result does not depend on scheduling. (Merging inside the first kernel
+// would need agent-scope release/acquire fences, which on the multi-XCD
+// MI355X write back and invalidate a whole L2 per workgroup.)
 //
 // Lane roles inside a wave for one 16 x 128 page:
 //   QK: lane = 4 t + c reads 64 contiguous bytes of key row t (dims 32c..),
@@ -30,15 +31,11 @@ __global__ __launch_bounds__(256) void attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kpool,
     const uint16_t* __restrict__ vpool, const int32_t* __restrict__ table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel,
-    const int32_t* __restrict__ cnt, float* __restrict__ part, uint32_t* __restrict__ counters,
-    float* __restrict__ out, float* __restrict__ lse_out, int64_t num_blocks, int H, int MP,
-    int max_budget, int nsplit, int ppw) {
+    const int32_t* __restrict__ cnt, float* __restrict__ part, int64_t num_blocks, int H,
+    int MP, int max_budget, int nsplit, int ppw) {
   constexpr int kPart = G * (kHeadDim + 2);
   __shared__ float sh_acc[kAttnWaves][G][kHeadDim];
   __shared__ float sh_ml[kAttnWaves][G][2];
-  __shared__ int sh_last;
-  __shared__ float sh_f[kAttnMaxSplits * G];  // merge factors of the splits
-  __shared__ float sh_M[2 * G];               // global max and total sum per query
 
   const int s = blockIdx.z, h = blockIdx.y, x = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -48,15 +45,7 @@ __global__ __launch_bounds__(256) void attn_kernel(
   const int n = clampi(cnt[sh_idx], 0, max_budget);
   const int per_wg = kAttnWaves * ppw;
   const int nact = (n + per_wg - 1) / per_wg;
-  float* o_base = out + (sh_idx * G) * kHeadDim;
-  if (n == 0) {
-    if (x == 0) {
-      for (int i = tid; i < G * kHeadDim; i += blockDim.x) o_base[i] = 0.f;
-      if (lse_out && tid < G) lse_out[sh_idx * G + tid] = -__builtin_inff();
-    }
-    return;
-  }
-  if (x >= nact || nact > kAttnMaxSplits) return;
+  if (x >= nact) return;
 
   // ---- query registers for the QK role: dims [32c, 32c+32) as bf16 pairs
   const int t_qk = lane >> 2, c_qk = lane & 3;
@@ -201,43 +190,47 @@ __global__ __launch_bounds__(256) void attn_kernel(
     }
   }
 
-  // ---- the last workgroup of this (sequence, KV head) merges all splits
-  __syncthreads();
-  if (tid == 0) {
-    __threadfence();
-    const uint32_t prev = __hip_atomic_fetch_add(&counters[sh_idx], 1u, __ATOMIC_ACQ_REL,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    sh_last = (prev == (uint32_t)(nact - 1));
+}
+
+// Merge of the split partials of one (sequence, KV head) per workgroup, in
+// split order; empty selections give out = 0 and lse = -inf.
+template <int G>
+__global__ __launch_bounds__(256) void attn_merge_kernel(
+    const int32_t* __restrict__ cnt, const float* __restrict__ part, float* __restrict__ out,
+    float* __restrict__ lse_out, int H, int max_budget, int nsplit, int ppw) {
+  constexpr int kPart = G * (kHeadDim + 2);
+  __shared__ float sh_f[kAttnMaxSplits * G];  // per split and query: max, then merge factor
+  __shared__ float sh_l[kAttnMaxSplits * G];  // per split and query: sum
+  __shared__ float sh_M[2 * G];               // global max and total sum per query
+  const int64_t sh_idx = (int64_t)blockIdx.y * H + blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n = clampi(cnt[sh_idx], 0, max_budget);
+  const int nact = min((n + kAttnWaves * ppw - 1) / (kAttnWaves * ppw), nsplit);
+  float* o_base = out + (sh_idx * G) * kHeadDim;
+  if (nact == 0) {
+    for (int i = tid; i < G * kHeadDim; i += blockDim.x) o_base[i] = 0.f;
+    if (lse_out && tid < G) lse_out[sh_idx * G + tid] = -__builtin_inff();
+    return;
   }
-  __syncthreads();
-  if (!sh_last) return;
-  __threadfence();
-  // Merge the nact split partials in split order. Per-split maxima and sums
-  // go through LDS first so that the accumulator loads below are independent
-  // of each other and can all be in flight at once.
   const float* parts = part + sh_idx * nsplit * kPart;
+  // per-split maxima and sums -> LDS (all loads independent)
   for (int i = tid; i < nact * G; i += blockDim.x) {
     const int y = i / G, g = i % G;
-    sh_f[i] = __builtin_nontemporal_load(parts + y * kPart + g * (kHeadDim + 2) + kHeadDim);
+    const float* py = parts + y * kPart + g * (kHeadDim + 2) + kHeadDim;
+    sh_f[i] = py[0];
+    sh_l[i] = py[1];
   }
   __syncthreads();
   if (tid < G) {
     float M = -__builtin_inff();
     for (int y = 0; y < nact; ++y) M = fmaxf(M, sh_f[y * G + tid]);
-    sh_M[tid] = M;
-  }
-  __syncthreads();
-  for (int i = tid; i < nact * G; i += blockDim.x) {
-    const int g = i % G;
-    const float M = sh_M[g];
-    sh_f[i] = (M == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(sh_f[i] - M);
-  }
-  __syncthreads();
-  if (tid < G) {
     float Lsum = 0.f;
-    for (int y = 0; y < nact; ++y)
-      Lsum += sh_f[y * G + tid] *
-              __builtin_nontemporal_load(parts + y * kPart + tid * (kHeadDim + 2) + kHeadDim + 1);
+    for (int y = 0; y < nact; ++y) {
+      const float f = (M == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(sh_f[y * G + tid] - M);
+      sh_f[y * G + tid] = f;
+      Lsum += f * sh_l[y * G + tid];
+    }
+    sh_M[tid] = M;
     sh_M[G + tid] = Lsum;
   }
   __syncthreads();
@@ -245,32 +238,30 @@ __global__ __launch_bounds__(256) void attn_kernel(
     const int g = i / kHeadDim, d = i % kHeadDim;
     float a = 0.f;
 #pragma unroll 8
-    for (int y = 0; y < nact; ++y)
-      a += sh_f[y * G + g] * __builtin_nontemporal_load(parts + y * kPart + g * (kHeadDim + 2) + d);
+    for (int y = 0; y < nact; ++y) a += sh_f[y * G + g] * parts[y * kPart + g * (kHeadDim + 2) + d];
     const float Lsum = sh_M[G + g];
     o_base[g * kHeadDim + d] = (Lsum > 0.f) ? a / Lsum : 0.f;
     if (lse_out && d == 0)
       lse_out[sh_idx * G + g] =
           (Lsum > 0.f) ? (sh_M[g] + __builtin_amdgcn_logf(Lsum)) * kLn2 : -__builtin_inff();
   }
-  if (tid == 0) counters[sh_idx] = 0u;
 }
 
 hipError_t launch_attn(int G, const void* q, const void* kpool, const void* vpool,
                        const int32_t* table, const int32_t* lens, const int32_t* sel,
-                       const int32_t* cnt, float* part, uint32_t* counters, float* out,
-                       float* lse_out, int64_t nb, int S, int H, int MP, int max_budget,
-                       int nsplit, int ppw, hipStream_t st) {
-  dim3 grid(nsplit, H, S);
+                       const int32_t* cnt, float* part, float* out, float* lse_out, int64_t nb,
+                       int S, int H, int MP, int max_budget, int nsplit, int ppw, hipStream_t st) {
+  dim3 grid(nsplit, H, S), mgrid(H, S);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint16_t* kk = static_cast<const uint16_t*>(kpool);
   const uint16_t* vv = static_cast<const uint16_t*>(vpool);
   switch (G) {
-#define LOCKS_G(GG)                                                                             \
-  case GG:                                                                                      \
-    hipLaunchKernelGGL(attn_kernel<GG>, grid, dim3(64 * kAttnWaves), 0, st, qq, kk, vv, table, \
-                       lens, sel, cnt, part, counters, out, lse_out, nb, H, MP, max_budget,    \
-                       nsplit, ppw);                                                            \
+#define LOCKS_G(GG)                                                                               \
+  case GG:                                                                                        \
+    hipLaunchKernelGGL(attn_kernel<GG>, grid, dim3(64 * kAttnWaves), 0, st, qq, kk, vv, table,   \
+                       lens, sel, cnt, part, nb, H, MP, max_budget, nsplit, ppw);                 \
+    hipLaunchKernelGGL(attn_merge_kernel<GG>, mgrid, dim3(256), 0, st, cnt, part, out, lse_out,  \
+                       H, max_budget, nsplit, ppw);                                               \
     break;
     LOCKS_G(1) LOCKS_G(2) LOCKS_G(4)
 #undef LOCKS_G

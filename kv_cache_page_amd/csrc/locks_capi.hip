@@ -10,15 +10,15 @@
 namespace locks {
 hipError_t launch_score(int r, int G, const void* q, const void* summ, const int32_t* table,
                         const int32_t* lens, float* scores, int64_t nb, int S, int H, int MP,
-                        int fill_nan, hipStream_t st);
+                        int fill_nan, float2* zpart, const void* knew, const void* vnew,
+                        void* kpool, void* vpool, hipStream_t st);
 hipError_t launch_select(int G, const float* scores, const int32_t* lens, const int32_t* budgets,
-                         int32_t* sel, int32_t* cnt, uint32_t* keybuf, int S, int H, int MP,
+                         int32_t* sel, int32_t* cnt, float* keybuf, int S, int H, int MP,
                          int max_budget, hipStream_t st);
 hipError_t launch_attn(int G, const void* q, const void* kpool, const void* vpool,
                        const int32_t* table, const int32_t* lens, const int32_t* sel,
-                       const int32_t* cnt, float* part, uint32_t* counters, float* out,
-                       float* lse_out, int64_t nb, int S, int H, int MP, int max_budget,
-                       int nsplit, int ppw, hipStream_t st);
+                       const int32_t* cnt, float* part, float* out, float* lse_out, int64_t nb,
+                       int S, int H, int MP, int max_budget, int nsplit, int ppw, hipStream_t st);
 hipError_t launch_build(int r, const void* kpool, int64_t nb, int H, const int32_t* ids, int n,
                         const int32_t* table, const int32_t* lens, int MP, void* summ,
                         hipStream_t st);
@@ -53,7 +53,7 @@ locks_status check_dims(const locks_dims* d) {
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Workspace {
-  size_t scores, keys, parts, counters, total;
+  size_t scores, keys, parts, total;
   int nsplit;
 };
 
@@ -63,8 +63,6 @@ Workspace carve(const locks_dims* d, int32_t S, int32_t MP, int32_t KB) {
   const int per_wg = kAttnWaves * attn_pages_per_wave(KB);
   w.nsplit = (KB + per_wg - 1) / per_wg;
   size_t off = 0;
-  w.counters = off;
-  off = align_up(off + sh * sizeof(uint32_t));
   w.scores = off;
   off = align_up(off + sh * MP * d->group_size * sizeof(float));
   w.keys = off;
@@ -175,10 +173,11 @@ locks_status locks_score_select(const locks_dims* d, const void* q, const void* 
   float* scores = scores_out ? scores_out : reinterpret_cast<float*>(ws + w.scores);
   const int H = d->num_kv_heads, G = d->group_size;
   hipError_t he = locks::launch_score(d->rank, G, q, summaries, block_table, seq_lens, scores, nb,
-                                      S, H, MP, scores_out ? 1 : 0, st);
+                                      S, H, MP, scores_out ? 1 : 0, nullptr, nullptr, nullptr, nullptr,
+                                      nullptr, st);
   if (he != hipSuccess) return LOCKS_ERR_HIP;
   he = locks::launch_select(G, scores, seq_lens, budgets, sel_pages, sel_count,
-                            reinterpret_cast<uint32_t*>(ws + w.keys), S, H, MP, KB, st);
+                            reinterpret_cast<float*>(ws + w.keys), S, H, MP, KB, st);
   return hip_status(he);
 }
 
@@ -193,7 +192,8 @@ locks_status locks_score_pages(const locks_dims* d, const void* q, const void* s
   if (!q || !summaries || !block_table || !seq_lens || !scores) return LOCKS_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(summaries)) return LOCKS_ERR_INVALID_ARG;
   return hip_status(locks::launch_score(d->rank, d->group_size, q, summaries, block_table,
-                                        seq_lens, scores, nb, S, d->num_kv_heads, MP, 0, st));
+                                        seq_lens, scores, nb, S, d->num_kv_heads, MP, 0, nullptr,
+                                        nullptr, nullptr, nullptr, nullptr, st));
 }
 
 locks_status locks_select_pages(const locks_dims* d, const float* scores, const int32_t* seq_lens,
@@ -210,7 +210,7 @@ locks_status locks_select_pages(const locks_dims* d, const float* scores, const 
   if (!workspace || ws_bytes < w.total) return LOCKS_ERR_WORKSPACE;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   return hip_status(locks::launch_select(d->group_size, scores, seq_lens, budgets, sel_pages,
-                                         sel_count, reinterpret_cast<uint32_t*>(ws + w.keys), S,
+                                         sel_count, reinterpret_cast<float*>(ws + w.keys), S,
                                          d->num_kv_heads, MP, KB, st));
 }
 
@@ -233,8 +233,8 @@ locks_status locks_sparse_attn(const locks_dims* d, const void* q, const void* k
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   return hip_status(locks::launch_attn(
       d->group_size, q, k_pool, v_pool, block_table, seq_lens, sel_pages, sel_count,
-      reinterpret_cast<float*>(ws + w.parts), reinterpret_cast<uint32_t*>(ws + w.counters), out,
-      lse_out, nb, S, d->num_kv_heads, MP, KB, w.nsplit, attn_pages_per_wave(KB), st));
+      reinterpret_cast<float*>(ws + w.parts), out, lse_out, nb, S, d->num_kv_heads, MP, KB,
+      w.nsplit, attn_pages_per_wave(KB), st));
 }
 
 }  // extern "C"

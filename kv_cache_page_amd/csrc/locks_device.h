@@ -78,4 +78,12 @@ __device__ __forceinline__ uint32_t float_to_ordered(float f) {
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// Online log-sum-exp state (max m, sum s of exp(x - m)): absorb (m2, s2).
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  const float M = fmaxf(m, m2);
+  if (M == -__builtin_inff()) return;
+  s = s * __expf(m - M) + s2 * __expf(m2 - M);
+  m = M;
+}
+
 }  // namespace locks

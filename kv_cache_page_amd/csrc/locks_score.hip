@@ -19,26 +19,84 @@
 // then each lane forms the logits of its four tokens and a second quad
 // reduction finishes the length-16 log-sum-exp.
 #include "locks_device.h"
+#include "locks_select.h"
 
 namespace locks {
 
 // ---------------------------------------------------------------------------
 // score
 // ---------------------------------------------------------------------------
+constexpr int kScorePagesPerWg = 128;  // 4 waves x 16 pages x 2 batches
+
+template <int R>
+struct SlotRegs {
+  uint4 vq[R];
+  uint4 mq0, mq1;
+  uint32_t cq[R];
+  uint16_t sv[R];
+  uint16_t scw[4];
+  uint16_t smw;
+};
+
+// Loads the lane's share of one slot. blk < 0 (page outside the range or a
+// block id out of range) loads block 0's slot as a stand-in.
+template <int R>
+__device__ __forceinline__ void load_slot(SlotRegs<R>& d, const uint8_t* __restrict__ summ, int H,
+                                          int h, int blk, int l4) {
+  constexpr SlotLayout L = slot_layout(R);
+  const uint8_t* slot = static_cast<const uint8_t*>(
+      __builtin_assume_aligned(summ + ((int64_t)(blk >= 0 ? blk : 0) * H + h) * L.stride, 16));
+#pragma unroll
+  for (int k = 0; k < R; ++k) d.vq[k] = *reinterpret_cast<const uint4*>(slot + 64 * k + 16 * l4);
+  d.mq0 = *reinterpret_cast<const uint4*>(slot + L.mu + 32 * l4);
+  d.mq1 = *reinterpret_cast<const uint4*>(slot + L.mu + 32 * l4 + 16);
+#pragma unroll
+  for (int e = 0; e < R; ++e)
+    d.cq[e] = *reinterpret_cast<const uint32_t*>(slot + L.c + 4 * R * l4 + 4 * e);
+#pragma unroll
+  for (int k = 0; k < R; ++k) d.sv[k] = *reinterpret_cast<const uint16_t*>(slot + L.sv + 2 * k);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    d.scw[i] = *reinterpret_cast<const uint16_t*>(slot + L.sc + 8 * l4 + 2 * i);
+  d.smw = *reinterpret_cast<const uint16_t*>(slot + L.smu);
+}
+
+// Grid (H, ceil(MP / kScorePagesPerWg), S): consecutive workgroup ids walk
+// the heads first, so with 8 heads all tiles of a head land on one XCD (ids
+// are dealt to the 8 XCDs round-robin) and its scores stay in that L2.
+// zpart (optional): per workgroup and query head, the (max, sum exp) of its
+// pages' scores, so that Z_g needs no second pass over all scores.
+// knew/vnew (optional): the workgroup with tile index 0 of each (sequence,
+// head) first appends the new token's key and value for that head.
 template <int R, int G>
 __global__ __launch_bounds__(256) void score_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ summ,
     const int32_t* __restrict__ table, const int32_t* __restrict__ seq_lens,
     float* __restrict__ scores, int64_t num_blocks, int H, int MP, int pages_per_wg,
-    int fill_nan) {
+    int fill_nan, float2* __restrict__ zpart, const uint16_t* __restrict__ knew,
+    const uint16_t* __restrict__ vnew, uint16_t* __restrict__ kpool,
+    uint16_t* __restrict__ vpool) {
   constexpr SlotLayout L = slot_layout(R);
   constexpr float kTwoM24 = 5.9604644775390625e-08f;  // 2^-24
-  const int s = blockIdx.z, h = blockIdx.y;
+  const int s = blockIdx.z, h = blockIdx.x, tile = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l4 = lane & 3;
   const int len = clampi(seq_lens[s], 0, MP * kPage);
   const int F = len / kPage;
-  const int j_lo = blockIdx.x * pages_per_wg;
+  const int j_lo = tile * pages_per_wg;
+  if (knew && tile == 0 && threadIdx.x < 2 * (kHeadDim / 8) && len >= 1) {
+    // decode-step append of the new token (position len - 1) for this head
+    const int blk = table[(int64_t)s * MP + (len - 1) / kPage];
+    if (blk >= 0 && blk < num_blocks) {
+      const int c = threadIdx.x % (kHeadDim / 8);
+      const int64_t src = ((int64_t)s * H + h) * kHeadDim + 8 * c;
+      const int64_t dst = (((int64_t)blk * H + h) * kPage + (len - 1) % kPage) * kHeadDim + 8 * c;
+      if (threadIdx.x < kHeadDim / 8)
+        *reinterpret_cast<uint4*>(kpool + dst) = *reinterpret_cast<const uint4*>(knew + src);
+      else
+        *reinterpret_cast<uint4*>(vpool + dst) = *reinterpret_cast<const uint4*>(vnew + src);
+    }
+  }
   const int j_hi = min(j_lo + pages_per_wg, MP);
   float* srow = scores + ((int64_t)s * H + h) * MP * G;
   if (fill_nan) {
@@ -89,31 +147,34 @@ __global__ __launch_bounds__(256) void score_kernel(
     fscale[g] = ldexpf(kLog2e * 0.08838834764831845f, 10 + ex);
   }
 
-  for (int jb = j_lo + wave * 16; jb < j_end; jb += 64) {
-    const int j = jb + (lane >> 2);
+  // Block ids of all the lane's pages are read first (independent loads);
+  // then a software pipeline loads the slot data of the next 16-page batch
+  // into registers while the current batch is computed.
+  constexpr int kMaxIter = kScorePagesPerWg / 64;
+  const int jw = j_lo + wave * 16 + (lane >> 2);
+  int blks[kMaxIter];
+#pragma unroll
+  for (int it = 0; it < kMaxIter; ++it) {
+    const int j = jw + 64 * it;
+    const int b = (j < j_end) ? table[(int64_t)s * MP + j] : -1;
+    blks[it] = (b >= 0 && b < num_blocks) ? b : -1;
+  }
+  float zm = -__builtin_inff(), zs = 0.f;  // running LSE of query head l4 over the pages
+  SlotRegs<R> cur, nxt;
+  load_slot<R>(cur, summ, H, h, blks[0], l4);
+#pragma unroll
+  for (int it = 0; it < kMaxIter; ++it) {
+    const int j = jw + 64 * it;
+    if (j - (lane >> 2) >= j_end) break;  // wave-uniform
     const bool in = j < j_end;
-    const int blk = in ? table[(int64_t)s * MP + j] : 0;
-    const bool ok = in && blk >= 0 && blk < num_blocks;
-    const uint8_t* slot = static_cast<const uint8_t*>(__builtin_assume_aligned(
-        summ + ((int64_t)(ok ? blk : 0) * H + h) * L.stride, 16));
-
-    uint4 vq[R];
-#pragma unroll
-    for (int k = 0; k < R; ++k) vq[k] = *reinterpret_cast<const uint4*>(slot + 64 * k + 16 * l4);
-    const uint4 mq0 = *reinterpret_cast<const uint4*>(slot + L.mu + 32 * l4);
-    const uint4 mq1 = *reinterpret_cast<const uint4*>(slot + L.mu + 32 * l4 + 16);
-    uint32_t cq[R];
-#pragma unroll
-    for (int e = 0; e < R; ++e)
-      cq[e] = *reinterpret_cast<const uint32_t*>(slot + L.c + 4 * R * l4 + 4 * e);
-    uint16_t sv[R];
-#pragma unroll
-    for (int k = 0; k < R; ++k) sv[k] = *reinterpret_cast<const uint16_t*>(slot + L.sv + 2 * k);
-    uint16_t scw[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      scw[i] = *reinterpret_cast<const uint16_t*>(slot + L.sc + 8 * l4 + 2 * i);
-    const uint16_t smw = *reinterpret_cast<const uint16_t*>(slot + L.smu);
+    const bool ok = blks[it] >= 0;
+    if (it + 1 < kMaxIter) load_slot<R>(nxt, summ, H, h, blks[it + 1 < kMaxIter ? it + 1 : it], l4);
+    const uint4* vq = cur.vq;
+    const uint4 mq0 = cur.mq0, mq1 = cur.mq1;
+    const uint32_t* cq = cur.cq;
+    const uint16_t* sv = cur.sv;
+    const uint16_t* scw = cur.scw;
+    const uint16_t smw = cur.smw;
 
     // ---- V^T q (partial over the lane's 32 dims)
     float acc[R][G];
@@ -205,102 +266,61 @@ __global__ __launch_bounds__(256) void score_kernel(
       if (l4 == g) outv = shat;
     }
     if (in && l4 < G) srow[(int64_t)j * G + l4] = ok ? outv : -__builtin_inff();
+    if (in && ok) lse_merge(zm, zs, outv, 1.f);
+    cur = nxt;
   }
-}
-
-// ---------------------------------------------------------------------------
-// block-wide helpers for 1024-thread workgroups
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ float wave_max(float v) {
+  if (zpart) {
+    // reduce over the lanes that hold the same query head, then over waves
+    __shared__ float zred[4][4][2];
 #pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
-  return v;
-}
-// Exclusive prefix sum of one int per thread over the workgroup (<= 16 waves).
-__device__ __forceinline__ int block_exclusive_scan(int v, int* sh_waves, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
+    for (int m = 4; m < 64; m <<= 1) {
+      const float m2 = __shfl_xor(zm, m, 64), s2 = __shfl_xor(zs, m, 64);
+      lse_merge(zm, zs, m2, s2);
+    }
+    if (lane < G) { zred[wave][lane][0] = zm; zred[wave][lane][1] = zs; }
+    __syncthreads();
+    if (threadIdx.x < G) {
+      float m = zred[0][threadIdx.x][0], t = zred[0][threadIdx.x][1];
+      for (int w = 1; w < 4; ++w) lse_merge(m, t, zred[w][threadIdx.x][0], zred[w][threadIdx.x][1]);
+      zpart[(((int64_t)s * H + h) * gridDim.y + tile) * G + threadIdx.x] = make_float2(m, t);
+    }
   }
-  if (lane == 63) sh_waves[wave] = x;
-  __syncthreads();
-  int base = 0, all = 0;
-  const int nw = blockDim.x >> 6;
-  for (int w = 0; w < nw; ++w) {
-    const int t = sh_waves[w];
-    if (w < wave) base += t;
-    all += t;
-  }
-  __syncthreads();
-  *total = all;
-  return base + x - v;
-}
-
-// Histogram increment with wave aggregation of repeated digits: the first
-// few distinct digits of the wave are counted with one LDS atomic each, the
-// remaining lanes add individually.
-__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t digit, bool act) {
-  const int lane = threadIdx.x & 63;
-  unsigned long long live = __ballot(act);
-#pragma unroll 1
-  for (int it = 0; it < 4 && live; ++it) {
-    const int leader = __ffsll(live) - 1;
-    const uint32_t d0 = __shfl((int)digit, leader, 64);
-    const bool same = act && digit == d0;
-    const unsigned long long grp = __ballot(same);
-    if (lane == leader) atomicAdd(&hist[d0], (uint32_t)__popcll(grp));
-    if (same) act = false;
-    live &= ~grp;
-  }
-  if (act) atomicAdd(&hist[digit], 1u);
 }
 
 // ---------------------------------------------------------------------------
 // select: one 1024-thread workgroup per (sequence, KV head)
+//
+// 1. scores -> registers; Z_g by a block max then a block exp-sum;
+// 2. key_j in LDS (or global memory for very wide tables), block max K;
+// 3. histogram of bin_j = min(511, floor((K - key_j) * 32)): bins are 1/32
+//    nat wide and order-preserving (key_a > key_b implies bin_a <= bin_b), so
+//    every candidate in a bin below the crossing bin t is selected;
+// 4. inside bin t the remaining slots go to the candidates of largest key,
+//    lower page first on ties, found by pairwise ranking (or, when more than
+//    1024 candidates share bin t, by an exact 8-bit radix select on the
+//    order-preserving key bits);
+// 5. membership bits in an LDS bitmap, one 32-page word per thread, and a
+//    block scan of word popcounts write the page ids in ascending order.
 // ---------------------------------------------------------------------------
 constexpr int kSelectThreads = 1024;
-constexpr int kSelectLdsPages = 12288;  // keys of up to this many pages live in LDS (48 KB)
-
-template <int G>
-__device__ __forceinline__ void load_scores(const float* p, float (&v)[G]) {
-  if constexpr (G == 4) {
-    const float4 x = *reinterpret_cast<const float4*>(p);
-    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
-  } else if constexpr (G == 2) {
-    const float2 x = *reinterpret_cast<const float2*>(p);
-    v[0] = x.x; v[1] = x.y;
-  } else {
-    v[0] = p[0];
-  }
-}
-
-// Online (max, sum-exp) merge: (m, s) absorbs (m2, s2).
-__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
-  const float M = fmaxf(m, m2);
-  if (M == -__builtin_inff()) return;
-  s = s * __expf(m - M) + s2 * __expf(m2 - M);
-  m = M;
-}
+constexpr int kSelectLdsPages = 10240;  // keys of up to this many pages live in LDS (40 KB)
+constexpr int kSelectRegPages = 8;      // pages per thread held in registers per chunk
+constexpr int kMaxBitmapWords = 65536 / 32;
 
 template <int G, bool kLdsKeys>
 __global__ __launch_bounds__(kSelectThreads) void select_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ budgets, int32_t* __restrict__ sel_pages,
-    int32_t* __restrict__ sel_count, uint32_t* __restrict__ keybuf, int H, int MP,
+    int32_t* __restrict__ sel_count, float* __restrict__ keybuf, int H, int MP,
     int max_budget) {
-  extern __shared__ uint32_t sh_keys[];
-  __shared__ uint32_t hist[256];
-  __shared__ float red_m[16][G], red_s[16][G];
+  extern __shared__ float sh_keys[];
+  __shared__ uint32_t bits[kMaxBitmapWords];
+  __shared__ uint32_t hist[kBins];
+  __shared__ float cand_key[kSelectThreads];
+  __shared__ int cand_page[kSelectThreads];
+  __shared__ float red[16][4];
   __shared__ int sh_waves[16];
-  __shared__ int sh_pick[2];
+  __shared__ int sh_int[4];
   const int s = blockIdx.y, h = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int nthr = kSelectThreads;
@@ -316,145 +336,196 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
   }
   // From here P >= 3, k < P and pages 0..P-2 are full (F >= P-1).
   const float* sc = scores + ((int64_t)s * H + h) * MP * G;
-  uint32_t* ukey = kLdsKeys ? sh_keys : keybuf + ((int64_t)s * H + h) * MP;
+  float* key = kLdsKeys ? sh_keys : keybuf + ((int64_t)s * H + h) * MP;
+  const int nwords = (P + 31) / 32;
+  for (int w = tid; w < nwords; w += nthr) bits[w] = 0u;
+  constexpr int kChunk = kSelectRegPages * nthr;
+  const bool one_chunk = F <= kChunk;
 
-  // ---- Z_g = LSE over the F summarised pages, one pass, 4 loads in flight
-  float zm[G], zs[G];
+  // ---- 1. Z_g
+  float v[kSelectRegPages][G];
+  float mx[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) { zm[g] = -__builtin_inff(); zs[g] = 0.f; }
-  for (int j0 = tid; j0 < F; j0 += 4 * nthr) {
-    float v[4][G];
+  for (int g = 0; g < G; ++g) mx[g] = -__builtin_inff();
+  for (int c0 = 0; c0 < F; c0 += kChunk) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = j0 + u * nthr;
+    for (int u = 0; u < kSelectRegPages; ++u) {
+      const int j = c0 + u * nthr + tid;
       if (j < F) {
         load_scores<G>(sc + (int64_t)j * G, v[u]);
       } else {
 #pragma unroll
         for (int g = 0; g < G; ++g) v[u][g] = -__builtin_inff();
       }
+#pragma unroll
+      for (int g = 0; g < G; ++g) mx[g] = fmaxf(mx[g], v[u][g]);
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int g = 0; g < G; ++g) lse_merge(zm[g], zs[g], v[u][g], 1.f);
   }
+  block_max_g<G>(mx, red);
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
+  for (int g = 0; g < G; ++g) if (mx[g] == -__builtin_inff()) mx[g] = 0.f;
+  float sm[G];
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const float m2 = __shfl_xor(zm[g], d, 64), s2 = __shfl_xor(zs[g], d, 64);
-      lse_merge(zm[g], zs[g], m2, s2);
+  for (int g = 0; g < G; ++g) sm[g] = 0.f;
+  for (int c0 = 0; c0 < F; c0 += kChunk) {
+#pragma unroll
+    for (int u = 0; u < kSelectRegPages; ++u) {
+      const int j = c0 + u * nthr + tid;
+      if (!one_chunk && j < F) load_scores<G>(sc + (int64_t)j * G, v[u]);
+      if (j < F)
+#pragma unroll
+        for (int g = 0; g < G; ++g) sm[g] += __expf(v[u][g] - mx[g]);
     }
-    if (lane == 0) { red_m[wave][g] = zm[g]; red_s[wave][g] = zs[g]; }
   }
-  __syncthreads();
+  block_sum_g<G>(sm, red);
   float logZ[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float m = red_m[0][g], t = red_s[0][g];
-    for (int w = 1; w < nthr / 64; ++w) lse_merge(m, t, red_m[w][g], red_s[w][g]);
-    logZ[g] = m + __logf(t);
-  }
+  for (int g = 0; g < G; ++g) logZ[g] = mx[g] + __logf(sm[g]);
 
-  // ---- key_j = log mean_g exp(s_hat_jg - Z_g) for candidates 1..P-2
+  // ---- 2. keys of the candidates 1..P-2 and their maximum
   const float logG = __logf((float)G);
-  for (int j0 = 1 + tid; j0 <= P - 2; j0 += 4 * nthr) {
-    float v[4][G];
+  float kmax = -__builtin_inff();
+  for (int c0 = 0; c0 < P - 1; c0 += kChunk) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = j0 + u * nthr;
-      if (j <= P - 2) load_scores<G>(sc + (int64_t)j * G, v[u]);
+    for (int u = 0; u < kSelectRegPages; ++u) {
+      const int j = c0 + u * nthr + tid;
+      if (j < 1 || j > P - 2) continue;
+      if (!one_chunk) load_scores<G>(sc + (int64_t)j * G, v[u]);
+      const float kj = group_key<G>(v[u], logZ, logG);
+      key[j] = kj;
+      kmax = fmaxf(kmax, kj);
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = j0 + u * nthr;
-      if (j > P - 2) continue;
-      float d[G], m = -__builtin_inff();
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        d[g] = v[u][g] - logZ[g];
-        m = fmaxf(m, d[g]);
+  }
+  {
+    float km[1] = {kmax};
+    block_max_g<1>(km, red);
+    kmax = km[0];
+  }
+  // ---- 3. histogram of the order-preserving bins below the best key
+  for (int i = tid; i < kBins; i += nthr) hist[i] = 0u;
+  __syncthreads();
+  auto bin_of = [&](float kj) -> int {
+    const float d = (kmax - kj) * kBinsPerNat;  // >= 0, +inf for -inf keys
+    return d < (float)(kBins - 1) ? (int)d : kBins - 1;
+  };
+  for (int j = 1 + tid; j <= P - 2; j += nthr) atomicAdd(&hist[bin_of(key[j])], 1u);
+  __syncthreads();
+  int need = k - 2;
+  int tbin = -1;  // crossing bin (-1: nothing to select beyond sink/recent)
+  if (need > 0) {
+    const int c = (tid < kBins) ? (int)hist[tid] : 0;
+    int tot;
+    const int before = block_exclusive_scan(c, sh_waves, &tot);
+    if (tid < kBins && before < need && before + c >= need) {
+      sh_int[0] = tid;
+      sh_int[1] = need - before;
+    }
+    __syncthreads();
+    tbin = sh_int[0];
+    need = sh_int[1];
+  }
+  __syncthreads();
+  // ---- 4. resolve inside bin tbin: take the `need` largest keys there
+  if (tbin >= 0) {
+    const int ct = (int)hist[tbin];
+    if (ct <= nthr) {
+      if (tid == 0) sh_int[2] = 0;
+      __syncthreads();
+      for (int j = 1 + tid; j <= P - 2; j += nthr) {
+        const float kj = key[j];
+        if (bin_of(kj) == tbin) {
+          const int slot = atomicAdd(&sh_int[2], 1);
+          cand_key[slot] = kj;
+          cand_page[slot] = j;
+        }
       }
-      float t = 0.f;
-#pragma unroll
-      for (int g = 0; g < G; ++g) t += __expf(d[g] - m);
-      float key = m + __logf(t) - logG;
-      if (!(key == key) || m == -__builtin_inff()) key = -__builtin_inff();
-      ukey[j] = float_to_ordered(key);
+      __syncthreads();
+      if (tid < ct) {
+        const float me = cand_key[tid];
+        const int mp = cand_page[tid];
+        int rank = 0;
+        for (int e = 0; e < ct; ++e) {
+          const float o = cand_key[e];
+          rank += (o > me || (o == me && cand_page[e] < mp)) ? 1 : 0;
+        }
+        if (rank < need) atomicOr(&bits[mp >> 5], 1u << (mp & 31));
+      }
+    } else {
+      // many candidates share the crossing bin (degenerate key distributions):
+      // exact 8-bit radix select on the order-preserving key bits
+      uint32_t prefix = 0u;
+      for (int sh = 24; sh >= 0; sh -= 8) {
+        for (int i = tid; i < 256; i += nthr) hist[i] = 0u;
+        __syncthreads();
+        for (int j = 1 + tid; j <= P - 2; j += nthr) {
+          const float kj = key[j];
+          const uint32_t u = float_to_ordered(kj);
+          if (bin_of(kj) == tbin && (sh == 24 || (u >> (sh + 8)) == prefix))
+            atomicAdd(&hist[255 - ((u >> sh) & 255u)], 1u);  // descending order
+        }
+        __syncthreads();
+        const int c = (tid < 256) ? (int)hist[tid] : 0;
+        int tot;
+        const int before = block_exclusive_scan(c, sh_waves, &tot);
+        if (tid < 256 && before < need && before + c >= need) {
+          sh_int[0] = 255 - tid;
+          sh_int[1] = need - before;
+        }
+        __syncthreads();
+        prefix = (prefix << 8) | (uint32_t)sh_int[0];
+        need = sh_int[1];
+        __syncthreads();
+      }
+      // keys above `prefix` in bin tbin are in; `need` of those equal, lowest pages
+      const int cpt = (P + nthr - 1) / nthr;
+      const int c0 = tid * cpt, c1 = min(c0 + cpt, P - 1);
+      int eq = 0;
+      for (int j = max(c0, 1); j < c1; ++j) {
+        const float kj = key[j];
+        eq += (bin_of(kj) == tbin && float_to_ordered(kj) == prefix) ? 1 : 0;
+      }
+      int tot;
+      int eq_before = block_exclusive_scan(eq, sh_waves, &tot);
+      for (int j = max(c0, 1); j < c1; ++j) {
+        const float kj = key[j];
+        if (bin_of(kj) != tbin) continue;
+        const uint32_t u = float_to_ordered(kj);
+        if (u > prefix || (u == prefix && eq_before++ < need))
+          atomicOr(&bits[j >> 5], 1u << (j & 31));
+      }
     }
   }
   __syncthreads();
-
-  // ---- radix select of the (k-2)-th largest ordered key, 8 bits per pass
-  uint32_t prefix = 0u, mask = 0u;
-  int need = k - 2;
-  if (need == 0) prefix = 0xFFFFFFFFu;  // k == 2: sink and recent only
-  for (int shift = 24; shift >= 0 && need > 0; shift -= 8) {
-    if (tid < 256) hist[tid] = 0u;
-    if (tid == 0) { sh_pick[0] = 0; sh_pick[1] = 0; }
-    __syncthreads();
-    for (int j0 = 1; j0 <= P - 2; j0 += nthr) {
-      const int j = j0 + tid;
-      const bool in = j <= P - 2;
-      const uint32_t u = in ? ukey[j] : 0u;
-      hist_add(hist, (u >> shift) & 255u, in && (u & mask) == prefix);
+  // ---- 5. membership bitmap -> ascending page list
+  for (int w = tid; w < nwords; w += nthr) {
+    uint32_t b = bits[w];
+    for (int e = 0; e < 32; ++e) {
+      const int j = 32 * w + e;
+      if (j >= P) break;
+      bool in = (j == 0 || j == P - 1);
+      if (!in && tbin >= 0) in = bin_of(key[j]) < tbin;
+      if (in) b |= 1u << e;
     }
-    __syncthreads();
-    // thread t < 256 handles digit 255 - t, so its inclusive prefix over t is
-    // the count of keys whose digit is >= 255 - t
-    int incl = 0;
-    if (tid < 256) {
-      incl = (int)hist[255 - tid];
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += y;
-      }
-      if (lane == 63) sh_waves[wave] = incl;
-    }
-    __syncthreads();
-    if (tid < 256) {
-      for (int w = 0; w < wave; ++w) incl += sh_waves[w];
-      const int c = (int)hist[255 - tid];
-      if (incl >= need && incl - c < need) {
-        sh_pick[0] = 255 - tid;
-        sh_pick[1] = incl - c;
-      }
-    }
-    __syncthreads();
-    const uint32_t D = (uint32_t)sh_pick[0];
-    need -= sh_pick[1];
-    prefix |= D << shift;
-    mask |= 255u << shift;
-    __syncthreads();
+    bits[w] = b;
   }
-  const uint32_t T = prefix;  // keys > T are in; `need` of the keys == T (lowest pages)
-
-  // ---- mark and compact in ascending page order (contiguous chunk per thread)
-  const int cpt = (P + nthr - 1) / nthr;  // pages per thread, <= 64
-  const int c0 = tid * cpt, c1 = min(c0 + cpt, P);
-  int eq = 0;
-  for (int j = c0; j < c1; ++j)
-    if (j >= 1 && j <= P - 2 && ukey[j] == T) ++eq;
+  __syncthreads();
+  // each thread owns words tid*wpt .. +wpt (wpt <= 2 for 65536 pages)
+  const int wpt = (nwords + nthr - 1) / nthr;
+  const int w0 = tid * wpt, w1 = min(w0 + wpt, nwords);
+  int cnt = 0;
+  for (int w = w0; w < w1; ++w) cnt += __popc(bits[w]);
   int tot;
-  int eq_before = block_exclusive_scan(eq, sh_waves, &tot);
-  unsigned long long bits = 0ull;
-  int nsel = 0;
-  for (int j = c0; j < c1; ++j) {
-    bool take;
-    if (j == 0 || j == P - 1) {
-      take = true;
-    } else {
-      const uint32_t u = ukey[j];
-      take = u > T || (u == T && eq_before++ < need);
+  int pos = block_exclusive_scan(cnt, sh_waves, &tot);
+  tot = min(tot, max_budget);  // == k <= max_budget by construction
+  for (int w = w0; w < w1; ++w) {
+    uint32_t b = bits[w];
+    while (b) {
+      const int e = __ffs(b) - 1;
+      b &= b - 1;
+      if (pos < max_budget) out[pos] = 32 * w + e;
+      ++pos;
     }
-    if (take) { bits |= 1ull << (j - c0); ++nsel; }
   }
-  int pos = block_exclusive_scan(nsel, sh_waves, &tot);
-  tot = min(tot, max_budget);  // never more than k <= max_budget by construction
-  for (int j = c0; j < c1; ++j)
-    if ((bits >> (j - c0) & 1ull) && pos < max_budget) out[pos++] = j;
   for (int i = tot + tid; i < max_budget; i += nthr) out[i] = -1;
   if (tid == 0) sel_count[(int64_t)s * H + h] = tot;
 }
@@ -465,22 +536,28 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
 template <int R, int G>
 static hipError_t launch_score_rg(const uint16_t* q, const uint8_t* summ, const int32_t* table,
                                   const int32_t* lens, float* scores, int64_t nb, int S, int H,
-                                  int MP, int fill_nan, hipStream_t st) {
-  const int ppw = 128;
-  dim3 grid((MP + ppw - 1) / ppw, H, S);
+                                  int MP, int fill_nan, float2* zpart, const void* knew,
+                                  const void* vnew, void* kpool, void* vpool, hipStream_t st) {
+  const int ppw = kScorePagesPerWg;
+  dim3 grid(H, (MP + ppw - 1) / ppw, S);
   hipLaunchKernelGGL((score_kernel<R, G>), grid, dim3(256), 0, st, q, summ, table, lens, scores,
-                     nb, H, MP, ppw, fill_nan);
+                     nb, H, MP, ppw, fill_nan, zpart, static_cast<const uint16_t*>(knew),
+                     static_cast<const uint16_t*>(vnew), static_cast<uint16_t*>(kpool),
+                     static_cast<uint16_t*>(vpool));
   return hipGetLastError();
 }
 
 template <int G>
 static hipError_t launch_score_g(int r, const uint16_t* q, const uint8_t* summ,
                                  const int32_t* table, const int32_t* lens, float* scores,
-                                 int64_t nb, int S, int H, int MP, int fill_nan, hipStream_t st) {
+                                 int64_t nb, int S, int H, int MP, int fill_nan, float2* zpart,
+                                 const void* knew, const void* vnew, void* kpool, void* vpool,
+                                 hipStream_t st) {
   switch (r) {
-#define LOCKS_R(RR) \
-  case RR:          \
-    return launch_score_rg<RR, G>(q, summ, table, lens, scores, nb, S, H, MP, fill_nan, st);
+#define LOCKS_R(RR)                                                                        \
+  case RR:                                                                                 \
+    return launch_score_rg<RR, G>(q, summ, table, lens, scores, nb, S, H, MP, fill_nan,   \
+                                  zpart, knew, vnew, kpool, vpool, st);
     LOCKS_R(1) LOCKS_R(2) LOCKS_R(3) LOCKS_R(4) LOCKS_R(5) LOCKS_R(6) LOCKS_R(7) LOCKS_R(8)
     LOCKS_R(9) LOCKS_R(10) LOCKS_R(11) LOCKS_R(12) LOCKS_R(13) LOCKS_R(14) LOCKS_R(15) LOCKS_R(16)
 #undef LOCKS_R
@@ -491,24 +568,27 @@ static hipError_t launch_score_g(int r, const uint16_t* q, const uint8_t* summ,
 
 hipError_t launch_score(int r, int G, const void* q, const void* summ, const int32_t* table,
                         const int32_t* lens, float* scores, int64_t nb, int S, int H, int MP,
-                        int fill_nan, hipStream_t st) {
+                        int fill_nan, float2* zpart, const void* knew, const void* vnew,
+                        void* kpool, void* vpool, hipStream_t st) {
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint8_t* ss = static_cast<const uint8_t*>(summ);
   switch (G) {
-    case 1: return launch_score_g<1>(r, qq, ss, table, lens, scores, nb, S, H, MP, fill_nan, st);
-    case 2: return launch_score_g<2>(r, qq, ss, table, lens, scores, nb, S, H, MP, fill_nan, st);
-    case 4: return launch_score_g<4>(r, qq, ss, table, lens, scores, nb, S, H, MP, fill_nan, st);
+#define LOCKS_ARGS qq, ss, table, lens, scores, nb, S, H, MP, fill_nan, zpart, knew, vnew, kpool, vpool, st
+    case 1: return launch_score_g<1>(r, LOCKS_ARGS);
+    case 2: return launch_score_g<2>(r, LOCKS_ARGS);
+    case 4: return launch_score_g<4>(r, LOCKS_ARGS);
+#undef LOCKS_ARGS
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int G>
 static void launch_select_g(dim3 grid, int MP, const float* scores, const int32_t* lens,
-                            const int32_t* budgets, int32_t* sel, int32_t* cnt, uint32_t* keybuf,
+                            const int32_t* budgets, int32_t* sel, int32_t* cnt, float* keybuf,
                             int H, int max_budget, hipStream_t st) {
   if (MP <= kSelectLdsPages) {
     hipLaunchKernelGGL((select_kernel<G, true>), grid, dim3(kSelectThreads),
-                       (size_t)MP * sizeof(uint32_t), st, scores, lens, budgets, sel, cnt, keybuf,
+                       (size_t)MP * sizeof(float), st, scores, lens, budgets, sel, cnt, keybuf,
                        H, MP, max_budget);
   } else {
     hipLaunchKernelGGL((select_kernel<G, false>), grid, dim3(kSelectThreads), 0, st, scores, lens,
@@ -517,7 +597,7 @@ static void launch_select_g(dim3 grid, int MP, const float* scores, const int32_
 }
 
 hipError_t launch_select(int G, const float* scores, const int32_t* lens, const int32_t* budgets,
-                         int32_t* sel, int32_t* cnt, uint32_t* keybuf, int S, int H, int MP,
+                         int32_t* sel, int32_t* cnt, float* keybuf, int S, int H, int MP,
                          int max_budget, hipStream_t st) {
   dim3 grid(H, S);
   switch (G) {

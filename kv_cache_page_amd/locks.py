@@ -130,8 +130,8 @@ def alloc_summaries(dims, num_blocks, device):
 
 
 def alloc_workspace(dims, num_seqs, max_pages, max_budget, device):
-    """Zero-filled workspace of locks_workspace_bytes bytes."""
-    return torch.zeros(max(workspace_bytes(dims, num_seqs, max_pages, max_budget), 1),
+    """Workspace of locks_workspace_bytes bytes (no initialisation needed)."""
+    return torch.empty(max(workspace_bytes(dims, num_seqs, max_pages, max_budget), 1),
                        dtype=torch.uint8, device=device)
 
 

@@ -170,6 +170,21 @@ def test_long_table_global_keys(L):
     _check_against_oracle(bw, summ, res, 8, 64)
 
 
+def test_equal_keys_take_lowest_pages(L):
+    """q = 0 gives every page the same score, so all keys tie: the selection
+    must be the sink, the recent page and the lowest-numbered candidates
+    (this also drives the exact fallback for a crowded crossing bin)."""
+    _say("[gpu] all keys equal")
+    b = synth.make_decode_batch([3000 * 16 + 7, 40 * 16], 1, 4, [100, 9], seed=77)
+    b.q.zero_()
+    summ = Hh.oracle_summaries(b.k_pool, b.block_table, b.seq_lens, 1, 8, b.num_blocks)
+    res = _run_decode(L, L.Dims(1, 4, 8), _to_dev(b), torch.from_numpy(summ).to(DEV), 100)
+    P0, P1 = 3001, 40
+    assert list(res["sel"][0, 0, :100]) == [0] + list(range(1, 99)) + [P0 - 1]
+    assert list(res["sel"][1, 0, :9]) == [0] + list(range(1, 8)) + [P1 - 1]
+    _check_against_oracle(b, summ, res, 8, 100)
+
+
 def test_invalid_block_ids_are_skipped(L):
     _say("[gpu] out-of-range block ids")
     b = synth.make_decode_batch([50 * 16], 1, 4, [10], seed=70)
