@@ -10,9 +10,10 @@ step runs at exactly 131072 tokens.
 
 One step = for every layer: append the new token's K/V, build the summary of
 the page that just filled (when one did), score every full page from the
-summaries, select sink + recent + top-126 pages, and attend over them. Each
-step is captured once as a HIP graph; W warm-up steps run, then K steps are
-timed between HIP events.
+summaries, select sink + recent + top-126 pages, and attend over them, all
+through locks_decode_step (two launches per layer, three on the steps whose
+token completes a page). Each step is captured once as a HIP graph; W
+warm-up steps run, then K steps are timed between HIP events.
 
 Throughput counts the metric's algorithmic bytes: 818 summary bytes per full
 page and KV head, plus 8192 bytes per selected full page (512 per valid token
@@ -177,7 +178,7 @@ def main():
         f"({build_pages / build_ms / 1e3:.2f} M pages/s)")
 
     # ---- per-step inputs: lengths, appended tokens (the cache already holds
-    # them; the append rewrites them through locks_append_kv), queries
+    # them; each step writes its token again), queries
     lens_dev = torch.tensor(lens, dtype=torch.int32, device=dev)
     budgets = torch.tensor([BUDGET], dtype=torch.int32, device=dev)
     kn = torch.empty(n_steps, LAYERS, 1, H, D, dtype=torch.bfloat16, device=dev)
@@ -187,31 +188,20 @@ def main():
         for l in range(LAYERS):
             kn[t, l, 0] = stack.k_pools[l][blk, :, slot]
             vn[t, l, 0] = stack.v_pools[l][blk, :, slot]
-    sel = torch.empty(1, H, BUDGET, dtype=torch.int32, device=dev)
-    cnt = torch.empty(1, H, dtype=torch.int32, device=dev)
+    lens_host = [torch.tensor([Lt], dtype=torch.int32) for Lt in lens]
     scores = torch.empty(1, H, MP, G, dtype=torch.float32, device=dev)
     out = torch.empty(1, H * G, D, dtype=torch.float32, device=dev)
     lse = torch.empty(1, H * G, dtype=torch.float32, device=dev)
     ws = L.alloc_workspace(dims, 1, MP, BUDGET, dev)
 
-    def layer_core(t, l):
-        ln = lens_dev[t:t + 1]
-        L.score_pages(dims, stack.q[t, l], summ[l], table, ln, scores)
-        L.select_pages(dims, scores, ln, budgets, MP, BUDGET, sel, cnt, ws)
-        L.sparse_attn(dims, stack.q[t, l], stack.k_pools[l], stack.v_pools[l], table, ln, sel,
-                      cnt, BUDGET, out, ws, lse_out=lse)
-
     def full_step(t):
+        # one decode step of every layer: append, build of the page the token
+        # completes (1 step in 16), score, select, attend
         ln = lens_dev[t:t + 1]
         for l in range(LAYERS):
-            L.append_kv(dims, kn[t, l], vn[t, l], stack.k_pools[l], stack.v_pools[l], table, ln)
-            if lens[t] % B == 0:
-                L.build_filled(dims, stack.k_pools[l], table, ln, summ[l])
-            layer_core(t, l)
-
-    def core_step(t):
-        for l in range(LAYERS):
-            layer_core(t, l)
+            L.decode_step(dims, stack.q[t, l], kn[t, l], vn[t, l], stack.k_pools[l],
+                          stack.v_pools[l], summ[l], table, ln, budgets, BUDGET, out, ws,
+                          lse_out=lse, seq_lens_host=lens_host[t])
 
     def score_only(t):
         for l in range(LAYERS):
@@ -243,7 +233,6 @@ def main():
 
     log(f"[bench] capturing {n_steps} step graphs ({LAYERS} layers each)")
     g_full = capture(full_step, range(n_steps))
-    g_core = capture(core_step, range(W, n_steps))
     g_score = capture(score_only, range(W, n_steps))
 
     log(f"[bench] warm-up {W} steps, then {K} timed steps")
@@ -251,14 +240,11 @@ def main():
         g_full[t].replay()
     torch.cuda.synchronize()
     full_ms = timed(g_full, range(W, n_steps))
-    core_ms = timed(g_core, range(W, n_steps))
     score_ms = timed(g_score, range(W, n_steps))
     timed_bytes = sum(step_bytes(lens[t]) for t in range(W, n_steps))
     ms_step = full_ms / K
     value = timed_bytes / (full_ms / 1e3) / 1e9
-    core_value = timed_bytes / (core_ms / 1e3) / 1e9
-    log(f"[bench] full step {ms_step * 1e3:.1f} us ({value:.0f} GB/s); "
-        f"score+select+attention only {core_ms / K * 1e3:.1f} us ({core_value:.0f} GB/s)")
+    log(f"[bench] decode step {ms_step * 1e3:.1f} us ({value:.0f} GB/s)")
 
     # dominant kernel: the page-score kernel, F x H slots of 818 bytes per launch
     score_launches = K * LAYERS
@@ -297,8 +283,6 @@ def main():
             "page_size": B, "rank": R, "budget_pages": BUDGET, "parallelism": "none (1 GPU)",
         },
         "bytes_per_step": round(timed_bytes / K),
-        "core_us_per_step": round(core_ms / K * 1e3, 2),
-        "core_gbps": round(core_value, 2),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "bulk_build_pages_per_s": round(build_pages / (build_ms / 1e3)),
         "roofline": {

@@ -92,8 +92,8 @@ size_t locks_summary_slot_bytes(const locks_dims* dims);  /* payload; 0 if dims 
 size_t locks_summary_slot_stride(const locks_dims* dims); /* bytes between slots; 0 if invalid */
 
 /*
- * Bytes of device workspace that locks_score_select, locks_select_pages and
- * locks_sparse_attn need for up to num_seqs sequences of up to max_pages pages
+ * Bytes of device workspace that locks_score_select, locks_select_pages,
+ * locks_sparse_attn and locks_decode_step need for up to num_seqs sequences of up to max_pages pages
  * and budgets of up to max_budget pages. One workspace may serve all of them
  * when the calls are ordered on one stream; its contents need no
  * initialisation and carry nothing between calls. Returns 0 for invalid
@@ -224,6 +224,42 @@ locks_status locks_sparse_attn(const locks_dims* dims, const void* q, const void
                                const int32_t* sel_pages, const int32_t* sel_count,
                                int32_t num_seqs, int32_t max_pages, int32_t max_budget,
                                float* out, float* lse_out, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * locks_decode_step -- one whole decode step of one layer, [N] §2 figure 1
+ * and §4.4 Algorithm 2 end to end, with the same results as the sequence
+ *   locks_append_kv -> locks_build_filled -> locks_score_select ->
+ *   locks_sparse_attn
+ * (up to floating-point summation order), in two or three launches:
+ *   1. only when a sequence's new token completes a page: append every new
+ *      token and build the summaries of the completed pages (their last key
+ *      is taken from k_new);
+ *   2. score every full page, keeping per 128-page tile the (max, sum exp)
+ *      of the scores for Z_g (and append the new tokens when step 1 did not
+ *      run);
+ *   3. select S and attend: every attention workgroup of a (sequence, KV
+ *      head) recomputes the same selection, attends its share of S, and the
+ *      last one to finish merges the shares in split order.
+ * Arguments are those of the calls above; seq_lens counts the new token.
+ * seq_lens_host (HOST pointer, optional): a host copy of seq_lens, used only
+ *   to skip step 1 when no length is a positive multiple of page_size; with
+ *   NULL step 1 always runs. It must equal seq_lens.
+ * sel_pages / sel_count (optional, both or neither): the selection, as
+ *   locks_score_select writes it.
+ * Tables of more than 16384 pages or budgets above 2048 pages take separate
+ *   select and attention launches, which need sel_pages / sel_count
+ *   (UNSUPPORTED without them).
+ * Errors as for locks_score_select, plus INVALID_ARG for a null k_new, v_new,
+ *   k_pool, v_pool or out, or only one of sel_pages / sel_count.
+ */
+locks_status locks_decode_step(const locks_dims* dims, const void* q, const void* k_new,
+                               const void* v_new, void* k_pool, void* v_pool, void* summaries,
+                               int64_t num_blocks, const int32_t* block_table,
+                               const int32_t* seq_lens, const int32_t* seq_lens_host,
+                               const int32_t* budgets, int32_t num_seqs, int32_t max_pages,
+                               int32_t max_budget, float* out, float* lse_out,
+                               int32_t* sel_pages, int32_t* sel_count, void* workspace,
                                size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus

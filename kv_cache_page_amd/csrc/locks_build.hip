@@ -91,11 +91,19 @@ __device__ __forceinline__ void jacobi_round(double (&b)[kPage], double (&ub)[kP
   for (int x = 0; x < kPage; ++x) b[x] = c * b[x] - sr * pr[x];
 }
 
+// Pages come from a list of block ids (ids != nullptr: all H heads of each)
+// or, in filled-page mode, from the sequences whose length is a multiple of
+// the page size (their last page). In filled-page mode knew/vnew (optional)
+// carry the token at position len - 1 of every sequence: it is appended to
+// kdst/vdst (the pools) and, where it completes a page, taken as that page's
+// last key straight from knew.
 template <int R>
 __global__ __launch_bounds__(64) void build_kernel(
     const uint16_t* __restrict__ kpool, int64_t num_blocks, int H,
     const int32_t* __restrict__ ids, int n, const int32_t* __restrict__ table,
-    const int32_t* __restrict__ lens, int MP, uint8_t* __restrict__ summ) {
+    const int32_t* __restrict__ lens, int MP, uint8_t* __restrict__ summ,
+    const uint16_t* __restrict__ knew, const uint16_t* __restrict__ vnew,
+    uint16_t* __restrict__ kdst, uint16_t* __restrict__ vdst) {
   constexpr SlotLayout L = slot_layout(R);
   __shared__ float kt[kBuildPages][kPage][kRowPad];
   __shared__ double urow[kBuildPages][kPage][kPage + 1];
@@ -108,6 +116,7 @@ __global__ __launch_bounds__(64) void build_kernel(
   // ---- which page this lane group builds
   int64_t slot = -1;
   int blk = 0, head = 0;
+  const uint8_t* last_key = nullptr;  // row 15 of the page, when it comes from knew
   {
     if (ids) {
       if (item < (int64_t)n * H) {
@@ -121,9 +130,23 @@ __global__ __launch_bounds__(64) void build_kernel(
         const int sq = (int)(item / H);
         head = (int)(item % H);
         const int len = lens[sq];
+        const int64_t src = ((int64_t)sq * H + head) * kHeadDim;
+        if (knew && len >= 1 && len <= MP * kPage) {
+          const int b = table[(int64_t)sq * MP + (len - 1) / kPage];
+          if (b >= 0 && b < num_blocks) {
+            const int64_t dst =
+                (((int64_t)b * H + head) * kPage + (len - 1) % kPage) * kHeadDim + 8 * i;
+            *reinterpret_cast<uint4*>(kdst + dst) = *reinterpret_cast<const uint4*>(knew + src + 8 * i);
+            *reinterpret_cast<uint4*>(vdst + dst) = *reinterpret_cast<const uint4*>(vnew + src + 8 * i);
+          }
+        }
         if (len > 0 && len % kPage == 0 && len / kPage <= MP) {
           const int b = table[(int64_t)sq * MP + len / kPage - 1];
-          if (b >= 0 && b < num_blocks) { blk = b; slot = (int64_t)b * H + head; }
+          if (b >= 0 && b < num_blocks) {
+            blk = b;
+            slot = (int64_t)b * H + head;
+            if (knew) last_key = reinterpret_cast<const uint8_t*>(knew + src);
+          }
         }
       }
     }
@@ -138,7 +161,9 @@ __global__ __launch_bounds__(64) void build_kernel(
     const uint8_t* kb = reinterpret_cast<const uint8_t*>(kpool + kofs);
 #pragma unroll 4
     for (int t = 0; t < kPage; ++t) {
-      const uint4 w = *reinterpret_cast<const uint4*>(kb + t * 256 + 16 * i);
+      const uint8_t* rowp = (last_key && t == kPage - 1) ? last_key : kb + t * 256;
+      const uint4 w = (slot >= 0) ? *reinterpret_cast<const uint4*>(rowp + 16 * i)
+                                  : make_uint4(0u, 0u, 0u, 0u);
       const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
       float f[8];
 #pragma unroll
@@ -370,24 +395,30 @@ __global__ void append_kernel(const uint16_t* __restrict__ knew, const uint16_t*
 template <int R>
 static hipError_t launch_build_r(const uint16_t* kpool, int64_t nb, int H, const int32_t* ids,
                                  int n, const int32_t* table, const int32_t* lens, int MP,
-                                 uint8_t* summ, hipStream_t st) {
+                                 uint8_t* summ, const uint16_t* knew, const uint16_t* vnew,
+                                 uint16_t* kdst, uint16_t* vdst, hipStream_t st) {
   const int64_t items = (int64_t)n * H;
   if (items == 0) return hipSuccess;
   const int64_t grid = (items + kBuildPages - 1) / kBuildPages;
   hipLaunchKernelGGL(build_kernel<R>, dim3((unsigned)grid), dim3(64), 0, st, kpool, nb, H, ids, n,
-                     table, lens, MP, summ);
+                     table, lens, MP, summ, knew, vnew, kdst, vdst);
   return hipGetLastError();
 }
 
+// knew/vnew (filled-page mode only, may be null): append the new token too.
 hipError_t launch_build(int r, const void* kpool, int64_t nb, int H, const int32_t* ids, int n,
                         const int32_t* table, const int32_t* lens, int MP, void* summ,
-                        hipStream_t st) {
+                        const void* knew, const void* vnew, void* vpool, hipStream_t st) {
   const uint16_t* kp = static_cast<const uint16_t*>(kpool);
   uint8_t* sm = static_cast<uint8_t*>(summ);
+  const uint16_t* kn = static_cast<const uint16_t*>(knew);
+  const uint16_t* vn = static_cast<const uint16_t*>(vnew);
+  uint16_t* kd = const_cast<uint16_t*>(kp);
+  uint16_t* vd = static_cast<uint16_t*>(vpool);
   switch (r) {
 #define LOCKS_R(RR) \
   case RR:          \
-    return launch_build_r<RR>(kp, nb, H, ids, n, table, lens, MP, sm, st);
+    return launch_build_r<RR>(kp, nb, H, ids, n, table, lens, MP, sm, kn, vn, kd, vd, st);
     LOCKS_R(1) LOCKS_R(2) LOCKS_R(3) LOCKS_R(4) LOCKS_R(5) LOCKS_R(6) LOCKS_R(7) LOCKS_R(8)
     LOCKS_R(9) LOCKS_R(10) LOCKS_R(11) LOCKS_R(12) LOCKS_R(13) LOCKS_R(14) LOCKS_R(15) LOCKS_R(16)
 #undef LOCKS_R

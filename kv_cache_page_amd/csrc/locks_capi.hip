@@ -11,7 +11,8 @@ namespace locks {
 hipError_t launch_score(int r, int G, const void* q, const void* summ, const int32_t* table,
                         const int32_t* lens, float* scores, int64_t nb, int S, int H, int MP,
                         int fill_nan, float2* zpart, const void* knew, const void* vnew,
-                        void* kpool, void* vpool, hipStream_t st);
+                        void* kpool, void* vpool, uint32_t* counters, float* mxout,
+                        hipStream_t st);
 hipError_t launch_select(int G, const float* scores, const int32_t* lens, const int32_t* budgets,
                          int32_t* sel, int32_t* cnt, float* keybuf, int S, int H, int MP,
                          int max_budget, hipStream_t st);
@@ -21,7 +22,14 @@ hipError_t launch_attn(int G, const void* q, const void* kpool, const void* vpoo
                        int S, int H, int MP, int max_budget, int nsplit, int ppw, hipStream_t st);
 hipError_t launch_build(int r, const void* kpool, int64_t nb, int H, const int32_t* ids, int n,
                         const int32_t* table, const int32_t* lens, int MP, void* summ,
-                        hipStream_t st);
+                        const void* knew, const void* vnew, void* vpool, hipStream_t st);
+bool decode_shape(int MP, int KB, int* ppw, int* nsplit);
+hipError_t launch_decode(int G, const float* escore, const float* pmax, const float2* zpart,
+                         int ntiles,
+                         const int32_t* lens, const int32_t* budgets, const void* q,
+                         const void* kpool, const void* vpool, const int32_t* table, int64_t nb,
+                         int S, int H, int MP, int KB, int nsplit, int ppw, float* part,
+                         float* out, float* lse_out, int32_t* sel, int32_t* cnt, hipStream_t st);
 hipError_t launch_append(const void* knew, const void* vnew, void* kpool, void* vpool, int64_t nb,
                          const int32_t* table, const int32_t* lens, int S, int H, int MP,
                          hipStream_t st);
@@ -52,23 +60,37 @@ locks_status check_dims(const locks_dims* d) {
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Workspace regions: page scores [S][H][MP][G] (or, for the fused decode
+// step, e_g per page and query); per-page maxima [S][H][MP]; per-tile base-2
+// (max, sum) partials [S][H][tiles][G]; selection keys of the separate select kernel
+// [S][H][MP]; attention partials [S][H][splits][G][kPartStride].
 struct Workspace {
-  size_t scores, keys, parts, total;
-  int nsplit;
+  size_t scores, pmax, zpart, keys, parts, total;
+  int nsplit, ntiles;
 };
+
+constexpr int kPartStride = locks::kHeadDim + 4;
 
 Workspace carve(const locks_dims* d, int32_t S, int32_t MP, int32_t KB) {
   Workspace w{};
   const size_t sh = (size_t)S * d->num_kv_heads;
   const int per_wg = kAttnWaves * attn_pages_per_wave(KB);
   w.nsplit = (KB + per_wg - 1) / per_wg;
+  w.ntiles = (MP + locks::kScorePagesPerWg - 1) / locks::kScorePagesPerWg;
+  int ppw_f, ns_f;
+  const int part_splits =
+      locks::decode_shape(MP, KB, &ppw_f, &ns_f) && ns_f > w.nsplit ? ns_f : w.nsplit;
   size_t off = 0;
   w.scores = off;
   off = align_up(off + sh * MP * d->group_size * sizeof(float));
+  w.pmax = off;
+  off = align_up(off + sh * MP * sizeof(float));
+  w.zpart = off;
+  off = align_up(off + sh * w.ntiles * d->group_size * 2 * sizeof(float));
   w.keys = off;
   off = align_up(off + sh * MP * sizeof(uint32_t));
   w.parts = off;
-  off = align_up(off + sh * w.nsplit * d->group_size * (locks::kHeadDim + 2) * sizeof(float));
+  off = align_up(off + sh * part_splits * d->group_size * kPartStride * sizeof(float));
   w.total = off;
   return w;
 }
@@ -123,7 +145,8 @@ locks_status locks_build(const locks_dims* d, const void* k_pool, int64_t nb,
   if (!k_pool || !block_ids || !summaries) return LOCKS_ERR_INVALID_ARG;
   if (!aligned16(k_pool) || !aligned16(summaries)) return LOCKS_ERR_INVALID_ARG;
   return hip_status(locks::launch_build(d->rank, k_pool, nb, d->num_kv_heads, block_ids, n,
-                                        nullptr, nullptr, 0, summaries, st));
+                                        nullptr, nullptr, 0, summaries, nullptr, nullptr, nullptr,
+                                        st));
 }
 
 locks_status locks_build_filled(const locks_dims* d, const void* k_pool, int64_t nb,
@@ -136,7 +159,8 @@ locks_status locks_build_filled(const locks_dims* d, const void* k_pool, int64_t
   if (!k_pool || !block_table || !seq_lens || !summaries) return LOCKS_ERR_INVALID_ARG;
   if (!aligned16(k_pool) || !aligned16(summaries)) return LOCKS_ERR_INVALID_ARG;
   return hip_status(locks::launch_build(d->rank, k_pool, nb, d->num_kv_heads, nullptr, S,
-                                        block_table, seq_lens, MP, summaries, st));
+                                        block_table, seq_lens, MP, summaries, nullptr, nullptr,
+                                        nullptr, st));
 }
 
 locks_status locks_append_kv(const locks_dims* d, const void* k_new, const void* v_new,
@@ -174,7 +198,7 @@ locks_status locks_score_select(const locks_dims* d, const void* q, const void* 
   const int H = d->num_kv_heads, G = d->group_size;
   hipError_t he = locks::launch_score(d->rank, G, q, summaries, block_table, seq_lens, scores, nb,
                                       S, H, MP, scores_out ? 1 : 0, nullptr, nullptr, nullptr, nullptr,
-                                      nullptr, st);
+                                      nullptr, nullptr, nullptr, st);
   if (he != hipSuccess) return LOCKS_ERR_HIP;
   he = locks::launch_select(G, scores, seq_lens, budgets, sel_pages, sel_count,
                             reinterpret_cast<float*>(ws + w.keys), S, H, MP, KB, st);
@@ -193,7 +217,7 @@ locks_status locks_score_pages(const locks_dims* d, const void* q, const void* s
   if (!aligned16(q) || !aligned16(summaries)) return LOCKS_ERR_INVALID_ARG;
   return hip_status(locks::launch_score(d->rank, d->group_size, q, summaries, block_table,
                                         seq_lens, scores, nb, S, d->num_kv_heads, MP, 0, nullptr,
-                                        nullptr, nullptr, nullptr, nullptr, st));
+                                        nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, st));
 }
 
 locks_status locks_select_pages(const locks_dims* d, const float* scores, const int32_t* seq_lens,
@@ -235,6 +259,71 @@ locks_status locks_sparse_attn(const locks_dims* d, const void* q, const void* k
       d->group_size, q, k_pool, v_pool, block_table, seq_lens, sel_pages, sel_count,
       reinterpret_cast<float*>(ws + w.parts), out, lse_out, nb, S, d->num_kv_heads, MP, KB,
       w.nsplit, attn_pages_per_wave(KB), st));
+}
+
+locks_status locks_decode_step(const locks_dims* d, const void* q, const void* k_new,
+                               const void* v_new, void* k_pool, void* v_pool, void* summaries,
+                               int64_t nb, const int32_t* block_table, const int32_t* seq_lens,
+                               const int32_t* seq_lens_host, const int32_t* budgets, int32_t S,
+                               int32_t MP, int32_t KB, float* out, float* lse_out,
+                               int32_t* sel_pages, int32_t* sel_count, void* workspace,
+                               size_t ws_bytes, hipStream_t st) {
+  locks_status e = check_dims(d);
+  if (e != LOCKS_OK) return e;
+  e = check_batch(S, MP, KB, nb);
+  if (e != LOCKS_OK) return e;
+  if (S == 0) return LOCKS_OK;
+  if (!q || !k_new || !v_new || !k_pool || !v_pool || !summaries || !block_table || !seq_lens ||
+      !budgets || !out)
+    return LOCKS_ERR_INVALID_ARG;
+  if ((sel_pages == nullptr) != (sel_count == nullptr)) return LOCKS_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) ||
+      !aligned16(v_pool) || !aligned16(summaries))
+    return LOCKS_ERR_INVALID_ARG;
+  const Workspace w = carve(d, S, MP, KB);
+  if (!workspace || ws_bytes < w.total) return LOCKS_ERR_WORKSPACE;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const int H = d->num_kv_heads, G = d->group_size;
+
+  // 1. append (+ summaries of the pages the new token completes)
+  bool completes = true;
+  if (seq_lens_host) {
+    completes = false;
+    for (int32_t i = 0; i < S; ++i)
+      if (seq_lens_host[i] > 0 && seq_lens_host[i] % locks::kPage == 0) completes = true;
+  }
+  if (completes) {
+    hipError_t he = locks::launch_build(d->rank, k_pool, nb, H, nullptr, S, block_table, seq_lens,
+                                        MP, summaries, k_new, v_new, v_pool, st);
+    if (he != hipSuccess) return LOCKS_ERR_HIP;
+  }
+  // 2. scores of all full pages and Z partials (and the append when no page
+  //    completes)
+  float* scores = reinterpret_cast<float*>(ws + w.scores);
+  float2* zpart = reinterpret_cast<float2*>(ws + w.zpart);
+  int ppw, nsplit;
+  const bool fused = locks::decode_shape(MP, KB, &ppw, &nsplit);
+  float* pmax = reinterpret_cast<float*>(ws + w.pmax);
+  hipError_t he = locks::launch_score(d->rank, G, q, summaries, block_table, seq_lens, scores, nb,
+                                      S, H, MP, 0, zpart, completes ? nullptr : k_new,
+                                      completes ? nullptr : v_new, k_pool, v_pool, nullptr,
+                                      fused ? pmax : nullptr, st);
+  if (he != hipSuccess) return LOCKS_ERR_HIP;
+  // 3. selection + attention + merge
+  float* parts = reinterpret_cast<float*>(ws + w.parts);
+  if (fused) {
+    return hip_status(locks::launch_decode(G, scores, pmax, zpart, w.ntiles, seq_lens, budgets, q,
+                                           k_pool, v_pool, block_table, nb, S, H, MP, KB, nsplit,
+                                           ppw, parts, out, lse_out, sel_pages, sel_count, st));
+  }
+  // long tables or budgets: the separate select and attention kernels
+  if (!sel_pages) return LOCKS_ERR_UNSUPPORTED;
+  he = locks::launch_select(G, scores, seq_lens, budgets, sel_pages, sel_count,
+                            reinterpret_cast<float*>(ws + w.keys), S, H, MP, KB, st);
+  if (he != hipSuccess) return LOCKS_ERR_HIP;
+  return hip_status(locks::launch_attn(G, q, k_pool, v_pool, block_table, seq_lens, sel_pages,
+                                       sel_count, parts, out, lse_out, nb, S, H, MP, KB,
+                                       w.nsplit, attn_pages_per_wave(KB), st));
 }
 
 }  // extern "C"

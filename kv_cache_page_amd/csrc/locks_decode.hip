@@ -1,0 +1,493 @@
+// LOCKS decode step, second kernel: page selection, sparse attention over the
+// selected pages, and the merge of the split partials, in one launch (gfx950).
+//
+// [N] = LOCKS reading notes (zhongzhuzhou.org 2026-07-29): §4.4 Algorithm 2
+// (query-aware selection of the sink page, the most recent page and the
+// top-(k-2) pages by the group-shared estimate of eq. 5), then §3.1 eq. 1
+// (softmax attention renormalised over the selected set S).
+//
+// Grid (H, nsplit, S) with 512-thread workgroups; consecutive workgroup ids
+// walk the KV heads first, so with 8 heads every split of a head runs on the
+// same XCD as the score tiles of that head. Every workgroup of a (sequence,
+// KV head) computes the whole selection itself: the computation is
+// deterministic, so all of them obtain the same ascending page list without
+// any inter-workgroup signal. Workgroup x then attends list entries
+// [x * 8 * ppw, (x + 1) * 8 * ppw), one wave per ppw pages, and writes one
+// partial (an empty one when it has no entries); a small second kernel merges
+// the nsplit partials of each (sequence, KV head) in split order. (A merge by
+// the last workgroup to arrive needs a release fence, an atomic round trip
+// and an acquire in the critical path: measured slower than the extra launch.)
+//
+// Inputs from the score kernel (decode layout): per page j and query g,
+// e_jg = 2^(s_jg - m_j) with m_j = max_g s_jg (base-2 scores), and m_j; per
+// 128-page tile and query, the base-2 (max, sum) of the scores. Thread t owns
+// pages t, t + 512, t + 1024, ...; their e, m and block ids are loaded at
+// kernel start, before the sequence length is known.
+//
+// Selection, in base-2 units:
+//   1. log2 Z_g from the tile partials (each wave reduces them by itself);
+//   2. key_j = log2 mean_g 2^(s_jg - log2 Z_g)
+//            = m_j - Zx + log2(sum_g e_jg W_g) - log2 G, W_g = 2^(Zx - log2 Z_g),
+//      Zx = max_g log2 Z_g, for candidates 1..P-2 (one log2 per page; exact
+//      while the group's log2 Z_g lie within 126 of each other). Keys are
+//      log-shares, so key_j <= 0;
+//   3. histogram of bin_j = floor(-key_j * 16), clamped to [0, 511] (1/16
+//      wide, order-preserving; bin 511, which holds the far tail and -inf
+//      keys, is counted by difference); one wave scans it for the bin t where
+//      the top-(k-2) count is crossed;
+//   4. inside bin t the remaining slots go to the largest keys, lower page
+//      first on ties (pairwise ranking, or an exact 8-bit radix select on the
+//      order-preserving key bits when more than 512 candidates share bin t);
+//   5. one 64-page ballot per wave and register slot builds the membership
+//      bitmap; one wave turns word popcounts into offsets, and each owner
+//      writes its selected pages (with their block ids) in ascending order.
+#include "locks_attn_core.h"
+#include "locks_select.h"
+
+namespace locks {
+
+constexpr int kDecThreads = 512;
+constexpr int kDecWaves = kDecThreads / 64;
+constexpr int kDecMaxBudget = 2048;  // selection list held in LDS
+constexpr int kDecMaxSplits = 32;
+constexpr int kDecMaxPpw = 8;  // pages per wave
+constexpr float kDecBinsPerUnit = 16.f;
+constexpr int kHistCopies = 8;  // lanes spread their histogram atomics over 8 copies
+static_assert(kBins == kDecThreads, "one histogram bin per thread");
+
+// Exclusive prefix sum over one wave.
+__device__ __forceinline__ int wave_exclusive_scan(int v, int lane) {
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x - v;
+}
+
+template <int G, int kRP>
+__global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
+    const float* __restrict__ escore, const float* __restrict__ pmax,
+    const float2* __restrict__ zpart, int ntiles, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ budgets, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ kpool, const uint16_t* __restrict__ vpool,
+    const int32_t* __restrict__ table, int64_t num_blocks, int H, int MP, int max_budget,
+    int nsplit, int ppw, float* __restrict__ part, int32_t* __restrict__ sel_pages,
+    int32_t* __restrict__ sel_count) {
+  constexpr int kWords = kRP * kDecThreads / 32;  // membership bitmap words (<= 512)
+  static_assert(kWords <= kDecThreads && kWords % 64 == 0, "bitmap words");
+  constexpr int kWordsPerLane = kWords / 64;
+  __shared__ uint32_t histc[kHistCopies][kBins + 1];  // padded: copy c of bin b in bank (b + c) % 32
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t bits[kWords];
+  __shared__ uint4 sh_q[G * kHeadDim / 8];
+  __shared__ int woff[kWords];
+  __shared__ float cand_key[kDecThreads];
+  __shared__ uint32_t cand_page[kDecThreads];  // also the tie bitmap of the radix path
+  __shared__ int sel_list[kDecMaxBudget];
+  __shared__ int sel_blk[kDecMaxBudget];
+  __shared__ int sh_waves[16];
+  __shared__ int sh_int[4];
+  __shared__ float sh_acc[kDecWaves][G][kHeadDim];
+  __shared__ float sh_ml[kDecWaves][G][2];
+
+  const int h = blockIdx.x, x = blockIdx.y, s = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t sh_idx = (int64_t)s * H + h;
+
+  // ---- every independent load first
+  const int len_raw = seq_lens[s];
+  const int bud_raw = budgets[s];
+  float ev[kRP][G], mv[kRP];
+  int bk[kRP];
+  {
+    const float* er = escore + sh_idx * MP * G;
+    const float* mr = pmax + sh_idx * MP;
+    const int32_t* tr = table + (int64_t)s * MP;
+#pragma unroll
+    for (int u = 0; u < kRP; ++u) {
+      const int j = u * kDecThreads + tid;
+      if (j < MP) {
+        load_scores<G>(er + (int64_t)j * G, ev[u]);
+        mv[u] = mr[j];
+        bk[u] = tr[j];
+      } else {
+#pragma unroll
+        for (int g = 0; g < G; ++g) ev[u][g] = 0.f;
+        mv[u] = -__builtin_inff();
+        bk[u] = -1;
+      }
+    }
+  }
+  if (tid < G * kHeadDim / 8) sh_q[tid] = reinterpret_cast<const uint4*>(q + sh_idx * G * kHeadDim)[tid];
+  float2 zl[2][G];
+  const float2* zp = zpart + sh_idx * ntiles * G;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int t = lane + 64 * c;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      zl[c][g] = (t < ntiles) ? zp[t * G + g] : make_float2(-__builtin_inff(), 0.f);
+  }
+
+  const int len = clampi(len_raw, 0, MP * kPage);
+  const int P = (len + kPage - 1) / kPage;
+  const int F = len / kPage;
+  const int k = clampi(bud_raw, 2, max_budget);
+  int n;
+  if (P == 0 || k >= P) {
+    n = P;  // every page (P <= k <= max_budget)
+#pragma unroll
+    for (int u = 0; u < kRP; ++u) {
+      const int j = u * kDecThreads + tid;
+      if (j < P) {
+        sel_list[j] = j;
+        sel_blk[j] = bk[u];
+      }
+    }
+  } else {
+    // From here P >= 3, k < P and pages 0..P-2 are full (F >= P-1).
+    // ---- 1. log2 Z_g over the F full pages (tiles beyond F hold nothing)
+    const int ntu = (F + kScorePagesPerWg - 1) / kScorePagesPerWg;
+    float lz[G], zx = -__builtin_inff();
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float m0 = (lane < ntu) ? zl[0][g].x : -__builtin_inff();
+      const float m1 = (lane + 64 < ntu) ? zl[1][g].x : -__builtin_inff();
+      const float M = wave_allmax(fmaxf(m0, m1));
+      float c = 0.f;
+      if (m0 != -__builtin_inff()) c += zl[0][g].y * __builtin_amdgcn_exp2f(m0 - M);
+      if (m1 != -__builtin_inff()) c += zl[1][g].y * __builtin_amdgcn_exp2f(m1 - M);
+      const float S = wave_allsum(c);
+      lz[g] = S > 0.f ? M + __builtin_amdgcn_logf(S) : -__builtin_inff();
+      zx = fmaxf(zx, lz[g]);
+    }
+    float wg[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      wg[g] = (lz[g] == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(fminf(zx - lz[g], 126.f));
+    const float log2G = (G == 1) ? 0.f : (G == 2) ? 1.f : 2.f;
+    // ---- 2. keys (<= 0) and their bins
+    auto is_cand = [&](int j) { return j >= 1 && j <= P - 2; };
+    float key[kRP];
+    int bin[kRP];
+#pragma unroll
+    for (int u = 0; u < kRP; ++u) {
+      const int j = u * kDecThreads + tid;
+      float t = 0.f;
+#pragma unroll
+      for (int g = 0; g < G; ++g) t = fmaf(ev[u][g], wg[g], t);
+      float kj = (mv[u] - zx) + (__builtin_amdgcn_logf(t) - log2G);
+      kj = (is_cand(j) && kj == kj) ? kj : -__builtin_inff();
+      key[u] = kj;
+      const float d = -kj * kDecBinsPerUnit;  // >= 0 up to rounding; +inf for -inf keys
+      bin[u] = d < (float)(kBins - 1) ? (d > 0.f ? (int)d : 0) : kBins - 1;
+    }
+    // ---- 3. histogram (bin 511 by difference) and crossing bin
+    for (int i = tid; i < kHistCopies * (kBins + 1); i += kDecThreads) (&histc[0][0])[i] = 0u;
+    if (tid == 0) { sh_int[0] = -1; sh_int[1] = 0; sh_int[2] = 0; sh_int[3] = 0; }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kRP; ++u)
+      if (bin[u] < kBins - 1) atomicAdd(&histc[lane & (kHistCopies - 1)][bin[u]], 1u);
+    __syncthreads();
+    {
+      uint32_t t = 0u;
+#pragma unroll
+      for (int c = 0; c < kHistCopies; ++c) t += histc[c][tid];
+      hist[tid] = t;
+    }
+    __syncthreads();
+    const int need0 = k - 2;
+    if (need0 > 0 && wave == 0) {
+      // lane l scans bins 8l .. 8l+7
+      int c8[8], tot = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { c8[e] = (int)hist[8 * lane + e]; tot += c8[e]; }
+      int before = wave_exclusive_scan(tot, lane);
+      if (lane == 63) c8[7] = (P - 2) - (before + tot - c8[7]);  // bin 511: the rest
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (before < need0 && before + c8[e] >= need0) {
+          sh_int[0] = 8 * lane + e;
+          sh_int[1] = need0 - before;
+          sh_int[2] = c8[e];
+        }
+        before += c8[e];
+      }
+    }
+    __syncthreads();
+    const int tbin = sh_int[0];
+    int need = sh_int[1];
+    const int ct = sh_int[2];
+    // ---- 4. pages below the crossing bin (and sink / recent) into the bitmap
+    {
+      // lane 2u + half of the wave collects word `half` of slot u's ballot
+      int wordv = 0;
+#pragma unroll
+      for (int u = 0; u < kRP; ++u) {
+        const int j = u * kDecThreads + tid;
+        const bool in = (j == 0 || j == P - 1) || (is_cand(j) && bin[u] < tbin);
+        const uint64_t bal = __ballot(in);
+        wordv = (lane == 2 * u) ? (int)(uint32_t)bal : wordv;
+        wordv = (lane == 2 * u + 1) ? (int)(uint32_t)(bal >> 32) : wordv;
+      }
+      if (lane < 2 * kRP) bits[(lane >> 1) * (kDecThreads / 32) + wave * 2 + (lane & 1)] = (uint32_t)wordv;
+    }
+    // ---- resolve inside the crossing bin
+    if (tbin >= 0) {
+      if (ct <= kDecThreads) {
+#pragma unroll
+        for (int u = 0; u < kRP; ++u) {
+          const int j = u * kDecThreads + tid;
+          if (is_cand(j) && bin[u] == tbin) {
+            const int slot = atomicAdd(&sh_int[3], 1);
+            cand_key[slot] = key[u];
+            cand_page[slot] = (uint32_t)j;
+          }
+        }
+        __syncthreads();
+        if (tid < ct) {
+          const float me = cand_key[tid];
+          const uint32_t mp = cand_page[tid];
+          int rank = 0;
+#pragma unroll 8
+          for (int e = 0; e < ct; ++e) {
+            const float o = cand_key[e];
+            rank += (o > me || (o == me && cand_page[e] < mp)) ? 1 : 0;
+          }
+          if (rank < need) atomicOr(&bits[mp >> 5], 1u << (mp & 31));
+        }
+      } else {
+        uint32_t prefix = 0u;
+        for (int shift = 24; shift >= 0; shift -= 8) {
+          __syncthreads();
+          if (tid < 256) hist[tid] = 0u;
+          __syncthreads();
+#pragma unroll
+          for (int u = 0; u < kRP; ++u) {
+            const int j = u * kDecThreads + tid;
+            const uint32_t o = float_to_ordered(key[u]);
+            if (is_cand(j) && bin[u] == tbin && (shift == 24 || (o >> (shift + 8)) == prefix))
+              atomicAdd(&hist[255 - ((o >> shift) & 255u)], 1u);  // descending order
+          }
+          __syncthreads();
+          const int c = (tid < 256) ? (int)hist[tid] : 0;
+          int tot;
+          const int before = block_exclusive_scan(c, sh_waves, &tot);
+          if (tid < 256 && before < need && before + c >= need) {
+            sh_int[0] = 255 - tid;
+            sh_int[1] = need - before;
+          }
+          __syncthreads();
+          prefix = (prefix << 8) | (uint32_t)sh_int[0];
+          need = sh_int[1];
+        }
+        // keys above `prefix` are in; of those equal to it, the `need` lowest pages
+        uint32_t* eqb = cand_page;
+        if (tid < kWords) eqb[tid] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kRP; ++u) {
+          const int j = u * kDecThreads + tid;
+          if (!is_cand(j) || bin[u] != tbin) continue;
+          const uint32_t o = float_to_ordered(key[u]);
+          if (o > prefix) atomicOr(&bits[j >> 5], 1u << (j & 31));
+          else if (o == prefix) atomicOr(&eqb[j >> 5], 1u << (j & 31));
+        }
+        __syncthreads();
+        const uint32_t ew = (tid < kWords) ? eqb[tid] : 0u;
+        int tot;
+        const int before = block_exclusive_scan(__popc(ew), sh_waves, &tot);
+        if (before < need) {
+          uint32_t w = ew, take = 0u;
+          for (int left = need - before; w && left > 0; --left) {
+            const uint32_t low = w & (0u - w);
+            take |= low;
+            w ^= low;
+          }
+          if (take) atomicOr(&bits[tid], take);
+        }
+      }
+    }
+    __syncthreads();
+    // ---- 5. word offsets (one wave), then owners write pages and block ids
+    if (wave == 0) {
+      int c[kWordsPerLane], tot = 0;
+#pragma unroll
+      for (int e = 0; e < kWordsPerLane; ++e) {
+        c[e] = __popc(bits[kWordsPerLane * lane + e]);
+        tot += c[e];
+      }
+      int before = wave_exclusive_scan(tot, lane);
+#pragma unroll
+      for (int e = 0; e < kWordsPerLane; ++e) {
+        woff[kWordsPerLane * lane + e] = before;
+        before += c[e];
+      }
+      if (lane == 63) sh_int[3] = before;
+    }
+    __syncthreads();
+    uint32_t wv[kRP];
+#pragma unroll
+    for (int u = 0; u < kRP; ++u) wv[u] = bits[(u * kDecThreads + tid) >> 5];
+    uint32_t mine = 0u;  // bit u: page u * 512 + tid is selected
+#pragma unroll
+    for (int u = 0; u < kRP; ++u) mine |= ((wv[u] >> (tid & 31)) & 1u) << u;
+    while (mine) {
+      const int u = __ffs(mine) - 1;
+      mine &= mine - 1u;
+      const int j = u * kDecThreads + tid;
+      int blk = bk[0];
+      uint32_t w = wv[0];
+#pragma unroll
+      for (int v = 1; v < kRP; ++v)
+        if (v == u) { blk = bk[v]; w = wv[v]; }
+      const int pos = woff[j >> 5] + __popc(w & ((1u << (j & 31)) - 1u));
+      if (pos < kDecMaxBudget) {
+        sel_list[pos] = j;
+        sel_blk[pos] = blk;
+      }
+    }
+    n = min(sh_int[3], max_budget);  // == k by construction
+  }
+  __syncthreads();
+
+  if (x == 0 && sel_pages) {
+    int32_t* o = sel_pages + sh_idx * max_budget;
+    for (int i = tid; i < max_budget; i += kDecThreads) o[i] = i < n ? sel_list[i] : -1;
+    if (tid == 0) sel_count[sh_idx] = n;
+  }
+  const int per_wg = kDecWaves * ppw;
+  const int base = x * per_wg + wave * ppw;
+  const int mine = clampi(n - base, 0, ppw);
+  // ---- attention over list entries [x * per_wg, (x + 1) * per_wg)
+  {
+    uint32_t qw[G][16];
+    attn_load_q<G>(qw, reinterpret_cast<const uint16_t*>(sh_q), lane);
+    AttnAcc<G> acc;
+    attn_init<G>(acc);
+    auto page_at = [&](int i, int64_t& off, int& nv) {
+      const int j = sel_list[base + i];
+      const int blk = sel_blk[base + i];
+      if (j < 0 || j >= P || blk < 0 || blk >= num_blocks) return;
+      off = ((int64_t)blk * H + h) * (kPage * kHeadDim);
+      nv = (j == P - 1) ? len - kPage * (P - 1) : kPage;
+    };
+    attn_wave_pages<G, kDecMaxPpw>(acc, qw, kpool, vpool, mine, page_at, lane);
+    attn_wave_to_lds<G>(acc, sh_acc[wave], sh_ml[wave], lane);
+  }
+  __syncthreads();
+  if (wave == 0)
+    wg_partial_store<G>(sh_acc, sh_ml, kDecWaves, part + (sh_idx * nsplit + x) * G * kPartStride,
+                        lane);
+}
+
+// Merge of the nsplit partials of one (sequence, KV head) in split order:
+// thread (g, d) owns output element d of query g. All partials exist (empty
+// ones carry max -inf, sum 0, acc 0); an empty selection gives out = 0 and
+// lse = -inf.
+template <int G>
+__global__ __launch_bounds__(kDecThreads) void decode_merge_kernel(
+    const float* __restrict__ part, float* __restrict__ out, float* __restrict__ lse_out, int H,
+    int nsplit) {
+  const int64_t sh_idx = (int64_t)blockIdx.y * H + blockIdx.x;
+  const int tid = threadIdx.x;
+  if (tid >= G * kHeadDim) return;
+  const int g = tid / kHeadDim, d = tid % kHeadDim;
+  const float* parts = part + sh_idx * nsplit * G * kPartStride;
+  float pm[kDecMaxSplits], pl[kDecMaxSplits], pa[kDecMaxSplits];
+#pragma unroll
+  for (int y = 0; y < kDecMaxSplits; ++y) {
+    if (y < nsplit) {
+      const float* py = parts + (y * G + g) * kPartStride;
+      pa[y] = py[d];
+      pm[y] = py[kHeadDim];
+      pl[y] = py[kHeadDim + 1];
+    } else {
+      pa[y] = 0.f; pm[y] = -__builtin_inff(); pl[y] = 0.f;
+    }
+  }
+  float M = -__builtin_inff(), L = 0.f, a = 0.f;
+#pragma unroll
+  for (int y = 0; y < kDecMaxSplits; ++y) {
+    float f2;
+    const float f1 = merge_factors(M, pm[y], f2);
+    L = L * f1 + pl[y] * f2;
+    a = a * f1 + pa[y] * f2;
+  }
+  out[(sh_idx * G + g) * kHeadDim + d] = (L > 0.f) ? a / L : 0.f;
+  if (lse_out && d == 0)
+    lse_out[sh_idx * G + g] = (L > 0.f) ? (M + __builtin_amdgcn_logf(L)) * kLn2 : -__builtin_inff();
+}
+
+// Launch shape of the fused kernel for a table of MP pages and a budget of KB
+// pages: false when it does not apply (the caller then runs the separate
+// select and attention kernels).
+bool decode_shape(int MP, int KB, int* ppw, int* nsplit) {
+  if (MP > 32 * kDecThreads || KB > kDecMaxBudget) return false;
+  int p = 1;
+  while (p < kDecMaxPpw && (KB + kDecWaves * p - 1) / (kDecWaves * p) > 16) p *= 2;
+  const int ns = (KB + kDecWaves * p - 1) / (kDecWaves * p);
+  if (ns > kDecMaxSplits) return false;
+  *ppw = p;
+  *nsplit = ns;
+  return true;
+}
+
+int decode_max_splits() { return kDecMaxSplits; }
+
+template <int G, int kRP>
+static void launch_decode_rp(const float* escore, const float* pmax, const float2* zpart,
+                             int ntiles, const int32_t* lens, const int32_t* budgets,
+                             const uint16_t* q, const uint16_t* kpool, const uint16_t* vpool,
+                             const int32_t* table, int64_t nb, int S, int H, int MP, int KB,
+                             int nsplit, int ppw, float* part, float* out, float* lse_out,
+                             int32_t* sel, int32_t* cnt, hipStream_t st) {
+  hipLaunchKernelGGL((decode_attn_kernel<G, kRP>), dim3(H, nsplit, S), dim3(kDecThreads), 0, st,
+                     escore, pmax, zpart, ntiles, lens, budgets, q, kpool, vpool, table, nb, H, MP,
+                     KB, nsplit, ppw, part, sel, cnt);
+  hipLaunchKernelGGL((decode_merge_kernel<G>), dim3(H, S), dim3(kDecThreads), 0, st, part, out,
+                     lse_out, H, nsplit);
+}
+
+template <int G>
+static void launch_decode_g(const float* escore, const float* pmax, const float2* zpart,
+                            int ntiles, const int32_t* lens, const int32_t* budgets,
+                            const uint16_t* q, const uint16_t* kpool, const uint16_t* vpool,
+                            const int32_t* table, int64_t nb, int S, int H, int MP, int KB,
+                            int nsplit, int ppw, float* part, float* out, float* lse_out,
+                            int32_t* sel, int32_t* cnt, hipStream_t st) {
+#define LOCKS_ARGS escore, pmax, zpart, ntiles, lens, budgets, q, kpool, vpool, table, nb, S, H, \
+                   MP, KB, nsplit, ppw, part, out, lse_out, sel, cnt, st
+  if (MP <= 4 * kDecThreads)
+    launch_decode_rp<G, 4>(LOCKS_ARGS);
+  else if (MP <= 16 * kDecThreads)
+    launch_decode_rp<G, 16>(LOCKS_ARGS);
+  else
+    launch_decode_rp<G, 32>(LOCKS_ARGS);
+#undef LOCKS_ARGS
+}
+
+hipError_t launch_decode(int G, const float* escore, const float* pmax, const float2* zpart,
+                         int ntiles, const int32_t* lens, const int32_t* budgets, const void* q,
+                         const void* kpool, const void* vpool, const int32_t* table, int64_t nb,
+                         int S, int H, int MP, int KB, int nsplit, int ppw, float* part,
+                         float* out, float* lse_out, int32_t* sel, int32_t* cnt, hipStream_t st) {
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint16_t* kk = static_cast<const uint16_t*>(kpool);
+  const uint16_t* vv = static_cast<const uint16_t*>(vpool);
+#define LOCKS_ARGS escore, pmax, zpart, ntiles, lens, budgets, qq, kk, vv, table, nb, S, H, MP, KB, \
+                   nsplit, ppw, part, out, lse_out, sel, cnt, st
+  switch (G) {
+    case 1: launch_decode_g<1>(LOCKS_ARGS); break;
+    case 2: launch_decode_g<2>(LOCKS_ARGS); break;
+    case 4: launch_decode_g<4>(LOCKS_ARGS); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef LOCKS_ARGS
+  return hipGetLastError();
+}
+
+}  // namespace locks

@@ -8,6 +8,8 @@ namespace locks {
 
 constexpr int kHeadDim = 128;
 constexpr int kPage = 16;
+// Pages one score workgroup covers (one Z partial per tile of this many).
+constexpr int kScorePagesPerWg = 128;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -70,6 +72,31 @@ __device__ __forceinline__ double swz_xor(double v) {
 
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
+// Full-wave reductions: DPP inside rows of 16 (quad xor 1, quad xor 2, half-
+// row mirror, row mirror), then a swizzle across rows of a half-wave and one
+// lane permute across the halves. Every lane ends with the result.
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_allmax(float v) {
+  v = fmaxf(v, dppf<0xB1>(v));
+  v = fmaxf(v, dppf<0x4E>(v));
+  v = fmaxf(v, dppf<0x141>(v));
+  v = fmaxf(v, dppf<0x140>(v));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));
+  return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+// Sum in a fixed order: lanes holding the same inputs get the same bits.
+__device__ __forceinline__ float wave_allsum(float v) {
+  v += dppf<0xB1>(v);
+  v += dppf<0x4E>(v);
+  v += dppf<0x141>(v);
+  v += dppf<0x140>(v);
+  v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+  return v + __shfl_xor(v, 32, 64);
+}
+
 // Order-preserving map of a float onto uint32 (larger float -> larger uint).
 __device__ __forceinline__ uint32_t float_to_ordered(float f) {
   uint32_t b = __float_as_uint(f);
@@ -83,6 +110,14 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
   const float M = fmaxf(m, m2);
   if (M == -__builtin_inff()) return;
   s = s * __expf(m - M) + s2 * __expf(m2 - M);
+  m = M;
+}
+
+// Same in base 2 (s is a sum of 2^(x - m)).
+__device__ __forceinline__ void lse2_merge(float& m, float& s, float m2, float s2) {
+  const float M = fmaxf(m, m2);
+  if (M == -__builtin_inff()) return;
+  s = s * __builtin_amdgcn_exp2f(m - M) + s2 * __builtin_amdgcn_exp2f(m2 - M);
   m = M;
 }
 

@@ -26,7 +26,7 @@ namespace locks {
 // ---------------------------------------------------------------------------
 // score
 // ---------------------------------------------------------------------------
-constexpr int kScorePagesPerWg = 128;  // 4 waves x 16 pages x 2 batches
+// kScorePagesPerWg = 4 waves x 16 pages x 2 batches
 
 template <int R>
 struct SlotRegs {
@@ -64,10 +64,16 @@ __device__ __forceinline__ void load_slot(SlotRegs<R>& d, const uint8_t* __restr
 // Grid (H, ceil(MP / kScorePagesPerWg), S): consecutive workgroup ids walk
 // the heads first, so with 8 heads all tiles of a head land on one XCD (ids
 // are dealt to the 8 XCDs round-robin) and its scores stay in that L2.
-// zpart (optional): per workgroup and query head, the (max, sum exp) of its
-// pages' scores, so that Z_g needs no second pass over all scores.
+// zpart (optional): per workgroup and query head, the base-2 (max, sum of
+// 2^(s - max)) of its pages' scores, so that Z_g needs no second pass.
+// mxout (optional, decode layout): scores then receives, per page and query,
+// e_g = 2^(s_g - max_g s_g) (base-2 s), and mxout[page] that maximum; the
+// selection then needs one log2 per page instead of G exponentials.
+// Otherwise scores receives s_hat in natural-log units.
 // knew/vnew (optional): the workgroup with tile index 0 of each (sequence,
 // head) first appends the new token's key and value for that head.
+// counters (optional): tile 0 also clears the (sequence, head) arrival
+// counter that the fused selection/attention kernel uses next.
 template <int R, int G>
 __global__ __launch_bounds__(256) void score_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ summ,
@@ -75,7 +81,7 @@ __global__ __launch_bounds__(256) void score_kernel(
     float* __restrict__ scores, int64_t num_blocks, int H, int MP, int pages_per_wg,
     int fill_nan, float2* __restrict__ zpart, const uint16_t* __restrict__ knew,
     const uint16_t* __restrict__ vnew, uint16_t* __restrict__ kpool,
-    uint16_t* __restrict__ vpool) {
+    uint16_t* __restrict__ vpool, uint32_t* __restrict__ counters, float* __restrict__ mxout) {
   constexpr SlotLayout L = slot_layout(R);
   constexpr float kTwoM24 = 5.9604644775390625e-08f;  // 2^-24
   const int s = blockIdx.z, h = blockIdx.x, tile = blockIdx.y;
@@ -84,6 +90,7 @@ __global__ __launch_bounds__(256) void score_kernel(
   const int len = clampi(seq_lens[s], 0, MP * kPage);
   const int F = len / kPage;
   const int j_lo = tile * pages_per_wg;
+  if (counters && tile == 0 && threadIdx.x == 0) counters[(int64_t)s * H + h] = 0u;
   if (knew && tile == 0 && threadIdx.x < 2 * (kHeadDim / 8) && len >= 1) {
     // decode-step append of the new token (position len - 1) for this head
     const int blk = table[(int64_t)s * MP + (len - 1) / kPage];
@@ -254,7 +261,8 @@ __global__ __launch_bounds__(256) void score_kernel(
         lg[i][g] = fscale[g] * fmaf(sc[i], x, A[g]);
       }
     }
-    float outv = 0.f;
+    // s_hat of query l4 in base-2 units (log2 of the page's sum of 2^logit)
+    float out2 = -__builtin_inff();
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float m = fmaxf(fmaxf(lg[0][g], lg[1][g]), fmaxf(lg[2][g], lg[3][g]));
@@ -262,11 +270,19 @@ __global__ __launch_bounds__(256) void score_kernel(
       float e = __builtin_amdgcn_exp2f(lg[0][g] - m) + __builtin_amdgcn_exp2f(lg[1][g] - m) +
                 __builtin_amdgcn_exp2f(lg[2][g] - m) + __builtin_amdgcn_exp2f(lg[3][g] - m);
       e = quad_sum(e);
-      const float shat = (m + __builtin_amdgcn_logf(e)) * kLn2;
-      if (l4 == g) outv = shat;
+      const float shat2 = m + __builtin_amdgcn_logf(e);
+      if (l4 == g && ok) out2 = shat2;
     }
-    if (in && l4 < G) srow[(int64_t)j * G + l4] = ok ? outv : -__builtin_inff();
-    if (in && ok) lse_merge(zm, zs, outv, 1.f);
+    if (mxout) {
+      // decode layout: e_g = 2^(s_g - max_g s_g) per query and the page max
+      const float mx = quad_max(out2);
+      const float ev = (l4 < G && mx != -__builtin_inff()) ? __builtin_amdgcn_exp2f(out2 - mx) : 0.f;
+      if (in && l4 < G) srow[(int64_t)j * G + l4] = ev;
+      if (in && l4 == 0) mxout[((int64_t)s * H + h) * MP + j] = mx;
+    } else if (in && l4 < G) {
+      srow[(int64_t)j * G + l4] = out2 * kLn2;
+    }
+    if (in && ok) lse2_merge(zm, zs, out2, 1.f);
     cur = nxt;
   }
   if (zpart) {
@@ -275,13 +291,13 @@ __global__ __launch_bounds__(256) void score_kernel(
 #pragma unroll
     for (int m = 4; m < 64; m <<= 1) {
       const float m2 = __shfl_xor(zm, m, 64), s2 = __shfl_xor(zs, m, 64);
-      lse_merge(zm, zs, m2, s2);
+      lse2_merge(zm, zs, m2, s2);
     }
     if (lane < G) { zred[wave][lane][0] = zm; zred[wave][lane][1] = zs; }
     __syncthreads();
     if (threadIdx.x < G) {
       float m = zred[0][threadIdx.x][0], t = zred[0][threadIdx.x][1];
-      for (int w = 1; w < 4; ++w) lse_merge(m, t, zred[w][threadIdx.x][0], zred[w][threadIdx.x][1]);
+      for (int w = 1; w < 4; ++w) lse2_merge(m, t, zred[w][threadIdx.x][0], zred[w][threadIdx.x][1]);
       zpart[(((int64_t)s * H + h) * gridDim.y + tile) * G + threadIdx.x] = make_float2(m, t);
     }
   }
@@ -537,13 +553,14 @@ template <int R, int G>
 static hipError_t launch_score_rg(const uint16_t* q, const uint8_t* summ, const int32_t* table,
                                   const int32_t* lens, float* scores, int64_t nb, int S, int H,
                                   int MP, int fill_nan, float2* zpart, const void* knew,
-                                  const void* vnew, void* kpool, void* vpool, hipStream_t st) {
+                                  const void* vnew, void* kpool, void* vpool, uint32_t* counters,
+                                  float* mxout, hipStream_t st) {
   const int ppw = kScorePagesPerWg;
   dim3 grid(H, (MP + ppw - 1) / ppw, S);
   hipLaunchKernelGGL((score_kernel<R, G>), grid, dim3(256), 0, st, q, summ, table, lens, scores,
                      nb, H, MP, ppw, fill_nan, zpart, static_cast<const uint16_t*>(knew),
                      static_cast<const uint16_t*>(vnew), static_cast<uint16_t*>(kpool),
-                     static_cast<uint16_t*>(vpool));
+                     static_cast<uint16_t*>(vpool), counters, mxout);
   return hipGetLastError();
 }
 
@@ -552,12 +569,12 @@ static hipError_t launch_score_g(int r, const uint16_t* q, const uint8_t* summ,
                                  const int32_t* table, const int32_t* lens, float* scores,
                                  int64_t nb, int S, int H, int MP, int fill_nan, float2* zpart,
                                  const void* knew, const void* vnew, void* kpool, void* vpool,
-                                 hipStream_t st) {
+                                 uint32_t* counters, float* mxout, hipStream_t st) {
   switch (r) {
 #define LOCKS_R(RR)                                                                        \
   case RR:                                                                                 \
     return launch_score_rg<RR, G>(q, summ, table, lens, scores, nb, S, H, MP, fill_nan,   \
-                                  zpart, knew, vnew, kpool, vpool, st);
+                                  zpart, knew, vnew, kpool, vpool, counters, mxout, st);
     LOCKS_R(1) LOCKS_R(2) LOCKS_R(3) LOCKS_R(4) LOCKS_R(5) LOCKS_R(6) LOCKS_R(7) LOCKS_R(8)
     LOCKS_R(9) LOCKS_R(10) LOCKS_R(11) LOCKS_R(12) LOCKS_R(13) LOCKS_R(14) LOCKS_R(15) LOCKS_R(16)
 #undef LOCKS_R
@@ -569,11 +586,12 @@ static hipError_t launch_score_g(int r, const uint16_t* q, const uint8_t* summ,
 hipError_t launch_score(int r, int G, const void* q, const void* summ, const int32_t* table,
                         const int32_t* lens, float* scores, int64_t nb, int S, int H, int MP,
                         int fill_nan, float2* zpart, const void* knew, const void* vnew,
-                        void* kpool, void* vpool, hipStream_t st) {
+                        void* kpool, void* vpool, uint32_t* counters, float* mxout,
+                        hipStream_t st) {
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint8_t* ss = static_cast<const uint8_t*>(summ);
   switch (G) {
-#define LOCKS_ARGS qq, ss, table, lens, scores, nb, S, H, MP, fill_nan, zpart, knew, vnew, kpool, vpool, st
+#define LOCKS_ARGS qq, ss, table, lens, scores, nb, S, H, MP, fill_nan, zpart, knew, vnew, kpool, vpool, counters, mxout, st
     case 1: return launch_score_g<1>(r, LOCKS_ARGS);
     case 2: return launch_score_g<2>(r, LOCKS_ARGS);
     case 4: return launch_score_g<4>(r, LOCKS_ARGS);

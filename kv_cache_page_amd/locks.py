@@ -29,6 +29,7 @@ ENTRY_POINTS = (
     "locks_status_string", "locks_summary_slot_bytes", "locks_summary_slot_stride",
     "locks_workspace_bytes", "locks_build", "locks_build_filled", "locks_append_kv",
     "locks_score_select", "locks_score_pages", "locks_select_pages", "locks_sparse_attn",
+    "locks_decode_step",
 )
 
 
@@ -78,6 +79,9 @@ _select_pages = _sig("locks_select_pages", ctypes.c_int,
 _sparse_attn = _sig("locks_sparse_attn", ctypes.c_int,
                     [_pd, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp,
                      _vp, _sz, _vp])
+_decode_step = _sig("locks_decode_step", ctypes.c_int,
+                    [_pd, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32,
+                     _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp])
 
 
 def status_string(status):
@@ -218,6 +222,33 @@ def sparse_attn(dims, q, k_pool, v_pool, block_table, seq_lens, sel_pages, sel_c
     _check(st, "locks_sparse_attn")
 
 
+def decode_step(dims, q, k_new, v_new, k_pool, v_pool, summaries, block_table, seq_lens, budgets,
+                max_budget, out, workspace, lse_out=None, sel_pages=None, sel_count=None,
+                seq_lens_host=None, stream=None):
+    """locks_decode_step. seq_lens_host: optional CPU int32 tensor equal to
+    seq_lens (lets the call skip the page-build launch when no page fills)."""
+    if seq_lens_host is not None:
+        if seq_lens_host.device.type != "cpu":
+            raise ValueError("seq_lens_host must be a CPU tensor")
+        if seq_lens_host.numel() != seq_lens.numel():
+            raise ValueError("seq_lens_host must have one entry per sequence")
+    st = _decode_step(ctypes.byref(dims), _ptr(q, torch.bfloat16, "q"),
+                      _ptr(k_new, torch.bfloat16, "k_new"), _ptr(v_new, torch.bfloat16, "v_new"),
+                      _ptr(k_pool, torch.bfloat16, "k_pool"), _ptr(v_pool, torch.bfloat16, "v_pool"),
+                      _ptr(summaries, torch.uint8, "summaries"), k_pool.shape[0],
+                      _ptr(block_table, torch.int32, "block_table"),
+                      _ptr(seq_lens, torch.int32, "seq_lens"),
+                      _ptr(seq_lens_host, torch.int32, "seq_lens_host"),
+                      _ptr(budgets, torch.int32, "budgets"), seq_lens.numel(),
+                      block_table.shape[1], max_budget, _ptr(out, torch.float32, "out"),
+                      _ptr(lse_out, torch.float32, "lse_out"),
+                      _ptr(sel_pages, torch.int32, "sel_pages"),
+                      _ptr(sel_count, torch.int32, "sel_count"),
+                      _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                      _stream(stream))
+    _check(st, "locks_decode_step")
+
+
 class Decoder:
     """Holds the per-layer output buffers and workspace of one decode step and
     calls score_select then sparse_attn on the current stream."""
@@ -237,4 +268,14 @@ class Decoder:
                      self.sel, self.cnt, self.ws, scores_out=scores_out, stream=stream)
         sparse_attn(self.dims, q, k_pool, v_pool, block_table, seq_lens, self.sel, self.cnt,
                     self.max_budget, self.out, self.ws, lse_out=self.lse, stream=stream)
+        return self.out
+
+    def decode(self, q, k_new, v_new, summaries, k_pool, v_pool, block_table, seq_lens, budgets,
+               seq_lens_host=None, stream=None):
+        """One fused decode step (append, build of filled pages, score,
+        select, attend) through locks_decode_step."""
+        decode_step(self.dims, q, k_new, v_new, k_pool, v_pool, summaries, block_table, seq_lens,
+                    budgets, self.max_budget, self.out, self.ws, lse_out=self.lse,
+                    sel_pages=self.sel, sel_count=self.cnt, seq_lens_host=seq_lens_host,
+                    stream=stream)
         return self.out
