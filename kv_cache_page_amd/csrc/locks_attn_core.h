@@ -219,14 +219,12 @@ __device__ __forceinline__ void wg_partial_store(const float (*sh_acc)[G][kHeadD
 
 // Base-2 online merge of (m, l) states: returns the factor for the old
 // state and sets f2 for the incoming one (both 0 when everything is empty).
+// Branch-free, so loads feeding a chain of merges can all be in flight.
 __device__ __forceinline__ float merge_factors(float& m, float m2, float& f2) {
   const float M = fmaxf(m, m2);
-  if (M == -__builtin_inff()) {
-    f2 = 0.f;
-    return 0.f;
-  }
-  const float f1 = __builtin_amdgcn_exp2f(m - M);
-  f2 = __builtin_amdgcn_exp2f(m2 - M);
+  const bool empty = (M == -__builtin_inff());
+  const float f1 = empty ? 0.f : __builtin_amdgcn_exp2f(m - M);
+  f2 = empty ? 0.f : __builtin_amdgcn_exp2f(m2 - M);
   m = M;
   return f1;
 }

@@ -11,8 +11,7 @@ namespace locks {
 hipError_t launch_score(int r, int G, const void* q, const void* summ, const int32_t* table,
                         const int32_t* lens, float* scores, int64_t nb, int S, int H, int MP,
                         int fill_nan, float2* zpart, const void* knew, const void* vnew,
-                        void* kpool, void* vpool, uint32_t* counters, float* mxout,
-                        hipStream_t st);
+                        void* kpool, void* vpool, float* mxout, hipStream_t st);
 hipError_t launch_select(int G, const float* scores, const int32_t* lens, const int32_t* budgets,
                          int32_t* sel, int32_t* cnt, float* keybuf, int S, int H, int MP,
                          int max_budget, hipStream_t st);
@@ -198,7 +197,7 @@ locks_status locks_score_select(const locks_dims* d, const void* q, const void* 
   const int H = d->num_kv_heads, G = d->group_size;
   hipError_t he = locks::launch_score(d->rank, G, q, summaries, block_table, seq_lens, scores, nb,
                                       S, H, MP, scores_out ? 1 : 0, nullptr, nullptr, nullptr, nullptr,
-                                      nullptr, nullptr, nullptr, st);
+                                      nullptr, nullptr, st);
   if (he != hipSuccess) return LOCKS_ERR_HIP;
   he = locks::launch_select(G, scores, seq_lens, budgets, sel_pages, sel_count,
                             reinterpret_cast<float*>(ws + w.keys), S, H, MP, KB, st);
@@ -217,7 +216,7 @@ locks_status locks_score_pages(const locks_dims* d, const void* q, const void* s
   if (!aligned16(q) || !aligned16(summaries)) return LOCKS_ERR_INVALID_ARG;
   return hip_status(locks::launch_score(d->rank, d->group_size, q, summaries, block_table,
                                         seq_lens, scores, nb, S, d->num_kv_heads, MP, 0, nullptr,
-                                        nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, st));
+                                        nullptr, nullptr, nullptr, nullptr, nullptr, st));
 }
 
 locks_status locks_select_pages(const locks_dims* d, const float* scores, const int32_t* seq_lens,
@@ -306,7 +305,7 @@ locks_status locks_decode_step(const locks_dims* d, const void* q, const void* k
   float* pmax = reinterpret_cast<float*>(ws + w.pmax);
   hipError_t he = locks::launch_score(d->rank, G, q, summaries, block_table, seq_lens, scores, nb,
                                       S, H, MP, 0, zpart, completes ? nullptr : k_new,
-                                      completes ? nullptr : v_new, k_pool, v_pool, nullptr,
+                                      completes ? nullptr : v_new, k_pool, v_pool,
                                       fused ? pmax : nullptr, st);
   if (he != hipSuccess) return LOCKS_ERR_HIP;
   // 3. selection + attention + merge

@@ -121,10 +121,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
     }
   }
   if (tid < G * kHeadDim / 8) sh_q[tid] = reinterpret_cast<const uint4*>(q + sh_idx * G * kHeadDim)[tid];
-  float2 zl[2][G];
   const float2* zp = zpart + sh_idx * ntiles * G;
+  constexpr int kZl = (kRP * kDecThreads + 64 * kScorePagesPerWg - 1) / (64 * kScorePagesPerWg);
+  float2 zl[kZl][G];  // tile partials t = lane + 64 c
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < kZl; ++c) {
     const int t = lane + 64 * c;
 #pragma unroll
     for (int g = 0; g < G; ++g)
@@ -153,12 +154,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
     float lz[G], zx = -__builtin_inff();
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const float m0 = (lane < ntu) ? zl[0][g].x : -__builtin_inff();
-      const float m1 = (lane + 64 < ntu) ? zl[1][g].x : -__builtin_inff();
-      const float M = wave_allmax(fmaxf(m0, m1));
+      float mt = -__builtin_inff();
+#pragma unroll
+      for (int c = 0; c < kZl; ++c)
+        if (lane + 64 * c < ntu) mt = fmaxf(mt, zl[c][g].x);
+      const float M = wave_allmax(mt);
       float c = 0.f;
-      if (m0 != -__builtin_inff()) c += zl[0][g].y * __builtin_amdgcn_exp2f(m0 - M);
-      if (m1 != -__builtin_inff()) c += zl[1][g].y * __builtin_amdgcn_exp2f(m1 - M);
+#pragma unroll
+      for (int cc = 0; cc < kZl; ++cc) {
+        const float mc = (lane + 64 * cc < ntu) ? zl[cc][g].x : -__builtin_inff();
+        if (mc != -__builtin_inff()) c += zl[cc][g].y * __builtin_amdgcn_exp2f(mc - M);
+      }
       const float S = wave_allsum(c);
       lz[g] = S > 0.f ? M + __builtin_amdgcn_logf(S) : -__builtin_inff();
       zx = fmaxf(zx, lz[g]);
@@ -400,15 +406,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_merge_kernel(
   float pm[kDecMaxSplits], pl[kDecMaxSplits], pa[kDecMaxSplits];
 #pragma unroll
   for (int y = 0; y < kDecMaxSplits; ++y) {
-    if (y < nsplit) {
-      const float* py = parts + (y * G + g) * kPartStride;
-      pa[y] = py[d];
-      pm[y] = py[kHeadDim];
-      pl[y] = py[kHeadDim + 1];
-    } else {
-      pa[y] = 0.f; pm[y] = -__builtin_inff(); pl[y] = 0.f;
-    }
+    // unconditional (clamped) loads, masked afterwards: all in flight at once
+    const float* py = parts + (min(y, nsplit - 1) * G + g) * kPartStride;
+    pa[y] = py[d];
+    const float2 ml = *reinterpret_cast<const float2*>(py + kHeadDim);
+    pm[y] = ml.x;
+    pl[y] = ml.y;
   }
+#pragma unroll
+  for (int y = 0; y < kDecMaxSplits; ++y)
+    if (y >= nsplit) { pa[y] = 0.f; pm[y] = -__builtin_inff(); pl[y] = 0.f; }
   float M = -__builtin_inff(), L = 0.f, a = 0.f;
 #pragma unroll
   for (int y = 0; y < kDecMaxSplits; ++y) {

@@ -106,18 +106,22 @@ __device__ __forceinline__ uint32_t float_to_ordered(float f) {
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 // Online log-sum-exp state (max m, sum s of exp(x - m)): absorb (m2, s2).
+// Branch-free (an empty state has m = -inf, s = 0).
 __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
   const float M = fmaxf(m, m2);
-  if (M == -__builtin_inff()) return;
-  s = s * __expf(m - M) + s2 * __expf(m2 - M);
+  const bool empty = (M == -__builtin_inff());
+  const float a = empty ? 0.f : __expf(m - M), b = empty ? 0.f : __expf(m2 - M);
+  s = s * a + s2 * b;
   m = M;
 }
 
 // Same in base 2 (s is a sum of 2^(x - m)).
 __device__ __forceinline__ void lse2_merge(float& m, float& s, float m2, float s2) {
   const float M = fmaxf(m, m2);
-  if (M == -__builtin_inff()) return;
-  s = s * __builtin_amdgcn_exp2f(m - M) + s2 * __builtin_amdgcn_exp2f(m2 - M);
+  const bool empty = (M == -__builtin_inff());
+  const float a = empty ? 0.f : __builtin_amdgcn_exp2f(m - M);
+  const float b = empty ? 0.f : __builtin_amdgcn_exp2f(m2 - M);
+  s = s * a + s2 * b;
   m = M;
 }
 

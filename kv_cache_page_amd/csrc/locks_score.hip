@@ -72,8 +72,6 @@ __device__ __forceinline__ void load_slot(SlotRegs<R>& d, const uint8_t* __restr
 // Otherwise scores receives s_hat in natural-log units.
 // knew/vnew (optional): the workgroup with tile index 0 of each (sequence,
 // head) first appends the new token's key and value for that head.
-// counters (optional): tile 0 also clears the (sequence, head) arrival
-// counter that the fused selection/attention kernel uses next.
 template <int R, int G>
 __global__ __launch_bounds__(256) void score_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ summ,
@@ -81,7 +79,7 @@ __global__ __launch_bounds__(256) void score_kernel(
     float* __restrict__ scores, int64_t num_blocks, int H, int MP, int pages_per_wg,
     int fill_nan, float2* __restrict__ zpart, const uint16_t* __restrict__ knew,
     const uint16_t* __restrict__ vnew, uint16_t* __restrict__ kpool,
-    uint16_t* __restrict__ vpool, uint32_t* __restrict__ counters, float* __restrict__ mxout) {
+    uint16_t* __restrict__ vpool, float* __restrict__ mxout) {
   constexpr SlotLayout L = slot_layout(R);
   constexpr float kTwoM24 = 5.9604644775390625e-08f;  // 2^-24
   const int s = blockIdx.z, h = blockIdx.x, tile = blockIdx.y;
@@ -90,7 +88,6 @@ __global__ __launch_bounds__(256) void score_kernel(
   const int len = clampi(seq_lens[s], 0, MP * kPage);
   const int F = len / kPage;
   const int j_lo = tile * pages_per_wg;
-  if (counters && tile == 0 && threadIdx.x == 0) counters[(int64_t)s * H + h] = 0u;
   if (knew && tile == 0 && threadIdx.x < 2 * (kHeadDim / 8) && len >= 1) {
     // decode-step append of the new token (position len - 1) for this head
     const int blk = table[(int64_t)s * MP + (len - 1) / kPage];
@@ -553,14 +550,14 @@ template <int R, int G>
 static hipError_t launch_score_rg(const uint16_t* q, const uint8_t* summ, const int32_t* table,
                                   const int32_t* lens, float* scores, int64_t nb, int S, int H,
                                   int MP, int fill_nan, float2* zpart, const void* knew,
-                                  const void* vnew, void* kpool, void* vpool, uint32_t* counters,
-                                  float* mxout, hipStream_t st) {
+                                  const void* vnew, void* kpool, void* vpool, float* mxout,
+                                  hipStream_t st) {
   const int ppw = kScorePagesPerWg;
   dim3 grid(H, (MP + ppw - 1) / ppw, S);
   hipLaunchKernelGGL((score_kernel<R, G>), grid, dim3(256), 0, st, q, summ, table, lens, scores,
                      nb, H, MP, ppw, fill_nan, zpart, static_cast<const uint16_t*>(knew),
                      static_cast<const uint16_t*>(vnew), static_cast<uint16_t*>(kpool),
-                     static_cast<uint16_t*>(vpool), counters, mxout);
+                     static_cast<uint16_t*>(vpool), mxout);
   return hipGetLastError();
 }
 
@@ -569,12 +566,12 @@ static hipError_t launch_score_g(int r, const uint16_t* q, const uint8_t* summ,
                                  const int32_t* table, const int32_t* lens, float* scores,
                                  int64_t nb, int S, int H, int MP, int fill_nan, float2* zpart,
                                  const void* knew, const void* vnew, void* kpool, void* vpool,
-                                 uint32_t* counters, float* mxout, hipStream_t st) {
+                                 float* mxout, hipStream_t st) {
   switch (r) {
 #define LOCKS_R(RR)                                                                        \
   case RR:                                                                                 \
     return launch_score_rg<RR, G>(q, summ, table, lens, scores, nb, S, H, MP, fill_nan,   \
-                                  zpart, knew, vnew, kpool, vpool, counters, mxout, st);
+                                  zpart, knew, vnew, kpool, vpool, mxout, st);
     LOCKS_R(1) LOCKS_R(2) LOCKS_R(3) LOCKS_R(4) LOCKS_R(5) LOCKS_R(6) LOCKS_R(7) LOCKS_R(8)
     LOCKS_R(9) LOCKS_R(10) LOCKS_R(11) LOCKS_R(12) LOCKS_R(13) LOCKS_R(14) LOCKS_R(15) LOCKS_R(16)
 #undef LOCKS_R
@@ -583,15 +580,23 @@ static hipError_t launch_score_g(int r, const uint16_t* q, const uint8_t* summ,
   }
 }
 
+bool score_mfma_supported(int r);
+hipError_t launch_score_mfma(int r, int G, const void* q, const void* summ, const int32_t* table,
+                             const int32_t* lens, float* scores, int64_t nb, int S, int H, int MP,
+                             int fill_nan, float2* zpart, const void* knew, const void* vnew,
+                             void* kpool, void* vpool, float* mxout, hipStream_t st);
+
 hipError_t launch_score(int r, int G, const void* q, const void* summ, const int32_t* table,
                         const int32_t* lens, float* scores, int64_t nb, int S, int H, int MP,
                         int fill_nan, float2* zpart, const void* knew, const void* vnew,
-                        void* kpool, void* vpool, uint32_t* counters, float* mxout,
-                        hipStream_t st) {
+                        void* kpool, void* vpool, float* mxout, hipStream_t st) {
+  if (score_mfma_supported(r))
+    return launch_score_mfma(r, G, q, summ, table, lens, scores, nb, S, H, MP, fill_nan, zpart,
+                             knew, vnew, kpool, vpool, mxout, st);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint8_t* ss = static_cast<const uint8_t*>(summ);
   switch (G) {
-#define LOCKS_ARGS qq, ss, table, lens, scores, nb, S, H, MP, fill_nan, zpart, knew, vnew, kpool, vpool, counters, mxout, st
+#define LOCKS_ARGS qq, ss, table, lens, scores, nb, S, H, MP, fill_nan, zpart, knew, vnew, kpool, vpool, mxout, st
     case 1: return launch_score_g<1>(r, LOCKS_ARGS);
     case 2: return launch_score_g<2>(r, LOCKS_ARGS);
     case 4: return launch_score_g<4>(r, LOCKS_ARGS);

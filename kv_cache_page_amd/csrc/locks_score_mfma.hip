@@ -1,0 +1,386 @@
+// LOCKS page scores on the matrix cores (gfx950), for ranks 4, 8 and 16.
+//
+// [N] = LOCKS reading notes (zhongzhuzhou.org 2026-07-29), §4.2 eq. 4: for
+// every full page j and query g of the GQA group,
+//   s_hat_jg = LSE_t ((q_g . mu_j + c_t . (V_j^T q_g)) / sqrt(d))
+// from the int4 basis, int8 coefficients and int8 centroid of the slot.
+//
+// Same contract and grid as the VALU score kernel (one 256-thread workgroup
+// per 128-page tile of one (sequence, KV head)); wave w takes the 32 pages
+// j_lo + 32 w + [0, 32) as 8 groups of 4 pages. Lane l = 16 q16 + r16.
+//
+// Stage 1, W = V^T q on v_mfma_f32_16x16x32_f16, per group and quarter of
+//   the ranks (ranks 4hh .. 4hh+3): A rows m = r16 are (page m / 4, rank
+//   4hh + m % 4), K = the 128 dims. The int4 codes become exact fp16
+//   denormals (c + 8) 2^-24 with two masks per nibble pair, and the K order
+//   inside a lane follows the slot's nibble order (lane q16 of chunk c holds
+//   dims 8 (4 q16 + c) .. +7, i.e. byte 16 q16 + 4c of the basis row), so each
+//   lane reads one 16-byte piece of one row. The B columns n carry query
+//   n % 4 (the G queries repeated), scaled by a power of two into fp16. The
+//   D layout then leaves, in lane (q16 = a, r16), the 4 ranks of that quarter
+//   for page a of the group and query r16 % 4: over the quarters, a lane holds
+//   the whole W of its page for its query, with no data exchange.
+// The centroid term mu . q uses one more MFMA chain per 16 pages with A rows
+//   in the order page 4 (m % 4) + m / 4, so that register i of lane q16 holds
+//   page 4 i + q16: again the page and query the lane needs.
+// Stage 2 (VALU, fp32): lane (a, r16 = 4 b + g) forms the logits of tokens
+//   4b .. 4b+3 of page a for query g from its W, the int8 coefficient rows and
+//   the token scales, and the LSE over the page's 16 tokens combines the 4
+//   token blocks (lanes r16 xor 4, xor 8).
+// The slot loads of the first three groups and of the centroids are issued
+// as soon as the block ids arrive; the query operands are built meanwhile,
+// and a 4-deep pipeline keeps three groups in flight while one is computed.
+#include "locks_device.h"
+
+namespace locks {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// 8 int4 codes of one basis word -> (c + 8) 2^-24 as fp16 denormals, in the
+// order [d0, d2, 16 d1, 16 d3, d4, d6, 16 d5, 16 d7] (bytes of the word hold
+// the dim pairs (0,1), (4,5), (2,3), (6,7), low nibble first).
+__device__ __forceinline__ half8 nib8(uint32_t w) {
+  w ^= 0x88888888u;
+  const uint32_t w8 = w >> 8;
+  return __builtin_bit_cast(half8, make_uint4(w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu,
+                                              w8 & 0x00F000F0u));
+}
+
+// 8 int8 codes (two words, byte order) -> (c + 128) 2^-24 as fp16
+// denormals, in the order [b0, b2, b1, b3, b4, b6, b5, b7].
+__device__ __forceinline__ half8 byte8(uint32_t w0, uint32_t w1) {
+  w0 ^= 0x80808080u;
+  w1 ^= 0x80808080u;
+  return __builtin_bit_cast(half8, make_uint4(w0 & 0x00FF00FFu, (w0 >> 8) & 0x00FF00FFu,
+                                              w1 & 0x00FF00FFu, (w1 >> 8) & 0x00FF00FFu));
+}
+
+__device__ __forceinline__ float half_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float half_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// Slot data of one 4-page group as one lane needs it.
+template <int R>
+struct GroupRegs {
+  uint4 v[R / 4];        // basis: row 4 hh + r16 % 4 of page r16 / 4, bytes 16 q16 ..
+  uint4 c[R / 4];        // coefficients of tokens 4 b .. 4 b + 3 of page q16
+  uint32_t sv[R / 2];    // fp16 basis-column scales of page q16
+  uint2 sc;              // fp16 scales of tokens 4 b .. 4 b + 3 of page q16
+  uint32_t smu;          // fp16 centroid scale of page q16 (low half)
+};
+
+template <int R>
+__device__ __forceinline__ void load_group(GroupRegs<R>& g, const uint8_t* __restrict__ summ,
+                                           int64_t offV, int64_t offC, int r16, int q16) {
+  constexpr SlotLayout L = slot_layout(R);
+  const int b = r16 >> 2;
+#pragma unroll
+  for (int hh = 0; hh < R / 4; ++hh)
+    g.v[hh] = *reinterpret_cast<const uint4*>(summ + offV + L.v + 64 * (4 * hh + (r16 & 3)) + 16 * q16);
+  // tokens 4b..4b+3 x R bytes = 4R contiguous bytes
+#pragma unroll
+  for (int e = 0; e < R / 4; ++e)
+    g.c[e] = *reinterpret_cast<const uint4*>(summ + offC + L.c + 4 * R * b + 16 * e);
+#pragma unroll
+  for (int e = 0; e < R / 2; ++e) g.sv[e] = *reinterpret_cast<const uint32_t*>(summ + offC + L.sv + 4 * e);
+  g.sc = *reinterpret_cast<const uint2*>(summ + offC + L.sc + 8 * b);
+  g.smu = *reinterpret_cast<const uint16_t*>(summ + offC + L.smu);
+}
+
+template <int R, int G>
+__global__ __launch_bounds__(256) void score_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ summ,
+    const int32_t* __restrict__ table, const int32_t* __restrict__ seq_lens,
+    float* __restrict__ scores, int64_t num_blocks, int H, int MP, int pages_per_wg,
+    int fill_nan, float2* __restrict__ zpart, const uint16_t* __restrict__ knew,
+    const uint16_t* __restrict__ vnew, uint16_t* __restrict__ kpool,
+    uint16_t* __restrict__ vpool, float* __restrict__ mxout) {
+  static_assert(R == 4 || R == 8 || R == 16, "matrix-core path covers ranks 4, 8, 16");
+  constexpr SlotLayout L = slot_layout(R);
+  constexpr int NHR = R / 4;
+  constexpr float kTwoM24 = 5.9604644775390625e-08f;  // 2^-24
+  constexpr int kWavePages = kScorePagesPerWg / 4;    // pages per wave
+  constexpr int kHalves = (kWavePages + 15) / 16;     // 16-page halves (centroid MFMAs)
+  constexpr int kGroups = kWavePages / 4;             // 4-page groups per wave
+  const int s = blockIdx.z, h = blockIdx.x, tile = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, q16 = lane >> 4;
+  const int gq = r16 & 3;  // this lane's query (B column r16 carries query r16 % 4)
+  const int len = clampi(seq_lens[s], 0, MP * kPage);
+  const int F = len / kPage;
+  const int j_lo = tile * pages_per_wg;
+  if (knew && tile == 0 && threadIdx.x < 2 * (kHeadDim / 8) && len >= 1) {
+    // decode-step append of the new token (position len - 1) for this head
+    const int blk = table[(int64_t)s * MP + (len - 1) / kPage];
+    if (blk >= 0 && blk < num_blocks) {
+      const int c = threadIdx.x % (kHeadDim / 8);
+      const int64_t src = ((int64_t)s * H + h) * kHeadDim + 8 * c;
+      const int64_t dst = (((int64_t)blk * H + h) * kPage + (len - 1) % kPage) * kHeadDim + 8 * c;
+      if (threadIdx.x < kHeadDim / 8)
+        *reinterpret_cast<uint4*>(kpool + dst) = *reinterpret_cast<const uint4*>(knew + src);
+      else
+        *reinterpret_cast<uint4*>(vpool + dst) = *reinterpret_cast<const uint4*>(vnew + src);
+    }
+  }
+  const int j_hi = min(j_lo + pages_per_wg, MP);
+  float* srow = scores + ((int64_t)s * H + h) * MP * G;
+  if (fill_nan) {
+    const int first = max(j_lo, F);
+    for (int idx = threadIdx.x; idx < (j_hi - first) * G; idx += blockDim.x)
+      srow[(int64_t)first * G + idx] = __builtin_nanf("");
+  }
+  if (j_lo >= F) return;
+  const int j_end = min(j_hi, F);
+  const int P0 = j_lo + kWavePages * wave;  // this wave's first page
+
+  // ---- raw query rows (independent of the block ids): column r16 carries
+  // query gq; lane q16 holds dims [32 q16, 32 q16 + 32) of it
+  const bool qok = gq < G;
+  uint4 qraw[4];
+  {
+    const uint4* qp = reinterpret_cast<const uint4*>(
+        q + ((int64_t)s * H * G + (int64_t)h * G + (qok ? gq : 0)) * kHeadDim + 32 * q16);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qraw[c] = qp[c];
+  }
+  // ---- block ids of the pages P0 + 16 u + r16, then the slot offsets each
+  // role needs, by lane permutes
+  int bo[kHalves];
+#pragma unroll
+  for (int u = 0; u < kHalves; ++u) {
+    const int j = P0 + 16 * u + r16;
+    const int b = (j < j_end) ? table[(int64_t)s * MP + j] : -1;
+    bo[u] = (b >= 0 && b < num_blocks) ? b : -1;
+  }
+
+  const int64_t hstride = (int64_t)L.stride;
+  auto slot_off = [&](int b) -> int64_t { return ((int64_t)(b < 0 ? 0 : b) * H + h) * hstride; };
+  auto shfl_i = [&](int v, int src) -> int { return __shfl(v, src, 64); };
+
+  // ---- centroid term per 16-page half: register i of lane q16 holds
+  // page 16 u + 4 i + q16, query gq
+  uint4 mw[kHalves][2];
+  {
+    const int src = 4 * (r16 & 3) + (r16 >> 2);  // A row r16 <- page src
+#pragma unroll
+    for (int u = 0; u < kHalves; ++u) {
+      const int64_t o = slot_off(shfl_i(bo[u], src)) + L.mu + 32 * q16;
+      mw[u][0] = *reinterpret_cast<const uint4*>(summ + o);
+      mw[u][1] = *reinterpret_cast<const uint4*>(summ + o + 16);
+    }
+  }
+  // ---- groups: pipeline of slot loads (three groups in flight while one is
+  // computed; two for rank 16)
+  float zm = -__builtin_inff(), zs = 0.f;  // running LSE (base 2) of query gq
+  constexpr int kDepth = (R >= 8) ? 3 : 4;  // register budget: three waves per SIMD up to rank 8
+  GroupRegs<R> buf[kDepth];
+  auto issue = [&](int gi, GroupRegs<R>& gr) {
+    const int u = gi >> 2, base = 4 * (gi & 3);
+    const int bV = shfl_i(bo[u], base + (r16 >> 2));
+    const int bC = shfl_i(bo[u], base + q16);
+    load_group<R>(gr, summ, slot_off(bV), slot_off(bC), r16, q16);
+  };
+#pragma unroll
+  for (int gi = 0; gi < kDepth - 1; ++gi)
+    if (P0 + 4 * gi < j_end) issue(gi, buf[gi]);
+  // ---- query operands, power-of-two scaled into fp16 (built while the slot
+  // loads are in flight)
+  half8 B1[4], Bm[4];
+  float vinit, minit, fs;
+  {
+    float x[32];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint4 w = qraw[c];
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[8 * c + 2 * e] = qok ? bf16_lo(ww[e]) : 0.f;
+        x[8 * c + 2 * e + 1] = qok ? bf16_hi(ww[e]) : 0.f;
+      }
+    }
+    float mx = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) mx = fmaxf(mx, fabsf(x[e]));
+    mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(mx), 0x401F)));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const int ex = (mx > 0.f && mx < __builtin_inff()) ? ilogbf(mx) : 0;
+    const float up = ldexpf(1.f, 14 - ex);  // max |q| * up < 2^15
+    float qs = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) qs += x[e] * up;
+    qs += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(qs), 0x401F));
+    qs += __shfl_xor(qs, 32, 64);
+    // stage-1 operand, chunk c: dims 8 (4 q16 + c) + [0,2,1,3,4,6,5,7] with the
+    // high nibbles' factor 16 divided out
+    // centroid operand, chunk c: dims 32 q16 + 8 c + [0,2,1,3,4,6,5,7]
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      // the lane's dims: local index 8 c' + e covers dim 32 q16 + 8 c' + e
+      const float* y = x + 8 * c;  // dims 32 q16 + 8 c .. : word (4 q16 + c)
+      B1[c] = half8{(_Float16)(y[0] * up), (_Float16)(y[2] * up),
+                    (_Float16)(y[1] * up * 0.0625f), (_Float16)(y[3] * up * 0.0625f),
+                    (_Float16)(y[4] * up), (_Float16)(y[6] * up),
+                    (_Float16)(y[5] * up * 0.0625f), (_Float16)(y[7] * up * 0.0625f)};
+      Bm[c] = half8{(_Float16)(y[0] * up), (_Float16)(y[2] * up), (_Float16)(y[1] * up),
+                    (_Float16)(y[3] * up), (_Float16)(y[4] * up), (_Float16)(y[6] * up),
+                    (_Float16)(y[5] * up), (_Float16)(y[7] * up)};
+    }
+    vinit = -8.f * kTwoM24 * qs;
+    minit = -128.f * kTwoM24 * qs;
+    // logits in log2 units: 2^(24 - (14 - ex)) * log2(e) / sqrt(d)
+    fs = ldexpf(kLog2e * 0.08838834764831845f, 10 + ex);
+  }
+
+  floatx4 Dm[kHalves];
+  {
+#pragma unroll
+    for (int u = 0; u < kHalves; ++u) {
+      const uint32_t w[8] = {mw[u][0].x, mw[u][0].y, mw[u][0].z, mw[u][0].w,
+                             mw[u][1].x, mw[u][1].y, mw[u][1].z, mw[u][1].w};
+      floatx4 d = {minit, minit, minit, minit};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(byte8(w[2 * c], w[2 * c + 1]), Bm[c], d, 0, 0, 0);
+      Dm[u] = d;
+    }
+  }
+
+#pragma unroll
+  for (int gi = 0; gi < kGroups; ++gi) {
+    if (P0 + 4 * gi >= j_end) break;  // wave-uniform
+    if (gi + kDepth - 1 < kGroups && P0 + 4 * (gi + kDepth - 1) < j_end)
+      issue(gi + kDepth - 1, buf[(gi + kDepth - 1) % kDepth]);
+    const GroupRegs<R>& gr = buf[gi % kDepth];
+    const int u = gi >> 2, base = 4 * (gi & 3);
+    // stage 1: W of page q16 of the group, query gq, ranks 4 hh + i
+    float W[R];
+#pragma unroll
+    for (int hh = 0; hh < NHR; ++hh) {
+      floatx4 d = {vinit, vinit, vinit, vinit};
+      const uint32_t vw[4] = {gr.v[hh].x, gr.v[hh].y, gr.v[hh].z, gr.v[hh].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(nib8(vw[c]), B1[c], d, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int k = 4 * hh + i;
+        const uint32_t sw = gr.sv[k >> 1];
+        W[k] = d[i] * ((k & 1) ? half_hi(sw) : half_lo(sw));
+      }
+    }
+    float wsum = 0.f;
+#pragma unroll
+    for (int k = 0; k < R; ++k) wsum += W[k];
+    // centroid term of page base + q16 (register (gi & 3) of half u)
+    const float muq = Dm[u][gi & 3] * half_lo(gr.smu);
+    // stage 2: logits of tokens 4b .. 4b+3 (base 2); the R words per token
+    // row become offset-binary bytes (c + 128) read by v_cvt_f32_ubyte*
+    uint32_t cx[R];
+#pragma unroll
+    for (int e = 0; e < R / 4; ++e) {
+      cx[4 * e + 0] = gr.c[e].x ^ 0x80808080u;
+      cx[4 * e + 1] = gr.c[e].y ^ 0x80808080u;
+      cx[4 * e + 2] = gr.c[e].z ^ 0x80808080u;
+      cx[4 * e + 3] = gr.c[e].w ^ 0x80808080u;
+    }
+    float lg[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x = -128.f * wsum;
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const int byte = R * i + k;  // token i, rank k within the 4R bytes
+        x = fmaf((float)((cx[byte >> 2] >> (8 * (byte & 3))) & 0xFFu), W[k], x);
+      }
+      const uint32_t sw = (i < 2) ? gr.sc.x : gr.sc.y;
+      const float sc = (i & 1) ? half_hi(sw) : half_lo(sw);
+      lg[i] = fs * fmaf(sc, x, muq);
+    }
+    // LSE over the 16 tokens: 4 here, the other token blocks in lanes r16 ^ 4, ^ 8
+    float m = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(m), 0x101F)));
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(m), 0x201F)));
+    float e = __builtin_amdgcn_exp2f(lg[0] - m) + __builtin_amdgcn_exp2f(lg[1] - m) +
+              __builtin_amdgcn_exp2f(lg[2] - m) + __builtin_amdgcn_exp2f(lg[3] - m);
+    e += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(e), 0x101F));
+    e += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(e), 0x201F));
+    const int jp = P0 + 4 * gi + q16;  // the lane's page
+    const bool ok = jp < j_end && shfl_i(bo[u], base + q16) >= 0 && gq < G;
+    const float out2 = ok ? m + __builtin_amdgcn_logf(e) : -__builtin_inff();
+    const bool writer = (r16 < 4) && jp < j_end;  // token block 0 writes
+    if (mxout) {
+      // decode layout: e_g = 2^(s_g - max_g s_g) per query and the page max;
+      // lanes r16 = 0..3 hold the page's 4 queries (a DPP quad)
+      const float mx = quad_max(out2);
+      const float ev = (gq < G && mx != -__builtin_inff()) ? __builtin_amdgcn_exp2f(out2 - mx) : 0.f;
+      if (writer && gq < G) srow[(int64_t)jp * G + gq] = ev;
+      if (writer && gq == 0) mxout[((int64_t)s * H + h) * MP + jp] = mx;
+    } else if (writer && gq < G) {
+      srow[(int64_t)jp * G + gq] = out2 * kLn2;
+    }
+    if (writer && ok) lse2_merge(zm, zs, out2, 1.f);
+  }
+  if (zpart) {
+    // lanes r16 < 4 carry query gq = r16; reduce over the other lanes of the
+    // same query (xor 4, 8: token blocks, empty; xor 16, 32: pages), then waves
+    __shared__ float zred[4][4][2];
+#pragma unroll
+    for (int mm = 4; mm < 64; mm <<= 1) {
+      const float m2 = __shfl_xor(zm, mm, 64), s2 = __shfl_xor(zs, mm, 64);
+      lse2_merge(zm, zs, m2, s2);
+    }
+    if (lane < G) { zred[wave][lane][0] = zm; zred[wave][lane][1] = zs; }
+    __syncthreads();
+    if (threadIdx.x < G) {
+      float m = zred[0][threadIdx.x][0], t = zred[0][threadIdx.x][1];
+      for (int w = 1; w < 4; ++w) lse2_merge(m, t, zred[w][threadIdx.x][0], zred[w][threadIdx.x][1]);
+      zpart[(((int64_t)s * H + h) * gridDim.y + tile) * G + threadIdx.x] = make_float2(m, t);
+    }
+  }
+}
+
+template <int R, int G>
+static hipError_t launch_r_g(const uint16_t* q, const uint8_t* summ, const int32_t* table,
+                             const int32_t* lens, float* scores, int64_t nb, int S, int H, int MP,
+                             int fill_nan, float2* zpart, const void* knew, const void* vnew,
+                             void* kpool, void* vpool, float* mxout, hipStream_t st) {
+  const int ppw = kScorePagesPerWg;
+  dim3 grid(H, (MP + ppw - 1) / ppw, S);
+  hipLaunchKernelGGL((score_mfma_kernel<R, G>), grid, dim3(256), 0, st, q, summ, table, lens,
+                     scores, nb, H, MP, ppw, fill_nan, zpart, static_cast<const uint16_t*>(knew),
+                     static_cast<const uint16_t*>(vnew), static_cast<uint16_t*>(kpool),
+                     static_cast<uint16_t*>(vpool), mxout);
+  return hipGetLastError();
+}
+
+bool score_mfma_supported(int r) { return r == 4 || r == 8 || r == 16; }
+
+hipError_t launch_score_mfma(int r, int G, const void* q, const void* summ, const int32_t* table,
+                             const int32_t* lens, float* scores, int64_t nb, int S, int H, int MP,
+                             int fill_nan, float2* zpart, const void* knew, const void* vnew,
+                             void* kpool, void* vpool, float* mxout, hipStream_t st) {
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint8_t* ss = static_cast<const uint8_t*>(summ);
+#define LOCKS_ARGS qq, ss, table, lens, scores, nb, S, H, MP, fill_nan, zpart, knew, vnew, kpool, vpool, mxout, st
+#define LOCKS_G(RR)                                  \
+  switch (G) {                                       \
+    case 1: return launch_r_g<RR, 1>(LOCKS_ARGS);    \
+    case 2: return launch_r_g<RR, 2>(LOCKS_ARGS);    \
+    case 4: return launch_r_g<RR, 4>(LOCKS_ARGS);    \
+    default: return hipErrorInvalidValue;            \
+  }
+  switch (r) {
+    case 4: LOCKS_G(4)
+    case 8: LOCKS_G(8)
+    case 16: LOCKS_G(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef LOCKS_G
+#undef LOCKS_ARGS
+}
+
+}  // namespace locks

@@ -103,8 +103,11 @@ def _check_against_oracle(b, summ, res, r, max_budget, heads=None, score_tol=1e-
 # score + select + attention from oracle-built summaries
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name,r", [("tiny", 8), ("ctx32k", 8), ("tiny", 4), ("tiny", 16)])
+@pytest.mark.parametrize("name,r", [("tiny", 8), ("ctx32k", 8), ("tiny", 4), ("tiny", 16),
+                                    ("tiny", 5), ("tiny", 12)])
 def test_decode_from_oracle_summaries(L, name, r):
+    """Ranks 4, 8 and 16 run the matrix-core score kernel; other ranks (5, 12
+    here) the vector-ALU one."""
     _say(f"[gpu] decode from oracle summaries: {name} r={r}")
     b = synth.config_batch(name)
     summ = Hh.oracle_summaries(b.k_pool, b.block_table, b.seq_lens, b.H, r, b.num_blocks)
