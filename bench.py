@@ -38,7 +38,7 @@ PAGE_KV_BYTES = 2 * B * D * 2
 HBM_PEAK_GBS = 8000.0
 METRIC = "decode-step µs and achieved HBM GB/s (summary+selected KV) at 128K ctx, 8 KV heads"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "score_kernel_ctx128k_counters.txt")
-SCORE_SRC = os.path.join(ROOT, "kv_cache_page_amd", "csrc", "locks_score.hip")
+SCORE_SRC = os.path.join(ROOT, "kv_cache_page_amd", "csrc", "locks_score_mfma.hip")
 
 
 def log(msg):
@@ -129,6 +129,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="oracle CPU-baseline budget (0 skips it)")
     ap.add_argument("--seed", type=int, default=2)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed region, run one elementwise copy that reads 1 GiB "
+                         "and writes 1 GiB (the reference for HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -256,6 +259,15 @@ def main():
     log(f"[bench] score kernel {score_us:.2f} us per launch, {achieved:.0f} GB/s "
         f"({achieved / HBM_PEAK_GBS:.1%} of {HBM_PEAK_GBS:.0f})")
 
+    if args.calibrate_copy:
+        x = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        y = torch.empty_like(x)
+        torch.cuda.synchronize()
+        torch.neg(x, out=y)   # one dispatch: reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del x, y
+        log("[bench] calibration copy done (1 GiB read + 1 GiB write)")
+
     cpu = None
     if args.cpu_seconds > 0:
         log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
@@ -286,7 +298,7 @@ def main():
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "bulk_build_pages_per_s": round(build_pages / (build_ms / 1e3)),
         "roofline": {
-            "kernel": "score_kernel<8,4> (locks_score_pages)",
+            "kernel": "score_mfma_kernel<8,4> (locks_score_pages)",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
