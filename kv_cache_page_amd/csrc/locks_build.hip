@@ -17,7 +17,7 @@
 // b[x] = A[i][i xor x]; then the diagonal is b[0], the pair element is b[m]
 // and every exchange is a xor lane shuffle. Sweeps stop when the off-diagonal
 // mass of all 4 pages is below 1e-28 of the Frobenius mass (at most 12).
-#include "locks_device.h"
+#include "locks_build_common.h"
 
 namespace locks {
 
@@ -38,21 +38,6 @@ __device__ __forceinline__ void rotation(double app, double aqq, double apq, dou
   t = zero ? 0.0 : t;
   c = 1.0 / sqrt(1.0 + t * t);
   s = t * c;
-}
-
-__device__ __forceinline__ uint16_t fp16_scale_bits(double absmax, float qmax) {
-  // scale = fp16(RNE(fp32(absmax) / qmax)); an infinite result saturates at 65504
-  _Float16 h = (_Float16)((float)absmax / qmax);
-  uint16_t b = __builtin_bit_cast(uint16_t, h);
-  if ((b & 0x7fffu) == 0x7c00u) b = 0x7bffu;
-  return b;
-}
-
-__device__ __forceinline__ int quant_code(double x, float scale, int qmax) {
-  if (scale == 0.f) return 0;
-  float r = rintf((float)x / scale);
-  r = fminf(fmaxf(r, (float)-qmax), (float)qmax);
-  return (int)r;
 }
 
 // One Jacobi round: rotate the 8 pairs (p, p xor M) of the page's 16 rows.
@@ -405,10 +390,20 @@ static hipError_t launch_build_r(const uint16_t* kpool, int64_t nb, int H, const
   return hipGetLastError();
 }
 
+hipError_t launch_build_page(int r, const void* kpool, int64_t nb, int H, const int32_t* ids, int n,
+                             const int32_t* table, const int32_t* lens, int MP, void* summ,
+                             const void* knew, const void* vnew, void* vpool, hipStream_t st);
+
+// Up to this many pages go to the one-page-per-wave form (shorter time to a
+// summary); larger lists to the 4-pages-per-wave form.
+constexpr int64_t kPageFormMaxItems = 4096;
+
 // knew/vnew (filled-page mode only, may be null): append the new token too.
 hipError_t launch_build(int r, const void* kpool, int64_t nb, int H, const int32_t* ids, int n,
                         const int32_t* table, const int32_t* lens, int MP, void* summ,
                         const void* knew, const void* vnew, void* vpool, hipStream_t st) {
+  if (!ids || (int64_t)n * H <= kPageFormMaxItems)
+    return launch_build_page(r, kpool, nb, H, ids, n, table, lens, MP, summ, knew, vnew, vpool, st);
   const uint16_t* kp = static_cast<const uint16_t*>(kpool);
   uint8_t* sm = static_cast<uint8_t*>(summ);
   const uint16_t* kn = static_cast<const uint16_t*>(knew);

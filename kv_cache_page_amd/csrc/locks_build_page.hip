@@ -1,0 +1,439 @@
+// LOCKS page-summary build, latency form: one 64-lane wave per page (gfx950).
+//
+// [N] = LOCKS reading notes (zhongzhuzhou.org 2026-07-29), §4.1 eq. 2-3 and
+// §4.3 Algorithm 1: centroid mu, deviations D = K - 1 mu^T, Gram D D^T,
+// descending eigendecomposition, basis V = D^T U_r Sigma_r^{-1}, coefficients
+// C = U_r Sigma_r, int4 basis / int8 coefficients / int8 centroid. Same
+// arithmetic rules and slot bytes as the 4-pages-per-wave build kernel (the
+// throughput form used for bulk builds); this form serves the few pages a
+// decode step completes, where the time to one summary is what counts.
+//
+// Mapping (one wave, lane l):
+//   keys  : lane l loads dims 32 (l % 4) .. +31 of token l / 4 into LDS (fp32,
+//           exact for bf16);
+//   Gram  : K K^T on v_mfma_f64_16x16x4f64, 32 chunks of 4 dims: lane l feeds
+//           K[l % 16][32 (l / 16) + c] as both operands; the result lands as
+//           rows l / 16 + 4 i, column l % 16; centring G = C (K K^T) C;
+//   Jacobi: lane 16 c + i holds entries x = 4c .. 4c+3 of row i in the
+//           permuted order b[e] = A[i][i xor x] (and U likewise); round M
+//           rotates the 8 pairs (p, p xor M) at once, with the diagonal, the
+//           pair elements, the rotations and the partner rows exchanged
+//           through LDS. Rotation angles are evaluated in fp32 (on operands
+//           scaled to a common exponent) and c = 1/sqrt(1 + t^2) is brought
+//           to fp64 accuracy, so every rotation is orthogonal to fp64
+//           rounding while a visit leaves |a_pq| at about 1e-7 of its value;
+//           sweeps stop at the same off-diagonal criterion as the throughput
+//           form;
+//   basis : lane l owns dims 2l, 2l+1 of every basis column; coefficients:
+//           lane t < 16 owns token row t.
+#include "locks_build_common.h"
+
+namespace locks {
+
+typedef double double4v __attribute__((ext_vector_type(4)));
+
+constexpr int kPgMaxSweeps = 12;
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+// Jacobi rotation for [[app, apq], [apq, aqq]] (Golub & Van Loan's symmetric
+// Schur 2x2, |angle| <= pi/4). t = sgn(tau) / (|tau| + sqrt(1 + tau^2)) is a
+// sum of positive terms, so fp32 gives it to a few ulps once the operands are
+// scaled to a common exponent; tau = +-inf (a_pq below fp32 resolution of the
+// gap) gives t = 0. c = 1/sqrt(1 + t^2) then comes from the fp32 estimate y
+// with one third-order correction y (1 + e/2 + 3e^2/8), e = 1 - x y^2, which
+// is exact to fp64 rounding, so c^2 + s^2 = 1 to fp64 rounding.
+__device__ __forceinline__ void rotation_fast(double app, double aqq, double apq, double& c,
+                                              double& s) {
+  const double num = aqq - app, den = 2.0 * apq;
+  const int e = __builtin_amdgcn_frexp_exp(fmax(fabs(num), fabs(den)));
+  const float n = (float)__builtin_amdgcn_ldexp(num, -e);
+  const float d = (float)__builtin_amdgcn_ldexp(den, -e);
+  const float tau = n * __builtin_amdgcn_rcpf(d);
+  float t = copysignf(1.f, tau) *
+            __builtin_amdgcn_rcpf(fabsf(tau) + __builtin_amdgcn_sqrtf(fmaf(tau, tau, 1.f)));
+  if (d == 0.f) t = 0.f;
+  const double td = (double)t;
+  const double x = fma(td, td, 1.0);
+  const double y = (double)__builtin_amdgcn_rsqf((float)x);
+  const double er = fma(-(x * y), y, 1.0);
+  c = fma(y * er, fma(0.375, er, 0.5), y);
+  s = td * c;
+}
+
+// LDS exchange area of the 64-lane Jacobi.
+constexpr int kApStride = kPage + 2;  // 16-byte aligned rows, rows spread over banks
+struct JacobiLds {
+  double dg[kPage];               // diagonal A[i][i]
+  double pq[kPage];               // A[i][i ^ M] of the current round
+  double2 cs[kPage];              // (c, signed s) of the pair of row i
+  double ap[kPage][kApStride];    // rows in permuted order: ap[i][x] = A[i][i ^ x]
+  double up[kPage][kApStride];    // the same for U
+};
+
+__device__ __forceinline__ void store4(double* p, const double (&v)[4]) {
+  reinterpret_cast<double2*>(p)[0] = make_double2(v[0], v[1]);
+  reinterpret_cast<double2*>(p)[1] = make_double2(v[2], v[3]);
+}
+template <int EM>
+__device__ __forceinline__ void load4_perm(double (&v)[4], const double* p) {
+  const double2 a = reinterpret_cast<const double2*>(p)[0];
+  const double2 b = reinterpret_cast<const double2*>(p)[1];
+  const double t[4] = {a.x, a.y, b.x, b.y};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = t[e ^ EM];
+}
+
+// One round of the 64-lane cyclic Jacobi: the 8 pairs (p, p xor M) at once.
+// Lane (i, qc) holds b[e] = A[i][i ^ x], x = 4 qc + e, and U likewise.
+// Column j = i ^ x turns with the rotation of row j's pair: new b[x] =
+// c_j b[x] - s_j b[x ^ M] with s_j signed as row j holds it (+s on the lower
+// row of a pair, -s on the upper); then row i mixes with row i ^ M.
+template <int M>
+__device__ __forceinline__ void jacobi64_round(double (&b)[4], double (&ub)[4], int i, int qc,
+                                               JacobiLds& sh) {
+  constexpr int HB = (M >= 8) ? 8 : (M >= 4) ? 4 : (M >= 2) ? 2 : 1;  // top bit of M
+  constexpr int QM = M >> 2, EM = M & 3;
+  if (qc == 0) sh.dg[i] = b[0];
+  if (qc == QM) sh.pq[i] = b[EM];
+  if (QM != 0) {
+    store4(&sh.ap[i][4 * qc], b);
+    store4(&sh.up[i][4 * qc], ub);
+  }
+  __syncthreads();
+  const double aii = sh.dg[i], ajj = sh.dg[i ^ M];
+  const double apq = 0.5 * (sh.pq[i] + sh.pq[i ^ M]);
+  double pb[4], pu[4];
+  if (QM == 0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { pb[e] = b[e ^ EM]; pu[e] = ub[e ^ EM]; }
+  } else {
+    load4_perm<EM>(pb, &sh.ap[i][4 * (qc ^ QM)]);
+    load4_perm<EM>(pu, &sh.up[i][4 * (qc ^ QM)]);
+  }
+  const bool lo = (i & HB) == 0;
+  double cr, s0;
+  rotation_fast(lo ? aii : ajj, lo ? ajj : aii, apq, cr, s0);
+  const double sr = lo ? s0 : -s0;
+  if (qc == 0) sh.cs[i] = make_double2(cr, sr);
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const double2 r = sh.cs[i ^ (4 * qc + e)];
+    b[e] = r.x * b[e] - r.y * pb[e];
+    ub[e] = r.x * ub[e] - r.y * pu[e];
+  }
+  // rows: the partner row's entry x ^ M sits at its permuted slot x ^ M
+  store4(&sh.ap[i][4 * qc], b);
+  __syncthreads();
+  double pr[4];
+  load4_perm<EM>(pr, &sh.ap[i ^ M][4 * (qc ^ QM)]);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) b[e] = cr * b[e] - sr * pr[e];
+}
+
+template <int R>
+__global__ __launch_bounds__(64) void build_page_kernel(
+    const uint16_t* __restrict__ kpool, int64_t num_blocks, int H,
+    const int32_t* __restrict__ ids, int n, const int32_t* __restrict__ table,
+    const int32_t* __restrict__ lens, int MP, uint8_t* __restrict__ summ,
+    const uint16_t* __restrict__ knew, const uint16_t* __restrict__ vnew,
+    uint16_t* __restrict__ kdst, uint16_t* __restrict__ vdst) {
+  constexpr SlotLayout L = slot_layout(R);
+  __shared__ float kt[kPage][kHeadDim + 4];
+  __shared__ double g_s[kPage][kPage + 1];
+  __shared__ double u_s[kPage][kPage + 1];
+  __shared__ double lam_s[kPage];
+  __shared__ int perm_s[kPage];
+  __shared__ double sig_s[kPage];
+  __shared__ double rm_s[kPage];
+  __shared__ JacobiLds jl;
+
+  const int lane = threadIdx.x;
+  const int64_t item = blockIdx.x;
+  // ---- which page (same selection rules as the throughput form)
+  int64_t slot = -1;
+  int blk = 0, head = (int)(item % H);
+  const uint8_t* last_key = nullptr;
+  if (ids) {
+    const int b = ids[item / H];
+    if (b >= 0 && b < num_blocks) { blk = b; slot = (int64_t)b * H + head; }
+  } else {
+    const int sq = (int)(item / H);
+    const int len = lens[sq];
+    const int64_t src = ((int64_t)sq * H + head) * kHeadDim;
+    if (knew && len >= 1 && len <= MP * kPage && lane < 2 * (kHeadDim / 8)) {
+      const int b = table[(int64_t)sq * MP + (len - 1) / kPage];
+      if (b >= 0 && b < num_blocks) {
+        const int c8 = lane % (kHeadDim / 8);
+        const int64_t dst = (((int64_t)b * H + head) * kPage + (len - 1) % kPage) * kHeadDim + 8 * c8;
+        if (lane < kHeadDim / 8)
+          *reinterpret_cast<uint4*>(kdst + dst) = *reinterpret_cast<const uint4*>(knew + src + 8 * c8);
+        else
+          *reinterpret_cast<uint4*>(vdst + dst) = *reinterpret_cast<const uint4*>(vnew + src + 8 * c8);
+      }
+    }
+    if (len > 0 && len % kPage == 0 && len / kPage <= MP) {
+      const int b = table[(int64_t)sq * MP + len / kPage - 1];
+      if (b >= 0 && b < num_blocks) {
+        blk = b;
+        slot = (int64_t)b * H + head;
+        if (knew) last_key = reinterpret_cast<const uint8_t*>(knew + src);
+      }
+    }
+  }
+  if (slot < 0) return;  // whole wave: nothing to build
+  uint8_t* sl = summ + slot * (int64_t)L.stride;
+
+  // ---- keys -> LDS; energy = sum of squares of all keys
+  double energy = 0.0;
+  {
+    const int t = lane >> 2, qq = lane & 3;
+    const uint8_t* rowp = (last_key && t == kPage - 1)
+                              ? last_key
+                              : reinterpret_cast<const uint8_t*>(
+                                    kpool + (((int64_t)blk * H + head) * kPage + t) * kHeadDim);
+    uint4 w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = *reinterpret_cast<const uint4*>(rowp + 64 * qq + 16 * e);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t ww[4] = {w[e].x, w[e].y, w[e].z, w[e].w};
+      float f[8];
+#pragma unroll
+      for (int h2 = 0; h2 < 4; ++h2) { f[2 * h2] = bf16_lo(ww[h2]); f[2 * h2 + 1] = bf16_hi(ww[h2]); }
+#pragma unroll
+      for (int h2 = 0; h2 < 8; ++h2) energy = fma((double)f[h2], (double)f[h2], energy);
+      *reinterpret_cast<float4*>(&kt[t][32 * qq + 8 * e]) = make_float4(f[0], f[1], f[2], f[3]);
+      *reinterpret_cast<float4*>(&kt[t][32 * qq + 8 * e + 4]) = make_float4(f[4], f[5], f[6], f[7]);
+    }
+  }
+  energy = wave_sum_d(energy);
+  __syncthreads();
+
+  // ---- Gram K K^T on the fp64 matrix core: rows l/16 + 4i, column l%16
+  double4v mk = {0.0, 0.0, 0.0, 0.0};
+  {
+    const int t = lane & 15, kg = lane >> 4;
+#pragma unroll
+    for (int c8 = 0; c8 < 8; ++c8) {
+      const float4 v = *reinterpret_cast<const float4*>(&kt[t][32 * kg + 4 * c8]);
+      const double vv[4] = {(double)v.x, (double)v.y, (double)v.z, (double)v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mk = __builtin_amdgcn_mfma_f64_16x16x4f64(vv[e], vv[e], mk, 0, 0, 0);
+    }
+  }
+  // centring: G = M - rm 1^T - 1 rm^T + mean(rm), rm = row means (M symmetric)
+  {
+    const int col = lane & 15, rg = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      double v = mk[i];
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) v += __shfl_xor(v, m, 64);
+      if (col == 0) rm_s[rg + 4 * i] = v * (1.0 / kPage);
+    }
+    __syncthreads();
+    double tall = 0.0;
+#pragma unroll
+    for (int r = 0; r < kPage; ++r) tall += rm_s[r];
+    tall *= (1.0 / kPage);
+    const double rc = rm_s[col];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = rg + 4 * i;
+      g_s[row][col] = (mk[i] - (rm_s[row] + rc)) + tall;
+    }
+  }
+  __syncthreads();
+
+  // ---- Jacobi
+  const int ii = lane & 15, qc = lane >> 4;
+  double b[4], ub[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    b[e] = g_s[ii][ii ^ (4 * qc + e)];
+    ub[e] = (qc == 0 && e == 0) ? 1.0 : 0.0;
+  }
+  const double trace = wave_sum_d((qc == 0) ? b[0] : 0.0);
+  for (int sweep = 0; sweep < kPgMaxSweeps; ++sweep) {
+    double off = 0.0, tot = 0.0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const double v = b[e] * b[e];
+      tot += v;
+      if (qc != 0 || e != 0) off += v;
+    }
+    off = wave_sum_d(off);
+    tot = wave_sum_d(tot);
+    if (!(off > 1e-28 * tot)) break;  // the same value in every lane
+    jacobi64_round<1>(b, ub, ii, qc, jl);
+    jacobi64_round<2>(b, ub, ii, qc, jl);
+    jacobi64_round<3>(b, ub, ii, qc, jl);
+    jacobi64_round<4>(b, ub, ii, qc, jl);
+    jacobi64_round<5>(b, ub, ii, qc, jl);
+    jacobi64_round<6>(b, ub, ii, qc, jl);
+    jacobi64_round<7>(b, ub, ii, qc, jl);
+    jacobi64_round<8>(b, ub, ii, qc, jl);
+    jacobi64_round<9>(b, ub, ii, qc, jl);
+    jacobi64_round<10>(b, ub, ii, qc, jl);
+    jacobi64_round<11>(b, ub, ii, qc, jl);
+    jacobi64_round<12>(b, ub, ii, qc, jl);
+    jacobi64_round<13>(b, ub, ii, qc, jl);
+    jacobi64_round<14>(b, ub, ii, qc, jl);
+    jacobi64_round<15>(b, ub, ii, qc, jl);
+  }
+  // eigenvalues (diagonal) and eigenvectors (columns of U) to LDS
+  if (qc == 0) lam_s[ii] = b[0];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) u_s[ii][ii ^ (4 * qc + e)] = ub[e];
+  __syncthreads();
+  // descending order, lower index first on ties
+  if (lane < kPage) {
+    const double lam = lam_s[lane];
+    int rank = 0;
+#pragma unroll
+    for (int j = 0; j < kPage; ++j) {
+      const double o = lam_s[j];
+      rank += (o > lam || (o == lam && j < lane)) ? 1 : 0;
+    }
+    perm_s[rank & (kPage - 1)] = lane;
+  }
+  __syncthreads();
+
+  const double thr = fmax(1e-6 * trace, 1e-12 * energy);
+  // ---- centroid (dims 2l, 2l+1) and the page's deviations in those dims
+  double mu[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) mu[e] = 0.0;
+#pragma unroll
+  for (int t = 0; t < kPage; ++t) {
+    const float2 v = *reinterpret_cast<const float2*>(&kt[t][2 * lane]);
+    mu[0] += (double)v.x;
+    mu[1] += (double)v.y;
+  }
+  mu[0] *= (1.0 / kPage);
+  mu[1] *= (1.0 / kPage);
+  double dv[kPage][2];
+#pragma unroll
+  for (int t = 0; t < kPage; ++t) {
+    const float2 v = *reinterpret_cast<const float2*>(&kt[t][2 * lane]);
+    dv[t][0] = (double)v.x - mu[0];
+    dv[t][1] = (double)v.y - mu[1];
+  }
+
+  // ---- basis columns: v_k = D^T u_k / sigma_k, canonical sign, int4 codes
+  const int wq = lane >> 2, pq = lane & 3;           // word of 8 dims, pair inside it
+  const int byte_of_pair = (pq == 0) ? 0 : (pq == 1) ? 2 : (pq == 2) ? 1 : 3;
+#pragma unroll 2
+  for (int k = 0; k < R; ++k) {
+    const int ck = perm_s[k] & (kPage - 1);
+    const double lk = lam_s[ck];
+    const bool act = lk > thr;
+    const double sig = act ? sqrt(lk) : 1.0;
+    double v0 = 0.0, v1 = 0.0;
+#pragma unroll
+    for (int t = 0; t < kPage; ++t) {
+      const double u = u_s[t][ck];
+      v0 = fma(dv[t][0], u, v0);
+      v1 = fma(dv[t][1], u, v1);
+    }
+    v0 = act ? v0 / sig : 0.0;
+    v1 = act ? v1 / sig : 0.0;
+    // largest |v| (lowest dim on ties) over the 128 dims
+    double amax = fabs(v0);
+    int aidx = 2 * lane;
+    if (fabs(v1) > amax) { amax = fabs(v1); aidx = 2 * lane + 1; }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const double oa = __shfl_xor(amax, m, 64);
+      const int oi = __shfl_xor(aidx, m, 64);
+      if (oa > amax || (oa == amax && oi < aidx)) { amax = oa; aidx = oi; }
+    }
+    const double vsel = ((aidx & 1) ? v1 : v0);
+    const double aval = __shfl(vsel, aidx >> 1, 64);
+    const double flip = (aval < 0.0) ? -1.0 : 1.0;
+    if (lane == 0) sig_s[k] = act ? sig * flip : 0.0;
+    const uint16_t sbits = act ? fp16_scale_bits(amax, 7.f) : (uint16_t)0;
+    const float scale = (float)__builtin_bit_cast(_Float16, sbits);
+    const int code0 = quant_code(v0 * flip, scale, 7) & 0xF;
+    const int code1 = quant_code(v1 * flip, scale, 7) & 0xF;
+    // the 4 pairs of a word: bytes hold the pairs (0,1), (4,5), (2,3), (6,7)
+    const uint32_t byte = (uint32_t)(code0 | (code1 << 4)) << (8 * byte_of_pair);
+    uint32_t word = byte | (uint32_t)__builtin_amdgcn_update_dpp(0, (int)byte, 0xB1, 0xF, 0xF, false);
+    word |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0x4E, 0xF, 0xF, false);
+    if (pq == 0) *reinterpret_cast<uint32_t*>(sl + L.v + 64 * k + 4 * wq) = word;
+    if (lane == 0) *reinterpret_cast<uint16_t*>(sl + L.sv + 2 * k) = sbits;
+  }
+  __syncthreads();
+
+  // ---- coefficients: lane t owns row c_t = U[t][c_k] sigma_k (signed), int8
+  if (lane < kPage) {
+    double cr[R];
+    double amax = 0.0;
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const double f = sig_s[k];
+      cr[k] = (f != 0.0) ? u_s[lane][perm_s[k] & (kPage - 1)] * fabs(f) * (f < 0.0 ? -1.0 : 1.0) : 0.0;
+      amax = fmax(amax, fabs(cr[k]));
+    }
+    const uint16_t sbits = amax > 0.0 ? fp16_scale_bits(amax, 127.f) : (uint16_t)0;
+    const float scale = (float)__builtin_bit_cast(_Float16, sbits);
+#pragma unroll
+    for (int k = 0; k < R; ++k) sl[L.c + lane * R + k] = (uint8_t)(quant_code(cr[k], scale, 127) & 0xFF);
+    *reinterpret_cast<uint16_t*>(sl + L.sc + 2 * lane) = sbits;
+  }
+
+  // ---- centroid: one scale for the page
+  {
+    double amax = fmax(fabs(mu[0]), fabs(mu[1]));
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) amax = fmax(amax, __shfl_xor(amax, m, 64));
+    const uint16_t sbits = amax > 0.0 ? fp16_scale_bits(amax, 127.f) : (uint16_t)0;
+    const float scale = (float)__builtin_bit_cast(_Float16, sbits);
+    const uint32_t lo = (uint32_t)(quant_code(mu[0], scale, 127) & 0xFF);
+    const uint32_t hi = (uint32_t)(quant_code(mu[1], scale, 127) & 0xFF);
+    *reinterpret_cast<uint16_t*>(sl + L.mu + 2 * lane) = (uint16_t)(lo | (hi << 8));
+    if (lane == 0) *reinterpret_cast<uint16_t*>(sl + L.smu) = sbits;
+    if (lane < L.stride - L.payload) sl[L.payload + lane] = 0;
+  }
+}
+
+template <int R>
+static hipError_t launch_build_page_r(const uint16_t* kpool, int64_t nb, int H, const int32_t* ids,
+                                      int n, const int32_t* table, const int32_t* lens, int MP,
+                                      uint8_t* summ, const uint16_t* knew, const uint16_t* vnew,
+                                      uint16_t* kdst, uint16_t* vdst, hipStream_t st) {
+  const int64_t items = (int64_t)n * H;
+  if (items == 0) return hipSuccess;
+  hipLaunchKernelGGL(build_page_kernel<R>, dim3((unsigned)items), dim3(64), 0, st, kpool, nb, H, ids,
+                     n, table, lens, MP, summ, knew, vnew, kdst, vdst);
+  return hipGetLastError();
+}
+
+hipError_t launch_build_page(int r, const void* kpool, int64_t nb, int H, const int32_t* ids, int n,
+                             const int32_t* table, const int32_t* lens, int MP, void* summ,
+                             const void* knew, const void* vnew, void* vpool, hipStream_t st) {
+  const uint16_t* kp = static_cast<const uint16_t*>(kpool);
+  uint8_t* sm = static_cast<uint8_t*>(summ);
+  const uint16_t* kn = static_cast<const uint16_t*>(knew);
+  const uint16_t* vn = static_cast<const uint16_t*>(vnew);
+  uint16_t* kd = const_cast<uint16_t*>(kp);
+  uint16_t* vd = static_cast<uint16_t*>(vpool);
+  switch (r) {
+#define LOCKS_R(RR) \
+  case RR:          \
+    return launch_build_page_r<RR>(kp, nb, H, ids, n, table, lens, MP, sm, kn, vn, kd, vd, st);
+    LOCKS_R(1) LOCKS_R(2) LOCKS_R(3) LOCKS_R(4) LOCKS_R(5) LOCKS_R(6) LOCKS_R(7) LOCKS_R(8)
+    LOCKS_R(9) LOCKS_R(10) LOCKS_R(11) LOCKS_R(12) LOCKS_R(13) LOCKS_R(14) LOCKS_R(15) LOCKS_R(16)
+#undef LOCKS_R
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace locks

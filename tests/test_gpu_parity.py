@@ -246,9 +246,11 @@ def _compare_codes(gpu_slots, keys, r):
     return frac, int(flag.sum()), int(amb.sum())
 
 
-@pytest.mark.parametrize("r", [4, 8, 16])
-def test_build_codes(L, r):
-    n = 8192
+@pytest.mark.parametrize("r,n", [(4, 8192), (8, 8192), (16, 8192), (4, 4096), (8, 4096), (16, 4096),
+                                 (7, 1000)])
+def test_build_codes(L, r, n):
+    """Lists of up to 4096 pages use the one-page-per-wave build, longer ones
+    the four-pages-per-wave build: both against the oracle's codes."""
     _say(f"[gpu] build parity r={r} n={n}")
     keys = synth.random_pages(n, seed=100 + r)                       # bf16 [n][16][128] on CPU
     pool = keys.view(n, 1, 16, 128).contiguous().to(DEV)
@@ -263,8 +265,11 @@ def test_build_codes(L, r):
     assert frac <= 1e-3
 
 
-def test_build_degenerate_pages(L):
-    _say("[gpu] build of degenerate pages")
+@pytest.mark.parametrize("pad", [0, 4200])
+def test_build_degenerate_pages(L, pad):
+    """Degenerate pages, alone (one-page-per-wave build) and followed by
+    `pad` random pages (four-pages-per-wave build)."""
+    _say(f"[gpu] build of degenerate pages (pad {pad})")
     n = 8
     k = torch.zeros(n, 16, 128)
     k[1] = 0.375                                          # all keys equal
@@ -275,13 +280,14 @@ def test_build_degenerate_pages(L):
     k[6] = torch.randn(16, 128) * 300
     k[7, ::2] = 1.0                                        # two distinct keys
     keys = k.to(torch.bfloat16)
+    allk = torch.cat([keys, synth.random_pages(pad, seed=77)]) if pad else keys
     for r in (1, 8, 16):
         dims = L.Dims(1, 4, r)
-        summ = L.alloc_summaries(dims, n, DEV)
-        L.build(dims, keys.view(n, 1, 16, 128).contiguous().to(DEV),
-                torch.arange(n, dtype=torch.int32, device=DEV), summ)
+        summ = L.alloc_summaries(dims, n + pad, DEV)
+        L.build(dims, allk.view(n + pad, 1, 16, 128).contiguous().to(DEV),
+                torch.arange(n + pad, dtype=torch.int32, device=DEV), summ)
         torch.cuda.synchronize()
-        got = summ[:, 0].cpu().numpy()
+        got = summ[:n, 0].cpu().numpy()
         ora, s, _ = O.build_slots(keys.double().numpy(), r)
         for p in (0, 1, 3):                               # exactly degenerate: byte-identical
             assert np.array_equal(got[p], ora[p]), (r, p)
@@ -316,6 +322,33 @@ def test_build_list_and_filled(L):
                 assert np.count_nonzero(got2[blk, h] != ora[0]) <= 4
             else:
                 assert not got2[blk, h].any()
+
+
+@pytest.mark.parametrize("r", [8, 13])
+def test_build_filled_many(L, r):
+    """Filled-page mode over 96 sequences x 8 KV heads (768 pages built at
+    once, the shape of a decode step where many sequences fill a page)."""
+    _say(f"[gpu] filled-page build, 96 x 8 pages, r={r}")
+    S, H = 96, 8
+    lens = [16 * (1 + (s * 7) % 11) for s in range(S)]
+    b = synth.make_decode_batch(lens, H, 4, [4] * S, seed=120 + r, needles_per_head=0)
+    dims = L.Dims(H, 4, r)
+    bd = _to_dev(b)
+    summ = L.alloc_summaries(dims, b.num_blocks, DEV)
+    L.build_filled(dims, bd.k_pool, bd.block_table, bd.seq_lens, summ)
+    torch.cuda.synchronize()
+    got = summ.cpu().numpy()
+    blks = [int(b.block_table[s, lens[s] // 16 - 1]) for s in range(S)]
+    keys = np.stack([Hh.np64(b.k_pool[blk, h]) for blk in blks for h in range(H)])
+    gpu = np.stack([got[blk, h] for blk in blks for h in range(H)])
+    frac, nflag, namb = _compare_codes(gpu, keys, r)
+    _say(f"    differing code entries {frac:.2e}; near-degenerate pages {nflag}; "
+         f"sign-ambiguous columns {namb}")
+    assert frac <= 1e-3
+    built = set(blks)
+    for blk in range(b.num_blocks):
+        if blk not in built:
+            assert not got[blk].any()
 
 
 def test_append(L):
