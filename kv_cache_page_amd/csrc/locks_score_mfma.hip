@@ -74,21 +74,21 @@ struct GroupRegs {
 };
 
 template <int R>
-__device__ __forceinline__ void load_group(GroupRegs<R>& g, const uint8_t* __restrict__ summ,
-                                           int64_t offV, int64_t offC, int r16, int q16) {
+__device__ __forceinline__ void load_group(GroupRegs<R>& g, const uint8_t* __restrict__ slotV,
+                                           const uint8_t* __restrict__ slotC, int r16, int q16) {
   constexpr SlotLayout L = slot_layout(R);
   const int b = r16 >> 2;
+  const uint8_t* pv = slotV + L.v + 64 * (r16 & 3) + 16 * q16;
 #pragma unroll
-  for (int hh = 0; hh < R / 4; ++hh)
-    g.v[hh] = *reinterpret_cast<const uint4*>(summ + offV + L.v + 64 * (4 * hh + (r16 & 3)) + 16 * q16);
+  for (int hh = 0; hh < R / 4; ++hh) g.v[hh] = *reinterpret_cast<const uint4*>(pv + 256 * hh);
   // tokens 4b..4b+3 x R bytes = 4R contiguous bytes
+  const uint8_t* pc = slotC + L.c + 4 * R * b;
 #pragma unroll
-  for (int e = 0; e < R / 4; ++e)
-    g.c[e] = *reinterpret_cast<const uint4*>(summ + offC + L.c + 4 * R * b + 16 * e);
+  for (int e = 0; e < R / 4; ++e) g.c[e] = *reinterpret_cast<const uint4*>(pc + 16 * e);
 #pragma unroll
-  for (int e = 0; e < R / 2; ++e) g.sv[e] = *reinterpret_cast<const uint32_t*>(summ + offC + L.sv + 4 * e);
-  g.sc = *reinterpret_cast<const uint2*>(summ + offC + L.sc + 8 * b);
-  g.smu = *reinterpret_cast<const uint16_t*>(summ + offC + L.smu);
+  for (int e = 0; e < R / 2; ++e) g.sv[e] = *reinterpret_cast<const uint32_t*>(slotC + L.sv + 4 * e);
+  g.sc = *reinterpret_cast<const uint2*>(slotC + L.sc + 8 * b);
+  g.smu = *reinterpret_cast<const uint16_t*>(slotC + L.smu);
 }
 
 template <int R, int G>
@@ -110,9 +110,17 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q16 = lane >> 4;
   const int gq = r16 & 3;  // this lane's query (B column r16 carries query r16 % 4)
+  const int j_lo = tile * pages_per_wg;
+  const int P0 = j_lo + kWavePages * wave;  // this wave's first page
+  // block ids of the pages P0 + 16 u + r16, read together with the length
+  int traw[kHalves];
+#pragma unroll
+  for (int u = 0; u < kHalves; ++u) {
+    const int j = P0 + 16 * u + r16;
+    traw[u] = (j < MP) ? table[(int64_t)s * MP + j] : -1;
+  }
   const int len = clampi(seq_lens[s], 0, MP * kPage);
   const int F = len / kPage;
-  const int j_lo = tile * pages_per_wg;
   if (knew && tile == 0 && threadIdx.x < 2 * (kHeadDim / 8) && len >= 1) {
     // decode-step append of the new token (position len - 1) for this head
     const int blk = table[(int64_t)s * MP + (len - 1) / kPage];
@@ -135,7 +143,6 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(
   }
   if (j_lo >= F) return;
   const int j_end = min(j_hi, F);
-  const int P0 = j_lo + kWavePages * wave;  // this wave's first page
 
   // ---- raw query rows (independent of the block ids): column r16 carries
   // query gq; lane q16 holds dims [32 q16, 32 q16 + 32) of it
@@ -147,18 +154,25 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(
 #pragma unroll
     for (int c = 0; c < 4; ++c) qraw[c] = qp[c];
   }
-  // ---- block ids of the pages P0 + 16 u + r16, then the slot offsets each
-  // role needs, by lane permutes
+  // ---- live block ids (-1: page past the end or id out of range); the slot
+  // addresses each role needs come by lane permutes. vbits[u] bit i: page
+  // P0 + 16 u + i is live.
   int bo[kHalves];
+  uint32_t vbits[kHalves];
 #pragma unroll
   for (int u = 0; u < kHalves; ++u) {
     const int j = P0 + 16 * u + r16;
-    const int b = (j < j_end) ? table[(int64_t)s * MP + j] : -1;
-    bo[u] = (b >= 0 && b < num_blocks) ? b : -1;
+    const int b = traw[u];
+    bo[u] = (j < j_end && b >= 0 && b < num_blocks) ? b : -1;
+    vbits[u] = (uint32_t)__ballot(bo[u] >= 0) & 0xFFFFu;
   }
 
-  const int64_t hstride = (int64_t)L.stride;
-  auto slot_off = [&](int b) -> int64_t { return ((int64_t)(b < 0 ? 0 : b) * H + h) * hstride; };
+  // slot of block b for this head: summ_h + b * (H * stride), one 32 x 32 -> 64 multiply-add
+  const uint8_t* summ_h = summ + (size_t)h * L.stride;
+  const uint32_t hs = (uint32_t)H * (uint32_t)L.stride;
+  auto slot_ptr = [&](int b) -> const uint8_t* {
+    return summ_h + (uint64_t)(uint32_t)(b < 0 ? 0 : b) * hs;
+  };
   auto shfl_i = [&](int v, int src) -> int { return __shfl(v, src, 64); };
 
   // ---- centroid term per 16-page half: register i of lane q16 holds
@@ -168,21 +182,23 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(
     const int src = 4 * (r16 & 3) + (r16 >> 2);  // A row r16 <- page src
 #pragma unroll
     for (int u = 0; u < kHalves; ++u) {
-      const int64_t o = slot_off(shfl_i(bo[u], src)) + L.mu + 32 * q16;
-      mw[u][0] = *reinterpret_cast<const uint4*>(summ + o);
-      mw[u][1] = *reinterpret_cast<const uint4*>(summ + o + 16);
+      const uint8_t* o = slot_ptr(shfl_i(bo[u], src)) + L.mu + 32 * q16;
+      mw[u][0] = *reinterpret_cast<const uint4*>(o);
+      mw[u][1] = *reinterpret_cast<const uint4*>(o + 16);
     }
   }
   // ---- groups: pipeline of slot loads (three groups in flight while one is
   // computed; two for rank 16)
-  float zm = -__builtin_inff(), zs = 0.f;  // running LSE (base 2) of query gq
+  float zv[kGroups];  // page LSEs (base 2) of query gq, for the tile's Z partial
+#pragma unroll
+  for (int gi = 0; gi < kGroups; ++gi) zv[gi] = -__builtin_inff();
   constexpr int kDepth = (R >= 8) ? 3 : 4;  // register budget: three waves per SIMD up to rank 8
   GroupRegs<R> buf[kDepth];
   auto issue = [&](int gi, GroupRegs<R>& gr) {
     const int u = gi >> 2, base = 4 * (gi & 3);
     const int bV = shfl_i(bo[u], base + (r16 >> 2));
     const int bC = shfl_i(bo[u], base + q16);
-    load_group<R>(gr, summ, slot_off(bV), slot_off(bC), r16, q16);
+    load_group<R>(gr, slot_ptr(bV), slot_ptr(bC), r16, q16);
   };
 #pragma unroll
   for (int gi = 0; gi < kDepth - 1; ++gi)
@@ -309,9 +325,10 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(
     e += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(e), 0x101F));
     e += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(e), 0x201F));
     const int jp = P0 + 4 * gi + q16;  // the lane's page
-    const bool ok = jp < j_end && shfl_i(bo[u], base + q16) >= 0 && gq < G;
+    const bool ok = ((vbits[u] >> (base + q16)) & 1u) && gq < G;
     const float out2 = ok ? m + __builtin_amdgcn_logf(e) : -__builtin_inff();
     const bool writer = (r16 < 4) && jp < j_end;  // token block 0 writes
+    zv[gi] = (r16 < 4) ? out2 : -__builtin_inff();
     if (mxout) {
       // decode layout: e_g = 2^(s_g - max_g s_g) per query and the page max;
       // lanes r16 = 0..3 hold the page's 4 queries (a DPP quad)
@@ -322,11 +339,19 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(
     } else if (writer && gq < G) {
       srow[(int64_t)jp * G + gq] = out2 * kLn2;
     }
-    if (writer && ok) lse2_merge(zm, zs, out2, 1.f);
   }
   if (zpart) {
-    // lanes r16 < 4 carry query gq = r16; reduce over the other lanes of the
-    // same query (xor 4, 8: token blocks, empty; xor 16, 32: pages), then waves
+    // the lane's page LSEs, then lanes r16 < 4 carry query gq = r16; reduce
+    // over the other lanes of the same query (xor 4, 8: token blocks, empty;
+    // xor 16, 32: pages), then waves
+    float zm = zv[0];
+#pragma unroll
+    for (int gi = 1; gi < kGroups; ++gi) zm = fmaxf(zm, zv[gi]);
+    float zs = 0.f;
+    if (zm != -__builtin_inff()) {
+#pragma unroll
+      for (int gi = 0; gi < kGroups; ++gi) zs += __builtin_amdgcn_exp2f(zv[gi] - zm);
+    }
     __shared__ float zred[4][4][2];
 #pragma unroll
     for (int mm = 4; mm < 64; mm <<= 1) {
