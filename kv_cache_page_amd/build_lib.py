@@ -31,13 +31,19 @@ FLAGS = [
 ]
 
 
+# Per-file additions. The score kernel never produces NaN from its own
+# arithmetic (it only stores NaN constants), so max/min need no NaN quieting
+# and fold into DPP forms.
+FILE_FLAGS = {"locks_score_mfma.hip": ["-fno-honor-nans"]}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src, verbose):
     obj = os.path.join(BUILD_DIR, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -5,9 +5,10 @@
 //   s_hat_jg = LSE_t ((q_g . mu_j + c_t . (V_j^T q_g)) / sqrt(d))
 // from the int4 basis, int8 coefficients and int8 centroid of the slot.
 //
-// Same contract and grid as the VALU score kernel (one 256-thread workgroup
-// per 128-page tile of one (sequence, KV head)); wave w takes the 32 pages
-// j_lo + 32 w + [0, 32) as 8 groups of 4 pages. Lane l = 16 q16 + r16.
+// Same contract and tiles as the VALU score kernel (128-page tiles of one
+// (sequence, KV head), one Z partial per tile, one 256-thread workgroup per
+// tile); wave w of a tile takes the 32 pages j_lo + 32 w + [0, 32) as 8
+// groups of 4 pages. Lane l = 16 q16 + r16.
 //
 // Stage 1, W = V^T q on v_mfma_f32_16x16x32_f16, per group and quarter of
 //   the ranks (ranks 4hh .. 4hh+3): A rows m = r16 are (page m / 4, rank
@@ -56,6 +57,12 @@ __device__ __forceinline__ half8 byte8(uint32_t w0, uint32_t w1) {
                                               w1 & 0x00FF00FFu, (w1 >> 8) & 0x00FF00FFu));
 }
 
+// Value of lane (r + K) mod 16 of the same 16-lane row (DPP row rotation).
+template <int K>
+__device__ __forceinline__ float row_ror(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x120 | K, 0xF, 0xF, true));
+}
+
 __device__ __forceinline__ float half_lo(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
 }
@@ -91,14 +98,16 @@ __device__ __forceinline__ void load_group(GroupRegs<R>& g, const uint8_t* __res
   g.smu = *reinterpret_cast<const uint16_t*>(slotC + L.smu);
 }
 
+// One 128-page tile, by 4 waves (wave = 0..3, tid = 64 wave + lane). Leaves
+// the wave's Z partial of query gq = lane % 4 in (zm, zs) of lanes 0..3.
 template <int R, int G>
-__global__ __launch_bounds__(256) void score_mfma_kernel(
+__device__ __forceinline__ void score_tile(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ summ,
     const int32_t* __restrict__ table, const int32_t* __restrict__ seq_lens,
     float* __restrict__ scores, int64_t num_blocks, int H, int MP, int pages_per_wg,
-    int fill_nan, float2* __restrict__ zpart, const uint16_t* __restrict__ knew,
-    const uint16_t* __restrict__ vnew, uint16_t* __restrict__ kpool,
-    uint16_t* __restrict__ vpool, float* __restrict__ mxout) {
+    int fill_nan, const uint16_t* __restrict__ knew, const uint16_t* __restrict__ vnew,
+    uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool, float* __restrict__ mxout,
+    int s, int h, int tile, int wave, int tid, float& zm, float& zs) {
   static_assert(R == 4 || R == 8 || R == 16, "matrix-core path covers ranks 4, 8, 16");
   constexpr SlotLayout L = slot_layout(R);
   constexpr int NHR = R / 4;
@@ -106,8 +115,7 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(
   constexpr int kWavePages = kScorePagesPerWg / 4;    // pages per wave
   constexpr int kHalves = (kWavePages + 15) / 16;     // 16-page halves (centroid MFMAs)
   constexpr int kGroups = kWavePages / 4;             // 4-page groups per wave
-  const int s = blockIdx.z, h = blockIdx.x, tile = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = tid & 63;
   const int r16 = lane & 15, q16 = lane >> 4;
   const int gq = r16 & 3;  // this lane's query (B column r16 carries query r16 % 4)
   const int j_lo = tile * pages_per_wg;
@@ -121,14 +129,14 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(
   }
   const int len = clampi(seq_lens[s], 0, MP * kPage);
   const int F = len / kPage;
-  if (knew && tile == 0 && threadIdx.x < 2 * (kHeadDim / 8) && len >= 1) {
+  if (knew && tile == 0 && tid < 2 * (kHeadDim / 8) && len >= 1) {
     // decode-step append of the new token (position len - 1) for this head
     const int blk = table[(int64_t)s * MP + (len - 1) / kPage];
     if (blk >= 0 && blk < num_blocks) {
-      const int c = threadIdx.x % (kHeadDim / 8);
+      const int c = tid % (kHeadDim / 8);
       const int64_t src = ((int64_t)s * H + h) * kHeadDim + 8 * c;
       const int64_t dst = (((int64_t)blk * H + h) * kPage + (len - 1) % kPage) * kHeadDim + 8 * c;
-      if (threadIdx.x < kHeadDim / 8)
+      if (tid < kHeadDim / 8)
         *reinterpret_cast<uint4*>(kpool + dst) = *reinterpret_cast<const uint4*>(knew + src);
       else
         *reinterpret_cast<uint4*>(vpool + dst) = *reinterpret_cast<const uint4*>(vnew + src);
@@ -138,8 +146,8 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(
   float* srow = scores + ((int64_t)s * H + h) * MP * G;
   if (fill_nan) {
     const int first = max(j_lo, F);
-    for (int idx = threadIdx.x; idx < (j_hi - first) * G; idx += blockDim.x)
-      srow[(int64_t)first * G + idx] = __builtin_nanf("");
+    for (int idx = tid; idx < (j_hi - first) * G; idx += 256)
+      reinterpret_cast<uint32_t*>(srow)[(int64_t)first * G + idx] = 0x7FC00000u;  // quiet NaN
   }
   if (j_lo >= F) return;
   const int j_end = min(j_hi, F);
@@ -192,7 +200,7 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(
   float zv[kGroups];  // page LSEs (base 2) of query gq, for the tile's Z partial
 #pragma unroll
   for (int gi = 0; gi < kGroups; ++gi) zv[gi] = -__builtin_inff();
-  constexpr int kDepth = (R >= 8) ? 3 : 4;  // register budget: three waves per SIMD up to rank 8
+  constexpr int kDepth = (R >= 8) ? 3 : 4;  // deeper prefetch only moves the stall to the issue
   GroupRegs<R> buf[kDepth];
   auto issue = [&](int gi, GroupRegs<R>& gr) {
     const int u = gi >> 2, base = 4 * (gi & 3);
@@ -317,13 +325,15 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(
       lg[i] = fs * fmaf(sc, x, muq);
     }
     // LSE over the 16 tokens: 4 here, the other token blocks in lanes r16 ^ 4, ^ 8
+    // (the 4 lanes r16 = g, g+4, g+8, g+12 form one orbit of the row rotations
+    // by 4 and 8)
     float m = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
-    m = fmaxf(m, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(m), 0x101F)));
-    m = fmaxf(m, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(m), 0x201F)));
+    m = fmaxf(m, row_ror<4>(m));
+    m = fmaxf(m, row_ror<8>(m));
     float e = __builtin_amdgcn_exp2f(lg[0] - m) + __builtin_amdgcn_exp2f(lg[1] - m) +
               __builtin_amdgcn_exp2f(lg[2] - m) + __builtin_amdgcn_exp2f(lg[3] - m);
-    e += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(e), 0x101F));
-    e += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(e), 0x201F));
+    e += row_ror<4>(e);
+    e += row_ror<8>(e);
     const int jp = P0 + 4 * gi + q16;  // the lane's page
     const bool ok = ((vbits[u] >> (base + q16)) & 1u) && gq < G;
     const float out2 = ok ? m + __builtin_amdgcn_logf(e) : -__builtin_inff();
@@ -340,30 +350,50 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(
       srow[(int64_t)jp * G + gq] = out2 * kLn2;
     }
   }
+  // the lane's page LSEs, then lanes r16 < 4 carry query gq = r16; reduce
+  // over the other lanes of the same query (xor 4, 8: token blocks, empty;
+  // xor 16, 32: pages)
+  zm = zv[0];
+#pragma unroll
+  for (int gi = 1; gi < kGroups; ++gi) zm = fmaxf(zm, zv[gi]);
+  zs = 0.f;
+  if (zm != -__builtin_inff()) {
+#pragma unroll
+    for (int gi = 0; gi < kGroups; ++gi) zs += __builtin_amdgcn_exp2f(zv[gi] - zm);
+  }
+#pragma unroll
+  for (int mm = 4; mm < 64; mm <<= 1) {
+    const float m2 = __shfl_xor(zm, mm, 64), s2 = __shfl_xor(zs, mm, 64);
+    lse2_merge(zm, zs, m2, s2);
+  }
+}
+
+// TPW tiles per workgroup (4 waves each).
+template <int R, int G, int TPW>
+__global__ __launch_bounds__(256 * TPW) void score_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ summ,
+    const int32_t* __restrict__ table, const int32_t* __restrict__ seq_lens,
+    float* __restrict__ scores, int64_t num_blocks, int H, int MP, int pages_per_wg,
+    int fill_nan, float2* __restrict__ zpart, const uint16_t* __restrict__ knew,
+    const uint16_t* __restrict__ vnew, uint16_t* __restrict__ kpool,
+    uint16_t* __restrict__ vpool, float* __restrict__ mxout) {
+  const int s = blockIdx.z, h = blockIdx.x;
+  const int sub = (TPW == 1) ? 0 : (int)(threadIdx.x >> 8);
+  const int tile = blockIdx.y * TPW + sub;
+  const int tid = threadIdx.x & 255, wave = tid >> 6, lane = tid & 63;
+  const int ntiles = (MP + pages_per_wg - 1) / pages_per_wg;
+  float zm = -__builtin_inff(), zs = 0.f;
+  if (tile < ntiles)
+    score_tile<R, G>(q, summ, table, seq_lens, scores, num_blocks, H, MP, pages_per_wg, fill_nan,
+                     knew, vnew, kpool, vpool, mxout, s, h, tile, wave, tid, zm, zs);
   if (zpart) {
-    // the lane's page LSEs, then lanes r16 < 4 carry query gq = r16; reduce
-    // over the other lanes of the same query (xor 4, 8: token blocks, empty;
-    // xor 16, 32: pages), then waves
-    float zm = zv[0];
-#pragma unroll
-    for (int gi = 1; gi < kGroups; ++gi) zm = fmaxf(zm, zv[gi]);
-    float zs = 0.f;
-    if (zm != -__builtin_inff()) {
-#pragma unroll
-      for (int gi = 0; gi < kGroups; ++gi) zs += __builtin_amdgcn_exp2f(zv[gi] - zm);
-    }
-    __shared__ float zred[4][4][2];
-#pragma unroll
-    for (int mm = 4; mm < 64; mm <<= 1) {
-      const float m2 = __shfl_xor(zm, mm, 64), s2 = __shfl_xor(zs, mm, 64);
-      lse2_merge(zm, zs, m2, s2);
-    }
-    if (lane < G) { zred[wave][lane][0] = zm; zred[wave][lane][1] = zs; }
+    __shared__ float zred[TPW][4][4][2];
+    if (lane < G) { zred[sub][wave][lane][0] = zm; zred[sub][wave][lane][1] = zs; }
     __syncthreads();
-    if (threadIdx.x < G) {
-      float m = zred[0][threadIdx.x][0], t = zred[0][threadIdx.x][1];
-      for (int w = 1; w < 4; ++w) lse2_merge(m, t, zred[w][threadIdx.x][0], zred[w][threadIdx.x][1]);
-      zpart[(((int64_t)s * H + h) * gridDim.y + tile) * G + threadIdx.x] = make_float2(m, t);
+    if (tid < G && tile < ntiles) {
+      float m = zred[sub][0][tid][0], t = zred[sub][0][tid][1];
+      for (int w = 1; w < 4; ++w) lse2_merge(m, t, zred[sub][w][tid][0], zred[sub][w][tid][1]);
+      zpart[(((int64_t)s * H + h) * ntiles + tile) * G + tid] = make_float2(m, t);
     }
   }
 }
@@ -373,9 +403,11 @@ static hipError_t launch_r_g(const uint16_t* q, const uint8_t* summ, const int32
                              const int32_t* lens, float* scores, int64_t nb, int S, int H, int MP,
                              int fill_nan, float2* zpart, const void* knew, const void* vnew,
                              void* kpool, void* vpool, float* mxout, hipStream_t st) {
+  constexpr int TPW = 1;
   const int ppw = kScorePagesPerWg;
-  dim3 grid(H, (MP + ppw - 1) / ppw, S);
-  hipLaunchKernelGGL((score_mfma_kernel<R, G>), grid, dim3(256), 0, st, q, summ, table, lens,
+  const int ntiles = (MP + ppw - 1) / ppw;
+  dim3 grid(H, (ntiles + TPW - 1) / TPW, S);
+  hipLaunchKernelGGL((score_mfma_kernel<R, G, TPW>), grid, dim3(256 * TPW), 0, st, q, summ, table, lens,
                      scores, nb, H, MP, ppw, fill_nan, zpart, static_cast<const uint16_t*>(knew),
                      static_cast<const uint16_t*>(vnew), static_cast<uint16_t*>(kpool),
                      static_cast<uint16_t*>(vpool), mxout);
