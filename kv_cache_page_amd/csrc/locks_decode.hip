@@ -20,9 +20,10 @@
 //
 // Inputs from the score kernel (decode layout): per page j and query g,
 // e_jg = 2^(s_jg - m_j) with m_j = max_g s_jg (base-2 scores), and m_j; per
-// 128-page tile and query, the base-2 (max, sum) of the scores. Thread t owns
-// pages t, t + 512, t + 1024, ...; their e, m and block ids are loaded at
-// kernel start, before the sequence length is known.
+// 128-page tile and query, the base-2 (max, sum) of the scores. Wave w owns
+// the pages [64 kRP w, 64 kRP (w + 1)), lane l of it the pages 64 u + l of
+// that range; their e, m and block ids are loaded at kernel start, before the
+// sequence length is known.
 //
 // Selection, in base-2 units:
 //   1. log2 Z_g from the tile partials (each wave reduces them by itself);
@@ -33,14 +34,15 @@
 //      log-shares, so key_j <= 0;
 //   3. histogram of bin_j = floor(-key_j * 16), clamped to [0, 511] (1/16
 //      wide, order-preserving; bin 511, which holds the far tail and -inf
-//      keys, is counted by difference); one wave scans it for the bin t where
-//      the top-(k-2) count is crossed;
+//      keys, is counted by difference); every wave scans it for the bin t
+//      where the top-(k-2) count is crossed;
 //   4. inside bin t the remaining slots go to the largest keys, lower page
-//      first on ties (pairwise ranking, or an exact 8-bit radix select on the
-//      order-preserving key bits when more than 512 candidates share bin t);
-//   5. one 64-page ballot per wave and register slot builds the membership
-//      bitmap; one wave turns word popcounts into offsets, and each owner
-//      writes its selected pages (with their block ids) in ascending order.
+//      first on ties (pairwise ranking of the bin's candidates, or an exact
+//      8-bit radix select on the order-preserving key bits when more than
+//      512 candidates share bin t), marked in a page bitmap;
+//   5. list positions in ascending page order from the wave totals and the
+//      wave's own ballots; each owner writes its selected pages (with their
+//      block ids).
 #include "locks_attn_core.h"
 #include "locks_select.h"
 
@@ -75,19 +77,19 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
     const int32_t* __restrict__ table, int64_t num_blocks, int H, int MP, int max_budget,
     int nsplit, int ppw, float* __restrict__ part, int32_t* __restrict__ sel_pages,
     int32_t* __restrict__ sel_count) {
-  constexpr int kWords = kRP * kDecThreads / 32;  // membership bitmap words (<= 512)
-  static_assert(kWords <= kDecThreads && kWords % 64 == 0, "bitmap words");
-  constexpr int kWordsPerLane = kWords / 64;
+  constexpr int kWords = kRP * kDecThreads / 32;  // page bitmap words (<= 512)
+  static_assert(kWords <= kDecThreads, "bitmap words");
+  constexpr int kWavePages = 64 * kRP;  // wave w owns pages [w * kWavePages, (w + 1) * kWavePages)
   __shared__ uint32_t histc[kHistCopies][kBins + 1];  // padded: copy c of bin b in bank (b + c) % 32
-  __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t bits[kWords];
+  __shared__ __align__(16) uint32_t hist[kBins];
+  __shared__ uint32_t bits[kWords];  // members of the crossing bin
   __shared__ uint4 sh_q[G * kHeadDim / 8];
-  __shared__ int woff[kWords];
   __shared__ float cand_key[kDecThreads];
   __shared__ uint32_t cand_page[kDecThreads];  // also the tie bitmap of the radix path
   __shared__ int sel_list[kDecMaxBudget];
   __shared__ int sel_blk[kDecMaxBudget];
   __shared__ int sh_waves[16];
+  __shared__ int sh_wcnt[kDecWaves];
   __shared__ int sh_int[4];
   __shared__ float sh_acc[kDecWaves][G][kHeadDim];
   __shared__ float sh_ml[kDecWaves][G][2];
@@ -95,6 +97,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
   const int h = blockIdx.x, x = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t sh_idx = (int64_t)s * H + h;
+  // page of register slot u of this thread
+  auto page_of = [&](int u) { return wave * kWavePages + 64 * u + lane; };
 
   // ---- every independent load first
   const int len_raw = seq_lens[s];
@@ -107,7 +111,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
     const int32_t* tr = table + (int64_t)s * MP;
 #pragma unroll
     for (int u = 0; u < kRP; ++u) {
-      const int j = u * kDecThreads + tid;
+      const int j = page_of(u);
       if (j < MP) {
         load_scores<G>(er + (int64_t)j * G, ev[u]);
         mv[u] = mr[j];
@@ -131,6 +135,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
     for (int g = 0; g < G; ++g)
       zl[c][g] = (t < ntiles) ? zp[t * G + g] : make_float2(-__builtin_inff(), 0.f);
   }
+  // histogram and bitmap cleared while the loads are in flight (the first
+  // barrier of the selection publishes this)
+  for (int i = tid; i < kHistCopies * (kBins + 1); i += kDecThreads) (&histc[0][0])[i] = 0u;
+  if (tid < kWords) bits[tid] = 0u;
+  if (tid == 0) sh_int[3] = 0;
 
   const int len = clampi(len_raw, 0, MP * kPage);
   const int P = (len + kPage - 1) / kPage;
@@ -141,7 +150,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
     n = P;  // every page (P <= k <= max_budget)
 #pragma unroll
     for (int u = 0; u < kRP; ++u) {
-      const int j = u * kDecThreads + tid;
+      const int j = page_of(u);
       if (j < P) {
         sel_list[j] = j;
         sel_blk[j] = bk[u];
@@ -180,7 +189,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
     int bin[kRP];
 #pragma unroll
     for (int u = 0; u < kRP; ++u) {
-      const int j = u * kDecThreads + tid;
+      const int j = page_of(u);
       float t = 0.f;
 #pragma unroll
       for (int g = 0; g < G; ++g) t = fmaf(ev[u][g], wg[g], t);
@@ -190,9 +199,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
       const float d = -kj * kDecBinsPerUnit;  // >= 0 up to rounding; +inf for -inf keys
       bin[u] = d < (float)(kBins - 1) ? (d > 0.f ? (int)d : 0) : kBins - 1;
     }
-    // ---- 3. histogram (bin 511 by difference) and crossing bin
-    for (int i = tid; i < kHistCopies * (kBins + 1); i += kDecThreads) (&histc[0][0])[i] = 0u;
-    if (tid == 0) { sh_int[0] = -1; sh_int[1] = 0; sh_int[2] = 0; sh_int[3] = 0; }
+    // ---- 3. histogram (bin 511 by difference)
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < kRP; ++u)
@@ -205,48 +212,50 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
       hist[tid] = t;
     }
     __syncthreads();
+    // ---- 4. crossing bin: every wave scans the histogram itself (lane l
+    // holds bins 8l .. 8l+7), so no broadcast is needed
     const int need0 = k - 2;
-    if (need0 > 0 && wave == 0) {
-      // lane l scans bins 8l .. 8l+7
-      int c8[8], tot = 0;
+    int tbin = -1, need = 0, ct = 0;
+    if (need0 > 0) {
+      const uint4 h0 = *reinterpret_cast<const uint4*>(&hist[8 * lane]);
+      const uint4 h1 = *reinterpret_cast<const uint4*>(&hist[8 * lane + 4]);
+      int c8[8] = {(int)h0.x, (int)h0.y, (int)h0.z, (int)h0.w, (int)h1.x, (int)h1.y, (int)h1.z, (int)h1.w};
+      int tot = 0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) { c8[e] = (int)hist[8 * lane + e]; tot += c8[e]; }
-      int before = wave_exclusive_scan(tot, lane);
+      for (int e = 0; e < 8; ++e) tot += c8[e];
+      int before = wave_inclusive_scan(tot) - tot;
       if (lane == 63) c8[7] = (P - 2) - (before + tot - c8[7]);  // bin 511: the rest
+      int fb = -1, fn = 0, fc = 0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        if (before < need0 && before + c8[e] >= need0) {
-          sh_int[0] = 8 * lane + e;
-          sh_int[1] = need0 - before;
-          sh_int[2] = c8[e];
-        }
+        if (before < need0 && before + c8[e] >= need0) { fb = 8 * lane + e; fn = need0 - before; fc = c8[e]; }
         before += c8[e];
       }
-    }
-    __syncthreads();
-    const int tbin = sh_int[0];
-    int need = sh_int[1];
-    const int ct = sh_int[2];
-    // ---- 4. pages below the crossing bin (and sink / recent) into the bitmap
-    {
-      // lane 2u + half of the wave collects word `half` of slot u's ballot
-      int wordv = 0;
-#pragma unroll
-      for (int u = 0; u < kRP; ++u) {
-        const int j = u * kDecThreads + tid;
-        const bool in = (j == 0 || j == P - 1) || (is_cand(j) && bin[u] < tbin);
-        const uint64_t bal = __ballot(in);
-        wordv = (lane == 2 * u) ? (int)(uint32_t)bal : wordv;
-        wordv = (lane == 2 * u + 1) ? (int)(uint32_t)(bal >> 32) : wordv;
+      const uint64_t found = __ballot(fb >= 0);
+      if (found) {  // wave-uniform; one lane holds the crossing
+        const int src = __builtin_ctzll(found);
+        tbin = __builtin_amdgcn_readlane(fb, src);
+        need = __builtin_amdgcn_readlane(fn, src);
+        ct = __builtin_amdgcn_readlane(fc, src);
       }
-      if (lane < 2 * kRP) bits[(lane >> 1) * (kDecThreads / 32) + wave * 2 + (lane & 1)] = (uint32_t)wordv;
     }
-    // ---- resolve inside the crossing bin
-    if (tbin >= 0) {
+    // ---- 5. membership: sink, recent, pages below the crossing bin, and
+    // inside it the `need` largest keys (lower page first on ties)
+    bool in[kRP];
+#pragma unroll
+    for (int u = 0; u < kRP; ++u) {
+      const int j = page_of(u);
+      const bool cand = (j >= 1) & (j <= P - 2);
+      in[u] = (j == 0) | (j == P - 1) | (cand & (bin[u] < tbin)) |
+              ((tbin >= 0) & (need == ct) & cand & (bin[u] == tbin));
+    }
+    if (tbin >= 0 && need < ct) {
+      // the members of the crossing bin go to the page bitmap
       if (ct <= kDecThreads) {
+        // its candidates to LDS; thread t < ct ranks candidate t
 #pragma unroll
         for (int u = 0; u < kRP; ++u) {
-          const int j = u * kDecThreads + tid;
+          const int j = page_of(u);
           if (is_cand(j) && bin[u] == tbin) {
             const int slot = atomicAdd(&sh_int[3], 1);
             cand_key[slot] = key[u];
@@ -266,14 +275,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
           if (rank < need) atomicOr(&bits[mp >> 5], 1u << (mp & 31));
         }
       } else {
+        // exact 8-bit radix select on the order-preserving key bits
         uint32_t prefix = 0u;
+#pragma unroll 1
         for (int shift = 24; shift >= 0; shift -= 8) {
           __syncthreads();
           if (tid < 256) hist[tid] = 0u;
           __syncthreads();
 #pragma unroll
           for (int u = 0; u < kRP; ++u) {
-            const int j = u * kDecThreads + tid;
+            const int j = page_of(u);
             const uint32_t o = float_to_ordered(key[u]);
             if (is_cand(j) && bin[u] == tbin && (shift == 24 || (o >> (shift + 8)) == prefix))
               atomicAdd(&hist[255 - ((o >> shift) & 255u)], 1u);  // descending order
@@ -296,7 +307,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
         __syncthreads();
 #pragma unroll
         for (int u = 0; u < kRP; ++u) {
-          const int j = u * kDecThreads + tid;
+          const int j = page_of(u);
           if (!is_cand(j) || bin[u] != tbin) continue;
           const uint32_t o = float_to_ordered(key[u]);
           if (o > prefix) atomicOr(&bits[j >> 5], 1u << (j & 31));
@@ -316,47 +327,44 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
           if (take) atomicOr(&bits[tid], take);
         }
       }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < kRP; ++u) {
+        const int j = page_of(u);
+        if (is_cand(j) && bin[u] == tbin) in[u] = (bits[j >> 5] >> (j & 31)) & 1u;
+      }
     }
+    // ---- 6. list positions in ascending page order: wave totals through
+    // LDS, then the wave's own ballots
+    uint64_t bal[kRP];
+    int wcnt = 0;
+#pragma unroll
+    for (int u = 0; u < kRP; ++u) {
+      bal[u] = __ballot(in[u]);
+      wcnt += __popcll(bal[u]);
+    }
+    if (lane == 0) sh_wcnt[wave] = wcnt;
     __syncthreads();
-    // ---- 5. word offsets (one wave), then owners write pages and block ids
-    if (wave == 0) {
-      int c[kWordsPerLane], tot = 0;
+    int pos = 0, total = 0;
 #pragma unroll
-      for (int e = 0; e < kWordsPerLane; ++e) {
-        c[e] = __popc(bits[kWordsPerLane * lane + e]);
-        tot += c[e];
-      }
-      int before = wave_exclusive_scan(tot, lane);
-#pragma unroll
-      for (int e = 0; e < kWordsPerLane; ++e) {
-        woff[kWordsPerLane * lane + e] = before;
-        before += c[e];
-      }
-      if (lane == 63) sh_int[3] = before;
+    for (int w = 0; w < kDecWaves; ++w) {
+      const int c = sh_wcnt[w];
+      pos += (w < wave) ? c : 0;
+      total += c;
     }
-    __syncthreads();
-    uint32_t wv[kRP];
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
-    for (int u = 0; u < kRP; ++u) wv[u] = bits[(u * kDecThreads + tid) >> 5];
-    uint32_t mine = 0u;  // bit u: page u * 512 + tid is selected
-#pragma unroll
-    for (int u = 0; u < kRP; ++u) mine |= ((wv[u] >> (tid & 31)) & 1u) << u;
-    while (mine) {
-      const int u = __ffs(mine) - 1;
-      mine &= mine - 1u;
-      const int j = u * kDecThreads + tid;
-      int blk = bk[0];
-      uint32_t w = wv[0];
-#pragma unroll
-      for (int v = 1; v < kRP; ++v)
-        if (v == u) { blk = bk[v]; w = wv[v]; }
-      const int pos = woff[j >> 5] + __popc(w & ((1u << (j & 31)) - 1u));
-      if (pos < kDecMaxBudget) {
-        sel_list[pos] = j;
-        sel_blk[pos] = blk;
+    for (int u = 0; u < kRP; ++u) {
+      if (in[u]) {
+        const int p = pos + __popcll(bal[u] & below);
+        if (p < kDecMaxBudget) {
+          sel_list[p] = page_of(u);
+          sel_blk[p] = bk[u];
+        }
       }
+      pos += __popcll(bal[u]);
     }
-    n = min(sh_int[3], max_budget);  // == k by construction
+    n = min(total, max_budget);  // == k by construction
   }
   __syncthreads();
 
@@ -385,46 +393,66 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
     attn_wave_to_lds<G>(acc, sh_acc[wave], sh_ml[wave], lane);
   }
   __syncthreads();
-  if (wave == 0)
-    wg_partial_store<G>(sh_acc, sh_ml, kDecWaves, part + (sh_idx * nsplit + x) * G * kPartStride,
-                        lane);
+  // ---- the workgroup's partial: thread (g, d) combines the 8 wave partials
+  if (tid < G * kHeadDim) {
+    const int g = tid / kHeadDim, d = tid % kHeadDim;
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, sh_ml[w][g][0]);
+    float a = 0.f, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float f = (M == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(sh_ml[w][g][0] - M);
+      a += f * sh_acc[w][g][d];
+      L += f * sh_ml[w][g][1];
+    }
+    float* p = part + (sh_idx * nsplit + x) * G * kPartStride + g * kPartStride;
+    p[d] = a;
+    if (d == 0) *reinterpret_cast<float2*>(p + kHeadDim) = make_float2(M, L);
+  }
 }
 
 // Merge of the nsplit partials of one (sequence, KV head) in split order:
-// thread (g, d) owns output element d of query g. All partials exist (empty
-// ones carry max -inf, sum 0, acc 0); an empty selection gives out = 0 and
-// lse = -inf.
-template <int G>
-__global__ __launch_bounds__(kDecThreads) void decode_merge_kernel(
+// thread (g, c) owns output elements 4c .. 4c+3 of query g. All partials exist
+// (empty ones carry max -inf, sum 0, acc 0); an empty selection gives out = 0
+// and lse = -inf. kMaxS >= nsplit bounds the unrolled load loop.
+template <int G, int kMaxS>
+__global__ __launch_bounds__(G * kHeadDim / 4) void decode_merge_kernel(
     const float* __restrict__ part, float* __restrict__ out, float* __restrict__ lse_out, int H,
     int nsplit) {
   const int64_t sh_idx = (int64_t)blockIdx.y * H + blockIdx.x;
   const int tid = threadIdx.x;
-  if (tid >= G * kHeadDim) return;
-  const int g = tid / kHeadDim, d = tid % kHeadDim;
+  const int g = tid / (kHeadDim / 4), d = 4 * (tid % (kHeadDim / 4));
   const float* parts = part + sh_idx * nsplit * G * kPartStride;
-  float pm[kDecMaxSplits], pl[kDecMaxSplits], pa[kDecMaxSplits];
+  float4 pa[kMaxS];
+  float pm[kMaxS], pl[kMaxS];
 #pragma unroll
-  for (int y = 0; y < kDecMaxSplits; ++y) {
+  for (int y = 0; y < kMaxS; ++y) {
     // unconditional (clamped) loads, masked afterwards: all in flight at once
     const float* py = parts + (min(y, nsplit - 1) * G + g) * kPartStride;
-    pa[y] = py[d];
+    pa[y] = *reinterpret_cast<const float4*>(py + d);
     const float2 ml = *reinterpret_cast<const float2*>(py + kHeadDim);
     pm[y] = ml.x;
     pl[y] = ml.y;
   }
 #pragma unroll
-  for (int y = 0; y < kDecMaxSplits; ++y)
-    if (y >= nsplit) { pa[y] = 0.f; pm[y] = -__builtin_inff(); pl[y] = 0.f; }
-  float M = -__builtin_inff(), L = 0.f, a = 0.f;
+  for (int y = 0; y < kMaxS; ++y)
+    if (y >= nsplit) { pa[y] = make_float4(0.f, 0.f, 0.f, 0.f); pm[y] = -__builtin_inff(); pl[y] = 0.f; }
+  float M = -__builtin_inff(), L = 0.f;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-  for (int y = 0; y < kDecMaxSplits; ++y) {
+  for (int y = 0; y < kMaxS; ++y) {
     float f2;
     const float f1 = merge_factors(M, pm[y], f2);
     L = L * f1 + pl[y] * f2;
-    a = a * f1 + pa[y] * f2;
+    a.x = a.x * f1 + pa[y].x * f2;
+    a.y = a.y * f1 + pa[y].y * f2;
+    a.z = a.z * f1 + pa[y].z * f2;
+    a.w = a.w * f1 + pa[y].w * f2;
   }
-  out[(sh_idx * G + g) * kHeadDim + d] = (L > 0.f) ? a / L : 0.f;
+  const bool some = L > 0.f;
+  *reinterpret_cast<float4*>(out + (sh_idx * G + g) * kHeadDim + d) =
+      some ? make_float4(a.x / L, a.y / L, a.z / L, a.w / L) : make_float4(0.f, 0.f, 0.f, 0.f);
   if (lse_out && d == 0)
     lse_out[sh_idx * G + g] = (L > 0.f) ? (M + __builtin_amdgcn_logf(L)) * kLn2 : -__builtin_inff();
 }
@@ -455,8 +483,14 @@ static void launch_decode_rp(const float* escore, const float* pmax, const float
   hipLaunchKernelGGL((decode_attn_kernel<G, kRP>), dim3(H, nsplit, S), dim3(kDecThreads), 0, st,
                      escore, pmax, zpart, ntiles, lens, budgets, q, kpool, vpool, table, nb, H, MP,
                      KB, nsplit, ppw, part, sel, cnt);
-  hipLaunchKernelGGL((decode_merge_kernel<G>), dim3(H, S), dim3(kDecThreads), 0, st, part, out,
-                     lse_out, H, nsplit);
+  const dim3 mg(H, S), mb(G * kHeadDim / 4);
+  if (nsplit <= 8)
+    hipLaunchKernelGGL((decode_merge_kernel<G, 8>), mg, mb, 0, st, part, out, lse_out, H, nsplit);
+  else if (nsplit <= 16)
+    hipLaunchKernelGGL((decode_merge_kernel<G, 16>), mg, mb, 0, st, part, out, lse_out, H, nsplit);
+  else
+    hipLaunchKernelGGL((decode_merge_kernel<G, kDecMaxSplits>), mg, mb, 0, st, part, out, lse_out, H,
+                       nsplit);
 }
 
 template <int G>

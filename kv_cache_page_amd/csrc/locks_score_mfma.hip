@@ -406,7 +406,7 @@ static hipError_t launch_r_g(const uint16_t* q, const uint8_t* summ, const int32
   constexpr int TPW = 1;
   const int ppw = kScorePagesPerWg;
   const int ntiles = (MP + ppw - 1) / ppw;
-  dim3 grid(H, (ntiles + TPW - 1) / TPW, S);
+  dim3 grid(H, (ntiles + TPW - 1) / TPW, S);  // heads first: 8 heads -> one XCD each
   hipLaunchKernelGGL((score_mfma_kernel<R, G, TPW>), grid, dim3(256 * TPW), 0, st, q, summ, table, lens,
                      scores, nb, H, MP, ppw, fill_nan, zpart, static_cast<const uint16_t*>(knew),
                      static_cast<const uint16_t*>(vnew), static_cast<uint16_t*>(kpool),

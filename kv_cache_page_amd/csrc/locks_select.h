@@ -45,6 +45,20 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* sh_waves, int* t
 }
 
 
+// Inclusive prefix sum over one wave with DPP row shifts and row broadcasts
+// (no LDS): rows of 16 first, then lane 15 of each row into the next row and
+// lane 31 into the upper half.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  int x = v + __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);         // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, v, 0x113, 0xF, 0xF, true);         // row_shr:3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xE, false);        // row_shr:4, lanes 4..15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xC, false);        // row_shr:8, lanes 8..15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);        // row_bcast:15, rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);        // row_bcast:31, rows 2, 3
+  return x;
+}
+
 template <int G>
 __device__ __forceinline__ void load_scores(const float* p, float (&v)[G]) {
   if constexpr (G == 4) {
