@@ -36,13 +36,17 @@
 //      wide, order-preserving; bin 511, which holds the far tail and -inf
 //      keys, is counted by difference); every wave scans it for the bin t
 //      where the top-(k-2) count is crossed;
-//   4. inside bin t the remaining slots go to the largest keys, lower page
-//      first on ties (pairwise ranking of the bin's candidates, or an exact
-//      8-bit radix select on the order-preserving key bits when more than
-//      512 candidates share bin t), marked in a page bitmap;
-//   5. list positions in ascending page order from the wave totals and the
-//      wave's own ballots; each owner writes its selected pages (with their
-//      block ids).
+//   4. list part A = sink, recent and the candidates below bin t (all of bin
+//      t when it fits), in ascending page order, positions from the wave
+//      totals and the wave's own ballots;
+//   5. part B = the `need` largest keys of bin t, lower page first on ties,
+//      in ascending page order after part A. Up to 64 candidates every wave
+//      ranks them in registers (while the loads of its first part-A page are
+//      already in flight); up to 512 they are ranked pairwise through LDS;
+//      beyond, an exact 8-bit radix select on the order-preserving key bits.
+// The attention partition (list positions per workgroup and wave) is thus a
+// deterministic function of the keys; the selection output, when asked for,
+// is rewritten as one ascending list.
 #include "locks_attn_core.h"
 #include "locks_select.h"
 
@@ -55,6 +59,7 @@ constexpr int kDecMaxSplits = 32;
 constexpr int kDecMaxPpw = 8;  // pages per wave
 constexpr float kDecBinsPerUnit = 16.f;
 constexpr int kHistCopies = 8;  // lanes spread their histogram atomics over 8 copies
+constexpr int kFastRank = 64;   // crossing bins up to this size are ranked in registers
 static_assert(kBins == kDecThreads, "one histogram bin per thread");
 
 // Exclusive prefix sum over one wave.
@@ -82,10 +87,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
   constexpr int kWavePages = 64 * kRP;  // wave w owns pages [w * kWavePages, (w + 1) * kWavePages)
   __shared__ uint32_t histc[kHistCopies][kBins + 1];  // padded: copy c of bin b in bank (b + c) % 32
   __shared__ __align__(16) uint32_t hist[kBins];
-  __shared__ uint32_t bits[kWords];  // members of the crossing bin
+  __shared__ uint32_t bits[kWords];      // members of a large crossing bin
+  __shared__ uint32_t bits_out[kWords];  // whole selection (selection output only)
   __shared__ uint4 sh_q[G * kHeadDim / 8];
   __shared__ float cand_key[kDecThreads];
   __shared__ uint32_t cand_page[kDecThreads];  // also the tie bitmap of the radix path
+  __shared__ int cand_blk[kDecThreads];
   __shared__ int sel_list[kDecMaxBudget];
   __shared__ int sel_blk[kDecMaxBudget];
   __shared__ int sh_waves[16];
@@ -138,16 +145,21 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
   // histogram and bitmap cleared while the loads are in flight (the first
   // barrier of the selection publishes this)
   for (int i = tid; i < kHistCopies * (kBins + 1); i += kDecThreads) (&histc[0][0])[i] = 0u;
-  if (tid < kWords) bits[tid] = 0u;
+  if (tid < kWords) { bits[tid] = 0u; bits_out[tid] = 0u; }
   if (tid == 0) sh_int[3] = 0;
 
   const int len = clampi(len_raw, 0, MP * kPage);
   const int P = (len + kPage - 1) / kPage;
   const int F = len / kPage;
   const int k = clampi(bud_raw, 2, max_budget);
-  int n;
-  if (P == 0 || k >= P) {
+  int n, nA;
+  int tbin = -1, need = 0, ct = 0;  // crossing bin, slots left in it, its size
+  bool part_bin = false, fast_b = false;
+  const bool sel_all = (P == 0 || k >= P);
+  uint64_t bal[kRP];
+  if (sel_all) {
     n = P;  // every page (P <= k <= max_budget)
+    nA = n;
 #pragma unroll
     for (int u = 0; u < kRP; ++u) {
       const int j = page_of(u);
@@ -215,7 +227,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
     // ---- 4. crossing bin: every wave scans the histogram itself (lane l
     // holds bins 8l .. 8l+7), so no broadcast is needed
     const int need0 = k - 2;
-    int tbin = -1, need = 0, ct = 0;
     if (need0 > 0) {
       const uint4 h0 = *reinterpret_cast<const uint4*>(&hist[8 * lane]);
       const uint4 h1 = *reinterpret_cast<const uint4*>(&hist[8 * lane + 4]);
@@ -239,30 +250,61 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
         ct = __builtin_amdgcn_readlane(fc, src);
       }
     }
-    // ---- 5. membership: sink, recent, pages below the crossing bin, and
-    // inside it the `need` largest keys (lower page first on ties)
-    bool in[kRP];
+    // ---- 5. list part A: sink, recent and the candidates below the crossing
+    // bin (with the whole crossing bin when it fits), in ascending page order;
+    // the crossing bin's candidates go to LDS when only part of it is taken
+    part_bin = (tbin >= 0) && (need < ct);
+    int wA = 0;
 #pragma unroll
     for (int u = 0; u < kRP; ++u) {
       const int j = page_of(u);
       const bool cand = (j >= 1) & (j <= P - 2);
-      in[u] = (j == 0) | (j == P - 1) | (cand & (bin[u] < tbin)) |
-              ((tbin >= 0) & (need == ct) & cand & (bin[u] == tbin));
+      const bool in = (j == 0) | (j == P - 1) | (cand & (bin[u] < tbin)) |
+                      ((tbin >= 0) & (need == ct) & cand & (bin[u] == tbin));
+      bal[u] = __ballot(in);
+      wA += __popcll(bal[u]);
     }
-    if (tbin >= 0 && need < ct) {
-      // the members of the crossing bin go to the page bitmap
-      if (ct <= kDecThreads) {
-        // its candidates to LDS; thread t < ct ranks candidate t
+    if (part_bin && ct <= kDecThreads) {
 #pragma unroll
-        for (int u = 0; u < kRP; ++u) {
-          const int j = page_of(u);
-          if (is_cand(j) && bin[u] == tbin) {
-            const int slot = atomicAdd(&sh_int[3], 1);
-            cand_key[slot] = key[u];
-            cand_page[slot] = (uint32_t)j;
+      for (int u = 0; u < kRP; ++u) {
+        const int j = page_of(u);
+        if (is_cand(j) && bin[u] == tbin) {
+          const int slot = atomicAdd(&sh_int[3], 1);
+          cand_key[slot] = key[u];
+          cand_page[slot] = (uint32_t)j;
+          cand_blk[slot] = bk[u];
+        }
+      }
+    }
+    if (lane == 0) sh_wcnt[wave] = wA;
+    __syncthreads();
+    nA = 0;
+    {
+      int pos = 0;
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) {
+        const int c = sh_wcnt[w];
+        pos += (w < wave) ? c : 0;
+        nA += c;
+      }
+#pragma unroll
+      for (int u = 0; u < kRP; ++u) {
+        if ((bal[u] >> lane) & 1ull) {
+          const int p = pos + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal[u] >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)bal[u], 0u));
+          if (p < kDecMaxBudget) {
+            sel_list[p] = page_of(u);
+            sel_blk[p] = bk[u];
           }
         }
-        __syncthreads();
+        pos += __popcll(bal[u]);
+      }
+    }
+    n = min(nA + (part_bin ? need : 0), max_budget);  // == k by construction
+    if (part_bin && ct > kFastRank) {
+      // ---- 6 (large crossing bin). Members into the bitmap, then their
+      // positions nA + (members with a lower page) written by their owners
+      if (ct <= kDecThreads) {
         if (tid < ct) {
           const float me = cand_key[tid];
           const uint32_t mp = cand_page[tid];
@@ -328,69 +370,145 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
         }
       }
       __syncthreads();
+      {
+        const uint32_t bw = (tid < kWords) ? bits[tid] : 0u;
+        int tot;
+        const int before = block_exclusive_scan(__popc(bw), sh_waves, &tot);
+        if (tid < kWords) hist[tid] = (uint32_t)before;  // word offsets (kWords <= kBins)
+      }
+      __syncthreads();
 #pragma unroll
       for (int u = 0; u < kRP; ++u) {
         const int j = page_of(u);
-        if (is_cand(j) && bin[u] == tbin) in[u] = (bits[j >> 5] >> (j & 31)) & 1u;
-      }
-    }
-    // ---- 6. list positions in ascending page order: wave totals through
-    // LDS, then the wave's own ballots
-    uint64_t bal[kRP];
-    int wcnt = 0;
-#pragma unroll
-    for (int u = 0; u < kRP; ++u) {
-      bal[u] = __ballot(in[u]);
-      wcnt += __popcll(bal[u]);
-    }
-    if (lane == 0) sh_wcnt[wave] = wcnt;
-    __syncthreads();
-    int pos = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) {
-      const int c = sh_wcnt[w];
-      pos += (w < wave) ? c : 0;
-      total += c;
-    }
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-#pragma unroll
-    for (int u = 0; u < kRP; ++u) {
-      if (in[u]) {
-        const int p = pos + __popcll(bal[u] & below);
-        if (p < kDecMaxBudget) {
-          sel_list[p] = page_of(u);
-          sel_blk[p] = bk[u];
+        if (!is_cand(j) || bin[u] != tbin) continue;
+        const uint32_t w = bits[j >> 5];
+        if ((w >> (j & 31)) & 1u) {
+          const int p = nA + (int)hist[j >> 5] + __popc(w & ((1u << (j & 31)) - 1u));
+          if (p < kDecMaxBudget) {
+            sel_list[p] = j;
+            sel_blk[p] = bk[u];
+          }
         }
       }
-      pos += __popcll(bal[u]);
+      nA = n;  // the whole list now sits in LDS
     }
-    n = min(total, max_budget);  // == k by construction
+    fast_b = part_bin && ct <= kFastRank;
   }
   __syncthreads();
 
-  if (x == 0 && sel_pages) {
-    int32_t* o = sel_pages + sh_idx * max_budget;
-    for (int i = tid; i < max_budget; i += kDecThreads) o[i] = i < n ? sel_list[i] : -1;
-    if (tid == 0) sel_count[sh_idx] = n;
-  }
+  // ---- the wave's pages: list positions base .. base + ppw - 1. Positions
+  // below nA come from LDS; the rest (a partly taken crossing bin of at most
+  // 64 candidates) from a ranking every wave repeats in registers, while the
+  // loads of its first page are already in flight
   const int per_wg = kDecWaves * ppw;
   const int base = x * per_wg + wave * ppw;
   const int mine = clampi(n - base, 0, ppw);
-  // ---- attention over list entries [x * per_wg, (x + 1) * per_wg)
+  uint32_t qw[G][16];
+  attn_load_q<G>(qw, reinterpret_cast<const uint16_t*>(sh_q), lane);
+  auto page_off = [&](int j, int blk, int64_t& off, int& nv) {
+    off = -1;
+    nv = 0;
+    if (j < 0 || j >= P || blk < 0 || blk >= num_blocks) return;
+    off = ((int64_t)blk * H + h) * (kPage * kHeadDim);
+    nv = (j == P - 1) ? len - kPage * (P - 1) : kPage;
+  };
+  int64_t off[kDecMaxPpw];
+  int nv[kDecMaxPpw];
+#pragma unroll
+  for (int i = 0; i < kDecMaxPpw; ++i) { off[i] = -1; nv[i] = 0; }
+#pragma unroll
+  for (int i = 0; i < kDecMaxPpw; ++i)
+    if (i < mine && base + i < nA) page_off(sel_list[base + i], sel_blk[base + i], off[i], nv[i]);
+  PageRegs cur, nxt;
+  if (mine > 0 && off[0] >= 0) attn_load_page(cur, kpool, vpool, off[0], lane);
+  if (fast_b && base + mine > nA) {
+    // lane e < ct holds candidate e; rank by key (lower page first on ties),
+    // then the members' positions nA + (members with a lower page)
+    float ck = -__builtin_inff();
+    uint32_t cp = 0xFFFFFFFFu;
+    int cb = -1;
+    if (lane < ct) { ck = cand_key[lane]; cp = cand_page[lane]; cb = cand_blk[lane]; }
+    int rank = 0;
+    for (int e = 0; e < ct; ++e) {
+      const float o = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ck), e));
+      const uint32_t op = (uint32_t)__builtin_amdgcn_readlane((int)cp, e);
+      rank += ((o > ck) | ((o == ck) & (op < cp))) ? 1 : 0;
+    }
+    const bool inB = (lane < ct) & (rank < need);
+    const uint64_t bm = __ballot(inB);
+    int bpos = nA;
+    for (int e = 0; e < ct; ++e) {
+      const uint32_t op = (uint32_t)__builtin_amdgcn_readlane((int)cp, e);
+      bpos += (((bm >> e) & 1ull) && op < cp) ? 1 : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < kDecMaxPpw; ++i) {
+      if (i < mine && base + i >= nA) {
+        const uint64_t hit = __ballot(inB && bpos == base + i);
+        if (hit) {
+          const int src = __builtin_ctzll(hit);
+          page_off(__builtin_amdgcn_readlane((int)cp, src), __builtin_amdgcn_readlane(cb, src), off[i], nv[i]);
+        }
+      }
+    }
+    if (mine > 0 && base >= nA && off[0] >= 0) attn_load_page(cur, kpool, vpool, off[0], lane);
+  }
+  // ---- attention over the wave's pages (next page loading while one is computed)
   {
-    uint32_t qw[G][16];
-    attn_load_q<G>(qw, reinterpret_cast<const uint16_t*>(sh_q), lane);
     AttnAcc<G> acc;
     attn_init<G>(acc);
-    auto page_at = [&](int i, int64_t& off, int& nv) {
-      const int j = sel_list[base + i];
-      const int blk = sel_blk[base + i];
-      if (j < 0 || j >= P || blk < 0 || blk >= num_blocks) return;
-      off = ((int64_t)blk * H + h) * (kPage * kHeadDim);
-      nv = (j == P - 1) ? len - kPage * (P - 1) : kPage;
-    };
-    attn_wave_pages<G, kDecMaxPpw>(acc, qw, kpool, vpool, mine, page_at, lane);
+#pragma unroll
+    for (int i = 0; i < kDecMaxPpw; ++i) {
+      if (i >= mine) break;
+      if (i + 1 < kDecMaxPpw && i + 1 < mine && off[i + 1 < kDecMaxPpw ? i + 1 : i] >= 0)
+        attn_load_page(nxt, kpool, vpool, off[i + 1 < kDecMaxPpw ? i + 1 : i], lane);
+      if (off[i] >= 0) attn_page<G>(acc, cur, qw, nv[i], lane);
+      cur = nxt;
+    }
     attn_wave_to_lds<G>(acc, sh_acc[wave], sh_ml[wave], lane);
+  }
+  // ---- selection output (first workgroup only): the ascending page list
+  if (x == 0 && sel_pages) {
+    int32_t* o = sel_pages + sh_idx * max_budget;
+    if (!sel_all) {
+      // membership bitmap: part A from the wave ballots, then the crossing
+      // bin's members (already in `bits` on the large-bin path)
+      if (lane == 0) {
+#pragma unroll
+        for (int u = 0; u < kRP; ++u) {
+          const int w0 = (wave * kWavePages + 64 * u) >> 5;
+          bits_out[w0] = (uint32_t)bal[u];
+          bits_out[w0 + 1] = (uint32_t)(bal[u] >> 32);
+        }
+      }
+      __syncthreads();
+      if (fast_b && wave == 0 && lane < ct) {
+        const float ck = cand_key[lane];
+        const uint32_t cp = cand_page[lane];
+        int rank = 0;
+        for (int e = 0; e < ct; ++e) {
+          const float o2 = cand_key[e];
+          rank += ((o2 > ck) | ((o2 == ck) & (cand_page[e] < cp))) ? 1 : 0;
+        }
+        if (rank < need) atomicOr(&bits_out[cp >> 5], 1u << (cp & 31));
+      }
+      if (part_bin && !fast_b && tid < kWords) atomicOr(&bits_out[tid], bits[tid]);
+      __syncthreads();
+      const uint32_t bw = (tid < kWords) ? bits_out[tid] : 0u;
+      int tot;
+      int before = block_exclusive_scan(__popc(bw), sh_waves, &tot);
+      uint32_t w = bw;
+      while (w) {
+        const int b = __builtin_ctz(w);
+        w &= w - 1u;
+        if (before < max_budget) o[before] = 32 * tid + b;
+        ++before;
+      }
+      for (int i = tot + tid; i < max_budget; i += kDecThreads) o[i] = -1;
+    } else {
+      for (int i = tid; i < max_budget; i += kDecThreads) o[i] = i < n ? sel_list[i] : -1;
+    }
+    if (tid == 0) sel_count[sh_idx] = n;
   }
   __syncthreads();
   // ---- the workgroup's partial: thread (g, d) combines the 8 wave partials

@@ -532,6 +532,19 @@ def test_decode_step_equal_keys(L):
     _check_step(b, 8, 100, res, kpa, vpa, sa, summ, completed)
 
 
+def test_decode_step_equal_keys_mid_size_bin(L):
+    """q = 0 with 68 and 298 tied candidates: the crossing bin is too large for
+    the register ranking and small enough for the pairwise LDS ranking."""
+    _say("[gpu] decode step, 68 / 298 equal keys")
+    b = synth.make_decode_batch([300 * 16 + 7, 70 * 16], 1, 4, [100, 50], seed=178)
+    b.q.zero_()
+    kp, vp, kn, vn, summ, completed = _step_state(b, 8)
+    res, kpa, vpa, sa = _run_step(L, L.Dims(1, 4, 8), b, kp, vp, kn, vn, summ, 100)
+    assert list(res["sel"][0, 0, :100]) == [0] + list(range(1, 99)) + [300]
+    assert list(res["sel"][1, 0, :50]) == [0] + list(range(1, 49)) + [69]
+    _check_step(b, 8, 100, res, kpa, vpa, sa, summ, completed)
+
+
 def test_decode_step_wide_table_fallback(L):
     """A table wider than 16384 pages takes the separate select and attention
     launches inside the same entry point."""
