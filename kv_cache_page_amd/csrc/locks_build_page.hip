@@ -34,11 +34,6 @@ typedef double double4v __attribute__((ext_vector_type(4)));
 
 constexpr int kPgMaxSweeps = 12;
 
-__device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
-  return v;
-}
 
 // Jacobi rotation for [[app, apq], [apq, aqq]] (Golub & Van Loan's symmetric
 // Schur 2x2, |angle| <= pi/4). t = sgn(tau) / (|tau| + sqrt(1 + tau^2)) is a
@@ -68,8 +63,6 @@ __device__ __forceinline__ void rotation_fast(double app, double aqq, double apq
 // LDS exchange area of the 64-lane Jacobi.
 constexpr int kApStride = kPage + 2;  // 16-byte aligned rows, rows spread over banks
 struct JacobiLds {
-  double dg[kPage];               // diagonal A[i][i]
-  double pq[kPage];               // A[i][i ^ M] of the current round
   double2 cs[kPage];              // (c, signed s) of the pair of row i
   double ap[kPage][kApStride];    // rows in permuted order: ap[i][x] = A[i][i ^ x]
   double up[kPage][kApStride];    // the same for U
@@ -90,30 +83,31 @@ __device__ __forceinline__ void load4_perm(double (&v)[4], const double* p) {
 
 // One round of the 64-lane cyclic Jacobi: the 8 pairs (p, p xor M) at once.
 // Lane (i, qc) holds b[e] = A[i][i ^ x], x = 4 qc + e, and U likewise.
-// Column j = i ^ x turns with the rotation of row j's pair: new b[x] =
-// c_j b[x] - s_j b[x ^ M] with s_j signed as row j holds it (+s on the lower
-// row of a pair, -s on the upper); then row i mixes with row i ^ M.
+// Column j = i ^ x turns with the rotation of row j's pair: b[x] <- c_j b[x]
+// - s_j b[x ^ M], s_j signed as row j holds it (+s on the lower row of a
+// pair, -s on the upper); then row i mixes with row i ^ M. The partner row's
+// column-turned entry is formed here from its pre-round entries, so a round
+// needs two exchanges: the pre-round rows (which also give the rotation
+// parameters), then the rotations.
 template <int M>
 __device__ __forceinline__ void jacobi64_round(double (&b)[4], double (&ub)[4], int i, int qc,
                                                JacobiLds& sh) {
   constexpr int HB = (M >= 8) ? 8 : (M >= 4) ? 4 : (M >= 2) ? 2 : 1;  // top bit of M
   constexpr int QM = M >> 2, EM = M & 3;
-  if (qc == 0) sh.dg[i] = b[0];
-  if (qc == QM) sh.pq[i] = b[EM];
-  if (QM != 0) {
-    store4(&sh.ap[i][4 * qc], b);
-    store4(&sh.up[i][4 * qc], ub);
-  }
+  store4(&sh.ap[i][4 * qc], b);
+  if (QM != 0) store4(&sh.up[i][4 * qc], ub);
   __syncthreads();
-  const double aii = sh.dg[i], ajj = sh.dg[i ^ M];
-  const double apq = 0.5 * (sh.pq[i] + sh.pq[i ^ M]);
-  double pb[4], pu[4];
+  const double aii = sh.ap[i][0], ajj = sh.ap[i ^ M][0];
+  const double apq = 0.5 * (sh.ap[i][M] + sh.ap[i ^ M][M]);
+  double pb[4], pu[4], px[4], pxm[4];
+  load4_perm<0>(px, &sh.ap[i ^ M][4 * qc]);  // partner row, entries x
   if (QM == 0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) { pb[e] = b[e ^ EM]; pu[e] = ub[e ^ EM]; }
+    for (int e = 0; e < 4; ++e) { pb[e] = b[e ^ EM]; pu[e] = ub[e ^ EM]; pxm[e] = px[e ^ EM]; }
   } else {
     load4_perm<EM>(pb, &sh.ap[i][4 * (qc ^ QM)]);
     load4_perm<EM>(pu, &sh.up[i][4 * (qc ^ QM)]);
+    load4_perm<EM>(pxm, &sh.ap[i ^ M][4 * (qc ^ QM)]);  // partner row, entries x ^ M
   }
   const bool lo = (i & HB) == 0;
   double cr, s0;
@@ -124,16 +118,54 @@ __device__ __forceinline__ void jacobi64_round(double (&b)[4], double (&ub)[4], 
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const double2 r = sh.cs[i ^ (4 * qc + e)];
-    b[e] = r.x * b[e] - r.y * pb[e];
+    const double b1 = r.x * b[e] - r.y * pb[e];      // own row, column turned
+    const double p1 = r.x * pxm[e] - r.y * px[e];    // partner row at column i ^ x, turned
     ub[e] = r.x * ub[e] - r.y * pu[e];
+    b[e] = cr * b1 - sr * p1;
   }
-  // rows: the partner row's entry x ^ M sits at its permuted slot x ^ M
-  store4(&sh.ap[i][4 * qc], b);
-  __syncthreads();
-  double pr[4];
-  load4_perm<EM>(pr, &sh.ap[i ^ M][4 * (qc ^ QM)]);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) b[e] = cr * b[e] - sr * pr[e];
+}
+
+// Wave-wide max of a double: DPP inside rows of 16, then xor 16 and xor 32.
+template <int C>
+__device__ __forceinline__ double dpp_d(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, C, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), C, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ double wave_max_d(double v) {
+  v = fmax(v, dpp_d<0xB1>(v));   // xor 1
+  v = fmax(v, dpp_d<0x4E>(v));   // xor 2
+  v = fmax(v, dpp_d<0x141>(v));  // half-row mirror: quads 0/1, 2/3
+  v = fmax(v, dpp_d<0x140>(v));  // row mirror: halves of the row
+  {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)u, 0x401F);  // xor 16
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)(u >> 32), 0x401F);
+    v = fmax(v, __longlong_as_double((long long)(((uint64_t)hi << 32) | lo)));
+  }
+  return fmax(v, __shfl_xor(v, 32, 64));
+}
+// Wave-wide sum in the same pairing order (symmetric, so every lane gets the
+// same bits).
+__device__ __forceinline__ double wave_sum_d(double v) {
+  v += dpp_d<0xB1>(v);
+  v += dpp_d<0x4E>(v);
+  v += dpp_d<0x141>(v);
+  v += dpp_d<0x140>(v);
+  {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)u, 0x401F);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)(u >> 32), 0x401F);
+    v += __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+  }
+  return v + __shfl_xor(v, 32, 64);
+}
+__device__ __forceinline__ double readlane_d(double v, int src) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, src);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), src);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
 template <int R>
@@ -344,18 +376,13 @@ __global__ __launch_bounds__(64) void build_page_kernel(
     }
     v0 = act ? v0 / sig : 0.0;
     v1 = act ? v1 / sig : 0.0;
-    // largest |v| (lowest dim on ties) over the 128 dims
-    double amax = fabs(v0);
-    int aidx = 2 * lane;
-    if (fabs(v1) > amax) { amax = fabs(v1); aidx = 2 * lane + 1; }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      const double oa = __shfl_xor(amax, m, 64);
-      const int oi = __shfl_xor(aidx, m, 64);
-      if (oa > amax || (oa == amax && oi < aidx)) { amax = oa; aidx = oi; }
-    }
-    const double vsel = ((aidx & 1) ? v1 : v0);
-    const double aval = __shfl(vsel, aidx >> 1, 64);
+    // largest |v| over the 128 dims, and its value at the lowest such dim
+    // (dims 2l, 2l+1 live in lane l)
+    const double a0 = fabs(v0), a1 = fabs(v1);
+    const double amax = wave_max_d(fmax(a0, a1));
+    const uint64_t m0 = __ballot(a0 == amax), m1 = __ballot(a1 == amax);
+    const int l0 = m0 ? __builtin_ctzll(m0) : 64, l1 = m1 ? __builtin_ctzll(m1) : 64;
+    const double aval = (l0 <= l1) ? readlane_d(v0, l0) : readlane_d(v1, l1);
     const double flip = (aval < 0.0) ? -1.0 : 1.0;
     if (lane == 0) sig_s[k] = act ? sig * flip : 0.0;
     const uint16_t sbits = act ? fp16_scale_bits(amax, 7.f) : (uint16_t)0;
