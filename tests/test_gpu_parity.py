@@ -472,15 +472,17 @@ def _check_step(b, r, kmax, res, kp_after, vp_after, summ_after, summ_before, co
     # the new tokens are in the pools, nothing else moved
     assert torch.equal(kp_after, b.k_pool) and torch.equal(vp_after, b.v_pool)
     # completed pages got GPU-built summaries within the build tolerance; others untouched
+    summ_ora = summ_before.copy()
     for blk in range(b.num_blocks):
         if blk in completed:
             for h in range(b.H):
                 ora, _, _ = O.build_slots(Hh.np64(b.k_pool[blk, h])[None], r)
                 assert np.count_nonzero(summ_after[blk, h] != ora[0]) <= 4, (blk, h)
+                summ_ora[blk, h] = ora[0]
         else:
             assert np.array_equal(summ_after[blk], summ_before[blk]), blk
-    # score/select/attend against the oracle fed the summaries the step used
-    return _check_against_oracle(b, summ_after, res, r, kmax)
+    # score/select/attend against the oracle fed its own summaries
+    return _check_against_oracle(b, summ_ora, res, r, kmax)
 
 
 @pytest.mark.parametrize("host_lens", [True, False])
@@ -595,3 +597,88 @@ def test_decode_step_full_size_128k(L):
     res, kpa, vpa, sa = _run_step(L, L.Dims(b.H, b.G, 8), b, kp, vp, kn, vn, summ, 128)
     ws, nmis, wo = _check_step(b, 8, 128, res, kpa, vpa, sa, summ, completed)
     _say(f"    near-tie swaps {nmis}, worst attn rel-L2 {wo:.2e}")
+
+
+def test_batch32_full_size_sampled(L):
+    """The batch of 32 sequences (8K..128K tokens, budgets max(8, ceil(P/16)))
+    at its real shape, through the separate entry points and through
+    locks_decode_step. Four sampled (sequence, KV head) pairs carry
+    oracle-built summaries and are checked against the oracle; every other
+    pair rides along with GPU-built summaries."""
+    _say("[gpu] batch of 32 sequences, full size, 4 sampled heads")
+    b = synth.config_batch("batch32", device=DEV)
+    S, H, G, r = b.num_seqs, b.H, b.G, 8
+    dims = L.Dims(H, G, r)
+    lens = [int(x) for x in b.seq_lens.tolist()]
+    kmax = int(b.budgets.max())
+    picks = [(0, 0), (9, 3), (20, 5), (31, 7)]
+
+    def sampled_oracle(res, completed_gpu=None):
+        worst = 0.0
+        for (sq, h) in picks:
+            Lq = lens[sq]
+            P, F = (Lq + 15) // 16, Lq // 16
+            blocks = b.block_table[sq, :P].long()
+            Kp = Hh.np64(b.k_pool[blocks, h])
+            Vp = Hh.np64(b.v_pool[blocks, h])
+            slots, _, _ = O.build_slots(Kp[:F], r)
+            if completed_gpu is not None:
+                got = completed_gpu[(sq, h)]
+                assert np.count_nonzero(got != slots[F - 1]) <= 4, (sq, h)
+            qq = Hh.np64(b.q[sq, h * G:(h + 1) * G])
+            ora = O.decode_head(qq, Kp, Vp, Lq, int(b.budgets[sq]), slots=slots, r=r)
+            n = int(res["cnt"][sq, h])
+            gsel = [int(j) for j in res["sel"][sq, h, :n]]
+            assert gsel == sorted(gsel) and n == min(max(int(b.budgets[sq]), 2), kmax, P)
+            Hh.selection_mismatch(gsel, ora["sel"], ora["key"], P)
+            tk = np.concatenate([Kp[j, :(16 if j < P - 1 else Lq - 16 * (P - 1))] for j in gsel])
+            tv = np.concatenate([Vp[j, :(16 if j < P - 1 else Lq - 16 * (P - 1))] for j in gsel])
+            o_ref, lse_ref = O.attend(qq, tk, tv)
+            e = Hh.rel_l2(res["out"][sq, h * G:(h + 1) * G], o_ref)
+            assert e <= 1e-2, (sq, h, e)
+            np.testing.assert_allclose(res["lse"][sq, h * G:(h + 1) * G], lse_ref, atol=1e-3)
+            worst = max(worst, e)
+        return worst
+
+    # summaries: GPU build of every full page, then oracle slots for the sampled pairs
+    summ = L.alloc_summaries(dims, b.num_blocks, DEV)
+    full = torch.cat([b.block_table[sq, :lens[sq] // 16] for sq in range(S)]).contiguous()
+    L.build(dims, b.k_pool, full, summ)
+    torch.cuda.synchronize()
+    for (sq, h) in picks:
+        F = lens[sq] // 16
+        blocks = b.block_table[sq, :F].long()
+        slots, _, _ = O.build_slots(Hh.np64(b.k_pool[blocks, h]), r)
+        summ[blocks, h] = torch.from_numpy(slots).to(DEV)
+    res = _run_decode(L, dims, b, summ, kmax, scores=False)
+    w1 = sampled_oracle(res)
+    _say(f"    separate entry points: worst attn rel-L2 {w1:.2e}")
+
+    # the same batch one token earlier, stepped by locks_decode_step: the
+    # token at len - 1 completes a page in every sequence (lengths are page
+    # multiples), which the step appends and builds
+    kp, vp = b.k_pool.clone(), b.v_pool.clone()
+    kn = torch.empty(S, H, 128, dtype=torch.bfloat16, device=DEV)
+    vn = torch.empty_like(kn)
+    last = []
+    for sq in range(S):
+        blk, t = int(b.block_table[sq, (lens[sq] - 1) // 16]), (lens[sq] - 1) % 16
+        kn[sq], vn[sq] = b.k_pool[blk, :, t], b.v_pool[blk, :, t]
+        kp[blk, :, t] = 3.0
+        vp[blk, :, t] = -3.0
+        summ[blk] = 0
+        last.append(blk)
+    out = torch.full((S, H * G, 128), 7.0, device=DEV)
+    lse = torch.full((S, H * G), 7.0, device=DEV)
+    sel = torch.full((S, H, kmax), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.full((S, H), -7, dtype=torch.int32, device=DEV)
+    ws = L.alloc_workspace(dims, S, b.max_pages, kmax, DEV)
+    L.decode_step(dims, b.q, kn, vn, kp, vp, summ, b.block_table, b.seq_lens, b.budgets, kmax, out,
+                  ws, lse_out=lse, sel_pages=sel, sel_count=cnt, seq_lens_host=b.seq_lens.cpu())
+    torch.cuda.synchronize()
+    assert torch.equal(kp, b.k_pool) and torch.equal(vp, b.v_pool)
+    completed_gpu = {(sq, h): summ[last[sq], h].cpu().numpy() for (sq, h) in picks}
+    res2 = dict(sel=sel.cpu().numpy(), cnt=cnt.cpu().numpy(), out=out.cpu().numpy(),
+                lse=lse.cpu().numpy())
+    w2 = sampled_oracle(res2, completed_gpu)
+    _say(f"    locks_decode_step: worst attn rel-L2 {w2:.2e}")
