@@ -12,7 +12,9 @@
 // are bf16, so K K^T accumulated in fp64 is exact to rounding of the sums,
 // and the Gram is formed as C (K K^T) C with the centring matrix
 // C = I - 11^T/B. The eigendecomposition is a cyclic two-sided Jacobi in
-// fp64: round m (m = 1..15) rotates the 8 disjoint pairs (i, i xor m), so a
+// fp64 (rotation angles evaluated in fp32 and made orthogonal to fp64
+// rounding, as in the one-page form): round m (m = 1..15) rotates the 8
+// disjoint pairs (i, i xor m), so a
 // sweep visits each of the 120 pairs once. Lane i keeps its rows permuted as
 // b[x] = A[i][i xor x]; then the diagonal is b[0], the pair element is b[m]
 // and every exchange is a xor lane shuffle. Sweeps stop when the off-diagonal
@@ -27,19 +29,6 @@ constexpr int kMaxSweeps = 12;
 
 __device__ __forceinline__ double shfl_xor_d(double v, int m) { return __shfl_xor(v, m, 64); }
 
-__device__ __forceinline__ void rotation(double app, double aqq, double apq, double& c,
-                                         double& s) {
-  // Symmetric Schur 2x2 (Golub & Van Loan): J = [[c, s], [-s, c]] makes
-  // (J^T A J)_pq = 0 with |angle| <= pi/4. Branch-free: apq == 0 gives the
-  // identity, and a huge |tau| gives t = 0 through sqrt(inf).
-  const bool zero = (apq == 0.0);
-  const double tau = (aqq - app) / (2.0 * (zero ? 1.0 : apq));
-  double t = (tau >= 0.0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
-  t = zero ? 0.0 : t;
-  c = 1.0 / sqrt(1.0 + t * t);
-  s = t * c;
-}
-
 // One Jacobi round: rotate the 8 pairs (p, p xor M) of the page's 16 rows.
 // Lane i holds b[x] = A[i][i^x] and ub[x] = U[i][i^x].
 template <int M>
@@ -49,7 +38,7 @@ __device__ __forceinline__ void jacobi_round(double (&b)[kPage], double (&ub)[kP
   const double aii = b[0], ajj = shfl_xor_d(b[0], M);
   const double apq = 0.5 * (b[M] + shfl_xor_d(b[M], M));
   double c, s;
-  rotation(lo ? aii : ajj, lo ? ajj : aii, apq, c, s);
+  rotation_fast(lo ? aii : ajj, lo ? ajj : aii, apq, c, s);
   // Signed sine: +s on the lower lane of the pair, -s on the upper one. For
   // column j of this row the pair's rotation enters with the sign that lane j
   // itself holds, so fetching (c, sr) from lane j = i^x needs no lane masks.
