@@ -556,17 +556,21 @@ __global__ __launch_bounds__(G * kHeadDim / 4) void decode_merge_kernel(
 #pragma unroll
   for (int y = 0; y < kMaxS; ++y)
     if (y >= nsplit) { pa[y] = make_float4(0.f, 0.f, 0.f, 0.f); pm[y] = -__builtin_inff(); pl[y] = 0.f; }
-  float M = -__builtin_inff(), L = 0.f;
+  // one common maximum, then every split's weight independently (no chain
+  // of rescalings), summed in split order
+  float M = -__builtin_inff();
+#pragma unroll
+  for (int y = 0; y < kMaxS; ++y) M = fmaxf(M, pm[y]);
+  float L = 0.f;
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int y = 0; y < kMaxS; ++y) {
-    float f2;
-    const float f1 = merge_factors(M, pm[y], f2);
-    L = L * f1 + pl[y] * f2;
-    a.x = a.x * f1 + pa[y].x * f2;
-    a.y = a.y * f1 + pa[y].y * f2;
-    a.z = a.z * f1 + pa[y].z * f2;
-    a.w = a.w * f1 + pa[y].w * f2;
+    const float f = (M == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(pm[y] - M);
+    L = fmaf(pl[y], f, L);
+    a.x = fmaf(pa[y].x, f, a.x);
+    a.y = fmaf(pa[y].y, f, a.y);
+    a.z = fmaf(pa[y].z, f, a.z);
+    a.w = fmaf(pa[y].w, f, a.w);
   }
   const bool some = L > 0.f;
   *reinterpret_cast<float4*>(out + (sh_idx * G + g) * kHeadDim + d) =
