@@ -110,6 +110,18 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
   // ---- every independent load first
   const int len_raw = seq_lens[s];
   const int bud_raw = budgets[s];
+  // tile Z partials first: the Z reduction can start while the page loads
+  // are still in flight
+  const float2* zp = zpart + sh_idx * ntiles * G;
+  constexpr int kZl = (kRP * kDecThreads + 64 * kScorePagesPerWg - 1) / (64 * kScorePagesPerWg);
+  float2 zl[kZl][G];  // tile partials t = lane + 64 c
+#pragma unroll
+  for (int c = 0; c < kZl; ++c) {
+    const int t = lane + 64 * c;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      zl[c][g] = (t < ntiles) ? zp[t * G + g] : make_float2(-__builtin_inff(), 0.f);
+  }
   float ev[kRP][G], mv[kRP];
   int bk[kRP];
   {
@@ -132,16 +144,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
     }
   }
   if (tid < G * kHeadDim / 8) sh_q[tid] = reinterpret_cast<const uint4*>(q + sh_idx * G * kHeadDim)[tid];
-  const float2* zp = zpart + sh_idx * ntiles * G;
-  constexpr int kZl = (kRP * kDecThreads + 64 * kScorePagesPerWg - 1) / (64 * kScorePagesPerWg);
-  float2 zl[kZl][G];  // tile partials t = lane + 64 c
-#pragma unroll
-  for (int c = 0; c < kZl; ++c) {
-    const int t = lane + 64 * c;
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-      zl[c][g] = (t < ntiles) ? zp[t * G + g] : make_float2(-__builtin_inff(), 0.f);
-  }
   // histogram and bitmap cleared while the loads are in flight (the first
   // barrier of the selection publishes this)
   for (int i = tid; i < kHistCopies * (kBins + 1); i += kDecThreads) (&histc[0][0])[i] = 0u;
