@@ -39,6 +39,19 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "decode-step µs and achieved HBM GB/s (summary+selected KV) at 128K ctx, 8 KV heads"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "score_kernel_ctx128k_counters.txt")
 SCORE_SRC = os.path.join(ROOT, "kv_cache_page_amd", "csrc", "locks_score_mfma.hip")
+SCORE_HDR = os.path.join(ROOT, "kv_cache_page_amd", "csrc", "locks_device.h")
+
+
+def score_kernel_fingerprint():
+    """sha256 over what decides the score kernel's machine code: its source,
+    the header it includes and its compile flags."""
+    from kv_cache_page_amd import build_lib
+    h = hashlib.sha256()
+    for path in (SCORE_SRC, SCORE_HDR):
+        h.update(open(path, "rb").read())
+    flags = build_lib.FLAGS + build_lib.FILE_FLAGS.get(os.path.basename(SCORE_SRC), [])
+    h.update(" ".join(flags).encode())
+    return h.hexdigest()
 
 
 def log(msg):
@@ -61,7 +74,7 @@ def step_bytes(seq_len):
 
 def traffic_from_counters():
     """HBM bytes per score-kernel launch from the committed rocprofv3 counter
-    summary, or None when absent or taken on a different kernel source."""
+    summary, or None when absent or taken on a different build of the kernel."""
     if not os.path.exists(COUNTERS_FILE):
         return None
     kv = {}
@@ -69,8 +82,7 @@ def traffic_from_counters():
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    sha = hashlib.sha256(open(SCORE_SRC, "rb").read()).hexdigest()
-    if kv.get("score_source_sha256") != sha:
+    if kv.get("score_kernel_sha256") != score_kernel_fingerprint():
         return None
     try:
         return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])

@@ -34,7 +34,11 @@ FLAGS = [
 # Per-file additions. The score kernel never produces NaN from its own
 # arithmetic (it only stores NaN constants), so max/min need no NaN quieting
 # and fold into DPP forms.
-FILE_FLAGS = {"locks_score_mfma.hip": ["-fno-honor-nans"]}
+FILE_FLAGS = {
+    # matrix-core results stay in ordinary VGPRs (no accumulator-register copies)
+    "locks_score_mfma.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "locks_build_page.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def sources():
