@@ -87,6 +87,9 @@ const char* locks_status_string(locks_status status);
  *                          page_size coefficient-row scales, 1 centroid scale
  *   then zero padding up to slot_stride (a multiple of 16 bytes).
  * Decoded values are code * scale. r = 8: 818 payload bytes, stride 832.
+ * The scoring calls take basis-column scales below 8 (the matrix-core path
+ * carries V^T q in fp16 parts); locks_build writes at most about 1/7, since
+ * its basis columns have unit norm.
  */
 size_t locks_summary_slot_bytes(const locks_dims* dims);  /* payload; 0 if dims invalid */
 size_t locks_summary_slot_stride(const locks_dims* dims); /* bytes between slots; 0 if invalid */

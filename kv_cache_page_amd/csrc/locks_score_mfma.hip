@@ -23,14 +23,27 @@
 //   the whole W of its page for its query, with no data exchange.
 // The centroid term mu . q uses one more MFMA chain per 16 pages with A rows
 //   in the order page 4 (m % 4) + m / 4, so that register i of lane q16 holds
-//   page 4 i + q16: again the page and query the lane needs.
-// Stage 2 (VALU, fp32): lane (a, r16 = 4 b + g) forms the logits of tokens
-//   4b .. 4b+3 of page a for query g from its W, the int8 coefficient rows and
-//   the token scales, and the LSE over the page's 16 tokens combines the 4
-//   token blocks (lanes r16 xor 4, xor 8).
-// The slot loads of the first three groups and of the centroids are issued
-// as soon as the block ids arrive; the query operands are built meanwhile,
-// and a 4-deep pipeline keeps three groups in flight while one is computed.
+//   page 4 i + q16 for query r16 % 4; one lane permute per register hands it
+//   to the lanes of stage 2's column (page r16 / 4).
+// Stage 2, the logits c_t . W, on the matrix cores too: one product per
+//   group (two for rank 16) with rows = the 16 tokens, K = (page, rank) and
+//   columns n = (page n / 4, query n % 4). The B operand is block diagonal:
+//   lane (a, r16) holds the W of page a for query r16 % 4, which is column
+//   r16's block exactly when a == r16 / 4, and zeros otherwise. W enters as
+//   an fp16 high part plus an fp16 low part (two products, about 22 bits),
+//   scaled by 2^12 into fp16's normal range (|W| < 2 s_k in these units, so
+//   basis-column scales s_k below 8 stay finite; unit basis columns give
+//   s_k <= 1/7); the int8 coefficients become
+//   exact fp16 through the 1024 + byte pattern. D leaves tokens 4a .. 4a+3 of
+//   page r16 / 4 for query r16 % 4 in lane (a, r16); the LSE over the page's
+//   16 tokens combines the four rows (row swaps, no LDS).
+// The query rows are loaded together with the block ids; the slot loads of
+// the first two groups and of the centroids are issued as soon as the ids
+// arrive, the query operands are built meanwhile, and a 3-deep pipeline keeps
+// two groups in flight while one is computed. Each loop iteration is one
+// straight-line block (no early exit, outputs stored after the loop, loads
+// unconditional) fenced by scheduling barriers: the compiler's memory wait
+// counts then stay exact and every group waits only for its own loads.
 #include "locks_device.h"
 
 namespace locks {
@@ -42,10 +55,42 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 // order [d0, d2, 16 d1, 16 d3, d4, d6, 16 d5, 16 d7] (bytes of the word hold
 // the dim pairs (0,1), (4,5), (2,3), (6,7), low nibble first).
 __device__ __forceinline__ half8 nib8(uint32_t w) {
-  w ^= 0x88888888u;
+  // (x ^ 8) & 15 per nibble: one three-input bit operation per output word
   const uint32_t w8 = w >> 8;
-  return __builtin_bit_cast(half8, make_uint4(w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu,
-                                              w8 & 0x00F000F0u));
+  return __builtin_bit_cast(half8, make_uint4((w ^ 0x00080008u) & 0x000F000Fu,
+                                              (w ^ 0x00800080u) & 0x00F000F0u,
+                                              (w8 ^ 0x00080008u) & 0x000F000Fu,
+                                              (w8 ^ 0x00800080u) & 0x00F000F0u));
+}
+
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+
+// 4 int8 codes (one word, byte order) -> 2 words of exact fp16 values: the
+// byte b = c + 128 becomes the half 0x64bb = 1024 + b, minus 1152.
+__device__ __forceinline__ void coef4(uint32_t w, uint32_t& h0, uint32_t& h1) {
+  const uint32_t y = w ^ 0x80808080u;
+  const half2v k = half2v{(_Float16)-1152.f, (_Float16)-1152.f};
+  h0 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, y, 0x04010400u)) + k);
+  h1 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, y, 0x04030402u)) + k);
+}
+
+// Max / sum over the 4 lanes l, l ^ 16, l ^ 32, l ^ 48 (same column of the
+// four 16-lane rows); the result is bit-identical in all four.
+__device__ __forceinline__ float xrow_max(float v) {
+  const uint32_t x = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t y = __float_as_uint(m);
+  const auto b = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float xrow_sum(float v) {
+  const uint32_t x = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  const float m = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t y = __float_as_uint(m);
+  const auto b = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // 8 int8 codes (two words, byte order) -> (c + 128) 2^-24 as fp16
@@ -74,28 +119,37 @@ __device__ __forceinline__ float half_hi(uint32_t w) {
 template <int R>
 struct GroupRegs {
   uint4 v[R / 4];        // basis: row 4 hh + r16 % 4 of page r16 / 4, bytes 16 q16 ..
-  uint4 c[R / 4];        // coefficients of tokens 4 b .. 4 b + 3 of page q16
+  uint32_t c[R / 4];     // coefficients of token r16 of page q16
   uint32_t sv[R / 2];    // fp16 basis-column scales of page q16
-  uint2 sc;              // fp16 scales of tokens 4 b .. 4 b + 3 of page q16
-  uint32_t smu;          // fp16 centroid scale of page q16 (low half)
+  uint2 sc;              // fp16 scales of tokens 4 q16 .. 4 q16 + 3 of page r16 / 4
+  uint32_t smu;          // fp16 centroid scale of page r16 / 4 (low half)
 };
 
 template <int R>
 __device__ __forceinline__ void load_group(GroupRegs<R>& g, const uint8_t* __restrict__ slotV,
                                            const uint8_t* __restrict__ slotC, int r16, int q16) {
   constexpr SlotLayout L = slot_layout(R);
-  const int b = r16 >> 2;
   const uint8_t* pv = slotV + L.v + 64 * (r16 & 3) + 16 * q16;
 #pragma unroll
   for (int hh = 0; hh < R / 4; ++hh) g.v[hh] = *reinterpret_cast<const uint4*>(pv + 256 * hh);
-  // tokens 4b..4b+3 x R bytes = 4R contiguous bytes
-  const uint8_t* pc = slotC + L.c + 4 * R * b;
-#pragma unroll
-  for (int e = 0; e < R / 4; ++e) g.c[e] = *reinterpret_cast<const uint4*>(pc + 16 * e);
+  const uint8_t* pc = slotC + L.c + R * r16;  // the R code bytes of token r16
+  if constexpr (R == 4) {
+    g.c[0] = *reinterpret_cast<const uint32_t*>(pc);
+  } else if constexpr (R == 8) {
+    const uint2 t = *reinterpret_cast<const uint2*>(pc);
+    g.c[0] = t.x;
+    g.c[1] = t.y;
+  } else {
+    const uint4 t = *reinterpret_cast<const uint4*>(pc);
+    g.c[0] = t.x;
+    g.c[1] = t.y;
+    g.c[2] = t.z;
+    g.c[3] = t.w;
+  }
 #pragma unroll
   for (int e = 0; e < R / 2; ++e) g.sv[e] = *reinterpret_cast<const uint32_t*>(slotC + L.sv + 4 * e);
-  g.sc = *reinterpret_cast<const uint2*>(slotC + L.sc + 8 * b);
-  g.smu = *reinterpret_cast<const uint16_t*>(slotC + L.smu);
+  g.sc = *reinterpret_cast<const uint2*>(slotV + L.sc + 8 * q16);
+  g.smu = *reinterpret_cast<const uint16_t*>(slotV + L.smu);
 }
 
 // One 128-page tile, by 4 waves (wave = 0..3, tid = 64 wave + lane). Leaves
@@ -127,6 +181,19 @@ __device__ __forceinline__ void score_tile(
     const int j = P0 + 16 * u + r16;
     traw[u] = (j < MP) ? table[(int64_t)s * MP + j] : -1;
   }
+  // raw query rows (independent of the block ids): column r16 carries query
+  // gq; lane q16 holds dims [32 q16, 32 q16 + 32) of it. Issued here, ahead
+  // of the wait for the block ids (the empty asm keeps the compiler from
+  // sinking the loads below it).
+  const bool qok = gq < G;
+  uint4 qraw[4];
+  {
+    const uint4* qp = reinterpret_cast<const uint4*>(
+        q + ((int64_t)s * H * G + (int64_t)h * G + (qok ? gq : 0)) * kHeadDim + 32 * q16);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qraw[c] = qp[c];
+  }
+  asm volatile("" ::: "memory");
   const int len = clampi(seq_lens[s], 0, MP * kPage);
   const int F = len / kPage;
   if (knew && tile == 0 && tid < 2 * (kHeadDim / 8) && len >= 1) {
@@ -152,16 +219,6 @@ __device__ __forceinline__ void score_tile(
   if (j_lo >= F) return;
   const int j_end = min(j_hi, F);
 
-  // ---- raw query rows (independent of the block ids): column r16 carries
-  // query gq; lane q16 holds dims [32 q16, 32 q16 + 32) of it
-  const bool qok = gq < G;
-  uint4 qraw[4];
-  {
-    const uint4* qp = reinterpret_cast<const uint4*>(
-        q + ((int64_t)s * H * G + (int64_t)h * G + (qok ? gq : 0)) * kHeadDim + 32 * q16);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) qraw[c] = qp[c];
-  }
   // ---- live block ids (-1: page past the end or id out of range); the slot
   // addresses each role needs come by lane permutes. vbits[u] bit i: page
   // P0 + 16 u + i is live.
@@ -200,17 +257,25 @@ __device__ __forceinline__ void score_tile(
   float zv[kGroups];  // page LSEs (base 2) of query gq, for the tile's Z partial
 #pragma unroll
   for (int gi = 0; gi < kGroups; ++gi) zv[gi] = -__builtin_inff();
-  constexpr int kDepth = (R >= 8) ? 3 : 4;  // deeper prefetch only moves the stall to the issue
+  constexpr int kDepth = (R >= 8) ? 3 : 4;  // a fourth group in flight measured no faster at rank 8
   GroupRegs<R> buf[kDepth];
-  auto issue = [&](int gi, GroupRegs<R>& gr) {
-    const int u = gi >> 2, base = 4 * (gi & 3);
-    const int bV = shfl_i(bo[u], base + (r16 >> 2));
-    const int bC = shfl_i(bo[u], base + q16);
-    load_group<R>(gr, slot_ptr(bV), slot_ptr(bC), r16, q16);
-  };
+  // block ids of every group's two lane roles, permuted once
+  int bVg[kGroups], bCg[kGroups];
 #pragma unroll
-  for (int gi = 0; gi < kDepth - 1; ++gi)
-    if (P0 + 4 * gi < j_end) issue(gi, buf[gi]);
+  for (int gi = 0; gi < kGroups; ++gi) {
+    const int u = gi >> 2, base = 4 * (gi & 3);
+    bVg[gi] = shfl_i(bo[u], base + (r16 >> 2));
+    bCg[gi] = shfl_i(bo[u], base + q16);
+  }
+  auto issue = [&](int gi, GroupRegs<R>& gr) {
+    load_group<R>(gr, slot_ptr(bVg[gi]), slot_ptr(bCg[gi]), r16, q16);
+  };
+  // Issues are unconditional (a group past the end reads block 0's slot,
+  // which exists): a load behind a branch makes the compiler's wait counts
+  // assume the worst case, and every group would then wait for all loads.
+#pragma unroll
+  for (int gi = 0; gi < kDepth - 1; ++gi) issue(gi, buf[gi]);
+  __builtin_amdgcn_sched_barrier(0);  // keep the first issues ahead of the query-operand work
   // ---- query operands, power-of-two scaled into fp16 (built while the slot
   // loads are in flight)
   half8 B1[4], Bm[4];
@@ -273,16 +338,42 @@ __device__ __forceinline__ void score_tile(
       Dm[u] = d;
     }
   }
+  // Stage-2 lane constants: the diagonal mask and the factor 2^12 ride on the
+  // basis-column scales (a packed fp16 multiply per scale pair).
+  const bool diag = q16 == (r16 >> 2);
+  const half2v msig = diag ? half2v{(_Float16)4096.f, (_Float16)4096.f}
+                           : half2v{(_Float16)0.f, (_Float16)0.f};
+  const float fsig = fs * (1.f / 4096.f);
+  // centroid term of the lane's stage-2 column: page 4 i + r16 / 4 of half u,
+  // query r16 % 4, from register i of lane 16 (r16 / 4) + r16 % 4
+  float muq[kHalves][4];
+  {
+    const int src = 4 * (16 * (r16 >> 2) + (r16 & 3));
+#pragma unroll
+    for (int u = 0; u < kHalves; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        muq[u][i] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(Dm[u][i])));
+  }
 
 #pragma unroll
   for (int gi = 0; gi < kGroups; ++gi) {
-    if (P0 + 4 * gi >= j_end) break;  // wave-uniform
-    if (gi + kDepth - 1 < kGroups && P0 + 4 * (gi + kDepth - 1) < j_end)
-      issue(gi + kDepth - 1, buf[(gi + kDepth - 1) % kDepth]);
+    // no early exit for groups past the end (their pages are not live, so
+    // nothing they compute is written): straight-line code keeps the
+    // compiler from sinking the early slot loads into later blocks
+    __builtin_amdgcn_sched_barrier(0);  // one iteration = the issue, then this group
+    if (gi + kDepth - 1 < kGroups) issue(gi + kDepth - 1, buf[(gi + kDepth - 1) % kDepth]);
+    __builtin_amdgcn_sched_barrier(0);
     const GroupRegs<R>& gr = buf[gi % kDepth];
     const int u = gi >> 2, base = 4 * (gi & 3);
-    // stage 1: W of page q16 of the group, query gq, ranks 4 hh + i
-    float W[R];
+    // stage 1: W of page q16 of the group, query gq, ranks 4 hh + i, times
+    // 2^12 on the diagonal lanes and zero on the others
+    uint32_t svm[R / 2];
+#pragma unroll
+    for (int e = 0; e < R / 2; ++e)
+      svm[e] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, gr.sv[e]) * msig);
+    float W[R];  // the stage-1 result d_k and the scale s_k, split below
+    float Ws[R];
 #pragma unroll
     for (int hh = 0; hh < NHR; ++hh) {
       floatx4 d = {vinit, vinit, vinit, vinit};
@@ -292,56 +383,77 @@ __device__ __forceinline__ void score_tile(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int k = 4 * hh + i;
-        const uint32_t sw = gr.sv[k >> 1];
-        W[k] = d[i] * ((k & 1) ? half_hi(sw) : half_lo(sw));
+        W[k] = d[i];
+        Ws[k] = (k & 1) ? half_hi(svm[k >> 1]) : half_lo(svm[k >> 1]);
       }
     }
-    float wsum = 0.f;
+    // stage 2: X[i] = 2^12 c_t . W for token t = 4 q16 + i of page r16 / 4 and
+    // query r16 % 4 (W = high + low fp16 parts)
+    floatx4 X = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (R == 4) {
+      uint32_t a0, a1;
+      coef4(gr.c[0], a0, a1);
+      const half4 A = __builtin_bit_cast(half4, make_uint2(a0, a1));
+      half4 Bh, Bl;
 #pragma unroll
-    for (int k = 0; k < R; ++k) wsum += W[k];
-    // centroid term of page base + q16 (register (gi & 3) of half u)
-    const float muq = Dm[u][gi & 3] * half_lo(gr.smu);
-    // stage 2: logits of tokens 4b .. 4b+3 (base 2); the R words per token
-    // row become offset-binary bytes (c + 128) read by v_cvt_f32_ubyte*
-    uint32_t cx[R];
+      for (int e = 0; e < 4; ++e) {
+        // high part: d s rounded once to fp16; low part: the exact remainder
+        // d s - high (one fma) rounded to fp16
+        const _Float16 hi = (_Float16)(W[e] * Ws[e]);
+        Bh[e] = hi;
+        Bl[e] = (_Float16)__builtin_fmaf(W[e], Ws[e], -(float)hi);
+      }
+      X = __builtin_amdgcn_mfma_f32_16x16x16f16(A, Bh, X, 0, 0, 0);
+      X = __builtin_amdgcn_mfma_f32_16x16x16f16(A, Bl, X, 0, 0, 0);
+    } else {
 #pragma unroll
-    for (int e = 0; e < R / 4; ++e) {
-      cx[4 * e + 0] = gr.c[e].x ^ 0x80808080u;
-      cx[4 * e + 1] = gr.c[e].y ^ 0x80808080u;
-      cx[4 * e + 2] = gr.c[e].z ^ 0x80808080u;
-      cx[4 * e + 3] = gr.c[e].w ^ 0x80808080u;
+      for (int hc = 0; hc < R / 8; ++hc) {
+        uint32_t a[4];
+        coef4(gr.c[2 * hc], a[0], a[1]);
+        coef4(gr.c[2 * hc + 1], a[2], a[3]);
+        const half8 A = __builtin_bit_cast(half8, make_uint4(a[0], a[1], a[2], a[3]));
+        half8 Bh, Bl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int k = 8 * hc + e;
+          const _Float16 hi = (_Float16)(W[k] * Ws[k]);
+          Bh[e] = hi;
+          Bl[e] = (_Float16)__builtin_fmaf(W[k], Ws[k], -(float)hi);
+        }
+        X = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bh, X, 0, 0, 0);
+        X = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl, X, 0, 0, 0);
+      }
     }
+    // logits (base 2) of tokens 4 q16 + i: fs (s_t c_t . W + q . mu)
+    const float bm = fs * (muq[u][gi & 3] * half_lo(gr.smu));
     float lg[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float x = -128.f * wsum;
-#pragma unroll
-      for (int k = 0; k < R; ++k) {
-        const int byte = R * i + k;  // token i, rank k within the 4R bytes
-        x = fmaf((float)((cx[byte >> 2] >> (8 * (byte & 3))) & 0xFFu), W[k], x);
-      }
       const uint32_t sw = (i < 2) ? gr.sc.x : gr.sc.y;
       const float sc = (i & 1) ? half_hi(sw) : half_lo(sw);
-      lg[i] = fs * fmaf(sc, x, muq);
+      lg[i] = fmaf(fsig * sc, X[i], bm);
     }
-    // LSE over the 16 tokens: 4 here, the other token blocks in lanes r16 ^ 4, ^ 8
-    // (the 4 lanes r16 = g, g+4, g+8, g+12 form one orbit of the row rotations
-    // by 4 and 8)
+    // LSE over the page's 16 tokens: 4 here, 12 in the other rows' lanes of
+    // the same column
     float m = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
-    m = fmaxf(m, row_ror<4>(m));
-    m = fmaxf(m, row_ror<8>(m));
+    m = xrow_max(m);
     float e = __builtin_amdgcn_exp2f(lg[0] - m) + __builtin_amdgcn_exp2f(lg[1] - m) +
               __builtin_amdgcn_exp2f(lg[2] - m) + __builtin_amdgcn_exp2f(lg[3] - m);
-    e += row_ror<4>(e);
-    e += row_ror<8>(e);
-    const int jp = P0 + 4 * gi + q16;  // the lane's page
-    const bool ok = ((vbits[u] >> (base + q16)) & 1u) && gq < G;
-    const float out2 = ok ? m + __builtin_amdgcn_logf(e) : -__builtin_inff();
-    const bool writer = (r16 < 4) && jp < j_end;  // token block 0 writes
-    zv[gi] = (r16 < 4) ? out2 : -__builtin_inff();
+    e = xrow_sum(e);
+    const bool ok = ((vbits[u] >> (base + (r16 >> 2))) & 1u) && gq < G;
+    zv[gi] = (ok && q16 == 0) ? m + __builtin_amdgcn_logf(e) : -__builtin_inff();
+  }
+  // outputs after the loop: stores behind lane conditions are branches, and
+  // a branch between a slot load and its use makes the compiler's wait
+  // counts assume the worst case
+#pragma unroll
+  for (int gi = 0; gi < kGroups; ++gi) {
+    const int jp = P0 + 4 * gi + (r16 >> 2);  // the lane's page
+    const bool writer = q16 == 0 && jp < j_end;  // row 0 writes
+    const float out2 = zv[gi];
     if (mxout) {
       // decode layout: e_g = 2^(s_g - max_g s_g) per query and the page max;
-      // lanes r16 = 0..3 hold the page's 4 queries (a DPP quad)
+      // lanes r16 = 4p .. 4p+3 hold page p's 4 queries (a DPP quad)
       const float mx = quad_max(out2);
       const float ev = (gq < G && mx != -__builtin_inff()) ? __builtin_amdgcn_exp2f(out2 - mx) : 0.f;
       if (writer && gq < G) srow[(int64_t)jp * G + gq] = ev;
@@ -350,9 +462,9 @@ __device__ __forceinline__ void score_tile(
       srow[(int64_t)jp * G + gq] = out2 * kLn2;
     }
   }
-  // the lane's page LSEs, then lanes r16 < 4 carry query gq = r16; reduce
-  // over the other lanes of the same query (xor 4, 8: token blocks, empty;
-  // xor 16, 32: pages)
+  // the lane's page LSEs (row 0 only), then lanes 0..3 carry query gq = r16;
+  // reduce over the other lanes of the same query (xor 4, 8: the group's
+  // pages; xor 16, 32: rows 1..3, empty)
   zm = zv[0];
 #pragma unroll
   for (int gi = 1; gi < kGroups; ++gi) zm = fmaxf(zm, zv[gi]);
