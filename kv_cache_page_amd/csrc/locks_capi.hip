@@ -11,7 +11,8 @@ namespace locks {
 hipError_t launch_score(int r, int G, const void* q, const void* summ, const int32_t* table,
                         const int32_t* lens, float* scores, int64_t nb, int S, int H, int MP,
                         int fill_nan, float2* zpart, const void* knew, const void* vnew,
-                        void* kpool, void* vpool, float* mxout, hipStream_t st);
+                        void* kpool, void* vpool, float* mxout, CoopZero coop,
+                        hipStream_t st);
 hipError_t launch_select(int G, const float* scores, const int32_t* lens, const int32_t* budgets,
                          int32_t* sel, int32_t* cnt, float* keybuf, int S, int H, int MP,
                          int max_budget, hipStream_t st);
@@ -22,13 +23,15 @@ hipError_t launch_attn(int G, const void* q, const void* kpool, const void* vpoo
 hipError_t launch_build(int r, const void* kpool, int64_t nb, int H, const int32_t* ids, int n,
                         const int32_t* table, const int32_t* lens, int MP, void* summ,
                         const void* knew, const void* vnew, void* vpool, hipStream_t st);
-bool decode_shape(int MP, int KB, int* ppw, int* nsplit);
+bool decode_shape(int MP, int KB, int* per_wg, int* nsplit, int* slice);
+int64_t decode_mailbox_words(int MP, int KB);
+int64_t decode_mailbox_zero_words(int MP, int KB);
 hipError_t launch_decode(int G, const float* escore, const float* pmax, const float2* zpart,
-                         int ntiles,
-                         const int32_t* lens, const int32_t* budgets, const void* q,
+                         int ntiles, const int32_t* lens, const int32_t* budgets, const void* q,
                          const void* kpool, const void* vpool, const int32_t* table, int64_t nb,
-                         int S, int H, int MP, int KB, int nsplit, int ppw, float* part,
-                         float* out, float* lse_out, int32_t* sel, int32_t* cnt, hipStream_t st);
+                         int S, int H, int MP, int KB, int nsplit, int slice, int per_wg,
+                         uint32_t* mbox, float* part, float* out, float* lse_out, int32_t* sel,
+                         int32_t* cnt, hipStream_t st);
 hipError_t launch_append(const void* knew, const void* vnew, void* kpool, void* vpool, int64_t nb,
                          const int32_t* table, const int32_t* lens, int S, int H, int MP,
                          hipStream_t st);
@@ -62,9 +65,10 @@ size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 // Workspace regions: page scores [S][H][MP][G] (or, for the fused decode
 // step, e_g per page and query); per-page maxima [S][H][MP]; per-tile base-2
 // (max, sum) partials [S][H][tiles][G]; selection keys of the separate select kernel
-// [S][H][MP]; attention partials [S][H][splits][G][kPartStride].
+// [S][H][MP]; attention partials [S][H][splits][G][kPartStride]; for the fused
+// decode step, the mailboxes of its workgroups [S][H][...].
 struct Workspace {
-  size_t scores, pmax, zpart, keys, parts, total;
+  size_t scores, pmax, zpart, keys, parts, mbox, total;
   int nsplit, ntiles;
 };
 
@@ -76,9 +80,9 @@ Workspace carve(const locks_dims* d, int32_t S, int32_t MP, int32_t KB) {
   const int per_wg = kAttnWaves * attn_pages_per_wave(KB);
   w.nsplit = (KB + per_wg - 1) / per_wg;
   w.ntiles = (MP + locks::kScorePagesPerWg - 1) / locks::kScorePagesPerWg;
-  int ppw_f, ns_f;
-  const int part_splits =
-      locks::decode_shape(MP, KB, &ppw_f, &ns_f) && ns_f > w.nsplit ? ns_f : w.nsplit;
+  int per_f, ns_f, slice_f;
+  const bool fused = locks::decode_shape(MP, KB, &per_f, &ns_f, &slice_f);
+  const int part_splits = fused && ns_f > w.nsplit ? ns_f : w.nsplit;
   size_t off = 0;
   w.scores = off;
   off = align_up(off + sh * MP * d->group_size * sizeof(float));
@@ -90,6 +94,8 @@ Workspace carve(const locks_dims* d, int32_t S, int32_t MP, int32_t KB) {
   off = align_up(off + sh * MP * sizeof(uint32_t));
   w.parts = off;
   off = align_up(off + sh * part_splits * d->group_size * kPartStride * sizeof(float));
+  w.mbox = off;
+  off = align_up(off + (fused ? sh * (size_t)locks::decode_mailbox_words(MP, KB) * sizeof(uint32_t) : 0));
   w.total = off;
   return w;
 }
@@ -197,7 +203,7 @@ locks_status locks_score_select(const locks_dims* d, const void* q, const void* 
   const int H = d->num_kv_heads, G = d->group_size;
   hipError_t he = locks::launch_score(d->rank, G, q, summaries, block_table, seq_lens, scores, nb,
                                       S, H, MP, scores_out ? 1 : 0, nullptr, nullptr, nullptr, nullptr,
-                                      nullptr, nullptr, st);
+                                      nullptr, nullptr, locks::CoopZero{}, st);
   if (he != hipSuccess) return LOCKS_ERR_HIP;
   he = locks::launch_select(G, scores, seq_lens, budgets, sel_pages, sel_count,
                             reinterpret_cast<float*>(ws + w.keys), S, H, MP, KB, st);
@@ -216,7 +222,7 @@ locks_status locks_score_pages(const locks_dims* d, const void* q, const void* s
   if (!aligned16(q) || !aligned16(summaries)) return LOCKS_ERR_INVALID_ARG;
   return hip_status(locks::launch_score(d->rank, d->group_size, q, summaries, block_table,
                                         seq_lens, scores, nb, S, d->num_kv_heads, MP, 0, nullptr,
-                                        nullptr, nullptr, nullptr, nullptr, nullptr, st));
+                                        nullptr, nullptr, nullptr, nullptr, nullptr, locks::CoopZero{}, st));
 }
 
 locks_status locks_select_pages(const locks_dims* d, const float* scores, const int32_t* seq_lens,
@@ -300,20 +306,25 @@ locks_status locks_decode_step(const locks_dims* d, const void* q, const void* k
   //    completes)
   float* scores = reinterpret_cast<float*>(ws + w.scores);
   float2* zpart = reinterpret_cast<float2*>(ws + w.zpart);
-  int ppw, nsplit;
-  const bool fused = locks::decode_shape(MP, KB, &ppw, &nsplit);
+  int per_wg, nsplit, slice;
+  const bool fused = locks::decode_shape(MP, KB, &per_wg, &nsplit, &slice);
+  const locks::CoopZero coop{fused ? reinterpret_cast<uint32_t*>(ws + w.mbox) : nullptr,
+                             locks::decode_mailbox_words(MP, KB),
+                             (int)locks::decode_mailbox_zero_words(MP, KB)};
   float* pmax = reinterpret_cast<float*>(ws + w.pmax);
   hipError_t he = locks::launch_score(d->rank, G, q, summaries, block_table, seq_lens, scores, nb,
                                       S, H, MP, 0, zpart, completes ? nullptr : k_new,
                                       completes ? nullptr : v_new, k_pool, v_pool,
-                                      fused ? pmax : nullptr, st);
+                                      fused ? pmax : nullptr,
+                                      coop, st);
   if (he != hipSuccess) return LOCKS_ERR_HIP;
   // 3. selection + attention + merge
   float* parts = reinterpret_cast<float*>(ws + w.parts);
   if (fused) {
-    return hip_status(locks::launch_decode(G, scores, pmax, zpart, w.ntiles, seq_lens, budgets, q,
-                                           k_pool, v_pool, block_table, nb, S, H, MP, KB, nsplit,
-                                           ppw, parts, out, lse_out, sel_pages, sel_count, st));
+    return hip_status(locks::launch_decode(
+        G, scores, pmax, zpart, w.ntiles, seq_lens, budgets, q, k_pool, v_pool, block_table, nb, S,
+        H, MP, KB, nsplit, slice, per_wg, reinterpret_cast<uint32_t*>(ws + w.mbox), parts, out,
+        lse_out, sel_pages, sel_count, st));
   }
   // long tables or budgets: the separate select and attention kernels
   if (!sel_pages) return LOCKS_ERR_UNSUPPORTED;

@@ -10,6 +10,28 @@ constexpr int kHeadDim = 128;
 constexpr int kPage = 16;
 // Pages one score workgroup covers (one Z partial per tile of this many).
 constexpr int kScorePagesPerWg = 128;
+// Exchange counters of the fused decode step, per (sequence, KV head): 4
+// counters, one 128-byte line each, at the start of its mailbox.
+constexpr int kCoopCounters = 4;
+constexpr int kCoopCtrWords = 32;
+
+// Where the score kernel of a fused decode step zeroes the decode kernel's
+// mailboxes: `words` words at base + sh * stride for every (sequence, KV
+// head) sh, shared out over the tile rows of that head.
+struct CoopZero {
+  uint32_t* base;
+  int64_t stride;
+  int words;
+};
+
+// Called by every workgroup of the score grid (tile row blockIdx.y of
+// gridDim.y); coherent agent-scope stores; no-op for a null base.
+__device__ __forceinline__ void zero_coop_mailbox(const CoopZero& z, int64_t sh) {
+  if (!z.base) return;
+  uint32_t* p = z.base + sh * z.stride;
+  for (int w = blockIdx.y * blockDim.x + threadIdx.x; w < z.words; w += gridDim.y * blockDim.x)
+    __hip_atomic_store(p + w, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

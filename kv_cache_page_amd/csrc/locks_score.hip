@@ -79,9 +79,10 @@ __global__ __launch_bounds__(256) void score_kernel(
     float* __restrict__ scores, int64_t num_blocks, int H, int MP, int pages_per_wg,
     int fill_nan, float2* __restrict__ zpart, const uint16_t* __restrict__ knew,
     const uint16_t* __restrict__ vnew, uint16_t* __restrict__ kpool,
-    uint16_t* __restrict__ vpool, float* __restrict__ mxout) {
+    uint16_t* __restrict__ vpool, float* __restrict__ mxout, CoopZero coop) {
   constexpr SlotLayout L = slot_layout(R);
   constexpr float kTwoM24 = 5.9604644775390625e-08f;  // 2^-24
+  zero_coop_mailbox(coop, (int64_t)blockIdx.z * H + blockIdx.x);
   const int s = blockIdx.z, h = blockIdx.x, tile = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l4 = lane & 3;
@@ -551,13 +552,13 @@ static hipError_t launch_score_rg(const uint16_t* q, const uint8_t* summ, const 
                                   const int32_t* lens, float* scores, int64_t nb, int S, int H,
                                   int MP, int fill_nan, float2* zpart, const void* knew,
                                   const void* vnew, void* kpool, void* vpool, float* mxout,
-                                  hipStream_t st) {
+                                  CoopZero coop, hipStream_t st) {
   const int ppw = kScorePagesPerWg;
   dim3 grid(H, (MP + ppw - 1) / ppw, S);
   hipLaunchKernelGGL((score_kernel<R, G>), grid, dim3(256), 0, st, q, summ, table, lens, scores,
                      nb, H, MP, ppw, fill_nan, zpart, static_cast<const uint16_t*>(knew),
                      static_cast<const uint16_t*>(vnew), static_cast<uint16_t*>(kpool),
-                     static_cast<uint16_t*>(vpool), mxout);
+                     static_cast<uint16_t*>(vpool), mxout, coop);
   return hipGetLastError();
 }
 
@@ -566,12 +567,12 @@ static hipError_t launch_score_g(int r, const uint16_t* q, const uint8_t* summ,
                                  const int32_t* table, const int32_t* lens, float* scores,
                                  int64_t nb, int S, int H, int MP, int fill_nan, float2* zpart,
                                  const void* knew, const void* vnew, void* kpool, void* vpool,
-                                 float* mxout, hipStream_t st) {
+                                 float* mxout, CoopZero coop, hipStream_t st) {
   switch (r) {
 #define LOCKS_R(RR)                                                                        \
   case RR:                                                                                 \
     return launch_score_rg<RR, G>(q, summ, table, lens, scores, nb, S, H, MP, fill_nan,   \
-                                  zpart, knew, vnew, kpool, vpool, mxout, st);
+                                  zpart, knew, vnew, kpool, vpool, mxout, coop, st);
     LOCKS_R(1) LOCKS_R(2) LOCKS_R(3) LOCKS_R(4) LOCKS_R(5) LOCKS_R(6) LOCKS_R(7) LOCKS_R(8)
     LOCKS_R(9) LOCKS_R(10) LOCKS_R(11) LOCKS_R(12) LOCKS_R(13) LOCKS_R(14) LOCKS_R(15) LOCKS_R(16)
 #undef LOCKS_R
@@ -584,19 +585,21 @@ bool score_mfma_supported(int r);
 hipError_t launch_score_mfma(int r, int G, const void* q, const void* summ, const int32_t* table,
                              const int32_t* lens, float* scores, int64_t nb, int S, int H, int MP,
                              int fill_nan, float2* zpart, const void* knew, const void* vnew,
-                             void* kpool, void* vpool, float* mxout, hipStream_t st);
+                             void* kpool, void* vpool, float* mxout, CoopZero coop,
+                             hipStream_t st);
 
 hipError_t launch_score(int r, int G, const void* q, const void* summ, const int32_t* table,
                         const int32_t* lens, float* scores, int64_t nb, int S, int H, int MP,
                         int fill_nan, float2* zpart, const void* knew, const void* vnew,
-                        void* kpool, void* vpool, float* mxout, hipStream_t st) {
+                        void* kpool, void* vpool, float* mxout, CoopZero coop,
+                        hipStream_t st) {
   if (score_mfma_supported(r))
     return launch_score_mfma(r, G, q, summ, table, lens, scores, nb, S, H, MP, fill_nan, zpart,
-                             knew, vnew, kpool, vpool, mxout, st);
+                             knew, vnew, kpool, vpool, mxout, coop, st);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint8_t* ss = static_cast<const uint8_t*>(summ);
   switch (G) {
-#define LOCKS_ARGS qq, ss, table, lens, scores, nb, S, H, MP, fill_nan, zpart, knew, vnew, kpool, vpool, mxout, st
+#define LOCKS_ARGS qq, ss, table, lens, scores, nb, S, H, MP, fill_nan, zpart, knew, vnew, kpool, vpool, mxout, coop, st
     case 1: return launch_score_g<1>(r, LOCKS_ARGS);
     case 2: return launch_score_g<2>(r, LOCKS_ARGS);
     case 4: return launch_score_g<4>(r, LOCKS_ARGS);

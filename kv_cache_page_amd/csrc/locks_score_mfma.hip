@@ -488,8 +488,9 @@ __global__ __launch_bounds__(256 * TPW) void score_mfma_kernel(
     float* __restrict__ scores, int64_t num_blocks, int H, int MP, int pages_per_wg,
     int fill_nan, float2* __restrict__ zpart, const uint16_t* __restrict__ knew,
     const uint16_t* __restrict__ vnew, uint16_t* __restrict__ kpool,
-    uint16_t* __restrict__ vpool, float* __restrict__ mxout) {
+    uint16_t* __restrict__ vpool, float* __restrict__ mxout, CoopZero coop) {
   const int s = blockIdx.z, h = blockIdx.x;
+  zero_coop_mailbox(coop, (int64_t)s * H + h);
   const int sub = (TPW == 1) ? 0 : (int)(threadIdx.x >> 8);
   const int tile = blockIdx.y * TPW + sub;
   const int tid = threadIdx.x & 255, wave = tid >> 6, lane = tid & 63;
@@ -514,7 +515,8 @@ template <int R, int G>
 static hipError_t launch_r_g(const uint16_t* q, const uint8_t* summ, const int32_t* table,
                              const int32_t* lens, float* scores, int64_t nb, int S, int H, int MP,
                              int fill_nan, float2* zpart, const void* knew, const void* vnew,
-                             void* kpool, void* vpool, float* mxout, hipStream_t st) {
+                             void* kpool, void* vpool, float* mxout, CoopZero coop,
+                             hipStream_t st) {
   constexpr int TPW = 1;
   const int ppw = kScorePagesPerWg;
   const int ntiles = (MP + ppw - 1) / ppw;
@@ -522,7 +524,7 @@ static hipError_t launch_r_g(const uint16_t* q, const uint8_t* summ, const int32
   hipLaunchKernelGGL((score_mfma_kernel<R, G, TPW>), grid, dim3(256 * TPW), 0, st, q, summ, table, lens,
                      scores, nb, H, MP, ppw, fill_nan, zpart, static_cast<const uint16_t*>(knew),
                      static_cast<const uint16_t*>(vnew), static_cast<uint16_t*>(kpool),
-                     static_cast<uint16_t*>(vpool), mxout);
+                     static_cast<uint16_t*>(vpool), mxout, coop);
   return hipGetLastError();
 }
 
@@ -531,10 +533,11 @@ bool score_mfma_supported(int r) { return r == 4 || r == 8 || r == 16; }
 hipError_t launch_score_mfma(int r, int G, const void* q, const void* summ, const int32_t* table,
                              const int32_t* lens, float* scores, int64_t nb, int S, int H, int MP,
                              int fill_nan, float2* zpart, const void* knew, const void* vnew,
-                             void* kpool, void* vpool, float* mxout, hipStream_t st) {
+                             void* kpool, void* vpool, float* mxout, CoopZero coop,
+                             hipStream_t st) {
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint8_t* ss = static_cast<const uint8_t*>(summ);
-#define LOCKS_ARGS qq, ss, table, lens, scores, nb, S, H, MP, fill_nan, zpart, knew, vnew, kpool, vpool, mxout, st
+#define LOCKS_ARGS qq, ss, table, lens, scores, nb, S, H, MP, fill_nan, zpart, knew, vnew, kpool, vpool, mxout, coop, st
 #define LOCKS_G(RR)                                  \
   switch (G) {                                       \
     case 1: return launch_r_g<RR, 1>(LOCKS_ARGS);    \
