@@ -6,8 +6,11 @@
 // top-(k-2) pages by the group-shared estimate of eq. 5), then §3.1 eq. 1
 // (softmax attention renormalised over the selected set S).
 //
-// Grid (nsplit, H, S), nsplit in {8, 16, 32}, 512-thread workgroups. The
-// nsplit workgroups of one (sequence, KV head) split the work: workgroup x
+// nsplit in {8, 16, 32} workgroups of 512 threads per (sequence, KV head),
+// whose ids interleave up to 8 heads (id = h % 8 + 8 x + ...): with the score
+// grid's heads-first order, every workgroup of head h then runs on the XCD
+// that wrote its inputs. The nsplit workgroups of one head split the work:
+// workgroup x
 // owns the page slice [x * slice, (x + 1) * slice) (slice <= 512, one page
 // per thread), selects within it and attends its own selected pages. They
 // exchange data through a per-(sequence, head) mailbox in the workspace whose
@@ -26,10 +29,10 @@
 // counted each wave waits for its own stores to complete. Waits poll with a
 // bound: a timeout (it needs a member of the group that never starts) skips
 // the rest of the selection and poisons the output with NaN instead of
-// hanging. Progress: workgroup ids put the members of a group next to each
-// other (split fastest) and each XCD starts its workgroups in id order, so the
-// lowest unfinished group always has all its members running while the
-// device holds at least nsplit workgroups. A crossing bin of more than 512
+// hanging. Progress: the members of a group lie within a window of 8 nsplit
+// (<= 256) consecutive workgroup ids and each XCD starts its workgroups in id
+// order, so the lowest unfinished group always has all its members running
+// while the device holds 8 nsplit workgroups (one per CU). A crossing bin of more than 512
 // candidates (degenerate keys) goes through a counted barrier instead and an
 // exact 8-bit radix select on the order-preserving key bits.
 //
@@ -189,7 +192,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
   __shared__ float sh_ml[kDecWaves][G][2];
   __shared__ float sh_mlm[kS * G * 2];  // (max, sum) of every split (merge)
 
-  const int x = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  // workgroup ids interleave up to 8 heads: id = h % HL + HL * (x + nsplit * ...)
+  const int HL = gridDim.x / nsplit;
+  const int h = blockIdx.y * HL + (int)blockIdx.x % HL, x = (int)blockIdx.x / HL, s = blockIdx.z;
+  if (h >= H) return;  // padding of the last head row
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t sh_idx = (int64_t)s * H + h;
   uint32_t* mb = mbox + sh_idx * coop_mailbox_words(nsplit, MP);
@@ -709,7 +715,9 @@ static void launch_decode_gs(const float* escore, const float* pmax, const float
                              const int32_t* table, int64_t nb, int S, int H, int MP, int KB,
                              int slice, int per_wg, uint32_t* mbox, float* part, float* out,
                              float* lse_out, int32_t* sel, int32_t* cnt, hipStream_t st) {
-  hipLaunchKernelGGL((decode_attn_kernel<G, kS>), dim3(kS, H, S), dim3(kDecThreads), 0, st, escore,
+  const int HL = H < 8 ? H : 8;
+  hipLaunchKernelGGL((decode_attn_kernel<G, kS>), dim3(HL * kS, (H + HL - 1) / HL, S), dim3(kDecThreads),
+                     0, st, escore,
                      pmax, zpart, ntiles, lens, budgets, q, kpool, vpool, table, nb, H, MP, KB,
                      slice, per_wg, mbox, part, out, lse_out, sel, cnt);
 }
