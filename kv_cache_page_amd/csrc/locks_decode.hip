@@ -130,15 +130,17 @@ __device__ __forceinline__ bool coop_wait(const uint32_t* c, uint32_t target, ui
 
 // Attention of one wave over list entries e = first, first + step, ... < cnt
 // (pages and block ids in LDS), the next page loading while one is computed.
-// Every step issues its load (past the end it repeats the current page), so
-// no load sits behind a branch and each page waits only for its own loads;
-// two register buffers, unrolled, so both stay in registers.
+// Chunks of up to four pages are unrolled with two register buffers: every
+// load is either followed by its use on the straight path or skipped by a
+// forward exit, so the compiler's memory wait counts stay exact (a loop back
+// edge would make it wait for everything at the top of every iteration).
 template <int G>
 __device__ __forceinline__ void attn_list(AttnAcc<G>& acc, const uint32_t (&qw)[G][16],
                                           const uint16_t* __restrict__ kpool,
                                           const uint16_t* __restrict__ vpool, const int* lpage,
                                           const int* lblk, int first, int step, int cnt, int P,
                                           int len, int H, int h, int64_t num_blocks, int lane) {
+  constexpr int kU = 4;  // pages per unrolled chunk
   // element offset of entry e (0 for an invalid entry, whose page is skipped)
   auto off_of = [&](int e, int& nv) -> int64_t {
     const int pj = lpage[e], blk = lblk[e];
@@ -146,17 +148,28 @@ __device__ __forceinline__ void attn_list(AttnAcc<G>& acc, const uint32_t (&qw)[
     nv = !valid ? 0 : (pj == P - 1) ? len - kPage * (P - 1) : kPage;
     return valid ? ((int64_t)blk * H + h) * (kPage * kHeadDim) : 0;
   };
-  if (first >= cnt) return;
-  int nv0, nv1;
-  PageRegs b0, b1;
-  attn_load_page(b0, kpool, vpool, off_of(first, nv0), lane);
-  for (int e = first; e < cnt; e += 2 * step) {
-    const int e1 = min(e + step, cnt - 1);
-    attn_load_page(b1, kpool, vpool, off_of(e1, nv1), lane);
+  for (int base = first; base < cnt; base += kU * step) {
+    PageRegs b0, b1;
+    int nv0, nv1;
+    attn_load_page(b0, kpool, vpool, off_of(base, nv0), lane);
+    if (base + step >= cnt) {
+      if (nv0 > 0) attn_page<G>(acc, b0, qw, nv0, lane);
+      continue;
+    }
+    attn_load_page(b1, kpool, vpool, off_of(base + step, nv1), lane);
     if (nv0 > 0) attn_page<G>(acc, b0, qw, nv0, lane);
-    if (e + step >= cnt) break;
-    const int e2 = min(e + 2 * step, cnt - 1);
-    attn_load_page(b0, kpool, vpool, off_of(e2, nv0), lane);
+    if (base + 2 * step >= cnt) {
+      if (nv1 > 0) attn_page<G>(acc, b1, qw, nv1, lane);
+      continue;
+    }
+    attn_load_page(b0, kpool, vpool, off_of(base + 2 * step, nv0), lane);
+    if (nv1 > 0) attn_page<G>(acc, b1, qw, nv1, lane);
+    if (base + 3 * step >= cnt) {
+      if (nv0 > 0) attn_page<G>(acc, b0, qw, nv0, lane);
+      continue;
+    }
+    attn_load_page(b1, kpool, vpool, off_of(base + 3 * step, nv1), lane);
+    if (nv0 > 0) attn_page<G>(acc, b0, qw, nv0, lane);
     if (nv1 > 0) attn_page<G>(acc, b1, qw, nv1, lane);
   }
 }
@@ -181,6 +194,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
   __shared__ int att_blk[kDecThreads];
   __shared__ int b_page[kDecThreads];    // this slice's part-B members and their blocks
   __shared__ int b_blk[kDecThreads];
+  __shared__ int cs_page[kDecWaves], cs_blk[kDecWaves];  // the slice's first crossing-bin candidates
+  __shared__ int cs_mem[kDecWaves];                      // ... and whether they are members
   __shared__ int my_blk[kDecThreads];    // block id of slice page tid
   __shared__ uint32_t slice_bits[kDecThreads / 32];  // selected pages of the slice (output)
   __shared__ int sh_cbase[kS + 1];  // crossing-bin candidates before slice y
@@ -401,9 +416,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
 #pragma unroll
         for (int w = 0; w < kDecWaves; ++w) preC += (w < wave) ? sh_wc[w] : 0;
         if (isc) {
-          const int cpos = sh_cbase[x] + preC +
-                           (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(balC >> 32),
-                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)balC, 0u));
+          const int kc = preC + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(balC >> 32),
+                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)balC, 0u));
+          const int cpos = sh_cbase[x] + kc;
+          if (kc < kDecWaves) {  // loaded ahead by wave kc, in case it is a member
+            cs_page[kc] = j;
+            cs_blk[kc] = bk;
+          }
           if (ct <= kFastCand)
             st_coh64(&mb_cand[cpos], (uint64_t)__float_as_uint(key) | ((uint64_t)(j + 1) << 32));
           else {
@@ -425,6 +444,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
   if (tid == 0) { sh_int[4] = 0; sh_int[5] = 0; sh_u[1] = 1u; }
   __syncthreads();
   attn_load_q<G>(qw, reinterpret_cast<const uint16_t*>(sh_q), lane);
+  // the K/V of the slice's first crossing-bin candidates load now (wave k
+  // takes candidate k) and are attended if ranking makes them members
+  const int nc = fast_b ? min(cb_hi - cb_lo, kDecWaves) : 0;
+  PageRegs bspec;
+  if (wave < nc) {
+    const int pj = cs_page[wave], blk = cs_blk[wave];
+    const bool valid = blk >= 0 && blk < num_blocks;  // candidates are full pages
+    attn_load_page(bspec, kpool, vpool, valid ? ((int64_t)blk * H + h) * (kPage * kHeadDim) : 0, lane);
+  }
   if (fast_b && wave == kDecWaves - 1) {
     // lane e < ct holds candidate e; rank by key (lower page first on ties)
     uint64_t v = 0ull;
@@ -446,13 +474,23 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
     }
     const bool mem = got && lane < ct && rank < need;
     const bool mine_m = mem && lane >= cb_lo && lane < cb_hi;
-    const uint64_t bmine = __ballot(mine_m);
-    if (mine_m) {
+    const int kc = lane - cb_lo;  // candidate index within the slice
+    if (kc >= 0 && kc < nc) {
+      const int r = (int)cp - x * slice;
+      cs_mem[kc] = (mine_m && my_blk[r] >= 0 && my_blk[r] < num_blocks) ? 1 : 0;
+    }
+    // members beyond the preloaded ones go to the list
+    const bool listed = mine_m && kc >= nc;
+    const uint64_t bmine = __ballot(listed);
+    if (listed) {
       const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bmine >> 32),
                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)bmine, 0u));
       const int r = (int)cp - x * slice;
       b_page[pos] = (int)cp;
       b_blk[pos] = my_blk[r];
+    }
+    if (mine_m) {
+      const int r = (int)cp - x * slice;
       atomicOr(&slice_bits[r >> 5], 1u << (r & 31));
     }
     const uint64_t bbef = __ballot(mem && lane < cb_lo);
@@ -564,6 +602,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
   __syncthreads();
   const int bbefore = sh_int[5];
   if (fast_b) ok = sh_u[1] != 0u;
+  if (ok && wave < nc && cs_mem[wave]) attn_page<G>(acc, bspec, qw, kPage, lane);
   attn_list<G>(acc, qw, kpool, vpool, b_page, b_blk, wave, kDecWaves, sh_int[4], P, len, H, h,
                num_blocks, lane);
   attn_wave_to_lds<G>(acc, sh_acc[wave], sh_ml[wave], lane);
