@@ -38,6 +38,8 @@ FILE_FLAGS = {
     # matrix-core results stay in ordinary VGPRs (no accumulator-register copies)
     "locks_score_mfma.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
     "locks_build_page.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "locks_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "locks_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

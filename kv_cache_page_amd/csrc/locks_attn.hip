@@ -38,10 +38,10 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_kernel(
   const int nact = (n + per_wg - 1) / per_wg;
   if (x >= nact) return;
 
-  uint32_t qw[G][16];
+  AttnQ qw;
   attn_load_q<G>(qw, q + sh_idx * G * kHeadDim, lane);
-  AttnAcc<G> acc;
-  attn_init<G>(acc);
+  AttnAcc acc;
+  attn_init(acc);
   const int32_t* row = sel + sh_idx * max_budget;
   const int base = x * per_wg + wave * ppw;
   const int mine = clampi(n - base, 0, ppw);
@@ -54,7 +54,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_kernel(
       off = ((int64_t)blk * H + h) * (kPage * kHeadDim);
       nv = (j == P - 1) ? len - kPage * (P - 1) : kPage;
     };
-    attn_wave_pages<G, kAttnChunk>(acc, qw, kpool, vpool, min(kAttnChunk, mine - c0), page_at,
+    attn_wave_pages<kAttnChunk>(acc, qw, kpool, vpool, min(kAttnChunk, mine - c0), page_at,
                                    lane);
   }
   attn_wave_to_lds<G>(acc, sh_acc[wave], sh_ml[wave], lane);

@@ -1,14 +1,26 @@
-// Wave-level flash-decoding core over 16 x 128 bf16 KV pages (gfx950).
+// Wave-level flash-decoding core over 16 x 128 bf16 KV pages on the matrix
+// cores (gfx950).
 //
-// Lane roles inside a wave for one page:
-//   QK: lane = 4 t + c reads 64 contiguous bytes of key row t (dims 32c..),
-//       so the wave reads the 4 KB key page in one coalesced sweep, and forms
-//       q_g . k_t with v_dot2c_f32_bf16 plus one quad butterfly.
-//   PV: lane = 16 ts + dg holds dims 8 dg.. of value rows ts, ts+4, ts+8,
-//       ts+12 (also one coalesced 4 KB sweep) and accumulates p_t v_t.
-// A wave streams its pages with an online softmax (base-2 logits); the block
-// ids of all its pages are read up front and the K/V of the next page load
-// while the current page is computed.
+// Per page, with lane l = 16 b + c (b = l / 16, c = l % 16):
+//   QK: S^T = K q^T on four v_mfma_f32_16x16x32_bf16 (M = the 16 tokens,
+//       N = the G queries padded to 16 with zeros, 32 dims each): lane l
+//       feeds dims 32 kk + 8 b .. +7 of key row c (16 contiguous bytes per
+//       load, so each load covers 64 contiguous bytes of every row) and the
+//       same dims of query c, and receives the logits of query c for tokens
+//       4 b .. 4 b + 3.
+//   softmax: the 4 lanes of column c hold the 16 tokens of query c; the
+//       page max and sum combine them with lane permutes across the four
+//       16-lane rows. The running (m, l) of query c live in those lanes.
+//   PV: O^T = V^T P^T on eight v_mfma_f32_16x16x16_bf16 (M = 16 dims,
+//       N = queries, K = the 16 tokens). P^T, rounded to bf16, is the QK
+//       result in place. Row m of dim tile T stands for dim 8 m + T, so lane
+//       l reads dims 8 c .. 8 c + 7 of value rows 4 b .. 4 b + 3 (16
+//       contiguous bytes each, one whole row per 16 lanes) and takes element
+//       T of each row for tile T. Lane l accumulates dims 32 b .. 32 b + 31
+//       of query c (dim 32 b + 8 i + T in acc[T][i]), so a wave's partial
+//       needs no cross-lane reduction.
+// A wave streams its pages with an online softmax (base-2 logits); the K/V of
+// the next page load while the current page is computed.
 #pragma once
 
 #include "locks_device.h"
@@ -19,42 +31,41 @@ namespace locks {
 // floats, so every query row starts 16-byte aligned.
 constexpr int kPartStride = kHeadDim + 4;
 
-template <int G>
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+
 struct AttnAcc {
-  float m[G], l[G], acc[G][8];
+  float m, l;        // running max (base 2) and sum of query lane % 16
+  float4v acc[8];    // acc[T][i]: dim 32 (lane / 16) + 8 i + T of that query
+};
+
+// Query fragment: dims 32 kk + 8 (lane / 16) .. +7 of query lane % 16 (zero
+// for the padding queries).
+struct AttnQ {
+  uint4 w[4];
 };
 
 struct PageRegs {
   uint4 k[4], v[4];
 };
 
-template <int G>
-__device__ __forceinline__ void attn_init(AttnAcc<G>& a) {
+__device__ __forceinline__ void attn_init(AttnAcc& a) {
+  a.m = -__builtin_inff();
+  a.l = 0.f;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    a.m[g] = -__builtin_inff();
-    a.l[g] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) a.acc[g][e] = 0.f;
-  }
+  for (int t = 0; t < 8; ++t) a.acc[t] = float4v{0.f, 0.f, 0.f, 0.f};
 }
 
-// Query registers for the QK role: dims [32c, 32c+32) of each of the G
-// queries (row-major G x 128 bf16 at qg) as bf16 pairs.
+// Query fragment from G x 128 bf16 queries, row-major at qg.
 template <int G>
-__device__ __forceinline__ void attn_load_q(uint32_t (&qw)[G][16], const uint16_t* qg, int lane) {
-  const int c = lane & 3;
+__device__ __forceinline__ void attn_load_q(AttnQ& q, const uint16_t* qg, int lane) {
+  const int c = lane & 15, b = lane >> 4;
+  const uint4* qp = reinterpret_cast<const uint4*>(qg + (c < G ? c : 0) * kHeadDim + 8 * b);
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const uint4* qp = reinterpret_cast<const uint4*>(qg + g * kHeadDim + 32 * c);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint4 w = qp[e];
-      qw[g][4 * e + 0] = w.x;
-      qw[g][4 * e + 1] = w.y;
-      qw[g][4 * e + 2] = w.z;
-      qw[g][4 * e + 3] = w.w;
-    }
+  for (int kk = 0; kk < 4; ++kk) {
+    const uint4 w = qp[4 * kk];  // dims 32 kk + 8 b ..
+    q.w[kk] = (c < G) ? w : make_uint4(0u, 0u, 0u, 0u);
   }
 }
 
@@ -62,79 +73,61 @@ __device__ __forceinline__ void attn_load_q(uint32_t (&qw)[G][16], const uint16_
 __device__ __forceinline__ void attn_load_page(PageRegs& p, const uint16_t* __restrict__ kpool,
                                                const uint16_t* __restrict__ vpool, int64_t off,
                                                int lane) {
-  const int t = lane >> 2, c = lane & 3, ts = lane >> 4, dg = lane & 15;
+  const int c = lane & 15, b = lane >> 4;
   const uint8_t* kb = reinterpret_cast<const uint8_t*>(kpool + off);
   const uint8_t* vb = reinterpret_cast<const uint8_t*>(vpool + off);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) p.k[e] = *reinterpret_cast<const uint4*>(kb + t * 256 + 64 * c + 16 * e);
+  for (int kk = 0; kk < 4; ++kk) p.k[kk] = *reinterpret_cast<const uint4*>(kb + c * 256 + 64 * kk + 16 * b);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) p.v[e] = *reinterpret_cast<const uint4*>(vb + (ts + 4 * e) * 256 + 16 * dg);
+  for (int i = 0; i < 4; ++i) p.v[i] = *reinterpret_cast<const uint4*>(vb + (4 * b + i) * 256 + 16 * c);
 }
 
-// Online-softmax update with one page whose first `nvalid` tokens are live.
-template <int G>
-__device__ __forceinline__ void attn_page(AttnAcc<G>& a, const PageRegs& p,
-                                          const uint32_t (&qw)[G][16], int nvalid, int lane) {
-  const int t_qk = lane >> 2, ts = lane >> 4;
-  const float qk_scale = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(d)
-  float lg[G];
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int w) {
+  return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w;
+}
+
+// Online-softmax update with one page whose first `nvalid` tokens are live
+// (token 0 always is).
+__device__ __forceinline__ void attn_page(AttnAcc& a, const PageRegs& p, const AttnQ& q, int nvalid,
+                                          int lane) {
+  const int b = lane >> 4;
+  constexpr float kScale = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(d)
+  float4v s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float s = 0.f;
+  for (int kk = 0; kk < 4; ++kk)
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, p.k[kk]),
+                                                 __builtin_bit_cast(bf16x8v, q.w[kk]), s, 0, 0, 0);
+  float lg[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t kk[4] = {p.k[e].x, p.k[e].y, p.k[e].z, p.k[e].w};
+  for (int i = 0; i < 4; ++i) lg[i] = (4 * b + i < nvalid) ? s[i] * kScale : -__builtin_inff();
+  const float pm = xrow_max(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])));
+  const float mn = fmaxf(a.m, pm);  // finite
+  const float alpha = __builtin_amdgcn_exp2f(a.m - mn);
+  float pr[4];
 #pragma unroll
-      for (int f = 0; f < 4; ++f)
-        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, kk[f]),
-                                            __builtin_bit_cast(bf16x2v, qw[g][4 * e + f]), s, false);
-    }
-    lg[g] = quad_sum(s) * qk_scale;
-    if (t_qk >= nvalid) lg[g] = -__builtin_inff();
-  }
-  float pv[G][4];
+  for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(lg[i] - mn);
+  // the sum in fp32; P^T goes to the matrix cores in bf16 (nearest)
+  const float ps = xrow_sum((pr[0] + pr[1]) + (pr[2] + pr[3]));
+  const bf16x2v p01 = {(__bf16)pr[0], (__bf16)pr[1]}, p23 = {(__bf16)pr[2], (__bf16)pr[3]};
+  const uint32_t w01 = __builtin_bit_cast(uint32_t, p01), w23 = __builtin_bit_cast(uint32_t, p23);
+  a.l = a.l * alpha + ps;
+  a.m = mn;
+  const short4v pb = __builtin_bit_cast(short4v, make_uint2(w01, w23));
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float pm = lg[g];
-    pm = fmaxf(pm, shfl_xor(pm, 4));
-    pm = fmaxf(pm, shfl_xor(pm, 8));
-    pm = fmaxf(pm, shfl_xor(pm, 16));
-    pm = fmaxf(pm, shfl_xor(pm, 32));
-    const float mn = fmaxf(a.m[g], pm);  // finite: token 0 of a page is always live
-    const float alpha = __builtin_amdgcn_exp2f(a.m[g] - mn);
-    const float pt = __builtin_amdgcn_exp2f(lg[g] - mn);
-    float ps = pt;
-    ps += shfl_xor(ps, 4);
-    ps += shfl_xor(ps, 8);
-    ps += shfl_xor(ps, 16);
-    ps += shfl_xor(ps, 32);
-    a.l[g] = a.l[g] * alpha + ps;
-    a.m[g] = mn;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) a.acc[g][e] *= alpha;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) pv[g][e] = __shfl(pt, 4 * (ts + 4 * e), 64);
-  }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint32_t vv[4] = {p.v[e].x, p.v[e].y, p.v[e].z, p.v[e].w};
-    float v8[8];
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      v8[2 * f] = bf16_lo(vv[f]);
-      v8[2 * f + 1] = bf16_hi(vv[f]);
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int f = 0; f < 8; ++f) a.acc[g][f] = fmaf(pv[g][e], v8[f], a.acc[g][f]);
+  for (int t = 0; t < 8; ++t) {
+    // element t of value rows 4 b .. 4 b + 3 (dim 8 c + t), as bf16 pairs
+    const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+    const uint32_t a01 = __builtin_amdgcn_perm(word_of(p.v[1], t >> 1), word_of(p.v[0], t >> 1), sel);
+    const uint32_t a23 = __builtin_amdgcn_perm(word_of(p.v[3], t >> 1), word_of(p.v[2], t >> 1), sel);
+    a.acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4v, make_uint2(a01, a23)), pb,
+                                                         a.acc[t] * alpha, 0, 0, 0);
   }
 }
 
 // Streams up to kMax pages. page_at(i, off, nvalid) gives the pool element
 // offset of the wave's i-th page (or off < 0 to skip it) and its live tokens.
-template <int G, int kMax, typename PageAt>
-__device__ __forceinline__ void attn_wave_pages(AttnAcc<G>& a, const uint32_t (&qw)[G][16],
+template <int kMax, typename PageAt>
+__device__ __forceinline__ void attn_wave_pages(AttnAcc& a, const AttnQ& qw,
                                                 const uint16_t* __restrict__ kpool,
                                                 const uint16_t* __restrict__ vpool, int cnt,
                                                 PageAt page_at, int lane) {
@@ -153,40 +146,26 @@ __device__ __forceinline__ void attn_wave_pages(AttnAcc<G>& a, const uint32_t (&
     if (i >= cnt) break;
     if (i + 1 < kMax && i + 1 < cnt && off[i + 1 < kMax ? i + 1 : i] >= 0)
       attn_load_page(nxt, kpool, vpool, off[i + 1 < kMax ? i + 1 : i], lane);
-    if (off[i] >= 0) attn_page<G>(a, cur, qw, nv[i], lane);
+    if (off[i] >= 0) attn_page(a, cur, qw, nv[i], lane);
     cur = nxt;
   }
 }
 
-// Sums the 4 value-row groups of the wave and leaves the wave's partial in
-// LDS: acc[G][128] and (m, l) per query.
+// Leaves the wave's partial in LDS: acc[G][128] and (m, l) per query.
 template <int G>
-__device__ __forceinline__ void attn_wave_to_lds(AttnAcc<G>& a, float (*sh_acc)[kHeadDim],
+__device__ __forceinline__ void attn_wave_to_lds(const AttnAcc& a, float (*sh_acc)[kHeadDim],
                                                  float (*sh_ml)[2], int lane) {
-  const int ts = lane >> 4, dg = lane & 15;
+  const int c = lane & 15, b = lane >> 4;
+  if (c < G) {
 #pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int f = 0; f < 8; ++f) {
-      float v = a.acc[g][f];
-      v += shfl_xor(v, 16);
-      v += shfl_xor(v, 32);
-      a.acc[g][f] = v;
+    for (int i = 0; i < 4; ++i) {
+      float* d = &sh_acc[c][32 * b + 8 * i];
+      *reinterpret_cast<float4*>(d) = make_float4(a.acc[0][i], a.acc[1][i], a.acc[2][i], a.acc[3][i]);
+      *reinterpret_cast<float4*>(d + 4) = make_float4(a.acc[4][i], a.acc[5][i], a.acc[6][i], a.acc[7][i]);
     }
-  if (ts == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      *reinterpret_cast<float4*>(&sh_acc[g][8 * dg]) =
-          make_float4(a.acc[g][0], a.acc[g][1], a.acc[g][2], a.acc[g][3]);
-      *reinterpret_cast<float4*>(&sh_acc[g][8 * dg + 4]) =
-          make_float4(a.acc[g][4], a.acc[g][5], a.acc[g][6], a.acc[g][7]);
-    }
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      sh_ml[g][0] = a.m[g];
-      sh_ml[g][1] = a.l[g];
+    if (b == 0) {
+      sh_ml[c][0] = a.m;
+      sh_ml[c][1] = a.l;
     }
   }
 }

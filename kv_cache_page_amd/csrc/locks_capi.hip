@@ -24,13 +24,13 @@ hipError_t launch_build(int r, const void* kpool, int64_t nb, int H, const int32
                         const int32_t* table, const int32_t* lens, int MP, void* summ,
                         const void* knew, const void* vnew, void* vpool, hipStream_t st);
 bool decode_shape(int MP, int KB, int* per_wg, int* nsplit, int* slice);
-int64_t decode_mailbox_words(int MP, int KB);
-int64_t decode_mailbox_zero_words(int MP, int KB);
+int64_t decode_mailbox_words(int MP, int KB, int G);
+int64_t decode_mailbox_zero_words(int MP, int KB, int G);
 hipError_t launch_decode(int G, const float* escore, const float* pmax, const float2* zpart,
                          int ntiles, const int32_t* lens, const int32_t* budgets, const void* q,
                          const void* kpool, const void* vpool, const int32_t* table, int64_t nb,
                          int S, int H, int MP, int KB, int nsplit, int slice, int per_wg,
-                         uint32_t* mbox, float* part, float* out, float* lse_out, int32_t* sel,
+                         uint32_t* mbox, float* out, float* lse_out, int32_t* sel,
                          int32_t* cnt, hipStream_t st);
 hipError_t launch_append(const void* knew, const void* vnew, void* kpool, void* vpool, int64_t nb,
                          const int32_t* table, const int32_t* lens, int S, int H, int MP,
@@ -65,8 +65,9 @@ size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 // Workspace regions: page scores [S][H][MP][G] (or, for the fused decode
 // step, e_g per page and query); per-page maxima [S][H][MP]; per-tile base-2
 // (max, sum) partials [S][H][tiles][G]; selection keys of the separate select kernel
-// [S][H][MP]; attention partials [S][H][splits][G][kPartStride]; for the fused
-// decode step, the mailboxes of its workgroups [S][H][...].
+// [S][H][MP]; attention partials of the separate attention kernel
+// [S][H][splits][G][kPartStride]; for the fused decode step, the mailboxes of
+// its workgroups [S][H][...] (which also carry its split partials).
 struct Workspace {
   size_t scores, pmax, zpart, keys, parts, mbox, total;
   int nsplit, ntiles;
@@ -82,7 +83,6 @@ Workspace carve(const locks_dims* d, int32_t S, int32_t MP, int32_t KB) {
   w.ntiles = (MP + locks::kScorePagesPerWg - 1) / locks::kScorePagesPerWg;
   int per_f, ns_f, slice_f;
   const bool fused = locks::decode_shape(MP, KB, &per_f, &ns_f, &slice_f);
-  const int part_splits = fused && ns_f > w.nsplit ? ns_f : w.nsplit;
   size_t off = 0;
   w.scores = off;
   off = align_up(off + sh * MP * d->group_size * sizeof(float));
@@ -93,9 +93,10 @@ Workspace carve(const locks_dims* d, int32_t S, int32_t MP, int32_t KB) {
   w.keys = off;
   off = align_up(off + sh * MP * sizeof(uint32_t));
   w.parts = off;
-  off = align_up(off + sh * part_splits * d->group_size * kPartStride * sizeof(float));
+  off = align_up(off + sh * w.nsplit * d->group_size * kPartStride * sizeof(float));
   w.mbox = off;
-  off = align_up(off + (fused ? sh * (size_t)locks::decode_mailbox_words(MP, KB) * sizeof(uint32_t) : 0));
+  off = align_up(off + (fused ? sh * (size_t)locks::decode_mailbox_words(MP, KB, d->group_size) * sizeof(uint32_t)
+                              : 0));
   w.total = off;
   return w;
 }
@@ -309,8 +310,8 @@ locks_status locks_decode_step(const locks_dims* d, const void* q, const void* k
   int per_wg, nsplit, slice;
   const bool fused = locks::decode_shape(MP, KB, &per_wg, &nsplit, &slice);
   const locks::CoopZero coop{fused ? reinterpret_cast<uint32_t*>(ws + w.mbox) : nullptr,
-                             locks::decode_mailbox_words(MP, KB),
-                             (int)locks::decode_mailbox_zero_words(MP, KB)};
+                             locks::decode_mailbox_words(MP, KB, G),
+                             (int)locks::decode_mailbox_zero_words(MP, KB, G)};
   float* pmax = reinterpret_cast<float*>(ws + w.pmax);
   hipError_t he = locks::launch_score(d->rank, G, q, summaries, block_table, seq_lens, scores, nb,
                                       S, H, MP, 0, zpart, completes ? nullptr : k_new,
@@ -319,13 +320,13 @@ locks_status locks_decode_step(const locks_dims* d, const void* q, const void* k
                                       coop, st);
   if (he != hipSuccess) return LOCKS_ERR_HIP;
   // 3. selection + attention + merge
-  float* parts = reinterpret_cast<float*>(ws + w.parts);
   if (fused) {
     return hip_status(locks::launch_decode(
         G, scores, pmax, zpart, w.ntiles, seq_lens, budgets, q, k_pool, v_pool, block_table, nb, S,
-        H, MP, KB, nsplit, slice, per_wg, reinterpret_cast<uint32_t*>(ws + w.mbox), parts, out,
-        lse_out, sel_pages, sel_count, st));
+        H, MP, KB, nsplit, slice, per_wg, reinterpret_cast<uint32_t*>(ws + w.mbox), out, lse_out,
+        sel_pages, sel_count, st));
   }
+  float* parts = reinterpret_cast<float*>(ws + w.parts);
   // long tables or budgets: the separate select and attention kernels
   if (!sel_pages) return LOCKS_ERR_UNSUPPORTED;
   he = locks::launch_select(G, scores, seq_lens, budgets, sel_pages, sel_count,

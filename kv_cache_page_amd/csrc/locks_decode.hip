@@ -22,11 +22,12 @@
 //   2. the crossing bin's candidates (key, page + 1) when only part of it is
 //      taken: every workgroup ranks them (part B) while its part-A pages are
 //      already being attended, then attends its slice's part-B members;
-//   3. the workgroup partials: the last workgroup to arrive (an agent-scope
-//      atomic counter) merges them in split order.
+//   3. the workgroup partials, normalised (o = acc / l, lse = m + log2 l) and
+//      tagged per element: the workgroup of the last split polls them and
+//      merges them in split order.
 // Mailbox accesses are agent-scope relaxed atomics (coherent across the XCDs
-// without cache write-back or invalidation); before a workgroup's arrival is
-// counted each wave waits for its own stores to complete. Waits poll with a
+// without cache write-back or invalidation); a tagged 64-bit slot is written
+// and read whole, so its value is valid once its tag is. Waits poll with a
 // bound: a timeout (it needs a member of the group that never starts) skips
 // the rest of the selection and poisons the output with NaN instead of
 // hanging. Progress: the members of a group lie within a window of 8 nsplit
@@ -73,15 +74,22 @@ constexpr int kFastCand = kDecThreads;  // crossing-bin candidates exchanged thr
 constexpr int kSpinMax = 1 << 22;   // polls of 64 clocks: about 0.1 s
 static_assert(kBins == kDecThreads, "one histogram bin per thread");
 
-// Mailbox words of one (sequence, KV head). Zeroed by the score kernel: the
-// counters [kCoopCounters][kCoopCtrWords], slice histograms [nsplit][512],
-// part-A counts [32] and fast candidates [512] (64-bit). Not zeroed: the
-// large-bin candidates (key bits, page) [MP] each.
-__host__ __device__ inline int64_t coop_zero_words(int nsplit) {
+// Mailbox words of one (sequence, KV head) and G queries per head. Zeroed by
+// the score kernel: the counters [kCoopCounters][kCoopCtrWords], slice
+// histograms [nsplit][512], part-A counts [32], fast candidates [512] and the
+// split partials [nsplit][G][128] and their log-sums [nsplit][G] (all three
+// 64-bit). Not zeroed: the large-bin candidates (key bits, page) [MP] each.
+__host__ __device__ inline int64_t coop_part_offset(int nsplit) {
   return (int64_t)kCoopCounters * kCoopCtrWords + (int64_t)nsplit * kBins + kDecMaxSplits + 2 * kFastCand;
 }
-__host__ __device__ inline int64_t coop_mailbox_words(int nsplit, int MP) {
-  return (coop_zero_words(nsplit) + 2LL * MP + 31) / 32 * 32;
+__host__ __device__ inline int64_t coop_zero_words(int nsplit, int G) {
+  return coop_part_offset(nsplit) + 2LL * nsplit * G * (kHeadDim + 1);
+}
+__host__ __device__ inline int64_t coop_mailbox_words(int nsplit, int G, int MP) {
+  return (coop_zero_words(nsplit, G) + 2LL * MP + 31) / 32 * 32;
+}
+__device__ __forceinline__ uint64_t* mb_part(uint32_t* mb, int nsplit) {
+  return reinterpret_cast<uint64_t*>(mb + coop_part_offset(nsplit));
 }
 
 // ---- coherent mailbox accesses (agent-scope relaxed atomics)
@@ -134,8 +142,7 @@ __device__ __forceinline__ bool coop_wait(const uint32_t* c, uint32_t target, ui
 // load is either followed by its use on the straight path or skipped by a
 // forward exit, so the compiler's memory wait counts stay exact (a loop back
 // edge would make it wait for everything at the top of every iteration).
-template <int G>
-__device__ __forceinline__ void attn_list(AttnAcc<G>& acc, const uint32_t (&qw)[G][16],
+__device__ __forceinline__ void attn_list(AttnAcc& acc, const AttnQ& qw,
                                           const uint16_t* __restrict__ kpool,
                                           const uint16_t* __restrict__ vpool, const int* lpage,
                                           const int* lblk, int first, int step, int cnt, int P,
@@ -153,24 +160,24 @@ __device__ __forceinline__ void attn_list(AttnAcc<G>& acc, const uint32_t (&qw)[
     int nv0, nv1;
     attn_load_page(b0, kpool, vpool, off_of(base, nv0), lane);
     if (base + step >= cnt) {
-      if (nv0 > 0) attn_page<G>(acc, b0, qw, nv0, lane);
+      if (nv0 > 0) attn_page(acc, b0, qw, nv0, lane);
       continue;
     }
     attn_load_page(b1, kpool, vpool, off_of(base + step, nv1), lane);
-    if (nv0 > 0) attn_page<G>(acc, b0, qw, nv0, lane);
+    if (nv0 > 0) attn_page(acc, b0, qw, nv0, lane);
     if (base + 2 * step >= cnt) {
-      if (nv1 > 0) attn_page<G>(acc, b1, qw, nv1, lane);
+      if (nv1 > 0) attn_page(acc, b1, qw, nv1, lane);
       continue;
     }
     attn_load_page(b0, kpool, vpool, off_of(base + 2 * step, nv0), lane);
-    if (nv1 > 0) attn_page<G>(acc, b1, qw, nv1, lane);
+    if (nv1 > 0) attn_page(acc, b1, qw, nv1, lane);
     if (base + 3 * step >= cnt) {
-      if (nv0 > 0) attn_page<G>(acc, b0, qw, nv0, lane);
+      if (nv0 > 0) attn_page(acc, b0, qw, nv0, lane);
       continue;
     }
     attn_load_page(b1, kpool, vpool, off_of(base + 3 * step, nv1), lane);
-    if (nv0 > 0) attn_page<G>(acc, b0, qw, nv0, lane);
-    if (nv1 > 0) attn_page<G>(acc, b1, qw, nv1, lane);
+    if (nv0 > 0) attn_page(acc, b0, qw, nv0, lane);
+    if (nv1 > 0) attn_page(acc, b1, qw, nv1, lane);
   }
 }
 
@@ -181,7 +188,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
     const int32_t* __restrict__ budgets, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ kpool, const uint16_t* __restrict__ vpool,
     const int32_t* __restrict__ table, int64_t num_blocks, int H, int MP, int max_budget,
-    int slice, int per_wg, uint32_t* __restrict__ mbox, float* __restrict__ part,
+    int slice, int per_wg, uint32_t* __restrict__ mbox,
     float* __restrict__ out, float* __restrict__ lse_out, int32_t* __restrict__ sel_pages,
     int32_t* __restrict__ sel_count) {
   constexpr int nsplit = kS;
@@ -205,7 +212,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
   __shared__ uint32_t sh_u[2];
   __shared__ float sh_acc[kDecWaves][G][kHeadDim];
   __shared__ float sh_ml[kDecWaves][G][2];
-  __shared__ float sh_mlm[kS * G * 2];  // (max, sum) of every split (merge)
 
   // workgroup ids interleave up to 8 heads: id = h % HL + HL * (x + nsplit * ...)
   const int HL = gridDim.x / nsplit;
@@ -213,12 +219,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
   if (h >= H) return;  // padding of the last head row
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t sh_idx = (int64_t)s * H + h;
-  uint32_t* mb = mbox + sh_idx * coop_mailbox_words(nsplit, MP);
+  uint32_t* mb = mbox + sh_idx * coop_mailbox_words(nsplit, G, MP);
   uint32_t* ctr = mb;                                            // [kCoopCounters][kCoopCtrWords]
   uint32_t* mb_hist = ctr + kCoopCounters * kCoopCtrWords;       // [nsplit][512], count + 1
   uint32_t* mb_acnt = mb_hist + nsplit * kBins;                  // [32], part-A count + 1
   uint64_t* mb_cand = reinterpret_cast<uint64_t*>(mb_acnt + kDecMaxSplits);  // [512]: key | (page + 1) << 32
-  uint32_t* mb_bkey = reinterpret_cast<uint32_t*>(mb_cand + kFastCand);     // [MP] (large bin)
+  uint32_t* mb_bkey = mb + coop_zero_words(nsplit, G);                       // [MP] (large bin)
   uint32_t* mb_bpage = mb_bkey + MP;                                          // [MP] (large bin)
 
   // ---- every independent load first: length, budget, the tile Z partials,
@@ -261,9 +267,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
   int tbin = -1, need = 0, ct = 0;
   bool part_bin = false;
 
-  uint32_t qw[G][16];
-  AttnAcc<G> acc;
-  attn_init<G>(acc);
+  AttnQ qw;
+  AttnAcc acc;
+  attn_init(acc);
 
   if (sel_all) {
     // positions = pages: workgroup x attends [x * per_wg, (x + 1) * per_wg)
@@ -501,7 +507,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
     }
   }
   // ---- attention over part A (or the positions)
-  attn_list<G>(acc, qw, kpool, vpool, att_page, att_blk, wave, kDecWaves, natt, P, len, H, h,
+  attn_list(acc, qw, kpool, vpool, att_page, att_blk, wave, kDecWaves, natt, P, len, H, h,
                num_blocks, lane);
   if (!sel_all && ok && part_bin && !fast_b) {
     // membership `mem` of candidate t (page `page`), called by every thread
@@ -602,10 +608,38 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
   __syncthreads();
   const int bbefore = sh_int[5];
   if (fast_b) ok = sh_u[1] != 0u;
-  if (ok && wave < nc && cs_mem[wave]) attn_page<G>(acc, bspec, qw, kPage, lane);
-  attn_list<G>(acc, qw, kpool, vpool, b_page, b_blk, wave, kDecWaves, sh_int[4], P, len, H, h,
+  if (ok && wave < nc && cs_mem[wave]) attn_page(acc, bspec, qw, kPage, lane);
+  attn_list(acc, qw, kpool, vpool, b_page, b_blk, wave, kDecWaves, sh_int[4], P, len, H, h,
                num_blocks, lane);
   attn_wave_to_lds<G>(acc, sh_acc[wave], sh_ml[wave], lane);
+  __syncthreads();
+
+  // ---- the workgroup's partial, normalised: thread (g, d) combines the 8
+  // wave partials into o = acc / l and lse = m + log2 l, published as tagged
+  // words (value | 1 << 32) that the merging workgroup polls
+  uint64_t* mb_po = mb_part(mb, nsplit);            // [nsplit][G][128]
+  uint64_t* mb_pl = mb_po + nsplit * G * kHeadDim;  // [nsplit][G]
+  if (tid < G * kHeadDim) {
+    const int g = tid / kHeadDim, d = tid % kHeadDim;
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, sh_ml[w][g][0]);
+    float a = 0.f, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float f = (M == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(sh_ml[w][g][0] - M);
+      a += f * sh_acc[w][g][d];
+      L += f * sh_ml[w][g][1];
+    }
+    float o = L > 0.f ? a / L : 0.f;
+    if (!ok) o = __builtin_nanf("");
+    constexpr uint64_t kTag = 1ull << 32;
+    st_coh64(&mb_po[(x * G + g) * kHeadDim + d], kTag | __float_as_uint(o));
+    if (d == 0) {
+      const float lse = L > 0.f ? M + __builtin_amdgcn_logf(L) : -__builtin_inff();
+      st_coh64(&mb_pl[x * G + g], kTag | __float_as_uint(lse));
+    }
+  }
 
   // ---- selection output: every workgroup writes its slice's selected pages
   // at their places in the ascending list
@@ -652,71 +686,46 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
       if (tid == 0) sel_count[sh_idx] = n;
     }
   }
-  __syncthreads();
 
-  // ---- the workgroup's partial (thread (g, d) combines the 8 wave partials),
-  // published; the last workgroup to arrive merges the nsplit partials in
+  // ---- the last split's workgroup merges: thread (g, d) waits for the
+  // nsplit partials of its element (bounded) and combines them in split order
+  if (x != nsplit - 1 || tid >= G * kHeadDim) return;
+  const int g = tid / kHeadDim, d = tid % kHeadDim;
+  uint64_t po[kS], pl[kS];
+  bool got = false;
+  for (int it = 0; it < kSpinMax; ++it) {
+    uint32_t miss = 0u;
+#pragma unroll
+    for (int y = 0; y < kS; ++y) {
+      po[y] = ld_coh64(&mb_po[(y * G + g) * kHeadDim + d]);
+      pl[y] = ld_coh64(&mb_pl[y * G + g]);
+    }
+#pragma unroll
+    for (int y = 0; y < kS; ++y) miss |= (uint32_t)((po[y] >> 32) == 0ull) | (uint32_t)((pl[y] >> 32) == 0ull);
+    if (miss == 0u) {
+      got = true;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  // one common maximum, then every split's weight 2^(lse_y - max), summed in
   // split order
-  float* parts = part + sh_idx * nsplit * G * kPartStride;
-  if (tid < G * kHeadDim) {
-    const int g = tid / kHeadDim, d = tid % kHeadDim;
-    float M = -__builtin_inff();
+  float M = -__builtin_inff();
 #pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, sh_ml[w][g][0]);
-    float a = 0.f, L = 0.f;
+  for (int y = 0; y < kS; ++y) M = fmaxf(M, __uint_as_float((uint32_t)pl[y]));
+  float W = 0.f, a = 0.f;
 #pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) {
-      const float f = (M == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(sh_ml[w][g][0] - M);
-      a += f * sh_acc[w][g][d];
-      L += f * sh_ml[w][g][1];
-    }
-    if (!ok) a = __builtin_nanf("");
-    float* p = parts + (x * G + g) * kPartStride;
-    st_cohf(p + d, a);
-    if (d == 0) {
-      st_cohf(p + kHeadDim, M);
-      st_cohf(p + kHeadDim + 1, L);
-    }
+  for (int y = 0; y < kS; ++y) {
+    const float ly = __uint_as_float((uint32_t)pl[y]);
+    const float f = (ly == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(ly - M);
+    W += f;
+    a = fmaf(__uint_as_float((uint32_t)po[y]), f, a);
   }
-  const uint32_t arrived = coop_arrive(&ctr[2 * kCoopCtrWords], &sh_u[0]);
-  if (arrived != (uint32_t)(nsplit - 1)) return;  // not the last: done
-  float pa[kS];
-  if (tid < G * kHeadDim) {
-    const int g = tid / kHeadDim, d = tid % kHeadDim;
-#pragma unroll
-    for (int y = 0; y < kS; ++y) pa[y] = ld_cohf(parts + (y * G + g) * kPartStride + d);
-  }
-  if (tid < 2 * kS * G) {  // (max, sum) of split y, query g
-    const int y = tid / (2 * G), g = (tid / 2) % G;
-    sh_mlm[tid] = ld_cohf(parts + (y * G + g) * kPartStride + kHeadDim + (tid & 1));
-  }
-  __syncthreads();
-  if (tid < G * kHeadDim) {
-    const int g = tid / kHeadDim, d = tid % kHeadDim;
-    const float* mls = sh_mlm;  // [kS][G][2]
-    float pm[kS], pl[kS];
-#pragma unroll
-    for (int y = 0; y < kS; ++y) {
-      pm[y] = mls[(y * G + g) * 2];
-      pl[y] = mls[(y * G + g) * 2 + 1];
-    }
-    // one common maximum, then every split's weight independently, summed in
-    // split order
-    float M = -__builtin_inff();
-#pragma unroll
-    for (int y = 0; y < kS; ++y) M = fmaxf(M, pm[y]);
-    float L = 0.f, a = 0.f;
-#pragma unroll
-    for (int y = 0; y < kS; ++y) {
-      const float f = (pm[y] == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(pm[y] - M);
-      L = fmaf(pl[y], f, L);
-      a = fmaf(pa[y], f, a);
-    }
-    const bool some = L > 0.f;
-    out[(sh_idx * G + g) * kHeadDim + d] = some ? a / L : (a == a ? 0.f : a);
-    if (lse_out && d == 0)
-      lse_out[sh_idx * G + g] = some ? (M + __builtin_amdgcn_logf(L)) * kLn2 : -__builtin_inff();
-  }
+  if (!got) a = __builtin_nanf("");
+  const bool some = W > 0.f;
+  out[(sh_idx * G + g) * kHeadDim + d] = some ? a / W : (a == a ? 0.f : a);
+  if (lse_out && d == 0)
+    lse_out[sh_idx * G + g] = some ? (M + __builtin_amdgcn_logf(W)) * kLn2 : -__builtin_inff();
 }
 
 // Launch shape for a table of MP pages and a budget of KB pages: false when
@@ -736,15 +745,15 @@ bool decode_shape(int MP, int KB, int* per_wg, int* nsplit, int* slice) {
 
 int decode_max_splits() { return kDecMaxSplits; }
 
-int64_t decode_mailbox_words(int MP, int KB) {
+int64_t decode_mailbox_words(int MP, int KB, int G) {
   int pw, ns, sl;
   if (!decode_shape(MP, KB, &pw, &ns, &sl)) return 0;
-  return coop_mailbox_words(ns, MP);
+  return coop_mailbox_words(ns, G, MP);
 }
-int64_t decode_mailbox_zero_words(int MP, int KB) {
+int64_t decode_mailbox_zero_words(int MP, int KB, int G) {
   int pw, ns, sl;
   if (!decode_shape(MP, KB, &pw, &ns, &sl)) return 0;
-  return coop_zero_words(ns);
+  return coop_zero_words(ns, G);
 }
 
 template <int G, int kS>
@@ -752,13 +761,13 @@ static void launch_decode_gs(const float* escore, const float* pmax, const float
                              int ntiles, const int32_t* lens, const int32_t* budgets,
                              const uint16_t* q, const uint16_t* kpool, const uint16_t* vpool,
                              const int32_t* table, int64_t nb, int S, int H, int MP, int KB,
-                             int slice, int per_wg, uint32_t* mbox, float* part, float* out,
+                             int slice, int per_wg, uint32_t* mbox, float* out,
                              float* lse_out, int32_t* sel, int32_t* cnt, hipStream_t st) {
   const int HL = H < 8 ? H : 8;
   hipLaunchKernelGGL((decode_attn_kernel<G, kS>), dim3(HL * kS, (H + HL - 1) / HL, S), dim3(kDecThreads),
                      0, st, escore,
                      pmax, zpart, ntiles, lens, budgets, q, kpool, vpool, table, nb, H, MP, KB,
-                     slice, per_wg, mbox, part, out, lse_out, sel, cnt);
+                     slice, per_wg, mbox, out, lse_out, sel, cnt);
 }
 
 template <int G>
@@ -766,10 +775,10 @@ static void launch_decode_g(int nsplit, const float* escore, const float* pmax, 
                             int ntiles, const int32_t* lens, const int32_t* budgets,
                             const uint16_t* q, const uint16_t* kpool, const uint16_t* vpool,
                             const int32_t* table, int64_t nb, int S, int H, int MP, int KB,
-                            int slice, int per_wg, uint32_t* mbox, float* part, float* out,
+                            int slice, int per_wg, uint32_t* mbox, float* out,
                             float* lse_out, int32_t* sel, int32_t* cnt, hipStream_t st) {
 #define LOCKS_ARGS escore, pmax, zpart, ntiles, lens, budgets, q, kpool, vpool, table, nb, S, H, MP, \
-                   KB, slice, per_wg, mbox, part, out, lse_out, sel, cnt, st
+                   KB, slice, per_wg, mbox, out, lse_out, sel, cnt, st
   if (nsplit <= 8)
     launch_decode_gs<G, 8>(LOCKS_ARGS);
   else if (nsplit <= 16)
@@ -783,13 +792,13 @@ hipError_t launch_decode(int G, const float* escore, const float* pmax, const fl
                          int ntiles, const int32_t* lens, const int32_t* budgets, const void* q,
                          const void* kpool, const void* vpool, const int32_t* table, int64_t nb,
                          int S, int H, int MP, int KB, int nsplit, int slice, int per_wg,
-                         uint32_t* mbox, float* part, float* out, float* lse_out, int32_t* sel,
+                         uint32_t* mbox, float* out, float* lse_out, int32_t* sel,
                          int32_t* cnt, hipStream_t st) {
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint16_t* kk = static_cast<const uint16_t*>(kpool);
   const uint16_t* vv = static_cast<const uint16_t*>(vpool);
 #define LOCKS_ARGS nsplit, escore, pmax, zpart, ntiles, lens, budgets, qq, kk, vv, table, nb, S, H, \
-                   MP, KB, slice, per_wg, mbox, part, out, lse_out, sel, cnt, st
+                   MP, KB, slice, per_wg, mbox, out, lse_out, sel, cnt, st
   switch (G) {
     case 1: launch_decode_g<1>(LOCKS_ARGS); break;
     case 2: launch_decode_g<2>(LOCKS_ARGS); break;

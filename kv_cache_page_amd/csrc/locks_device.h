@@ -119,6 +119,25 @@ __device__ __forceinline__ float wave_allsum(float v) {
   return v + __shfl_xor(v, 32, 64);
 }
 
+// Max / sum over the 4 lanes l, l ^ 16, l ^ 32, l ^ 48 (same column of the
+// four 16-lane rows); the result is bit-identical in all four.
+__device__ __forceinline__ float xrow_max(float v) {
+  const uint32_t x = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t y = __float_as_uint(m);
+  const auto b = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float xrow_sum(float v) {
+  const uint32_t x = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  const float m = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t y = __float_as_uint(m);
+  const auto b = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Order-preserving map of a float onto uint32 (larger float -> larger uint).
 __device__ __forceinline__ uint32_t float_to_ordered(float f) {
   uint32_t b = __float_as_uint(f);

@@ -74,25 +74,6 @@ __device__ __forceinline__ void coef4(uint32_t w, uint32_t& h0, uint32_t& h1) {
   h1 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, y, 0x04030402u)) + k);
 }
 
-// Max / sum over the 4 lanes l, l ^ 16, l ^ 32, l ^ 48 (same column of the
-// four 16-lane rows); the result is bit-identical in all four.
-__device__ __forceinline__ float xrow_max(float v) {
-  const uint32_t x = __float_as_uint(v);
-  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const uint32_t y = __float_as_uint(m);
-  const auto b = __builtin_amdgcn_permlane32_swap(y, y, false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float xrow_sum(float v) {
-  const uint32_t x = __float_as_uint(v);
-  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-  const float m = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const uint32_t y = __float_as_uint(m);
-  const auto b = __builtin_amdgcn_permlane32_swap(y, y, false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 // 8 int8 codes (two words, byte order) -> (c + 128) 2^-24 as fp16
 // denormals, in the order [b0, b2, b1, b3, b4, b6, b5, b7].
 __device__ __forceinline__ half8 byte8(uint32_t w0, uint32_t w1) {
