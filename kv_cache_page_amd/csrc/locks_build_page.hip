@@ -56,6 +56,37 @@ __device__ __forceinline__ void load4_perm(double (&v)[4], const double* p) {
   for (int e = 0; e < 4; ++e) v[e] = t[e ^ EM];
 }
 
+// Wave-wide max / sum of a double: DPP inside rows of 16, then the rows
+// pairwise by lane permutes (rows 0-1 and 2-3, then the two halves). Each
+// permute hands both lanes of a pair the same (lower row, upper row) values,
+// so every lane ends with the same bits.
+template <int C>
+__device__ __forceinline__ double dpp_d(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, C, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), C, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ double join_d(uint32_t lo, uint32_t hi) {
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+// (lower, upper) of the row pair (xor 16) or half pair (xor 32) holding v
+template <bool kHalves>
+__device__ __forceinline__ void pair_d(double v, double& a, double& b) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+  if (kHalves) {
+    const auto l = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto h = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    a = join_d(l[0], h[0]);
+    b = join_d(l[1], h[1]);
+  } else {
+    const auto l = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto h = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    a = join_d(l[0], h[0]);
+    b = join_d(l[1], h[1]);
+  }
+}
 // One round of the 64-lane cyclic Jacobi: the 8 pairs (p, p xor M) at once.
 // Lane (i, qc) holds b[e] = A[i][i ^ x], x = 4 qc + e, and U likewise.
 // Column j = i ^ x turns with the rotation of row j's pair: b[x] <- c_j b[x]
@@ -100,41 +131,25 @@ __device__ __forceinline__ void jacobi64_round(double (&b)[4], double (&ub)[4], 
   }
 }
 
-// Wave-wide max of a double: DPP inside rows of 16, then xor 16 and xor 32.
-template <int C>
-__device__ __forceinline__ double dpp_d(double v) {
-  const uint64_t u = (uint64_t)__double_as_longlong(v);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, C, 0xF, 0xF, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), C, 0xF, 0xF, false);
-  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
-}
 __device__ __forceinline__ double wave_max_d(double v) {
   v = fmax(v, dpp_d<0xB1>(v));   // xor 1
   v = fmax(v, dpp_d<0x4E>(v));   // xor 2
   v = fmax(v, dpp_d<0x141>(v));  // half-row mirror: quads 0/1, 2/3
   v = fmax(v, dpp_d<0x140>(v));  // row mirror: halves of the row
-  {
-    const uint64_t u = (uint64_t)__double_as_longlong(v);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)u, 0x401F);  // xor 16
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)(u >> 32), 0x401F);
-    v = fmax(v, __longlong_as_double((long long)(((uint64_t)hi << 32) | lo)));
-  }
-  return fmax(v, __shfl_xor(v, 32, 64));
+  double a, b;
+  pair_d<false>(v, a, b);
+  pair_d<true>(fmax(a, b), a, b);
+  return fmax(a, b);
 }
-// Wave-wide sum in the same pairing order (symmetric, so every lane gets the
-// same bits).
 __device__ __forceinline__ double wave_sum_d(double v) {
   v += dpp_d<0xB1>(v);
   v += dpp_d<0x4E>(v);
   v += dpp_d<0x141>(v);
   v += dpp_d<0x140>(v);
-  {
-    const uint64_t u = (uint64_t)__double_as_longlong(v);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)u, 0x401F);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)(u >> 32), 0x401F);
-    v += __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
-  }
-  return v + __shfl_xor(v, 32, 64);
+  double a, b;
+  pair_d<false>(v, a, b);
+  pair_d<true>(a + b, a, b);
+  return a + b;
 }
 __device__ __forceinline__ double readlane_d(double v, int src) {
   const uint64_t u = (uint64_t)__double_as_longlong(v);
@@ -239,9 +254,11 @@ __global__ __launch_bounds__(64) void build_page_kernel(
     const int col = lane & 15, rg = lane >> 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      double v = mk[i];
-#pragma unroll
-      for (int m = 1; m < 16; m <<= 1) v += __shfl_xor(v, m, 64);
+      double v = mk[i];  // row sum inside the 16-lane row
+      v += dpp_d<0xB1>(v);
+      v += dpp_d<0x4E>(v);
+      v += dpp_d<0x141>(v);
+      v += dpp_d<0x140>(v);
       if (col == 0) rm_s[rg + 4 * i] = v * (1.0 / kPage);
     }
     __syncthreads();
@@ -336,7 +353,7 @@ __global__ __launch_bounds__(64) void build_page_kernel(
   // ---- basis columns: v_k = D^T u_k / sigma_k, canonical sign, int4 codes
   const int wq = lane >> 2, pq = lane & 3;           // word of 8 dims, pair inside it
   const int byte_of_pair = (pq == 0) ? 0 : (pq == 1) ? 2 : (pq == 2) ? 1 : 3;
-#pragma unroll 2
+#pragma unroll
   for (int k = 0; k < R; ++k) {
     const int ck = perm_s[k] & (kPage - 1);
     const double lk = lam_s[ck];
@@ -392,9 +409,7 @@ __global__ __launch_bounds__(64) void build_page_kernel(
 
   // ---- centroid: one scale for the page
   {
-    double amax = fmax(fabs(mu[0]), fabs(mu[1]));
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) amax = fmax(amax, __shfl_xor(amax, m, 64));
+    const double amax = wave_max_d(fmax(fabs(mu[0]), fabs(mu[1])));
     const uint16_t sbits = amax > 0.0 ? fp16_scale_bits(amax, 127.f) : (uint16_t)0;
     const float scale = (float)__builtin_bit_cast(_Float16, sbits);
     const uint32_t lo = (uint32_t)(quant_code(mu[0], scale, 127) & 0xFF);
