@@ -39,15 +39,16 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "decode-step µs and achieved HBM GB/s (summary+selected KV) at 128K ctx, 8 KV heads"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "score_kernel_ctx128k_counters.txt")
 SCORE_SRC = os.path.join(ROOT, "kv_cache_page_amd", "csrc", "locks_score_mfma.hip")
-SCORE_HDR = os.path.join(ROOT, "kv_cache_page_amd", "csrc", "locks_device.h")
+SCORE_HDRS = [os.path.join(ROOT, "kv_cache_page_amd", "csrc", f)
+              for f in ("locks_score_tile.h", "locks_device.h")]
 
 
 def score_kernel_fingerprint():
     """sha256 over what decides the score kernel's machine code: its source,
-    the header it includes and its compile flags."""
+    the headers it includes and its compile flags."""
     from kv_cache_page_amd import build_lib
     h = hashlib.sha256()
-    for path in (SCORE_SRC, SCORE_HDR):
+    for path in [SCORE_SRC] + SCORE_HDRS:
         h.update(open(path, "rb").read())
     flags = build_lib.FLAGS + build_lib.FILE_FLAGS.get(os.path.basename(SCORE_SRC), [])
     h.update(" ".join(flags).encode())

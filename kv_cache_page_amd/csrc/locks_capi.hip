@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include "locks_device.h"
+#include "locks_step.h"
 
 namespace locks {
 hipError_t launch_score(int r, int G, const void* q, const void* summ, const int32_t* table,
@@ -26,12 +27,8 @@ hipError_t launch_build(int r, const void* kpool, int64_t nb, int H, const int32
 bool decode_shape(int MP, int KB, int* per_wg, int* nsplit, int* slice);
 int64_t decode_mailbox_words(int MP, int KB, int G);
 int64_t decode_mailbox_zero_words(int MP, int KB, int G);
-hipError_t launch_decode(int G, const float* escore, const float* pmax, const float2* zpart,
-                         int ntiles, const int32_t* lens, const int32_t* budgets, const void* q,
-                         const void* kpool, const void* vpool, const int32_t* table, int64_t nb,
-                         int S, int H, int MP, int KB, int nsplit, int slice, int per_wg,
-                         uint32_t* mbox, float* out, float* lse_out, int32_t* sel,
-                         int32_t* cnt, hipStream_t st);
+hipError_t launch_decode(int G, const StepLaunch& a, hipStream_t st);
+bool decode_step_fuses_score(int r);
 hipError_t launch_append(const void* knew, const void* vnew, void* kpool, void* vpool, int64_t nb,
                          const int32_t* table, const int32_t* lens, int S, int H, int MP,
                          hipStream_t st);
@@ -304,7 +301,9 @@ locks_status locks_decode_step(const locks_dims* d, const void* q, const void* k
     if (he != hipSuccess) return LOCKS_ERR_HIP;
   }
   // 2. scores of all full pages and Z partials (and the append when no page
-  //    completes)
+  //    completes), 3. selection + attention + merge: one launch for ranks 4,
+  //    8 and 16 (score workgroups first), else a score launch and then the
+  //    selection + attention launch
   float* scores = reinterpret_cast<float*>(ws + w.scores);
   float2* zpart = reinterpret_cast<float2*>(ws + w.zpart);
   int per_wg, nsplit, slice;
@@ -313,19 +312,49 @@ locks_status locks_decode_step(const locks_dims* d, const void* q, const void* k
                              locks::decode_mailbox_words(MP, KB, G),
                              (int)locks::decode_mailbox_zero_words(MP, KB, G)};
   float* pmax = reinterpret_cast<float*>(ws + w.pmax);
-  hipError_t he = locks::launch_score(d->rank, G, q, summaries, block_table, seq_lens, scores, nb,
-                                      S, H, MP, 0, zpart, completes ? nullptr : k_new,
-                                      completes ? nullptr : v_new, k_pool, v_pool,
-                                      fused ? pmax : nullptr,
-                                      coop, st);
-  if (he != hipSuccess) return LOCKS_ERR_HIP;
-  // 3. selection + attention + merge
+  const void* kn = completes ? nullptr : k_new;
+  const void* vn = completes ? nullptr : v_new;
   if (fused) {
-    return hip_status(locks::launch_decode(
-        G, scores, pmax, zpart, w.ntiles, seq_lens, budgets, q, k_pool, v_pool, block_table, nb, S,
-        H, MP, KB, nsplit, slice, per_wg, reinterpret_cast<uint32_t*>(ws + w.mbox), out, lse_out,
-        sel_pages, sel_count, st));
+    locks::StepLaunch a{};
+    a.escore = scores;
+    a.pmax = pmax;
+    a.zpart = zpart;
+    a.ntiles = w.ntiles;
+    a.lens = seq_lens;
+    a.budgets = budgets;
+    a.q = q;
+    a.kpool = k_pool;
+    a.vpool = v_pool;
+    a.table = block_table;
+    a.nb = nb;
+    a.S = S;
+    a.H = H;
+    a.MP = MP;
+    a.KB = KB;
+    a.nsplit = nsplit;
+    a.slice = slice;
+    a.per_wg = per_wg;
+    a.mbox = reinterpret_cast<uint32_t*>(ws + w.mbox);
+    a.out = out;
+    a.lse_out = lse_out;
+    a.sel = sel_pages;
+    a.cnt = sel_count;
+    a.summ = summaries;
+    a.knew = kn;
+    a.vnew = vn;
+    a.coop = coop;
+    a.r = locks::decode_step_fuses_score(d->rank) ? d->rank : 0;
+    if (a.r == 0) {
+      hipError_t he = locks::launch_score(d->rank, G, q, summaries, block_table, seq_lens, scores, nb,
+                                          S, H, MP, 0, zpart, kn, vn, k_pool, v_pool, pmax, coop, st);
+      if (he != hipSuccess) return LOCKS_ERR_HIP;
+    }
+    return hip_status(locks::launch_decode(G, a, st));
   }
+  hipError_t he = locks::launch_score(d->rank, G, q, summaries, block_table, seq_lens, scores, nb,
+                                      S, H, MP, 0, zpart, kn, vn, k_pool, v_pool, nullptr,
+                                      locks::CoopZero{}, st);
+  if (he != hipSuccess) return LOCKS_ERR_HIP;
   float* parts = reinterpret_cast<float*>(ws + w.parts);
   // long tables or budgets: the separate select and attention kernels
   if (!sel_pages) return LOCKS_ERR_UNSUPPORTED;

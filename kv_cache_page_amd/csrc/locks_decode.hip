@@ -59,7 +59,9 @@
 // slice's pages after the part-A counts of the earlier slices (published with
 // their tag) and their part-B members.
 #include "locks_attn_core.h"
+#include "locks_score_tile.h"
 #include "locks_select.h"
+#include "locks_step.h"
 
 namespace locks {
 
@@ -85,9 +87,17 @@ __host__ __device__ inline int64_t coop_part_offset(int nsplit) {
 __host__ __device__ inline int64_t coop_zero_words(int nsplit, int G) {
   return coop_part_offset(nsplit) + 2LL * nsplit * G * (kHeadDim + 1);
 }
+// After the zeroed words: the step region (not zeroed) of a fused launch,
+// [0] the epoch (see step_tag) and [32 ..) one completion flag per score
+// workgroup of the head; then the large-bin candidates.
+constexpr int kStepWords = 128;
+constexpr int kMaxScorePairs = 64;  // one polling lane each
 __host__ __device__ inline int64_t coop_mailbox_words(int nsplit, int G, int MP) {
-  return (coop_zero_words(nsplit, G) + 2LL * MP + 31) / 32 * 32;
+  return (coop_zero_words(nsplit, G) + kStepWords + 2LL * MP + 31) / 32 * 32;
 }
+// Completion tag of epoch E: a bijective scramble, so a flag left by another
+// epoch, zeroed memory or a small count never reads as this epoch's tag.
+__host__ __device__ inline uint32_t step_tag(uint32_t E) { return (E * 0x9E3779B1u) ^ 0x5BD1E995u; }
 __device__ __forceinline__ uint64_t* mb_part(uint32_t* mb, int nsplit) {
   return reinterpret_cast<uint64_t*>(mb + coop_part_offset(nsplit));
 }
@@ -181,17 +191,92 @@ __device__ __forceinline__ void attn_list(AttnAcc& acc, const AttnQ& qw,
   }
 }
 
-template <int G, int kS>
-__global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
-    const float* __restrict__ escore, const float* __restrict__ pmax,
-    const float2* __restrict__ zpart, int ntiles, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ budgets, const uint16_t* __restrict__ q,
-    const uint16_t* __restrict__ kpool, const uint16_t* __restrict__ vpool,
+// Coherent (agent-scope) loads of score outputs that a fused launch's own
+// score workgroups wrote.
+template <int G>
+__device__ __forceinline__ void load_scores_coh(const float* p, float (&v)[G]) {
+  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+  if constexpr (G == 1) {
+    v[0] = ld_cohf(p);
+  } else {
+#pragma unroll
+    for (int i = 0; i < G / 2; ++i) {
+      const uint64_t w = ld_coh64(q + i);
+      v[2 * i] = __uint_as_float((uint32_t)w);
+      v[2 * i + 1] = __uint_as_float((uint32_t)(w >> 32));
+    }
+  }
+}
+
+// The score part of a fused launch: workgroup (h, pair) scores the tiles
+// 2 pair and 2 pair + 1 of head h (waves 0-3 and 4-7), writes the decode-layout
+// outputs and the tiles' Z partials, zeroes its share of the head's mailbox,
+// and, once every store of the workgroup has completed, sets its completion
+// flag to the tag of the head's current epoch. Everything a decode workgroup
+// reads from it (score outputs, Z partials, the appended K/V row, mailbox
+// zeros) is written with agent-scope stores and read with agent-scope loads,
+// so the two may run on different XCDs.
+template <int R, int G>
+__device__ __forceinline__ void step_score_part(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ summ,
+    const int32_t* __restrict__ table, const int32_t* __restrict__ seq_lens,
+    float* __restrict__ escore, float* __restrict__ pmax, float2* __restrict__ zpart, int ntiles,
+    int64_t num_blocks, int H, int MP, int npairs, const uint16_t* __restrict__ knew,
+    const uint16_t* __restrict__ vnew, uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool,
+    CoopZero coop, uint32_t* step) {
+  const int bid = blockIdx.x, s = blockIdx.z;
+  const int h = bid % H, pair = bid / H;
+  const int64_t sh_idx = (int64_t)s * H + h;
+  const uint32_t E = ld_coh(step);
+  zero_coop_mailbox(coop, sh_idx, pair, npairs);
+  const int sub = threadIdx.x >> 8, tid = threadIdx.x & 255, wave = tid >> 6, lane = tid & 63;
+  const int tile = 2 * pair + sub;
+  float zm = -__builtin_inff(), zs = 0.f;
+  if (tile < ntiles)
+    score_tile<R, G>(q, summ, table, seq_lens, escore, num_blocks, H, MP, kScorePagesPerWg, 0, knew,
+                     vnew, kpool, vpool, pmax, s, h, tile, wave, tid, zm, zs);
+  __shared__ float zred[2][4][4][2];
+  if (lane < G) {
+    zred[sub][wave][lane][0] = zm;
+    zred[sub][wave][lane][1] = zs;
+  }
+  __syncthreads();
+  if (tid < G && tile < ntiles) {
+    float m = zred[sub][0][tid][0], t = zred[sub][0][tid][1];
+    for (int w = 1; w < 4; ++w) lse2_merge(m, t, zred[sub][w][tid][0], zred[sub][w][tid][1]);
+    st_coh64(reinterpret_cast<uint64_t*>(zpart + (sh_idx * ntiles + tile) * G + tid),
+             (uint64_t)__float_as_uint(m) | ((uint64_t)__float_as_uint(t) << 32));
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0) st_coh(&step[32 + pair], step_tag(E));
+}
+
+// R > 0: one fused launch per step, the score workgroups first (H x npairs,
+// heads first), then the decode workgroups, which wait for their head's
+// score workgroups. R = 0: the decode workgroups alone, after a separate
+// score kernel.
+template <int R, int G, int kS>
+__global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
+    float* __restrict__ escore, float* __restrict__ pmax, float2* __restrict__ zpart, int ntiles,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ budgets,
+    const uint16_t* __restrict__ q, uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool,
     const int32_t* __restrict__ table, int64_t num_blocks, int H, int MP, int max_budget,
-    int slice, int per_wg, uint32_t* __restrict__ mbox,
-    float* __restrict__ out, float* __restrict__ lse_out, int32_t* __restrict__ sel_pages,
-    int32_t* __restrict__ sel_count) {
+    int slice, int per_wg, uint32_t* __restrict__ mbox, float* __restrict__ out,
+    float* __restrict__ lse_out, int32_t* __restrict__ sel_pages, int32_t* __restrict__ sel_count,
+    const uint8_t* __restrict__ summ, int npairs, const uint16_t* __restrict__ knew,
+    const uint16_t* __restrict__ vnew, CoopZero coop) {
   constexpr int nsplit = kS;
+  const int n_score = (R > 0) ? H * npairs : 0;
+  if constexpr (R > 0) {
+    if ((int)blockIdx.x < n_score) {
+      uint32_t* step = mbox + ((int64_t)blockIdx.z * H + (int)blockIdx.x % H) * coop_mailbox_words(nsplit, G, MP) +
+                       coop_zero_words(nsplit, G);
+      step_score_part<R, G>(q, summ, table, seq_lens, escore, pmax, zpart, ntiles, num_blocks, H, MP,
+                            npairs, knew, vnew, kpool, vpool, coop, step);
+      return;
+    }
+  }
   __shared__ uint32_t histc[kHistCopies][kBins + 1];  // padded: copy c of bin b in bank (b + c) % 32
   __shared__ __align__(16) uint32_t hist[kBins];
   __shared__ uint4 sh_q[G * kHeadDim / 8];
@@ -210,12 +295,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
   __shared__ int sh_wa[kDecWaves], sh_wc[kDecWaves];
   __shared__ int sh_int[8];
   __shared__ uint32_t sh_u[2];
+  __shared__ uint32_t sh_ready;
   __shared__ float sh_acc[kDecWaves][G][kHeadDim];
   __shared__ float sh_ml[kDecWaves][G][2];
 
-  // workgroup ids interleave up to 8 heads: id = h % HL + HL * (x + nsplit * ...)
-  const int HL = gridDim.x / nsplit;
-  const int h = blockIdx.y * HL + (int)blockIdx.x % HL, x = (int)blockIdx.x / HL, s = blockIdx.z;
+  // workgroup ids interleave up to HL = 8 heads: id = h % HL + HL (x + nsplit (h / HL))
+  const int HL = H < 8 ? H : 8;
+  const int bid = (int)blockIdx.x - n_score;
+  const int hr = bid / (HL * nsplit), rr = bid % (HL * nsplit);
+  const int h = hr * HL + rr % HL, x = rr / HL, s = blockIdx.z;
   if (h >= H) return;  // padding of the last head row
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t sh_idx = (int64_t)s * H + h;
@@ -224,14 +312,43 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
   uint32_t* mb_hist = ctr + kCoopCounters * kCoopCtrWords;       // [nsplit][512], count + 1
   uint32_t* mb_acnt = mb_hist + nsplit * kBins;                  // [32], part-A count + 1
   uint64_t* mb_cand = reinterpret_cast<uint64_t*>(mb_acnt + kDecMaxSplits);  // [512]: key | (page + 1) << 32
-  uint32_t* mb_bkey = mb + coop_zero_words(nsplit, G);                       // [MP] (large bin)
+  uint32_t* mb_step = mb + coop_zero_words(nsplit, G);                       // epoch, score flags
+  uint32_t* mb_bkey = mb_step + kStepWords;                                   // [MP] (large bin)
   uint32_t* mb_bpage = mb_bkey + MP;                                          // [MP] (large bin)
 
-  // ---- every independent load first: length, budget, the tile Z partials,
-  // and the e, m and block id of this thread's page (clamped, so the loads
-  // are unconditional)
+  // ---- loads that need no score output first: length, budget, the block id
+  // of this thread's page (clamped, so the loads are unconditional), queries
+  const uint32_t epoch = (R > 0) ? ld_coh(mb_step) : 0u;
   const int len_raw = seq_lens[s];
   const int bud_raw = budgets[s];
+  const int j = x * slice + tid;  // this thread's page
+  const bool jin = tid < slice && j < MP;
+  const int jj = jin ? j : 0;
+  const int bk = table[(int64_t)s * MP + jj];
+  if (tid < G * kHeadDim / 8) sh_q[tid] = reinterpret_cast<const uint4*>(q + sh_idx * G * kHeadDim)[tid];
+  for (int i = tid; i < kHistCopies * (kBins + 1); i += kDecThreads) (&histc[0][0])[i] = 0u;
+  if (tid < kDecThreads / 32) slice_bits[tid] = 0u;
+  my_blk[tid] = bk;
+  bool ok = true;       // false after a timed-out wait
+  if constexpr (R > 0) {
+    // ---- wait (bounded) for the head's score workgroups of this epoch
+    if (wave == 0) {
+      const uint32_t want = step_tag(epoch);
+      uint32_t done = 0u;
+      for (int it = 0; it < kSpinMax; ++it) {
+        const uint32_t v = (lane < npairs) ? ld_coh(&mb_step[32 + lane]) : want;
+        if (__ballot(v != want) == 0ull) {
+          done = 1u;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (lane == 0) sh_ready = done;
+    }
+    __syncthreads();
+    ok = sh_ready != 0u;
+  }
+  // ---- the tile Z partials, and the e and m of this thread's page
   const float2* zp = zpart + sh_idx * ntiles * G;
   constexpr int kZl = (kDecMaxSplits * kDecThreads + 64 * kScorePagesPerWg - 1) / (64 * kScorePagesPerWg);
   float2 zl[kZl][G];  // tile partials t = lane + 64 c
@@ -239,29 +356,20 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
   for (int c = 0; c < kZl; ++c) {
     const int t = min(lane + 64 * c, ntiles - 1);
 #pragma unroll
-    for (int g = 0; g < G; ++g) zl[c][g] = zp[t * G + g];
+    for (int g = 0; g < G; ++g) {
+      const uint64_t w = ld_coh64(reinterpret_cast<const uint64_t*>(zp + t * G + g));
+      zl[c][g] = make_float2(__uint_as_float((uint32_t)w), __uint_as_float((uint32_t)(w >> 32)));
+    }
   }
-  const int j = x * slice + tid;  // this thread's page
-  const bool jin = tid < slice && j < MP;
-  float ev[G], mv;
-  int bk;
-  {
-    const int jj = jin ? j : 0;
-    load_scores<G>(escore + (sh_idx * MP + jj) * G, ev);
-    mv = pmax[sh_idx * MP + jj];
-    bk = table[(int64_t)s * MP + jj];
-  }
-  if (tid < G * kHeadDim / 8) sh_q[tid] = reinterpret_cast<const uint4*>(q + sh_idx * G * kHeadDim)[tid];
-  for (int i = tid; i < kHistCopies * (kBins + 1); i += kDecThreads) (&histc[0][0])[i] = 0u;
-  if (tid < kDecThreads / 32) slice_bits[tid] = 0u;
-  my_blk[tid] = bk;
+  float ev[G];
+  load_scores_coh<G>(escore + (sh_idx * MP + jj) * G, ev);
+  const float mv = ld_cohf(pmax + sh_idx * MP + jj);
 
   const int len = clampi(len_raw, 0, MP * kPage);
   const int P = (len + kPage - 1) / kPage;
   const int F = len / kPage;
   const int k = clampi(bud_raw, 2, max_budget);
   const bool sel_all = (P == 0 || k >= P);
-  bool ok = true;       // false after a timed-out wait
   bool in = false;      // this thread's page is in part A
   int natt = 0;         // pages in att_page (part A, or the positions when every page is selected)
   int tbin = -1, need = 0, ct = 0;
@@ -344,7 +452,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
         }
         if (pending) __builtin_amdgcn_s_sleep(1);
       }
-      ok = __syncthreads_and(pending == 0u);
+      ok = __syncthreads_and(pending == 0u) && ok;
       uint32_t t = 0u;
 #pragma unroll
       for (int y = 0; y < kS; ++y) {
@@ -721,11 +829,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
     W += f;
     a = fmaf(__uint_as_float((uint32_t)po[y]), f, a);
   }
-  if (!got) a = __builtin_nanf("");
+  if (!got || !ok) a = __builtin_nanf("");
   const bool some = W > 0.f;
   out[(sh_idx * G + g) * kHeadDim + d] = some ? a / W : (a == a ? 0.f : a);
   if (lse_out && d == 0)
     lse_out[sh_idx * G + g] = some ? (M + __builtin_amdgcn_logf(W)) * kLn2 : -__builtin_inff();
+  // every workgroup of the head has read the epoch (each published a partial
+  // after reading it), so the next step's launch may use the next one
+  if (R > 0 && tid == 0) st_coh(mb_step, epoch + 1u);
 }
 
 // Launch shape for a table of MP pages and a budget of KB pages: false when
@@ -756,57 +867,52 @@ int64_t decode_mailbox_zero_words(int MP, int KB, int G) {
   return coop_zero_words(ns, G);
 }
 
-template <int G, int kS>
-static void launch_decode_gs(const float* escore, const float* pmax, const float2* zpart,
-                             int ntiles, const int32_t* lens, const int32_t* budgets,
-                             const uint16_t* q, const uint16_t* kpool, const uint16_t* vpool,
-                             const int32_t* table, int64_t nb, int S, int H, int MP, int KB,
-                             int slice, int per_wg, uint32_t* mbox, float* out,
-                             float* lse_out, int32_t* sel, int32_t* cnt, hipStream_t st) {
-  const int HL = H < 8 ? H : 8;
-  hipLaunchKernelGGL((decode_attn_kernel<G, kS>), dim3(HL * kS, (H + HL - 1) / HL, S), dim3(kDecThreads),
-                     0, st, escore,
-                     pmax, zpart, ntiles, lens, budgets, q, kpool, vpool, table, nb, H, MP, KB,
-                     slice, per_wg, mbox, out, lse_out, sel, cnt);
+template <int R, int G, int kS>
+static void launch_step_rgs(const StepLaunch& a, hipStream_t st) {
+  const int HL = a.H < 8 ? a.H : 8;
+  const int npairs = (a.ntiles + 1) / 2;
+  const int n_score = R > 0 ? a.H * npairs : 0;
+  const int n_dec = HL * kS * ((a.H + HL - 1) / HL);
+  hipLaunchKernelGGL((decode_step_kernel<R, G, kS>), dim3(n_score + n_dec, 1, a.S), dim3(kDecThreads), 0, st,
+                     a.escore, a.pmax, a.zpart, a.ntiles, a.lens, a.budgets,
+                     static_cast<const uint16_t*>(a.q), static_cast<uint16_t*>(a.kpool),
+                     static_cast<uint16_t*>(a.vpool), a.table, a.nb, a.H, a.MP, a.KB, a.slice, a.per_wg,
+                     a.mbox, a.out, a.lse_out, a.sel, a.cnt, static_cast<const uint8_t*>(a.summ), npairs,
+                     static_cast<const uint16_t*>(a.knew), static_cast<const uint16_t*>(a.vnew), a.coop);
+}
+
+template <int R, int G>
+static void launch_step_rg(const StepLaunch& a, hipStream_t st) {
+  if (a.nsplit <= 8)
+    launch_step_rgs<R, G, 8>(a, st);
+  else if (a.nsplit <= 16)
+    launch_step_rgs<R, G, 16>(a, st);
+  else
+    launch_step_rgs<R, G, 32>(a, st);
 }
 
 template <int G>
-static void launch_decode_g(int nsplit, const float* escore, const float* pmax, const float2* zpart,
-                            int ntiles, const int32_t* lens, const int32_t* budgets,
-                            const uint16_t* q, const uint16_t* kpool, const uint16_t* vpool,
-                            const int32_t* table, int64_t nb, int S, int H, int MP, int KB,
-                            int slice, int per_wg, uint32_t* mbox, float* out,
-                            float* lse_out, int32_t* sel, int32_t* cnt, hipStream_t st) {
-#define LOCKS_ARGS escore, pmax, zpart, ntiles, lens, budgets, q, kpool, vpool, table, nb, S, H, MP, \
-                   KB, slice, per_wg, mbox, out, lse_out, sel, cnt, st
-  if (nsplit <= 8)
-    launch_decode_gs<G, 8>(LOCKS_ARGS);
-  else if (nsplit <= 16)
-    launch_decode_gs<G, 16>(LOCKS_ARGS);
-  else
-    launch_decode_gs<G, 32>(LOCKS_ARGS);
-#undef LOCKS_ARGS
-}
-
-hipError_t launch_decode(int G, const float* escore, const float* pmax, const float2* zpart,
-                         int ntiles, const int32_t* lens, const int32_t* budgets, const void* q,
-                         const void* kpool, const void* vpool, const int32_t* table, int64_t nb,
-                         int S, int H, int MP, int KB, int nsplit, int slice, int per_wg,
-                         uint32_t* mbox, float* out, float* lse_out, int32_t* sel,
-                         int32_t* cnt, hipStream_t st) {
-  const uint16_t* qq = static_cast<const uint16_t*>(q);
-  const uint16_t* kk = static_cast<const uint16_t*>(kpool);
-  const uint16_t* vv = static_cast<const uint16_t*>(vpool);
-#define LOCKS_ARGS nsplit, escore, pmax, zpart, ntiles, lens, budgets, qq, kk, vv, table, nb, S, H, \
-                   MP, KB, slice, per_wg, mbox, out, lse_out, sel, cnt, st
-  switch (G) {
-    case 1: launch_decode_g<1>(LOCKS_ARGS); break;
-    case 2: launch_decode_g<2>(LOCKS_ARGS); break;
-    case 4: launch_decode_g<4>(LOCKS_ARGS); break;
+static hipError_t launch_step_g(const StepLaunch& a, hipStream_t st) {
+  switch (a.r) {
+    case 0: launch_step_rg<0, G>(a, st); break;
+    case 4: launch_step_rg<4, G>(a, st); break;
+    case 8: launch_step_rg<8, G>(a, st); break;
+    case 16: launch_step_rg<16, G>(a, st); break;
     default: return hipErrorInvalidValue;
   }
-#undef LOCKS_ARGS
   return hipGetLastError();
+}
+
+bool decode_step_fuses_score(int r) { return r == 4 || r == 8 || r == 16; }
+
+hipError_t launch_decode(int G, const StepLaunch& a, hipStream_t st) {
+  if (a.r != 0 && (a.ntiles + 1) / 2 > kMaxScorePairs) return hipErrorInvalidValue;
+  switch (G) {
+    case 1: return launch_step_g<1>(a, st);
+    case 2: return launch_step_g<2>(a, st);
+    case 4: return launch_step_g<4>(a, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace locks

@@ -26,10 +26,23 @@ struct CoopZero {
 
 // Called by every workgroup of the score grid (tile row blockIdx.y of
 // gridDim.y); coherent agent-scope stores; no-op for a null base.
-__device__ __forceinline__ void zero_coop_mailbox(const CoopZero& z, int64_t sh) {
+// Stores that reach memory coherently for every XCD (agent-scope relaxed
+// atomics), for data read by other workgroups of the same launch.
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint4* p, uint4 v) {
+  uint64_t* q = reinterpret_cast<uint64_t*>(p);
+  __hip_atomic_store(q, (uint64_t)v.x | ((uint64_t)v.y << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, (uint64_t)v.z | ((uint64_t)v.w << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Workgroup `part` of `nparts` zeroes its share of mailbox `sh`.
+__device__ __forceinline__ void zero_coop_mailbox(const CoopZero& z, int64_t sh, int part, int nparts) {
   if (!z.base) return;
   uint32_t* p = z.base + sh * z.stride;
-  for (int w = blockIdx.y * blockDim.x + threadIdx.x; w < z.words; w += gridDim.y * blockDim.x)
+  for (int w = part * blockDim.x + threadIdx.x; w < z.words; w += nparts * blockDim.x)
     __hip_atomic_store(p + w, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 constexpr float kLog2e = 1.4426950408889634f;

@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256) void score_kernel(
     uint16_t* __restrict__ vpool, float* __restrict__ mxout, CoopZero coop) {
   constexpr SlotLayout L = slot_layout(R);
   constexpr float kTwoM24 = 5.9604644775390625e-08f;  // 2^-24
-  zero_coop_mailbox(coop, (int64_t)blockIdx.z * H + blockIdx.x);
+  zero_coop_mailbox(coop, (int64_t)blockIdx.z * H + blockIdx.x, blockIdx.y, gridDim.y);
   const int s = blockIdx.z, h = blockIdx.x, tile = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l4 = lane & 3;

@@ -1,0 +1,37 @@
+// Launch arguments of the decode step's selection + attention kernel (host
+// side, shared by its launcher and the C-ABI implementation).
+#pragma once
+
+#include "locks_device.h"
+
+namespace locks {
+
+struct StepLaunch {
+  float* escore;        // per page and query e = 2^(s - m) (decode layout)
+  float* pmax;          // per page m = max_g s (base 2)
+  float2* zpart;        // per 128-page tile and query, base-2 (max, sum)
+  int ntiles;
+  const int32_t* lens;
+  const int32_t* budgets;
+  const void* q;
+  void* kpool;
+  void* vpool;
+  const int32_t* table;
+  int64_t nb;
+  int S, H, MP, KB, nsplit, slice, per_wg;
+  uint32_t* mbox;
+  float* out;
+  float* lse_out;
+  int32_t* sel;
+  int32_t* cnt;
+  // fused score part: rank r in {4, 8, 16} scores the pages in the same
+  // launch (summ, and knew / vnew for the append when no page build runs);
+  // r = 0: the scores come from a separate score kernel
+  int r;
+  const void* summ;
+  const void* knew;
+  const void* vnew;
+  CoopZero coop;
+};
+
+}  // namespace locks
