@@ -11,7 +11,7 @@ step runs at exactly 131072 tokens.
 One step = for every layer: append the new token's K/V, build the summary of
 the page that just filled (when one did), score every full page from the
 summaries, select sink + recent + top-126 pages, and attend over them, all
-through locks_decode_step (two launches per layer, three on the steps whose
+through locks_decode_step (one launch per layer, two on the steps whose
 token completes a page). Each step is captured once as a HIP graph; W
 warm-up steps run, then K steps are timed between HIP events.
 
@@ -37,20 +37,29 @@ SLOT_PAYLOAD = 818
 PAGE_KV_BYTES = 2 * B * D * 2
 HBM_PEAK_GBS = 8000.0
 METRIC = "decode-step µs and achieved HBM GB/s (summary+selected KV) at 128K ctx, 8 KV heads"
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "score_kernel_ctx128k_counters.txt")
-SCORE_SRC = os.path.join(ROOT, "kv_cache_page_amd", "csrc", "locks_score_mfma.hip")
-SCORE_HDRS = [os.path.join(ROOT, "kv_cache_page_amd", "csrc", f)
-              for f in ("locks_score_tile.h", "locks_device.h")]
+CSRC = os.path.join(ROOT, "kv_cache_page_amd", "csrc")
+# (counter summary, source, headers) of the two kernels bench.py reports on:
+# the decode-step kernel (score + selection + attention in one launch) and the
+# stand-alone page-score kernel
+KERNELS = {
+    "step": (os.path.join(ROOT, "profiles", "decode_step_kernel_ctx128k_counters.txt"),
+             "locks_decode.hip",
+             ["locks_score_tile.h", "locks_attn_core.h", "locks_select.h", "locks_step.h",
+              "locks_device.h"]),
+    "score": (os.path.join(ROOT, "profiles", "score_kernel_ctx128k_counters.txt"),
+              "locks_score_mfma.hip", ["locks_score_tile.h", "locks_device.h"]),
+}
 
 
-def score_kernel_fingerprint():
-    """sha256 over what decides the score kernel's machine code: its source,
-    the headers it includes and its compile flags."""
+def kernel_fingerprint(which):
+    """sha256 over what decides a kernel's machine code: its source, the
+    headers it includes and its compile flags."""
     from kv_cache_page_amd import build_lib
+    _, src, hdrs = KERNELS[which]
     h = hashlib.sha256()
-    for path in [SCORE_SRC] + SCORE_HDRS:
-        h.update(open(path, "rb").read())
-    flags = build_lib.FLAGS + build_lib.FILE_FLAGS.get(os.path.basename(SCORE_SRC), [])
+    for f in [src] + hdrs:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    flags = build_lib.FLAGS + build_lib.FILE_FLAGS.get(src, [])
     h.update(" ".join(flags).encode())
     return h.hexdigest()
 
@@ -73,17 +82,18 @@ def step_bytes(seq_len):
     return LAYERS * H * (s + kv)
 
 
-def traffic_from_counters():
-    """HBM bytes per score-kernel launch from the committed rocprofv3 counter
+def traffic_from_counters(which):
+    """HBM bytes per launch of a kernel from its committed rocprofv3 counter
     summary, or None when absent or taken on a different build of the kernel."""
-    if not os.path.exists(COUNTERS_FILE):
+    path = KERNELS[which][0]
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(COUNTERS_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("score_kernel_sha256") != score_kernel_fingerprint():
+    if kv.get("kernel_sha256") != kernel_fingerprint(which):
         return None
     try:
         return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
@@ -152,8 +162,9 @@ def main():
               "(see the sharding paragraph of DESIGN.md); use --gpus 1", file=sys.stderr)
         sys.exit(2)
     W, K = args.warmup, args.steps
-    if W < 0 or K < 1 or W + K > 256:
-        print("need 0 <= warmup, 1 <= steps, warmup + steps <= 256 decode steps", file=sys.stderr)
+    if W < 0 or K < 1 or W + K < 2 or W + K > 256:
+        print("need 0 <= warmup, 1 <= steps, 2 <= warmup + steps <= 256 decode steps",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -256,21 +267,34 @@ def main():
         g_full[t].replay()
     torch.cuda.synchronize()
     full_ms = timed(g_full, range(W, n_steps))
+    # the steps whose token completes no page launch the decode-step kernel
+    # alone, once per layer: their time per launch is that kernel's duration
+    plain = [t for t in range(n_steps) if lens[t] % B != 0]
+    step_ms = timed(g_full, plain)
     score_ms = timed(g_score, range(W, n_steps))
     timed_bytes = sum(step_bytes(lens[t]) for t in range(W, n_steps))
     ms_step = full_ms / K
     value = timed_bytes / (full_ms / 1e3) / 1e9
     log(f"[bench] decode step {ms_step * 1e3:.1f} us ({value:.0f} GB/s)")
 
-    # dominant kernel: the page-score kernel, F x H slots of 818 bytes per launch
+    # dominant kernel: the decode-step kernel (score + selection + attention),
+    # the metric's bytes of one layer per launch
+    step_launches = len(plain) * LAYERS
+    step_us = step_ms * 1e3 / step_launches
+    step_bytes_per_launch = sum(step_bytes(lens[t]) for t in plain) / step_launches
+    achieved = step_bytes_per_launch / (step_us * 1e-6) / 1e9
+    traffic = traffic_from_counters("step")
+    log(f"[bench] decode-step kernel {step_us:.2f} us per launch, {achieved:.0f} GB/s "
+        f"({achieved / HBM_PEAK_GBS:.1%} of {HBM_PEAK_GBS:.0f})")
+    # the score stage alone (stand-alone score kernel): F x H slots of 818 bytes
     score_launches = K * LAYERS
     score_us = score_ms * 1e3 / score_launches
     score_bytes = sum(LAYERS * (lens[t] // B) * H * SLOT_PAYLOAD for t in range(W, n_steps))
     score_bytes_per_launch = score_bytes / score_launches
-    achieved = score_bytes_per_launch / (score_us * 1e-6) / 1e9
-    traffic = traffic_from_counters()
-    log(f"[bench] score kernel {score_us:.2f} us per launch, {achieved:.0f} GB/s "
-        f"({achieved / HBM_PEAK_GBS:.1%} of {HBM_PEAK_GBS:.0f})")
+    score_achieved = score_bytes_per_launch / (score_us * 1e-6) / 1e9
+    score_traffic = traffic_from_counters("score")
+    log(f"[bench] score kernel {score_us:.2f} us per launch, {score_achieved:.0f} GB/s "
+        f"({score_achieved / HBM_PEAK_GBS:.1%} of {HBM_PEAK_GBS:.0f})")
 
     if args.calibrate_copy:
         x = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
@@ -311,13 +335,24 @@ def main():
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "bulk_build_pages_per_s": round(build_pages / (build_ms / 1e3)),
         "roofline": {
-            "kernel": "score_mfma_kernel<8,4> (locks_score_pages)",
+            "kernel": "decode_step_kernel<8,4,16> (locks_decode_step: score + select + attend)",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None if traffic is None else round(traffic),
+            "bytes_per_launch": round(step_bytes_per_launch),
+            "us_per_launch": round(step_us, 3),
+        },
+        "score_stage": {
+            "kernel": "score_mfma_kernel<8,4,1> (locks_score_pages)",
+            "bound": "hbm",
+            "achieved": round(score_achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(score_achieved / HBM_PEAK_GBS, 4),
+            "traffic": None if score_traffic is None else round(score_traffic),
             "bytes_per_launch": round(score_bytes_per_launch),
             "us_per_launch": round(score_us, 3),
         },
