@@ -99,8 +99,10 @@ size_t locks_summary_slot_stride(const locks_dims* dims); /* bytes between slots
  * locks_sparse_attn and locks_decode_step need for up to num_seqs sequences of up to max_pages pages
  * and budgets of up to max_budget pages. One workspace may serve all of them
  * when the calls are ordered on one stream; its contents need no
- * initialisation and carry nothing between calls. Returns 0 for invalid
- * arguments.
+ * initialisation. Between calls it carries only a per-(sequence, KV head)
+ * epoch that locks_decode_step advances (it tells one call's completion
+ * flags from another's); no result depends on its value. Returns 0 for
+ * invalid arguments.
  */
 size_t locks_workspace_bytes(const locks_dims* dims, int32_t num_seqs, int32_t max_pages,
                              int32_t max_budget);
@@ -234,16 +236,20 @@ locks_status locks_sparse_attn(const locks_dims* dims, const void* q, const void
  * and §4.4 Algorithm 2 end to end, with the same results as the sequence
  *   locks_append_kv -> locks_build_filled -> locks_score_select ->
  *   locks_sparse_attn
- * (up to floating-point summation order), in two or three launches:
+ * (up to floating-point summation order; the probabilities enter the
+ * value product in bf16), in one launch, two when a page completes:
  *   1. only when a sequence's new token completes a page: append every new
  *      token and build the summaries of the completed pages (their last key
  *      is taken from k_new);
  *   2. score every full page, keeping per 128-page tile the (max, sum exp)
  *      of the scores for Z_g (and append the new tokens when step 1 did not
- *      run);
- *   3. select S and attend: every attention workgroup of a (sequence, KV
- *      head) recomputes the same selection, attends its share of S, and the
- *      last one to finish merges the shares in split order.
+ *      run), then select S and attend: the attention workgroups of a
+ *      (sequence, KV head) wait for its score workgroups, share the selection
+ *      (each selects within its own slice of the pages and they exchange
+ *      histograms and candidates through the workspace), attend their own
+ *      selected pages, and the workgroup of the last slice merges the shares
+ *      in split order. Ranks other than 4, 8 and 16 score in a launch of
+ *      their own before the selection and attention launch.
  * Arguments are those of the calls above; seq_lens counts the new token.
  * seq_lens_host (HOST pointer, optional): a host copy of seq_lens, used only
  *   to skip step 1 when no length is a positive multiple of page_size; with
