@@ -85,8 +85,9 @@ const char* locks_status_string(locks_status status);
  *   next              muq  d int8 (centroid codes in dim order)
  *   next              scales, fp16 little-endian: r basis-column scales,
  *                          page_size coefficient-row scales, 1 centroid scale
- *   then zero padding up to slot_stride (a multiple of 16 bytes).
- * Decoded values are code * scale. r = 8: 818 payload bytes, stride 832.
+ *   then zero padding up to slot_stride (a multiple of 128 bytes, so slots
+ *   start on cache lines and share none).
+ * Decoded values are code * scale. r = 8: 818 payload bytes, stride 896.
  * The scoring calls take basis-column scales below 8 (the matrix-core path
  * carries V^T q in fp16 parts); locks_build writes at most about 1/7, since
  * its basis columns have unit norm.

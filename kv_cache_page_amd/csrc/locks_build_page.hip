@@ -416,7 +416,7 @@ __global__ __launch_bounds__(64) void build_page_kernel(
     const uint32_t hi = (uint32_t)(quant_code(mu[1], scale, 127) & 0xFF);
     *reinterpret_cast<uint16_t*>(sl + L.mu + 2 * lane) = (uint16_t)(lo | (hi << 8));
     if (lane == 0) *reinterpret_cast<uint16_t*>(sl + L.smu) = sbits;
-    if (lane < L.stride - L.payload) sl[L.payload + lane] = 0;
+    for (int p = L.payload + lane; p < L.stride; p += 64) sl[p] = 0;
   }
 }
 

@@ -52,6 +52,9 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 
 // Summary slot byte layout: [Vq r*d/2][Cq B*r][muq d][fp16 scales r+B+1][pad].
+// The stride is a whole number of 128-byte lines, so every slot starts on a
+// line and no two slots (read by the workgroups of different heads, on
+// different XCDs) share one.
 struct SlotLayout {
   int v, c, mu, sv, sc, smu, payload, stride;
 };
@@ -64,7 +67,7 @@ __host__ __device__ constexpr SlotLayout slot_layout(int r) {
                     r * (kHeadDim / 2) + kPage * r + kHeadDim + 2 * r,
                     r * (kHeadDim / 2) + kPage * r + kHeadDim + 2 * (r + kPage),
                     r * (kHeadDim / 2) + kPage * r + kHeadDim + 2 * (r + kPage + 1),
-                    (r * (kHeadDim / 2) + kPage * r + kHeadDim + 2 * (r + kPage + 1) + 15) / 16 * 16};
+                    (r * (kHeadDim / 2) + kPage * r + kHeadDim + 2 * (r + kPage + 1) + 127) / 128 * 128};
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

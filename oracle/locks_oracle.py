@@ -181,7 +181,7 @@ def slot_layout(r, B=16, d=128):
     off_mu = off_c + B * r
     off_s = off_mu + d
     payload = off_s + 2 * (r + B + 1)
-    stride = (payload + 15) // 16 * 16
+    stride = (payload + 127) // 128 * 128
     return dict(v=off_v, c=off_c, mu=off_mu, s_v=off_s, s_c=off_s + 2 * r,
                 s_mu=off_s + 2 * (r + B), payload=payload, stride=stride)
 

@@ -27,11 +27,11 @@ def test_exports_every_declared_symbol():
 
 
 def test_slot_sizes():
-    assert L.slot_bytes(L.Dims(8, 4, 8)) == 818 and L.slot_stride(L.Dims(8, 4, 8)) == 832
+    assert L.slot_bytes(L.Dims(8, 4, 8)) == 818 and L.slot_stride(L.Dims(8, 4, 8)) == 896
     assert L.slot_bytes(L.Dims(8, 4, 4)) == 490 and L.slot_bytes(L.Dims(8, 4, 16)) == 1474
     for r in range(1, 17):
         assert L.slot_bytes(L.Dims(8, 4, r)) == 64 * r + 16 * r + 128 + 2 * (r + 17)
-        assert L.slot_stride(L.Dims(8, 4, r)) % 16 == 0
+        assert L.slot_stride(L.Dims(8, 4, r)) % 128 == 0
 
 
 def test_invalid_dims_rejected():

@@ -166,7 +166,7 @@ def test_slot_sizes():
     L = O.slot_layout(8)
     assert L["payload"] - 2 * (8 + 16 + 1) == 768
     assert abs(768 / 8192 - 0.094) < 0.001
-    assert L["payload"] == 818 and L["stride"] == 832
+    assert L["payload"] == 818 and L["stride"] == 896
     assert abs(818 / 8192 - 0.1) < 0.001
     assert O.slot_layout(4)["payload"] == 490 and O.slot_layout(16)["payload"] == 1474
 
