@@ -85,8 +85,8 @@ Workspace carve(const locks_dims* d, int32_t S, int32_t MP, int32_t KB) {
   off = align_up(off + sh * MP * d->group_size * sizeof(float));
   w.pmax = off;
   off = align_up(off + sh * MP * sizeof(float));
-  w.zpart = off;
-  off = align_up(off + sh * w.ntiles * d->group_size * 2 * sizeof(float));
+  w.zpart = off;  // (the fused decode step pads it to 64 bytes per tile, tiles rounded up to even)
+  off = align_up(off + sh * (size_t)((w.ntiles + 1) / 2 * 2) * 64);
   w.keys = off;
   off = align_up(off + sh * MP * sizeof(uint32_t));
   w.parts = off;

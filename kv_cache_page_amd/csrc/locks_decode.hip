@@ -191,31 +191,14 @@ __device__ __forceinline__ void attn_list(AttnAcc& acc, const AttnQ& qw,
   }
 }
 
-// Coherent (agent-scope) loads of score outputs that a fused launch's own
-// score workgroups wrote.
-template <int G>
-__device__ __forceinline__ void load_scores_coh(const float* p, float (&v)[G]) {
-  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
-  if constexpr (G == 1) {
-    v[0] = ld_cohf(p);
-  } else {
-#pragma unroll
-    for (int i = 0; i < G / 2; ++i) {
-      const uint64_t w = ld_coh64(q + i);
-      v[2 * i] = __uint_as_float((uint32_t)w);
-      v[2 * i + 1] = __uint_as_float((uint32_t)(w >> 32));
-    }
-  }
-}
-
 // The score part of a fused launch: workgroup (h, pair) scores the tiles
 // 2 pair and 2 pair + 1 of head h (waves 0-3 and 4-7), writes the decode-layout
 // outputs and the tiles' Z partials, zeroes its share of the head's mailbox,
 // and, once every store of the workgroup has completed, sets its completion
 // flag to the tag of the head's current epoch. Everything a decode workgroup
 // reads from it (score outputs, Z partials, the appended K/V row, mailbox
-// zeros) is written with agent-scope stores and read with agent-scope loads,
-// so the two may run on different XCDs.
+// zeros) is written with agent-scope stores, which reach memory before the
+// flag, so the two may run on different XCDs.
 template <int R, int G>
 __device__ __forceinline__ void step_score_part(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ summ,
@@ -244,7 +227,9 @@ __device__ __forceinline__ void step_score_part(
   if (tid < G && tile < ntiles) {
     float m = zred[sub][0][tid][0], t = zred[sub][0][tid][1];
     for (int w = 1; w < 4; ++w) lse2_merge(m, t, zred[sub][w][tid][0], zred[sub][w][tid][1]);
-    st_coh64(reinterpret_cast<uint64_t*>(zpart + (sh_idx * ntiles + tile) * G + tid),
+    // padded layout: 64 bytes per tile, so a 128-byte line holds the two
+    // tiles of one workgroup and no other writer's data
+    st_coh64(reinterpret_cast<uint64_t*>(zpart + (sh_idx * 2 * npairs + tile) * 8 + tid),
              (uint64_t)__float_as_uint(m) | ((uint64_t)__float_as_uint(t) << 32));
   }
   __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
@@ -348,22 +333,25 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     __syncthreads();
     ok = sh_ready != 0u;
   }
-  // ---- the tile Z partials, and the e and m of this thread's page
-  const float2* zp = zpart + sh_idx * ntiles * G;
+  // ---- the tile Z partials, and the e and m of this thread's page. In a
+  // fused launch they come from this launch's score workgroups, complete now:
+  // each 128-byte line of them has one writer (a score workgroup, which stored
+  // it coherently), and no workgroup on this XCD read the line earlier in the
+  // launch, so plain loads return the written values (the caches hold no copy
+  // from before the launch).
+  const float2* zp = zpart + ((R > 0) ? sh_idx * 2 * npairs * 8 : sh_idx * ntiles * G);
+  const int zstride = (R > 0) ? 8 : G;  // float2 per tile
   constexpr int kZl = (kDecMaxSplits * kDecThreads + 64 * kScorePagesPerWg - 1) / (64 * kScorePagesPerWg);
   float2 zl[kZl][G];  // tile partials t = lane + 64 c
 #pragma unroll
   for (int c = 0; c < kZl; ++c) {
     const int t = min(lane + 64 * c, ntiles - 1);
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const uint64_t w = ld_coh64(reinterpret_cast<const uint64_t*>(zp + t * G + g));
-      zl[c][g] = make_float2(__uint_as_float((uint32_t)w), __uint_as_float((uint32_t)(w >> 32)));
-    }
+    for (int g = 0; g < G; ++g) zl[c][g] = zp[t * zstride + g];
   }
   float ev[G];
-  load_scores_coh<G>(escore + (sh_idx * MP + jj) * G, ev);
-  const float mv = ld_cohf(pmax + sh_idx * MP + jj);
+  load_scores<G>(escore + (sh_idx * MP + jj) * G, ev);
+  const float mv = pmax[sh_idx * MP + jj];
 
   const int len = clampi(len_raw, 0, MP * kPage);
   const int P = (len + kPage - 1) / kPage;
