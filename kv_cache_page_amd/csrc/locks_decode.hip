@@ -52,7 +52,9 @@
 //      order-preserving); exchange 1; every wave scans the summed histogram;
 //   4. part A = sink, recent and the candidates below bin t (all of bin t
 //      when it fits);
-//   5. part B = the `need` largest keys of bin t, lower page first on ties.
+//   5. part B = the `need` largest keys of bin t, lower page first on ties:
+//      ranked from the slices' top candidates (published with exchange 1)
+//      when they hold all of bin t, else after exchange 2 of its candidates.
 // When every page is selected (k >= P) there is no selection and workgroup x
 // attends the pages [x * per_wg, (x + 1) * per_wg) instead. The selection
 // output, when asked for, is the ascending list: each workgroup writes its
@@ -75,14 +77,24 @@ constexpr int kHistCopies = 8;      // lanes spread their histogram atomics over
 constexpr int kFastCand = kDecThreads;  // crossing-bin candidates exchanged through tagged slots
 constexpr int kSpinMax = 1 << 22;   // polls of 64 clocks: about 0.1 s
 static_assert(kBins == kDecThreads, "one histogram bin per thread");
+constexpr uint64_t kTopEmpty = 0xFFFFFFFFull << 32;  // unused top-candidate slot
+
+// Bin of a key (<= 0, or -inf): floor(-key * 16) clamped to [0, 511]. The
+// publisher of a top candidate and its readers call this same function.
+__device__ __forceinline__ int dec_bin(float key) {
+  const float d = -key * kDecBinsPerUnit;  // >= 0 up to rounding; +inf for -inf keys
+  return d < (float)(kBins - 1) ? (d > 0.f ? (int)d : 0) : kBins - 1;
+}
 
 // Mailbox words of one (sequence, KV head) and G queries per head. Zeroed by
 // the score kernel: the counters [kCoopCounters][kCoopCtrWords], slice
-// histograms [nsplit][512], part-A counts [32], fast candidates [512] and the
-// split partials [nsplit][G][128] and their log-sums [nsplit][G] (all three
-// 64-bit). Not zeroed: the large-bin candidates (key bits, page) [MP] each.
+// histograms [nsplit][512], part-A counts [32], fast candidates [512], the
+// slices' top candidates [nsplit][512 / nsplit] and the split partials
+// [nsplit][G][128] and their log-sums [nsplit][G] (the last four 64-bit).
+// Not zeroed: the large-bin candidates (key bits, page) [MP] each.
 __host__ __device__ inline int64_t coop_part_offset(int nsplit) {
-  return (int64_t)kCoopCounters * kCoopCtrWords + (int64_t)nsplit * kBins + kDecMaxSplits + 2 * kFastCand;
+  return (int64_t)kCoopCounters * kCoopCtrWords + (int64_t)nsplit * kBins + kDecMaxSplits + 2 * kFastCand +
+         2 * kDecThreads;
 }
 __host__ __device__ inline int64_t coop_zero_words(int nsplit, int G) {
   return coop_part_offset(nsplit) + 2LL * nsplit * G * (kHeadDim + 1);
@@ -252,6 +264,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     const uint8_t* __restrict__ summ, int npairs, const uint16_t* __restrict__ knew,
     const uint16_t* __restrict__ vnew, CoopZero coop) {
   constexpr int nsplit = kS;
+  constexpr int kTop = kDecThreads / kS;  // top-candidate slots per slice
+  static_assert(kTop * kS == kDecThreads, "one top-candidate slot per thread");
   const int n_score = (R > 0) ? H * npairs : 0;
   if constexpr (R > 0) {
     if ((int)blockIdx.x < n_score) {
@@ -277,7 +291,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
   __shared__ uint32_t slice_bits[kDecThreads / 32];  // selected pages of the slice (output)
   __shared__ int sh_cbase[kS + 1];  // crossing-bin candidates before slice y
   __shared__ int sh_waves[16];
-  __shared__ int sh_wa[kDecWaves], sh_wc[kDecWaves];
+  __shared__ int sh_wa[kDecWaves], sh_wc[kDecWaves], sh_wt[kDecWaves];
+  __shared__ int sh_nocov;  // some slice's top candidates stop before the crossing bin
   __shared__ int sh_int[8];
   __shared__ uint32_t sh_u[2];
   __shared__ uint32_t sh_ready;
@@ -297,6 +312,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
   uint32_t* mb_hist = ctr + kCoopCounters * kCoopCtrWords;       // [nsplit][512], count + 1
   uint32_t* mb_acnt = mb_hist + nsplit * kBins;                  // [32], part-A count + 1
   uint64_t* mb_cand = reinterpret_cast<uint64_t*>(mb_acnt + kDecMaxSplits);  // [512]: key | (page + 1) << 32
+  uint64_t* mb_top = mb_cand + kFastCand;  // [nsplit][kTop]: key | (page + 1) << 32, last: sbin | 1 << 32
   uint32_t* mb_step = mb + coop_zero_words(nsplit, G);                       // epoch, score flags
   uint32_t* mb_bkey = mb_step + kStepWords;                                   // [MP] (large bin)
   uint32_t* mb_bpage = mb_bkey + MP;                                          // [MP] (large bin)
@@ -313,6 +329,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
   if (tid < G * kHeadDim / 8) sh_q[tid] = reinterpret_cast<const uint4*>(q + sh_idx * G * kHeadDim)[tid];
   for (int i = tid; i < kHistCopies * (kBins + 1); i += kDecThreads) (&histc[0][0])[i] = 0u;
   if (tid < kDecThreads / 32) slice_bits[tid] = 0u;
+  if (tid == 0) sh_nocov = 0;
   my_blk[tid] = bk;
   bool ok = true;       // false after a timed-out wait
   if constexpr (R > 0) {
@@ -362,6 +379,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
   int natt = 0;         // pages in att_page (part A, or the positions when every page is selected)
   int tbin = -1, need = 0, ct = 0;
   bool part_bin = false;
+  bool lds_b = false;   // the crossing bin's candidates came with exchange 1 (in cand_key/cand_page)
 
   AttnQ qw;
   AttnAcc acc;
@@ -414,8 +432,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
       float kj = (mv - zx) + (__builtin_amdgcn_logf(t) - log2G);
       kj = (cand && kj == kj) ? kj : -__builtin_inff();
       key = kj;
-      const float d = -kj * kDecBinsPerUnit;  // >= 0 up to rounding; +inf for -inf keys
-      bin = d < (float)(kBins - 1) ? (d > 0.f ? (int)d : 0) : kBins - 1;
+      bin = dec_bin(kj);
     }
     // ---- 3. slice histogram (candidates only), published; exchange 1
     __syncthreads();
@@ -426,9 +443,53 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
 #pragma unroll
       for (int c = 0; c < kHistCopies; ++c) t += histc[c][tid];
       st_coh(&mb_hist[x * kBins + tid], t);
+      hist[tid] = t - 1u;
     }
-    // every slice's count of bin tid (kept in registers)
+    // ---- the slice's top candidates, published beside its histogram: the
+    // candidates of the bins before sbin, the first bin at which the slice's
+    // running count exceeds kTop - 1, in page order; the last slot holds sbin.
+    // When every slice's sbin lies beyond the crossing bin, all the crossing
+    // bin's candidates are among them and its ranking needs no second exchange.
+    __syncthreads();
+    {
+      const uint4 h0 = *reinterpret_cast<const uint4*>(&hist[8 * lane]);
+      const uint4 h1 = *reinterpret_cast<const uint4*>(&hist[8 * lane + 4]);
+      const int c8[8] = {(int)h0.x, (int)h0.y, (int)h0.z, (int)h0.w,
+                         (int)h1.x, (int)h1.y, (int)h1.z, (int)h1.w};
+      int tot = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tot += c8[e];
+      int run = wave_inclusive_scan(tot) - tot, fb = -1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        run += c8[e];
+        if (fb < 0 && run > kTop - 1) fb = 8 * lane + e;
+      }
+      const uint64_t found = __ballot(fb >= 0);
+      const int sbin = found ? __builtin_amdgcn_readlane(fb, __builtin_ctzll(found)) : kBins;
+      const bool pub = cand && bin < sbin;  // at most kTop - 1 of them
+      const uint64_t balP = __ballot(pub);
+      if (lane == 0) sh_wt[wave] = __popcll(balP);
+      __syncthreads();
+      int preP = 0, totP = 0;
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) {
+        preP += (w < wave) ? sh_wt[w] : 0;
+        totP += sh_wt[w];
+      }
+      uint64_t* top = mb_top + x * kTop;
+      if (pub) {
+        const int pos = preP + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(balP >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)balP, 0u));
+        st_coh64(&top[pos], (uint64_t)__float_as_uint(key) | ((uint64_t)(j + 1) << 32));
+      }
+      if (tid >= totP && tid < kTop - 1) st_coh64(&top[tid], kTopEmpty);
+      if (tid == kTop - 1) st_coh64(&top[tid], (1ull << 32) | (uint32_t)sbin);
+    }
+    // every slice's count of bin tid (kept in registers) and top-candidate
+    // slot tid (slice tid / kTop)
     uint32_t hy[kS];
+    uint64_t tv = 0ull;
     {
       uint32_t pending = 1u;
       for (int it = 0; pending && it < kSpinMax; ++it) {
@@ -438,6 +499,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
           hy[y] = ld_coh(&mb_hist[y * kBins + tid]);
           pending |= (hy[y] == 0u) ? 1u : 0u;
         }
+        tv = ld_coh64(&mb_top[tid]);
+        pending |= ((tv >> 32) == 0ull) ? 1u : 0u;
         if (pending) __builtin_amdgcn_s_sleep(1);
       }
       ok = __syncthreads_and(pending == 0u) && ok;
@@ -492,13 +555,33 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
       in = jin && j < P &&
            ((j == 0) | (j == P - 1) | (cand & (bin < tbin)) | ((tbin >= 0) & (need == ct) & cand & (bin == tbin)));
       const uint64_t balA = __ballot(in);
-      if (lane == 0) sh_wa[wave] = __popcll(balA);
+      // the crossing bin's candidates among the published top candidates
+      const bool tmark = tid % kTop == kTop - 1;
+      const float tkey = __uint_as_float((uint32_t)tv);
+      const bool te = part_bin && ct <= 64 && !tmark && (tv & kTopEmpty) != kTopEmpty && dec_bin(tkey) == tbin;
+      const uint64_t balT = __ballot(te);
+      if (lane == 0) {
+        sh_wa[wave] = __popcll(balA);
+        sh_wt[wave] = __popcll(balT);
+      }
+      if (tmark && part_bin && (int)(uint32_t)tv <= tbin) sh_nocov = 1;
       __syncthreads();
-      int preA = 0, totA = 0;
+      int preA = 0, totA = 0, preT = 0, totT = 0;
 #pragma unroll
       for (int w = 0; w < kDecWaves; ++w) {
         preA += (w < wave) ? sh_wa[w] : 0;
         totA += sh_wa[w];
+        preT += (w < wave) ? sh_wt[w] : 0;
+        totT += sh_wt[w];
+      }
+      // the same decision in every workgroup of the head: all its inputs are
+      // the exchanged histograms and top candidates
+      lds_b = part_bin && ct <= 64 && sh_nocov == 0 && totT == ct;
+      if (lds_b && te) {  // the candidate list, in slice and page order
+        const int pos = preT + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(balT >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)balT, 0u));
+        cand_key[pos] = tkey;
+        cand_page[pos] = (uint32_t)(tv >> 32) - 1u;
       }
       if (in) {
         const int pos = preA + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(balA >> 32),
@@ -509,7 +592,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
       }
       natt = totA;
       if (tid == 0) st_coh(&mb_acnt[x], (uint32_t)totA + 1u);
-      if (part_bin) {
+      if (part_bin && !lds_b) {
         const bool isc = cand && bin == tbin;
         const uint64_t balC = __ballot(isc);
         if (lane == 0) sh_wc[wave] = __popcll(balC);
@@ -544,6 +627,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
   const int cb_lo = part_bin ? sh_cbase[x] : 0, cb_hi = part_bin ? sh_cbase[x + 1] : 0;
   const bool fast_b = !sel_all && ok && part_bin && ct <= 64;
   if (tid == 0) { sh_int[4] = 0; sh_int[5] = 0; sh_u[1] = 1u; }
+  if (lds_b && tid < min(cb_hi - cb_lo, kDecWaves)) {
+    const int pj = (int)cand_page[cb_lo + tid];
+    cs_page[tid] = pj;
+    cs_blk[tid] = my_blk[clampi(pj - x * slice, 0, kDecThreads - 1)];
+  }
   __syncthreads();
   attn_load_q<G>(qw, reinterpret_cast<const uint16_t*>(sh_q), lane);
   // the K/V of the slice's first crossing-bin candidates load now (wave k
@@ -558,7 +646,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
   if (fast_b && wave == kDecWaves - 1) {
     // lane e < ct holds candidate e; rank by key (lower page first on ties)
     uint64_t v = 0ull;
-    if (lane < ct) {
+    if (lds_b) {
+      if (lane < ct) v = (uint64_t)__float_as_uint(cand_key[lane]) | ((uint64_t)(cand_page[lane] + 1u) << 32);
+    } else if (lane < ct) {
       for (int it = 0; it < kSpinMax; ++it) {
         v = ld_coh64(&mb_cand[lane]);
         if ((v >> 32) != 0ull) break;

@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import synth
+from synth.locks_inputs import NEEDLE_NORM
 from oracle import locks_oracle as O
 from tests import locks_harness as Hh
 
@@ -544,6 +545,25 @@ def test_decode_step_equal_keys_mid_size_bin(L):
     res, kpa, vpa, sa = _run_step(L, L.Dims(1, 4, 8), b, kp, vp, kn, vn, summ, 100)
     assert list(res["sel"][0, 0, :100]) == [0] + list(range(1, 99)) + [300]
     assert list(res["sel"][1, 0, :50]) == [0] + list(range(1, 49)) + [69]
+    _check_step(b, 8, 100, res, kpa, vpa, sa, summ, completed)
+
+
+def test_decode_step_slice_with_many_top_pages(L):
+    """80 needle pages inside one 250-page slice of a 2000-page sequence (8
+    splits), budget 100: that slice holds more of the selected pages than the
+    63 top candidates a slice publishes beside its histogram, so the crossing
+    bin's candidates cannot all come with the first exchange."""
+    _say("[gpu] decode step, one slice holding 80 of the 100 selected pages")
+    b = synth.make_decode_batch([2000 * 16 - 3], 1, 4, [100], seed=181, needles_per_head=0)
+    u = b.q[0, :b.G].float().mean(0)
+    u = u / u.norm()
+    for j in range(260, 340):
+        b.k_pool[int(b.block_table[0, j]), 0, 5] = (NEEDLE_NORM * u).to(torch.bfloat16)
+    kp, vp, kn, vn, summ, completed = _step_state(b, 8)
+    ora = Hh.oracle_head(b.q, b.k_pool, b.v_pool, b.block_table, b.seq_lens, b.budgets, summ,
+                         0, 0, b.G, 8)
+    assert sum(1 for j in ora["sel"] if 250 <= j < 500) > 63
+    res, kpa, vpa, sa = _run_step(L, L.Dims(1, b.G, 8), b, kp, vp, kn, vn, summ, 100)
     _check_step(b, 8, 100, res, kpa, vpa, sa, summ, completed)
 
 
