@@ -248,8 +248,8 @@ locks_status locks_sparse_attn(const locks_dims* dims, const void* q, const void
  *      (sequence, KV head) wait for its score workgroups, share the selection
  *      (each selects within its own slice of the pages and they exchange
  *      histograms and candidates through the workspace), attend their own
- *      selected pages, and the workgroup of the last slice merges the shares
- *      in split order. Ranks other than 4, 8 and 16 score in a launch of
+ *      selected pages, and each merges the splits' shares of 1/nsplit of
+ *      the output elements in split order. Ranks other than 4, 8 and 16 score in a launch of
  *      their own before the selection and attention launch.
  * Arguments are those of the calls above; seq_lens counts the new token.
  * seq_lens_host (HOST pointer, optional): a host copy of seq_lens, used only

@@ -23,8 +23,8 @@
 //      taken: every workgroup ranks them (part B) while its part-A pages are
 //      already being attended, then attends its slice's part-B members;
 //   3. the workgroup partials, normalised (o = acc / l, lse = m + log2 l) and
-//      tagged per element: the workgroup of the last split polls them and
-//      merges them in split order.
+//      tagged per element: each workgroup polls those of its 1/nsplit share
+//      of the output elements and merges them in split order.
 // Mailbox accesses are agent-scope relaxed atomics (coherent across the XCDs
 // without cache write-back or invalidation); a tagged 64-bit slot is written
 // and read whole, so its value is valid once its tag is. Waits poll with a
@@ -802,7 +802,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
 
   // ---- the workgroup's partial, normalised: thread (g, d) combines the 8
   // wave partials into o = acc / l and lse = m + log2 l, published as tagged
-  // words (value | 1 << 32) that the merging workgroup polls
+  // words (value | 1 << 32) that the merging workgroups poll
   uint64_t* mb_po = mb_part(mb, nsplit);            // [nsplit][G][128]
   uint64_t* mb_pl = mb_po + nsplit * G * kHeadDim;  // [nsplit][G]
   if (tid < G * kHeadDim) {
@@ -873,10 +873,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     }
   }
 
-  // ---- the last split's workgroup merges: thread (g, d) waits for the
-  // nsplit partials of its element (bounded) and combines them in split order
-  if (x != nsplit - 1 || tid >= G * kHeadDim) return;
-  const int g = tid / kHeadDim, d = tid % kHeadDim;
+  // ---- the merge, spread over the head's workgroups: workgroup x takes the
+  // elements [x kE, (x + 1) kE) of the G x 128 outputs; thread e of them waits
+  // (bounded) for the nsplit partials of its element and combines them in
+  // split order
+  constexpr int kE = G * kHeadDim / kS;
+  static_assert(kE * kS == G * kHeadDim, "whole elements per workgroup");
+  if (tid >= kE) return;
+  const int g = (x * kE + tid) / kHeadDim, d = (x * kE + tid) % kHeadDim;
   uint64_t po[kS], pl[kS];
   bool got = false;
   for (int it = 0; it < kSpinMax; ++it) {
@@ -914,7 +918,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     lse_out[sh_idx * G + g] = some ? (M + __builtin_amdgcn_logf(W)) * kLn2 : -__builtin_inff();
   // every workgroup of the head has read the epoch (each published a partial
   // after reading it), so the next step's launch may use the next one
-  if (R > 0 && tid == 0) st_coh(mb_step, epoch + 1u);
+  if (R > 0 && x == nsplit - 1 && tid == 0) st_coh(mb_step, epoch + 1u);
 }
 
 // Launch shape for a table of MP pages and a budget of KB pages: false when
