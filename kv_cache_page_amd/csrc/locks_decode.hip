@@ -16,12 +16,14 @@
 // exchange data through a per-(sequence, head) mailbox in the workspace whose
 // slots carry their own "written" tag (the score kernel of the same step
 // zeroes them), so a reader waits for exactly the data it needs:
-//   1. slice histograms of the key bins (count + 1 per bin): every workgroup
-//      sums them, finds the crossing bin t of the top-(k-2) count, and knows
-//      each slice's count in t;
-//   2. the crossing bin's candidates (key, page + 1) when only part of it is
-//      taken: every workgroup ranks them (part B) while its part-A pages are
-//      already being attended, then attends its slice's part-B members;
+//   1. slice histograms of the key bins (count + 1 per bin), each with the
+//      slice's top candidates (key, page + 1) up to a cut-off bin: every
+//      workgroup sums the histograms, finds the crossing bin t of the
+//      top-(k-2) count, and knows each slice's count in t;
+//   2. when only part of bin t is taken, its candidates: from the top lists
+//      when every cut-off lies beyond t, else published by each slice. Every
+//      workgroup ranks them (part B) while its part-A pages are already being
+//      attended, then attends its slice's part-B members;
 //   3. the workgroup partials, normalised (o = acc / l, lse = m + log2 l) and
 //      tagged per element: each workgroup polls those of its 1/nsplit share
 //      of the output elements and merges them in split order.
