@@ -59,7 +59,10 @@ def kernel_fingerprint(which):
     h = hashlib.sha256()
     for f in [src] + hdrs:
         h.update(open(os.path.join(CSRC, f), "rb").read())
-    flags = build_lib.FLAGS + build_lib.FILE_FLAGS.get(src, [])
+    # include paths relative to the repository, so the hash does not depend
+    # on where the checkout sits
+    flags = [os.path.relpath(f, ROOT) if os.path.isabs(f) else f
+             for f in build_lib.FLAGS + build_lib.FILE_FLAGS.get(src, [])]
     h.update(" ".join(flags).encode())
     return h.hexdigest()
 

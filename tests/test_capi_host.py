@@ -86,3 +86,22 @@ def test_status_strings():
         assert L.status_string(s) and L.status_string(s) != "unknown status"
     with pytest.raises(L.LocksError):
         L._check(L.ERR_WORKSPACE, "x")
+
+
+def test_kernel_fingerprint_does_not_depend_on_the_checkout_path(tmp_path):
+    """bench.py reports counter traffic only while a kernel's fingerprint equals
+    the one recorded beside its counters; the fingerprint must therefore be the
+    same for the same sources wherever the repository sits."""
+    import shutil
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    dst = os.path.join(str(tmp_path), "elsewhere")
+    shutil.copytree(root, dst, ignore=shutil.ignore_patterns(
+        ".git", "_work", "gpurun_out", "_build", "*.so", "__pycache__", "profiles"))
+    code = "import bench; print(bench.kernel_fingerprint('step'), bench.kernel_fingerprint('score'))"
+    here = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
+                          check=True).stdout
+    there = subprocess.run([sys.executable, "-c", code], cwd=dst, capture_output=True, text=True,
+                           check=True).stdout
+    assert here == there and len(here.split()) == 2
