@@ -567,6 +567,17 @@ def test_decode_step_slice_with_many_top_pages(L):
     _check_step(b, 8, 100, res, kpa, vpa, sa, summ, completed)
 
 
+def test_decode_step_32_splits(L):
+    """A 9000-page table with budgets up to 1100 pages takes 32 splits (slices
+    of 282 pages, 15 top candidates published per slice): a small budget on
+    the long sequence, and a budget that selects most of a 1200-page one."""
+    _say("[gpu] decode step, 32 splits (9000-page table, budgets 64 and 1100)")
+    b = synth.make_decode_batch([9000 * 16 - 5, 1200 * 16 + 3], 1, 4, [64, 1100], seed=183)
+    kp, vp, kn, vn, summ, completed = _step_state(b, 8)
+    res, kpa, vpa, sa = _run_step(L, L.Dims(1, 4, 8), b, kp, vp, kn, vn, summ, 1100)
+    _check_step(b, 8, 1100, res, kpa, vpa, sa, summ, completed)
+
+
 def test_decode_step_wide_table_fallback(L):
     """A table wider than 16384 pages takes the separate select and attention
     launches inside the same entry point."""
