@@ -31,7 +31,7 @@
 //   columns n = (page n / 4, query n % 4). The B operand is block diagonal:
 //   lane (a, r16) holds the W of page a for query r16 % 4, which is column
 //   r16's block exactly when a == r16 / 4, and zeros otherwise. W enters as
-//   an fp16 high part plus an fp16 low part (two products, about 22 bits),
+//   an fp16 high part plus an fp16 low part (two products, about 21 bits),
 //   scaled by 2^12 into fp16's normal range (|W| < 2 s_k in these units, so
 //   basis-column scales s_k below 8 stay finite; unit basis columns give
 //   s_k <= 1/7); the int8 coefficients become
@@ -134,6 +134,23 @@ __device__ __forceinline__ void load_group(GroupRegs<R>& g, const uint8_t* __res
   for (int e = 0; e < R / 2; ++e) g.sv[e] = *reinterpret_cast<const uint32_t*>(slotC + L.sv + 4 * e);
   g.sc = *reinterpret_cast<const uint2*>(slotV + L.sc + 8 * q16);
   g.smu = *reinterpret_cast<const uint16_t*>(slotV + L.smu);
+}
+
+// Splits the products p0 = w0 s0 and p1 = w1 s1 into fp16 high parts and
+// fp16 low parts that together carry about 21 bits: hi = fp16(p) rounded
+// toward zero by one packed conversion, lo = fp16(p - hi) (the remainder is
+// exact in fp32). Both parts come from the one converted hi: when the
+// compiler was free to round the product to fp16 twice (once fused into a
+// mixed-precision FMA, once from the fp32 product), the two roundings could
+// differ by an fp16 ulp on a rounding tie and hi + lo was then off by twice
+// the low part.
+__device__ __forceinline__ void split_hi_lo2(float w0, float s0, float w1, float s1, uint32_t& hi,
+                                             uint32_t& lo) {
+  const float p0 = w0 * s0, p1 = w1 * s1;
+  const auto h = __builtin_amdgcn_cvt_pkrtz(p0, p1);
+  const auto l = __builtin_amdgcn_cvt_pkrtz(p0 - (float)h[0], p1 - (float)h[1]);
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, l);
 }
 
 // One 128-page tile, by 4 waves (wave = 0..3, tid = 64 wave + lane). Leaves
@@ -378,15 +395,11 @@ __device__ __forceinline__ void score_tile(
       uint32_t a0, a1;
       coef4(gr.c[0], a0, a1);
       const half4 A = __builtin_bit_cast(half4, make_uint2(a0, a1));
-      half4 Bh, Bl;
+      uint32_t bh[2], bl[2];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // high part: d s rounded once to fp16; low part: the exact remainder
-        // d s - high (one fma) rounded to fp16
-        const _Float16 hi = (_Float16)(W[e] * Ws[e]);
-        Bh[e] = hi;
-        Bl[e] = (_Float16)__builtin_fmaf(W[e], Ws[e], -(float)hi);
-      }
+      for (int e = 0; e < 2; ++e) split_hi_lo2(W[2 * e], Ws[2 * e], W[2 * e + 1], Ws[2 * e + 1], bh[e], bl[e]);
+      const half4 Bh = __builtin_bit_cast(half4, make_uint2(bh[0], bh[1]));
+      const half4 Bl = __builtin_bit_cast(half4, make_uint2(bl[0], bl[1]));
       X = __builtin_amdgcn_mfma_f32_16x16x16f16(A, Bh, X, 0, 0, 0);
       X = __builtin_amdgcn_mfma_f32_16x16x16f16(A, Bl, X, 0, 0, 0);
     } else {
@@ -396,14 +409,14 @@ __device__ __forceinline__ void score_tile(
         coef4(gr.c[2 * hc], a[0], a[1]);
         coef4(gr.c[2 * hc + 1], a[2], a[3]);
         const half8 A = __builtin_bit_cast(half8, make_uint4(a[0], a[1], a[2], a[3]));
-        half8 Bh, Bl;
+        uint32_t bh[4], bl[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int k = 8 * hc + e;
-          const _Float16 hi = (_Float16)(W[k] * Ws[k]);
-          Bh[e] = hi;
-          Bl[e] = (_Float16)__builtin_fmaf(W[k], Ws[k], -(float)hi);
+        for (int e = 0; e < 4; ++e) {
+          const int k = 8 * hc + 2 * e;
+          split_hi_lo2(W[k], Ws[k], W[k + 1], Ws[k + 1], bh[e], bl[e]);
         }
+        const half8 Bh = __builtin_bit_cast(half8, make_uint4(bh[0], bh[1], bh[2], bh[3]));
+        const half8 Bl = __builtin_bit_cast(half8, make_uint4(bl[0], bl[1], bl[2], bl[3]));
         X = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bh, X, 0, 0, 0);
         X = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl, X, 0, 0, 0);
       }

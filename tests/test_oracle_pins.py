@@ -204,6 +204,116 @@ def test_slot_roundtrip_random():
             assert np.array_equal(back[n], qs[n]), (r, n)
 
 
+def _exact_summary(n, r, seed, B=16, d=128):
+    """A summary whose entries are integer codes times power-of-two scales,
+    with one entry of every quantised slice at +-qmax: the quantiser of
+    readings R1-R2 must return exactly these codes and scales. The scales
+    differ from column to column of V and from row to row of C, so a scale
+    applied along the wrong axis changes the values even at r = B = 16,
+    where the two shapes coincide."""
+    rng = _rng(seed)
+
+    def codes(shape, qmax, axis):
+        c = rng.integers(-qmax + 1, qmax, shape)
+        # put +-qmax at one random position of every slice along `axis`
+        moved = np.moveaxis(c, axis, -1)
+        idx = rng.integers(0, moved.shape[-1], moved.shape[:-1])
+        sign = rng.choice([-1, 1], moved.shape[:-1])
+        np.put_along_axis(moved, idx[..., None], (sign * qmax)[..., None], axis=-1)
+        return np.moveaxis(moved, -1, axis)
+
+    Vq = codes((n, d, r), 7, axis=1)                     # absmax over d, per column
+    Cq = codes((n, B, r), 127, axis=2)                   # absmax over r, per token row
+    muq = codes((n, d), 127, axis=1)
+    sV = 2.0 ** -(2 + (np.arange(r)[None, :] + np.arange(n)[:, None]) % 6)
+    sC = 2.0 ** -(1 + (3 * np.arange(B)[None, :] + np.arange(n)[:, None]) % 9)
+    smu = 2.0 ** -(3 + np.arange(n) % 4)
+    summary = dict(V=Vq * sV[:, None, :], C=Cq * sC[:, :, None], mu=muq * smu[:, None])
+    codes_ = dict(Vq=Vq, sV=sV.astype(np.float16), Cq=Cq, sC=sC.astype(np.float16),
+                  muq=muq, smu=smu.astype(np.float16))
+    return summary, codes_
+
+
+def test_exactly_representable_summary_round_trips():
+    """Codes times power-of-two scales, each slice reaching +-qmax: quantise,
+    pack, unpack and dequantise must return the values exactly, and the score
+    of eq. 4 ([N] §4.2) from the decoded slot must equal the score of the
+    unquantised values (to summation-order rounding: the arrays are equal but
+    laid out differently)."""
+    q = _rng(20).standard_normal((4, 128)) * 1.5
+    for r in (4, 8, 16):
+        summ, want = _exact_summary(9, r, 30 + r)
+        qs = O.quantise_summary(summ)
+        for n in want:
+            assert np.array_equal(qs[n], want[n]), (r, n)
+        slots = O.pack_slots(qs)
+        assert slots.shape[1] == O.slot_layout(r)["stride"]
+        dq = O.dequantise(O.unpack_slots(slots, r))
+        for n in ("V", "C", "mu"):
+            assert np.array_equal(dq[n], summ[n]), (r, n)
+        s_dec = O.page_scores(q, dq["mu"], dq["V"], dq["C"])
+        s_raw = O.page_scores(q, summ["mu"], summ["V"], summ["C"])
+        np.testing.assert_allclose(s_dec, s_raw, rtol=0, atol=1e-12)
+
+
+def _quant_step_bound(x, qmax, axis):
+    """A-priori elementwise bound on |decoded - x| for symmetric absmax
+    quantisation with one scale per slice along `axis`, whatever the
+    rounding of the stored fp16 scale: half a step plus what the fp16
+    rounding of the scale can move the largest entry (reading R1)."""
+    amax = np.max(np.abs(x), axis=axis, keepdims=True)
+    return 0.5 * amax / qmax * (1 + 2.0 ** -9) + amax * 2.0 ** -10
+
+
+def test_quantised_summary_within_quantiser_step():
+    """Decoded basis, coefficients and centroid of realistic pages lie within
+    half a quantiser step of the unquantised values, slice by slice: basis per
+    column, coefficients per token row, centroid per page ([N] §4.1 storage
+    paragraph; readings R1-R2). A scale applied along the wrong axis breaks
+    this at r = 16 as well."""
+    keys = _structured_pages(40, 17)
+    for r in (4, 8, 16):
+        slots, s, _ = O.build_slots(keys, r)
+        dq = O.dequantise(O.unpack_slots(slots, r))
+        for n, qmax, axis in (("V", 7, 1), ("C", 127, 2), ("mu", 127, 1)):
+            bound = _quant_step_bound(s[n], qmax, axis)
+            assert (np.abs(dq[n] - s[n]) <= bound + 1e-15).all(), (r, n)
+
+
+def test_quantised_score_error_bound():
+    """|s_hat(quantised) - s_hat(unquantised)| is bounded by the decoded
+    deltas. Per token, the logit (q.mu + (V^T q).c_i)/sqrt(d) of [N] §4.2
+    eq. 4 moves by q.dmu + (dV^T q).c_hat_i + (V^T q).dc_i, and the
+    log-sum-exp is 1-Lipschitz in the max norm (the argument of the eq. 7
+    bound), so
+      |ds| sqrt(d) <= |q| |dmu| + |dV^T q| max_i |c_hat_i| + |V^T q| max_i |dc_i|.
+    The deltas themselves are pinned slice by slice against the quantiser
+    step (test_quantised_summary_within_quantiser_step)."""
+    keys = _structured_pages(50, 18)
+    q = _rng(21).standard_normal((4, 128)) * 1.2
+    worst = 0.0
+    for r in (4, 8, 16):
+        slots, s, _ = O.build_slots(keys, r)
+        dq = O.dequantise(O.unpack_slots(slots, r))
+        s_q = O.page_scores(q, dq["mu"], dq["V"], dq["C"])
+        s_u = O.page_scores(q, s["mu"], s["V"], s["C"])
+        for p in range(keys.shape[0]):
+            dmu = np.linalg.norm(dq["mu"][p] - s["mu"][p])
+            dVq = np.linalg.norm(q @ (dq["V"][p] - s["V"][p]), axis=1)          # (G,)
+            chat = np.linalg.norm(dq["C"][p], axis=1).max()
+            dc = np.linalg.norm(dq["C"][p] - s["C"][p], axis=1).max()
+            Vtq = np.linalg.norm(q @ s["V"][p], axis=1)                       # (G,)
+            bound = (np.linalg.norm(q, axis=1) * dmu + dVq * chat + Vtq * dc) / math.sqrt(128)
+            err = np.abs(s_q[p] - s_u[p])
+            assert (err <= bound + 1e-12).all(), (r, p, err, bound)
+            worst = max(worst, float((err / bound).max()))
+        # quantisation does move the score, by far less than a logit
+        assert 1e-6 < np.abs(s_q - s_u).max() < 0.5, r
+    # the bound is tight enough to mean something: some page comes within a
+    # factor of 20 of it
+    assert worst > 0.05, worst
+
+
 # ---------------------------------------------------------------------------
 # Score, shares, select ([N] §4.2 eq. 4-5)
 # ---------------------------------------------------------------------------
