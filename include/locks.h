@@ -16,8 +16,15 @@
  *     asynchronous and ordered on `stream`; none allocates, frees or
  *     synchronises the host.
  *   - The caller owns every buffer (pools, tables, outputs, workspace). The
- *     library keeps no mutable global state; calls on different streams with
- *     different output/workspace buffers may run concurrently.
+ *     library's only process-wide state is a per-device table of device
+ *     properties it queries once (see locks_decode_step). Calls on different
+ *     streams with different output and workspace buffers may run
+ *     concurrently, with one caveat for locks_decode_step: its single-launch
+ *     form needs the selection workgroups of a (sequence, KV head) running at
+ *     the same time (they exchange data); a concurrent kernel that holds the
+ *     compute units long enough (for instance another locks_decode_step on
+ *     another stream) can make their bounded waits time out, and the step then
+ *     writes NaN and poisons its workspace (see there) instead of hanging.
  *   - Errors: arguments known on the host are validated before anything is
  *     enqueued; a call that returns an error has enqueued nothing. A failed
  *     kernel launch returns LOCKS_ERR_HIP.
@@ -51,7 +58,7 @@ extern "C" {
 #endif
 
 /* Version of the summary slot byte layout described below. */
-#define LOCKS_SLOT_LAYOUT_VERSION 1
+#define LOCKS_SLOT_LAYOUT_VERSION 2  /* 2: stride rounded up to 128 bytes */
 
 typedef struct {
     int32_t head_dim;     /* d: 128 */
@@ -102,8 +109,8 @@ size_t locks_summary_slot_stride(const locks_dims* dims); /* bytes between slots
  * when the calls are ordered on one stream; its contents need no
  * initialisation. Between calls it carries only a per-(sequence, KV head)
  * epoch that locks_decode_step advances (it tells one call's completion
- * flags from another's); no result depends on its value. Returns 0 for
- * invalid arguments.
+ * flags from another's; no result depends on its value) and the poison word
+ * described under locks_decode_step. Returns 0 for invalid arguments.
  */
 size_t locks_workspace_bytes(const locks_dims* dims, int32_t num_seqs, int32_t max_pages,
                              int32_t max_budget);
@@ -257,9 +264,18 @@ locks_status locks_sparse_attn(const locks_dims* dims, const void* q, const void
  *   NULL step 1 always runs. It must equal seq_lens.
  * sel_pages / sel_count (optional, both or neither): the selection, as
  *   locks_score_select writes it.
- * Tables of more than 16384 pages or budgets above 2048 pages take separate
- *   select and attention launches, which need sel_pages / sel_count
- *   (UNSUPPORTED without them).
+ * Path: tables of more than 16384 pages, budgets above 2048 pages, and
+ *   devices that cannot hold min(H, 8) x nsplit of the kernel's 512-thread
+ *   workgroups at once (queried once per device) take separate score, select
+ *   and attention launches (the selection then goes through the workspace
+ *   when sel_pages is NULL). The choice, and every argument check, is made
+ *   before anything is enqueued.
+ * Timeouts: the single-launch form waits with a bound (it cannot hang). A
+ *   wait that times out (only possible when another kernel holds the compute
+ *   units, see the conventions above) makes that step's out and lse NaN and
+ *   poisons the workspace: every later locks_decode_step on it writes NaN
+ *   until the caller zeroes the whole workspace (e.g. hipMemsetAsync), after
+ *   the stream has finished the poisoned call.
  * Errors as for locks_score_select, plus INVALID_ARG for a null k_new, v_new,
  *   k_pool, v_pool or out, or only one of sel_pages / sel_count.
  */

@@ -29,6 +29,7 @@ int64_t decode_mailbox_words(int MP, int KB, int G);
 int64_t decode_mailbox_zero_words(int MP, int KB, int G);
 hipError_t launch_decode(int G, const StepLaunch& a, hipStream_t st);
 bool decode_step_fuses_score(int r);
+int decode_resident_capacity(int r, int G, int nsplit);
 hipError_t launch_append(const void* knew, const void* vnew, void* kpool, void* vpool, int64_t nb,
                          const int32_t* table, const int32_t* lens, int S, int H, int MP,
                          hipStream_t st);
@@ -63,10 +64,12 @@ size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 // step, e_g per page and query); per-page maxima [S][H][MP]; per-tile base-2
 // (max, sum) partials [S][H][tiles][G]; selection keys of the separate select kernel
 // [S][H][MP]; attention partials of the separate attention kernel
-// [S][H][splits][G][kPartStride]; for the fused decode step, the mailboxes of
-// its workgroups [S][H][...] (which also carry its split partials).
+// [S][H][splits][G][kPartStride]; the selection [S][H][KB] and its counts
+// [S][H] when locks_decode_step takes the separate launches without caller
+// outputs; for the fused decode step, the mailboxes of its workgroups
+// [S][H][...] (which also carry its split partials).
 struct Workspace {
-  size_t scores, pmax, zpart, keys, parts, mbox, total;
+  size_t scores, pmax, zpart, keys, parts, sel, cnt, mbox, total;
   int nsplit, ntiles;
 };
 
@@ -91,6 +94,10 @@ Workspace carve(const locks_dims* d, int32_t S, int32_t MP, int32_t KB) {
   off = align_up(off + sh * MP * sizeof(uint32_t));
   w.parts = off;
   off = align_up(off + sh * w.nsplit * d->group_size * kPartStride * sizeof(float));
+  w.sel = off;
+  off = align_up(off + sh * KB * sizeof(int32_t));
+  w.cnt = off;
+  off = align_up(off + sh * sizeof(int32_t));
   w.mbox = off;
   off = align_up(off + (fused ? sh * (size_t)locks::decode_mailbox_words(MP, KB, d->group_size) * sizeof(uint32_t)
                               : 0));
@@ -288,33 +295,46 @@ locks_status locks_decode_step(const locks_dims* d, const void* q, const void* k
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const int H = d->num_kv_heads, G = d->group_size;
 
-  // 1. append (+ summaries of the pages the new token completes)
+  // Every decision is taken before the first launch, so that a call that
+  // returns an error has enqueued nothing.
+  // (i) page build: only when some sequence's new token completes a page
   bool completes = true;
   if (seq_lens_host) {
     completes = false;
     for (int32_t i = 0; i < S; ++i)
       if (seq_lens_host[i] > 0 && seq_lens_host[i] % locks::kPage == 0) completes = true;
   }
+  // (ii) one launch (score + selection + attention) when the table and budget
+  //      fit it and the device holds every workgroup of its exchange window at
+  //      once; else the separate score, select and attention launches
+  int per_wg, nsplit, slice;
+  bool fused = locks::decode_shape(MP, KB, &per_wg, &nsplit, &slice);
+  const int rfused = locks::decode_step_fuses_score(d->rank) ? d->rank : 0;
+  if (fused) {
+    const int HL = H < 8 ? H : 8;
+    fused = locks::decode_resident_capacity(rfused, G, nsplit) >= HL * nsplit;
+  }
+  // (iii) where the selection goes: the caller's outputs, else the workspace
+  int32_t* sel = sel_pages ? sel_pages : reinterpret_cast<int32_t*>(ws + w.sel);
+  int32_t* cnt = sel_count ? sel_count : reinterpret_cast<int32_t*>(ws + w.cnt);
+
+  // 1. append (+ summaries of the pages the new token completes)
   if (completes) {
     hipError_t he = locks::launch_build(d->rank, k_pool, nb, H, nullptr, S, block_table, seq_lens,
                                         MP, summaries, k_new, v_new, v_pool, st);
     if (he != hipSuccess) return LOCKS_ERR_HIP;
   }
   // 2. scores of all full pages and Z partials (and the append when no page
-  //    completes), 3. selection + attention + merge: one launch for ranks 4,
-  //    8 and 16 (score workgroups first), else a score launch and then the
-  //    selection + attention launch
+  //    completes), 3. selection + attention + merge
   float* scores = reinterpret_cast<float*>(ws + w.scores);
   float2* zpart = reinterpret_cast<float2*>(ws + w.zpart);
-  int per_wg, nsplit, slice;
-  const bool fused = locks::decode_shape(MP, KB, &per_wg, &nsplit, &slice);
-  const locks::CoopZero coop{fused ? reinterpret_cast<uint32_t*>(ws + w.mbox) : nullptr,
-                             locks::decode_mailbox_words(MP, KB, G),
-                             (int)locks::decode_mailbox_zero_words(MP, KB, G)};
   float* pmax = reinterpret_cast<float*>(ws + w.pmax);
   const void* kn = completes ? nullptr : k_new;
   const void* vn = completes ? nullptr : v_new;
   if (fused) {
+    const locks::CoopZero coop{reinterpret_cast<uint32_t*>(ws + w.mbox),
+                               locks::decode_mailbox_words(MP, KB, G),
+                               (int)locks::decode_mailbox_zero_words(MP, KB, G)};
     locks::StepLaunch a{};
     a.escore = scores;
     a.pmax = pmax;
@@ -343,7 +363,7 @@ locks_status locks_decode_step(const locks_dims* d, const void* q, const void* k
     a.knew = kn;
     a.vnew = vn;
     a.coop = coop;
-    a.r = locks::decode_step_fuses_score(d->rank) ? d->rank : 0;
+    a.r = rfused;
     if (a.r == 0) {
       hipError_t he = locks::launch_score(d->rank, G, q, summaries, block_table, seq_lens, scores, nb,
                                           S, H, MP, 0, zpart, kn, vn, k_pool, v_pool, pmax, coop, st);
@@ -355,15 +375,12 @@ locks_status locks_decode_step(const locks_dims* d, const void* q, const void* k
                                       S, H, MP, 0, zpart, kn, vn, k_pool, v_pool, nullptr,
                                       locks::CoopZero{}, st);
   if (he != hipSuccess) return LOCKS_ERR_HIP;
-  float* parts = reinterpret_cast<float*>(ws + w.parts);
-  // long tables or budgets: the separate select and attention kernels
-  if (!sel_pages) return LOCKS_ERR_UNSUPPORTED;
-  he = locks::launch_select(G, scores, seq_lens, budgets, sel_pages, sel_count,
+  he = locks::launch_select(G, scores, seq_lens, budgets, sel, cnt,
                             reinterpret_cast<float*>(ws + w.keys), S, H, MP, KB, st);
   if (he != hipSuccess) return LOCKS_ERR_HIP;
-  return hip_status(locks::launch_attn(G, q, k_pool, v_pool, block_table, seq_lens, sel_pages,
-                                       sel_count, parts, out, lse_out, nb, S, H, MP, KB,
-                                       w.nsplit, attn_pages_per_wave(KB), st));
+  return hip_status(locks::launch_attn(G, q, k_pool, v_pool, block_table, seq_lens, sel, cnt,
+                                       reinterpret_cast<float*>(ws + w.parts), out, lse_out, nb, S,
+                                       H, MP, KB, w.nsplit, attn_pages_per_wave(KB), st));
 }
 
 }  // extern "C"

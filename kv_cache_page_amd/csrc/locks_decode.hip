@@ -30,12 +30,15 @@
 // Mailbox accesses are agent-scope relaxed atomics (coherent across the XCDs
 // without cache write-back or invalidation); a tagged 64-bit slot is written
 // and read whole, so its value is valid once its tag is. Waits poll with a
-// bound: a timeout (it needs a member of the group that never starts) skips
-// the rest of the selection and poisons the output with NaN instead of
-// hanging. Progress: the members of a group lie within a window of 8 nsplit
-// (<= 256) consecutive workgroup ids and each XCD starts its workgroups in id
-// order, so the lowest unfinished group always has all its members running
-// while the device holds 8 nsplit workgroups (one per CU). A crossing bin of more than 512
+// bound: a timeout (it needs a member of the group that never starts, e.g.
+// when another kernel holds the compute units) skips the rest of the
+// selection, writes NaN instead of hanging and poisons the workspace (see the
+// step region below). Progress: the members of a group lie within a window of
+// HL nsplit (<= 256, HL = min(H, 8)) consecutive workgroup ids and each XCD
+// starts its workgroups in id order, so the lowest unfinished group always has
+// all its members running while the device can hold HL nsplit workgroups at
+// once; the host takes the separate select and attention launches on a device
+// that cannot (decode_resident_capacity). A crossing bin of more than 512
 // candidates (degenerate keys) goes through a counted barrier instead and an
 // exact 8-bit radix select on the order-preserving key bits.
 //
@@ -62,6 +65,8 @@
 // output, when asked for, is the ascending list: each workgroup writes its
 // slice's pages after the part-A counts of the earlier slices (published with
 // their tag) and their part-B members.
+#include <atomic>
+
 #include "locks_attn_core.h"
 #include "locks_score_tile.h"
 #include "locks_select.h"
@@ -77,7 +82,7 @@ constexpr int kDecMaxPpw = 8;       // positions per wave when every page is sel
 constexpr float kDecBinsPerUnit = 16.f;
 constexpr int kHistCopies = 8;      // lanes spread their histogram atomics over 8 copies
 constexpr int kFastCand = kDecThreads;  // crossing-bin candidates exchanged through tagged slots
-constexpr int kSpinMax = 1 << 22;   // polls of 64 clocks: about 0.1 s
+constexpr int kSpinMax = 1 << 22;   // polls, each a coherent load and a 64-clock sleep
 static_assert(kBins == kDecThreads, "one histogram bin per thread");
 constexpr uint64_t kTopEmpty = 0xFFFFFFFFull << 32;  // unused top-candidate slot
 
@@ -102,9 +107,15 @@ __host__ __device__ inline int64_t coop_zero_words(int nsplit, int G) {
   return coop_part_offset(nsplit) + 2LL * nsplit * G * (kHeadDim + 1);
 }
 // After the zeroed words: the step region (not zeroed) of a fused launch,
-// [0] the epoch (see step_tag) and [32 ..) one completion flag per score
-// workgroup of the head; then the large-bin candidates.
+// [0] the epoch (see step_tag), [1] the poison word and [32 ..) one
+// completion flag per score workgroup of the head; then the large-bin
+// candidates. A workgroup whose bounded wait timed out stores kPoison in the
+// poison word; every later launch on the workspace then skips its waits and
+// writes NaN, until the caller zeroes the workspace. (After a timeout a late
+// score workgroup of the same launch may read the next epoch and leave a flag
+// that the next launch would take for its own.)
 constexpr int kStepWords = 128;
+constexpr uint32_t kPoison = 0x504F4953u;  // not a value a zeroed or stale-filled workspace holds by chance
 constexpr int kMaxScorePairs = 64;  // one polling lane each
 __host__ __device__ inline int64_t coop_mailbox_words(int nsplit, int G, int MP) {
   return (coop_zero_words(nsplit, G) + kStepWords + 2LL * MP + 31) / 32 * 32;
@@ -322,6 +333,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
   // ---- loads that need no score output first: length, budget, the block id
   // of this thread's page (clamped, so the loads are unconditional), queries
   const uint32_t epoch = (R > 0) ? ld_coh(mb_step) : 0u;
+  const bool poisoned = ld_coh(mb_step + 1) == kPoison;
   const int len_raw = seq_lens[s];
   const int bud_raw = budgets[s];
   const int j = x * slice + tid;  // this thread's page
@@ -333,10 +345,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
   if (tid < kDecThreads / 32) slice_bits[tid] = 0u;
   if (tid == 0) sh_nocov = 0;
   my_blk[tid] = bk;
-  bool ok = true;       // false after a timed-out wait
+  bool ok = !poisoned;  // false after a timed-out wait (here or in an earlier launch)
   if constexpr (R > 0) {
     // ---- wait (bounded) for the head's score workgroups of this epoch
-    if (wave == 0) {
+    if (wave == 0 && !poisoned) {
       const uint32_t want = step_tag(epoch);
       uint32_t done = 0u;
       for (int it = 0; it < kSpinMax; ++it) {
@@ -349,6 +361,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
       }
       if (lane == 0) sh_ready = done;
     }
+    else if (wave == 0 && lane == 0) sh_ready = 0u;
     __syncthreads();
     ok = sh_ready != 0u;
   }
@@ -493,7 +506,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     uint32_t hy[kS];
     uint64_t tv = 0ull;
     {
-      uint32_t pending = 1u;
+      uint32_t pending = ok ? 1u : 0u;  // a workgroup that already failed does not wait
       for (int it = 0; pending && it < kSpinMax; ++it) {
         pending = 0u;
 #pragma unroll
@@ -913,7 +926,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     W += f;
     a = fmaf(__uint_as_float((uint32_t)po[y]), f, a);
   }
-  if (!got || !ok) a = __builtin_nanf("");
+  if (!got || !ok) {
+    a = __builtin_nanf("");
+    if (!poisoned) st_coh(mb_step + 1, kPoison);
+  }
   const bool some = W > 0.f;
   out[(sh_idx * G + g) * kHeadDim + d] = some ? a / W : (a == a ? 0.f : a);
   if (lse_out && d == 0)
@@ -988,6 +1004,53 @@ static hipError_t launch_step_g(const StepLaunch& a, hipStream_t st) {
 }
 
 bool decode_step_fuses_score(int r) { return r == 4 || r == 8 || r == 16; }
+
+template <int R, int G, int kS>
+static int capacity_of(int dev) {
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void*>(&decode_step_kernel<R, G, kS>), kDecThreads, 0) !=
+      hipSuccess)
+    return -1;
+  return cus * per_cu;
+}
+
+template <int R, int G>
+static int capacity_rg(int dev, int si) {
+  return si == 0 ? capacity_of<R, G, 8>(dev) : si == 1 ? capacity_of<R, G, 16>(dev) : capacity_of<R, G, 32>(dev);
+}
+
+template <int R>
+static int capacity_r(int dev, int gi, int si) {
+  return gi == 0 ? capacity_rg<R, 1>(dev, si) : gi == 1 ? capacity_rg<R, 2>(dev, si) : capacity_rg<R, 4>(dev, si);
+}
+
+// Workgroups of decode_step_kernel<r, G, nsplit> that the current device
+// holds at once (compute units x workgroups resident per compute unit).
+// Queried once per device and shape and kept in a small per-device table
+// (the library's only process-wide state: device properties); 0 if a query
+// fails.
+int decode_resident_capacity(int r, int G, int nsplit) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices][4][3][3];  // 0: not queried yet, -1: failed
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  const int ri = r == 4 ? 1 : r == 8 ? 2 : r == 16 ? 3 : 0;
+  const int gi = G == 1 ? 0 : G == 2 ? 1 : 2;
+  const int si = nsplit <= 8 ? 0 : nsplit <= 16 ? 1 : 2;
+  std::atomic<int>& slot = cache[dev][ri][gi][si];
+  int c = slot.load(std::memory_order_relaxed);
+  if (c == 0) {
+    c = ri == 0 ? capacity_r<0>(dev, gi, si)
+        : ri == 1 ? capacity_r<4>(dev, gi, si)
+        : ri == 2 ? capacity_r<8>(dev, gi, si)
+                  : capacity_r<16>(dev, gi, si);
+    if (c == 0) c = -1;
+    slot.store(c, std::memory_order_relaxed);
+  }
+  return c > 0 ? c : 0;
+}
 
 hipError_t launch_decode(int G, const StepLaunch& a, hipStream_t st) {
   if (a.r != 0 && (a.ntiles + 1) / 2 > kMaxScorePairs) return hipErrorInvalidValue;

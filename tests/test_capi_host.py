@@ -105,3 +105,36 @@ def test_kernel_fingerprint_does_not_depend_on_the_checkout_path(tmp_path):
     there = subprocess.run([sys.executable, "-c", code], cwd=dst, capture_output=True, text=True,
                            check=True).stdout
     assert here == there and len(here.split()) == 2
+
+
+def test_decode_step_rejects_before_launch():
+    """locks_decode_step validates everything on the host first (fake device
+    pointers: none of these calls may reach a launch). The 17000-page table
+    takes the separate launches, whose selection fits in the workspace, so a
+    workspace one byte short is rejected, and NULL selection outputs are
+    accepted by validation (they are optional on every path)."""
+    d = L.Dims(2, 4, 8)
+    fake = ctypes.c_void_p(256)
+    host_lens = (ctypes.c_int32 * 2)(17000 * 16 - 3, 300)
+    need = L.workspace_bytes(d, 2, 17000, 64)
+    assert need > 0
+
+    def call(**kw):
+        a = dict(q=fake, k_new=fake, v_new=fake, k_pool=fake, v_pool=fake, summ=fake, nb=40000,
+                 table=fake, lens=fake, lens_host=ctypes.cast(host_lens, ctypes.c_void_p),
+                 budgets=fake, S=2, MP=17000, KB=64, out=fake, lse=None, sel=None, cnt=None,
+                 ws=fake, ws_bytes=need - 1)
+        a.update(kw)
+        return L._decode_step(ctypes.byref(d), a["q"], a["k_new"], a["v_new"], a["k_pool"],
+                              a["v_pool"], a["summ"], a["nb"], a["table"], a["lens"],
+                              a["lens_host"], a["budgets"], a["S"], a["MP"], a["KB"], a["out"],
+                              a["lse"], a["sel"], a["cnt"], a["ws"], a["ws_bytes"], None)
+
+    assert call() == L.ERR_WORKSPACE                       # one byte short, NULL selection outputs
+    assert call(ws=None, ws_bytes=need) == L.ERR_WORKSPACE
+    assert call(sel=fake) == L.ERR_INVALID_ARG              # only one of sel_pages / sel_count
+    assert call(out=None) == L.ERR_INVALID_ARG
+    assert call(k_new=ctypes.c_void_p(264)) == L.ERR_INVALID_ARG   # not 16-byte aligned
+    assert call(MP=70000) == L.ERR_UNSUPPORTED
+    assert call(KB=1) == L.ERR_INVALID_ARG
+    assert call(S=0) == L.OK                                # empty batch: nothing to do
