@@ -288,6 +288,34 @@ locks_status locks_decode_step(const locks_dims* dims, const void* q, const void
                                int32_t* sel_pages, int32_t* sel_count, void* workspace,
                                size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * locks_decode_step_noalloc -- locks_decode_step for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same step, arguments and results
+ * (same kernels), without a workspace argument. Its workspace is a built-in
+ * scratch array of LOCKS_NOALLOC_SCRATCH_BYTES per device, which the library
+ * holds until the process ends; the call itself allocates and frees nothing.
+ * A shape whose locks_workspace_bytes exceeds LOCKS_NOALLOC_SCRATCH_BYTES is
+ * rejected with LOCKS_ERR_WORKSPACE before anything is enqueued (16 MiB
+ * covers, for instance, one sequence of a 65536-page table with budgets up to
+ * 2048 pages, or four 8192-page sequences with budgets up to 256, at 8 KV
+ * heads and G = 4). Every call on a device shares that device's scratch and
+ * each call first clears the parts that must start cleared (one small fill
+ * launch), so a timed-out step poisons only itself; calls that overlap on one
+ * device (different streams, or different host threads) race and must not
+ * be made. Errors as for locks_decode_step; HIP also when the scratch address
+ * cannot be obtained.
+ */
+#define LOCKS_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+locks_status locks_decode_step_noalloc(const locks_dims* dims, const void* q, const void* k_new,
+                                       const void* v_new, void* k_pool, void* v_pool,
+                                       void* summaries, int64_t num_blocks,
+                                       const int32_t* block_table, const int32_t* seq_lens,
+                                       const int32_t* seq_lens_host, const int32_t* budgets,
+                                       int32_t num_seqs, int32_t max_pages, int32_t max_budget,
+                                       float* out, float* lse_out, int32_t* sel_pages,
+                                       int32_t* sel_count, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

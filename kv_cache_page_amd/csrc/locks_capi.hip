@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "locks_device.h"
 #include "locks_step.h"
 
@@ -30,6 +32,7 @@ int64_t decode_mailbox_zero_words(int MP, int KB, int G);
 hipError_t launch_decode(int G, const StepLaunch& a, hipStream_t st);
 bool decode_step_fuses_score(int r);
 int decode_resident_capacity(int r, int G, int nsplit);
+hipError_t launch_step_reset(uint32_t* mbox, int64_t sh, int MP, int KB, int G, hipStream_t st);
 hipError_t launch_append(const void* knew, const void* vnew, void* kpool, void* vpool, int64_t nb,
                          const int32_t* table, const int32_t* lens, int S, int H, int MP,
                          hipStream_t st);
@@ -271,13 +274,17 @@ locks_status locks_sparse_attn(const locks_dims* d, const void* q, const void* k
       w.nsplit, attn_pages_per_wave(KB), st));
 }
 
-locks_status locks_decode_step(const locks_dims* d, const void* q, const void* k_new,
-                               const void* v_new, void* k_pool, void* v_pool, void* summaries,
-                               int64_t nb, const int32_t* block_table, const int32_t* seq_lens,
-                               const int32_t* seq_lens_host, const int32_t* budgets, int32_t S,
-                               int32_t MP, int32_t KB, float* out, float* lse_out,
-                               int32_t* sel_pages, int32_t* sel_count, void* workspace,
-                               size_t ws_bytes, hipStream_t st) {
+}  // extern "C"
+
+namespace {
+
+// Host checks of locks_decode_step's arguments (everything but the workspace).
+locks_status decode_step_check(const locks_dims* d, const void* q, const void* k_new,
+                               const void* v_new, const void* k_pool, const void* v_pool,
+                               const void* summaries, int64_t nb, const int32_t* block_table,
+                               const int32_t* seq_lens, const int32_t* budgets, int32_t S,
+                               int32_t MP, int32_t KB, const float* out, const int32_t* sel_pages,
+                               const int32_t* sel_count) {
   locks_status e = check_dims(d);
   if (e != LOCKS_OK) return e;
   e = check_batch(S, MP, KB, nb);
@@ -290,9 +297,20 @@ locks_status locks_decode_step(const locks_dims* d, const void* q, const void* k
   if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) ||
       !aligned16(v_pool) || !aligned16(summaries))
     return LOCKS_ERR_INVALID_ARG;
-  const Workspace w = carve(d, S, MP, KB);
-  if (!workspace || ws_bytes < w.total) return LOCKS_ERR_WORKSPACE;
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  return LOCKS_OK;
+}
+
+// The launches of one decode step on a checked workspace `ws` laid out as
+// `w`. reset_step: first clear the step regions of the mailboxes (epoch,
+// poison word, completion flags), for a workspace that persists from call to
+// call without the caller zeroing it.
+locks_status decode_step_run(const locks_dims* d, const void* q, const void* k_new,
+                             const void* v_new, void* k_pool, void* v_pool, void* summaries,
+                             int64_t nb, const int32_t* block_table, const int32_t* seq_lens,
+                             const int32_t* seq_lens_host, const int32_t* budgets, int32_t S,
+                             int32_t MP, int32_t KB, float* out, float* lse_out,
+                             int32_t* sel_pages, int32_t* sel_count, const Workspace& w,
+                             uint8_t* ws, bool reset_step, hipStream_t st) {
   const int H = d->num_kv_heads, G = d->group_size;
 
   // Every decision is taken before the first launch, so that a call that
@@ -318,6 +336,11 @@ locks_status locks_decode_step(const locks_dims* d, const void* q, const void* k
   int32_t* sel = sel_pages ? sel_pages : reinterpret_cast<int32_t*>(ws + w.sel);
   int32_t* cnt = sel_count ? sel_count : reinterpret_cast<int32_t*>(ws + w.cnt);
 
+  if (fused && reset_step) {
+    hipError_t he = locks::launch_step_reset(reinterpret_cast<uint32_t*>(ws + w.mbox),
+                                             (int64_t)S * H, MP, KB, G, st);
+    if (he != hipSuccess) return LOCKS_ERR_HIP;
+  }
   // 1. append (+ summaries of the pages the new token completes)
   if (completes) {
     hipError_t he = locks::launch_build(d->rank, k_pool, nb, H, nullptr, S, block_table, seq_lens,
@@ -381,6 +404,69 @@ locks_status locks_decode_step(const locks_dims* d, const void* q, const void* k
   return hip_status(locks::launch_attn(G, q, k_pool, v_pool, block_table, seq_lens, sel, cnt,
                                        reinterpret_cast<float*>(ws + w.parts), out, lse_out, nb, S,
                                        H, MP, KB, w.nsplit, attn_pages_per_wave(KB), st));
+}
+
+// Built-in scratch of locks_decode_step_noalloc, one per device (each GPU the
+// library runs on holds its own copy until the process ends). In host code
+// `scratch` is a stand-in, not a device address: scratch_ptr() gives the
+// address.
+constexpr size_t kScratchBytes = LOCKS_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// Device address of the current device's scratch, taken once per device with
+// that device current; null if a HIP call fails.
+void* scratch_ptr() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> ptrs[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = ptrs[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    ptrs[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+locks_status locks_decode_step_noalloc(const locks_dims* d, const void* q, const void* k_new,
+                                       const void* v_new, void* k_pool, void* v_pool,
+                                       void* summaries, int64_t nb, const int32_t* block_table,
+                                       const int32_t* seq_lens, const int32_t* seq_lens_host,
+                                       const int32_t* budgets, int32_t S, int32_t MP, int32_t KB,
+                                       float* out, float* lse_out, int32_t* sel_pages,
+                                       int32_t* sel_count, hipStream_t st) {
+  locks_status e = decode_step_check(d, q, k_new, v_new, k_pool, v_pool, summaries, nb, block_table,
+                                     seq_lens, budgets, S, MP, KB, out, sel_pages, sel_count);
+  if (e != LOCKS_OK || S == 0) return e;
+  const Workspace w = carve(d, S, MP, KB);
+  if (w.total > kScratchBytes) return LOCKS_ERR_WORKSPACE;
+  void* ws = scratch_ptr();
+  if (!ws) return LOCKS_ERR_HIP;
+  return decode_step_run(d, q, k_new, v_new, k_pool, v_pool, summaries, nb, block_table, seq_lens,
+                         seq_lens_host, budgets, S, MP, KB, out, lse_out, sel_pages, sel_count, w,
+                         static_cast<uint8_t*>(ws), true, st);
+}
+
+
+locks_status locks_decode_step(const locks_dims* d, const void* q, const void* k_new,
+                               const void* v_new, void* k_pool, void* v_pool, void* summaries,
+                               int64_t nb, const int32_t* block_table, const int32_t* seq_lens,
+                               const int32_t* seq_lens_host, const int32_t* budgets, int32_t S,
+                               int32_t MP, int32_t KB, float* out, float* lse_out,
+                               int32_t* sel_pages, int32_t* sel_count, void* workspace,
+                               size_t ws_bytes, hipStream_t st) {
+  locks_status e = decode_step_check(d, q, k_new, v_new, k_pool, v_pool, summaries, nb, block_table,
+                                     seq_lens, budgets, S, MP, KB, out, sel_pages, sel_count);
+  if (e != LOCKS_OK || S == 0) return e;
+  const Workspace w = carve(d, S, MP, KB);
+  if (!workspace || ws_bytes < w.total) return LOCKS_ERR_WORKSPACE;
+  return decode_step_run(d, q, k_new, v_new, k_pool, v_pool, summaries, nb, block_table, seq_lens,
+                         seq_lens_host, budgets, S, MP, KB, out, lse_out, sel_pages, sel_count, w,
+                         static_cast<uint8_t*>(workspace), false, st);
 }
 
 }  // extern "C"

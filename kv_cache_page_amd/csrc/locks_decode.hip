@@ -1005,6 +1005,23 @@ static hipError_t launch_step_g(const StepLaunch& a, hipStream_t st) {
 
 bool decode_step_fuses_score(int r) { return r == 4 || r == 8 || r == 16; }
 
+// Clears the step region (epoch, poison word, completion flags) of mailbox
+// blockIdx.x.
+__global__ __launch_bounds__(kStepWords) void step_reset_kernel(uint32_t* __restrict__ mbox,
+                                                                int64_t stride, int64_t offset) {
+  mbox[(int64_t)blockIdx.x * stride + offset + threadIdx.x] = 0u;
+}
+
+// The step regions of the `sh` (sequence, KV head) mailboxes of a fused
+// decode step over MP pages and budgets up to KB; nothing for other shapes.
+hipError_t launch_step_reset(uint32_t* mbox, int64_t sh, int MP, int KB, int G, hipStream_t st) {
+  int pw, ns, sl;
+  if (sh <= 0 || !decode_shape(MP, KB, &pw, &ns, &sl)) return hipSuccess;
+  hipLaunchKernelGGL(step_reset_kernel, dim3((unsigned)sh), dim3(kStepWords), 0, st, mbox,
+                     coop_mailbox_words(ns, G, MP), coop_zero_words(ns, G));
+  return hipGetLastError();
+}
+
 template <int R, int G, int kS>
 static int capacity_of(int dev) {
   int cus = 0, per_cu = 0;

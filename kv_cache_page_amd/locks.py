@@ -29,8 +29,9 @@ ENTRY_POINTS = (
     "locks_status_string", "locks_summary_slot_bytes", "locks_summary_slot_stride",
     "locks_workspace_bytes", "locks_build", "locks_build_filled", "locks_append_kv",
     "locks_score_select", "locks_score_pages", "locks_select_pages", "locks_sparse_attn",
-    "locks_decode_step",
+    "locks_decode_step", "locks_decode_step_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 16 << 20   # LOCKS_NOALLOC_SCRATCH_BYTES
 
 
 class Dims(ctypes.Structure):
@@ -82,6 +83,10 @@ _sparse_attn = _sig("locks_sparse_attn", ctypes.c_int,
 _decode_step = _sig("locks_decode_step", ctypes.c_int,
                     [_pd, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32,
                      _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp])
+
+_decode_step_noalloc = _sig("locks_decode_step_noalloc", ctypes.c_int,
+                            [_pd, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32,
+                             _i32, _i32, _vp, _vp, _vp, _vp, _vp])
 
 
 def status_string(status):
@@ -247,6 +252,29 @@ def decode_step(dims, q, k_new, v_new, k_pool, v_pool, summaries, block_table, s
                       _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
                       _stream(stream))
     _check(st, "locks_decode_step")
+
+
+def decode_step_noalloc(dims, q, k_new, v_new, k_pool, v_pool, summaries, block_table, seq_lens,
+                        budgets, max_budget, out, lse_out=None, sel_pages=None, sel_count=None,
+                        seq_lens_host=None, stream=None):
+    """locks_decode_step_noalloc: decode_step on the library's built-in
+    per-device scratch (no workspace argument, nothing allocated)."""
+    if seq_lens_host is not None:
+        if seq_lens_host.device.type != "cpu":
+            raise ValueError("seq_lens_host must be a CPU tensor")
+        if seq_lens_host.numel() != seq_lens.numel():
+            raise ValueError("seq_lens_host must have one entry per sequence")
+    st = _decode_step_noalloc(
+        ctypes.byref(dims), _ptr(q, torch.bfloat16, "q"), _ptr(k_new, torch.bfloat16, "k_new"),
+        _ptr(v_new, torch.bfloat16, "v_new"), _ptr(k_pool, torch.bfloat16, "k_pool"),
+        _ptr(v_pool, torch.bfloat16, "v_pool"), _ptr(summaries, torch.uint8, "summaries"),
+        k_pool.shape[0], _ptr(block_table, torch.int32, "block_table"),
+        _ptr(seq_lens, torch.int32, "seq_lens"), _ptr(seq_lens_host, torch.int32, "seq_lens_host"),
+        _ptr(budgets, torch.int32, "budgets"), seq_lens.numel(), block_table.shape[1], max_budget,
+        _ptr(out, torch.float32, "out"), _ptr(lse_out, torch.float32, "lse_out"),
+        _ptr(sel_pages, torch.int32, "sel_pages"), _ptr(sel_count, torch.int32, "sel_count"),
+        _stream(stream))
+    _check(st, "locks_decode_step_noalloc")
 
 
 class Decoder:
