@@ -55,6 +55,12 @@ design notes of the repository):
                  holding the newest token, possibly partial). P == 1 gives {0}.
   R9 budget      k counts distinct pages including sink and recent; k >= P
                  selects every page. Equal keys rank the lower page first.
+  R17 deferred   the pages put the build of a filled page outside the decode
+      build      critical path. In the deferred reading the step whose token
+                 completes page P-1 scores only the pages full before that
+                 token, F' = floor((len - 1) / B): the just-completed page is
+                 this step's unsummarised recent page (selected, not in Z_g)
+                 and is summarised after the step.
 """
 from __future__ import annotations
 
@@ -321,19 +327,20 @@ def n_full_pages(seq_len, B=16):
     return seq_len // B
 
 
-def decode_head(q, Kp, Vp, seq_len, k, slots=None, r=8, mode="quantised", B=16):
+def decode_head(q, Kp, Vp, seq_len, k, slots=None, r=8, mode="quantised", B=16, deferred=False):
     """Score -> share -> select -> attend for one (seq, KV head).
 
     q: (G, d). Kp, Vp: (>=P, B, d) logical pages (the tail page may be
     partial). slots: (F, stride) uint8 summary slots of the full pages, or
     None to build them here. mode: "quantised" scores from the codes (eq. 4 as
     deployed), "unquantised" from the fp64 summary, "exact" ranks by the
-    exact page LSE (the Lemma 1 selector of [N] §3.1).
+    exact page LSE (the Lemma 1 selector of [N] §3.1). deferred: reading R17,
+    only the pages full before the current token are summarised and scored.
     Returns dict(scores (F, G), key (F,), sel (list), out (G, d), lse (G,))."""
     q = np.asarray(q, dtype=np.float64)
     G, d = q.shape
     P = n_pages(seq_len, B)
-    F = n_full_pages(seq_len, B)
+    F = n_full_pages(max(seq_len - 1, 0), B) if deferred else n_full_pages(seq_len, B)
     Kp = np.asarray(Kp, dtype=np.float64)[:P]
     Vp = np.asarray(Vp, dtype=np.float64)[:P]
     if F > 0:

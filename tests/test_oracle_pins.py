@@ -507,3 +507,34 @@ def test_eq8_retention_bound():
         cov = m_exact[sel].sum(axis=0).mean()
         cov_ex = m_exact[sel_ex].sum(axis=0).mean()
         assert cov >= math.exp(-4 * eta) * cov_ex - 1e-12
+
+
+def test_deferred_build_scores_pages_full_before_the_token():
+    """Reading R17 (the build of a filled page outside the decode critical
+    path, [N] §2): the step whose token completes page P-1 scores only the F-1
+    pages full before that token, with the shares of eq. 5 ([N] §4.2)
+    normalised over those pages (written out here), keeps page P-1 as the
+    recent page, and attends the same kind of set; on a step that completes
+    no page the two readings coincide."""
+    b = synth.make_decode_batch([40 * 16, 40 * 16 + 5, 2 * 16], 1, 4, [9, 9, 4], seed=31)
+    for s in range(3):
+        Lq = int(b.seq_lens[s])
+        q, Kp, Vp = _head_pages(b, s, 0)
+        normal = O.decode_head(q, Kp, Vp, Lq, int(b.budgets[s]))
+        defer = O.decode_head(q, Kp, Vp, Lq, int(b.budgets[s]), deferred=True)
+        if Lq % 16:
+            for n in ("scores", "key", "out", "lse"):
+                np.testing.assert_array_equal(defer[n], normal[n])
+            assert defer["sel"] == normal["sel"]
+            continue
+        F = Lq // 16
+        P = F
+        assert defer["scores"].shape[0] == F - 1
+        np.testing.assert_allclose(defer["scores"], normal["scores"][:F - 1], atol=1e-12)
+        S = defer["scores"]
+        m = np.exp(S) / np.exp(S).sum(axis=0, keepdims=True)      # eq. 5 over pages 0..F-2
+        np.testing.assert_allclose(np.exp(defer["key"]), m.mean(axis=1), rtol=1e-12)
+        assert 0 in defer["sel"] and P - 1 in defer["sel"]
+        assert len(defer["sel"]) == min(int(b.budgets[s]), P)
+        toks = np.concatenate([Kp[j] for j in defer["sel"]]), np.concatenate([Vp[j] for j in defer["sel"]])
+        np.testing.assert_allclose(defer["out"], O.attend(q, *toks)[0], atol=1e-12)
