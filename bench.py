@@ -8,12 +8,17 @@ head. The KV cache holds 131072 tokens' worth of pages; the sequence starts
 W+K tokens short of 131072 and every decode step appends one token, so the
 last timed step runs at exactly 131072 tokens.
 
-One step = for every layer: append the new token's K/V, build the summary of
-the page that just filled (when one did), score every full page from the
-summaries, select sink + recent + top-126 pages, and attend over them, all
-through locks_decode_step (one launch per layer, two on the steps whose
-token completes a page). Each step is captured once as a HIP graph; W
-warm-up steps run, then K steps are timed between HIP events.
+One step = for every layer: append the new token's K/V, score every page that
+was full before it from the summaries, select sink + recent + top-126 pages
+and attend over them, through locks_decode_step (one launch per layer). The
+summary of a page the token completes is built outside the decode critical
+path: the layers' pools are slices of one allocation, so after the layer loop
+one locks_build call over that page's block id in every layer summarises all
+256 (layer, KV head) pages in one parallel launch (the step whose token
+completes a page leaves that page out of the shares; it is the recent page
+and always selected). The page-completing step is also timed with the build
+inside each layer's step (locks_decode_step's default). Each step is captured once as
+a HIP graph; W warm-up steps run, then K steps are timed between HIP events.
 
 Throughput counts the metric's algorithmic bytes: 818 summary bytes per full
 page and KV head, plus 8192 bytes per selected full page (512 per valid token
@@ -210,7 +215,9 @@ def run_ctx128k(torch, L, synth, dev, W, K, seed):
     table = stack.block_table
 
     # ---- prefill -> decode boundary: bulk build of every full page, all layers
-    summ = [L.alloc_summaries(dims, NB, dev) for _ in range(LAYERS)]
+    # (summaries, like the pools, are slices of one allocation)
+    summ_all = L.alloc_summaries(dims, LAYERS * NB, dev)
+    summ = [summ_all[l * NB:(l + 1) * NB] for l in range(LAYERS)]
     F0 = len0 // B
     ids0 = table[0, :F0].contiguous()
     for l in range(LAYERS):
@@ -233,10 +240,24 @@ def run_ctx128k(torch, L, synth, dev, W, K, seed):
     out = torch.empty(LAYERS, 1, H * G, D, dtype=torch.float32, device=dev)
     lse = torch.empty(LAYERS, 1, H * G, dtype=torch.float32, device=dev)
     ws = L.alloc_workspace(dims, 1, MP, BUDGET, dev)
+    # block ids (in the whole allocation) of the page each step's token
+    # completes, one per layer; empty when the token completes none
+    ids_done = [torch.tensor([int(table[0, Lt // B - 1]) + l * NB for l in range(LAYERS)],
+                             dtype=torch.int32, device=dev) if Lt % B == 0 else None for Lt in lens]
 
     def full_step(t):
-        # one decode step of every layer: append, build of the page the token
-        # completes (1 step in 16), score, select, attend
+        # one decode step of every layer: append, score, select, attend; then
+        # the page the token completes (1 step in 16), every layer at once
+        ln = lens_dev[t:t + 1]
+        for l in range(LAYERS):
+            L.decode_step(dims, stack.q[t, l], kn[t, l], vn[t, l], stack.k_pools[l],
+                          stack.v_pools[l], summ[l], table, ln, budgets, BUDGET, out[l], ws,
+                          lse_out=lse[l], seq_lens_host=lens_host[t], defer_build=True)
+        if ids_done[t] is not None:
+            L.build(dims, stack.k_all, ids_done[t], summ_all)
+
+    def in_step_build(t):
+        # the same step with the page build inside locks_decode_step
         ln = lens_dev[t:t + 1]
         for l in range(LAYERS):
             L.decode_step(dims, stack.q[t, l], kn[t, l], vn[t, l], stack.k_pools[l],
@@ -248,6 +269,9 @@ def run_ctx128k(torch, L, synth, dev, W, K, seed):
             L.score_pages(dims, stack.q[t, l], summ[l], table, lens_dev[t:t + 1], scores)
 
     full_step(0)            # eager warm-up of every kernel before capture
+    first_comp = next(t for t in range(n_steps) if lens[t] % B == 0)
+    in_step_build(first_comp)
+    full_step(first_comp)
     torch.cuda.synchronize()
     log(f"[bench] capturing {n_steps} step graphs ({LAYERS} layers each)")
     g_full = capture(torch, full_step, range(n_steps))
@@ -268,6 +292,13 @@ def run_ctx128k(torch, L, synth, dev, W, K, seed):
     step_ms = timed(torch, g_full, plain)
     comp_ms = timed(torch, g_full, completing) if completing else float("nan")
     score_ms = timed(torch, g_score, range(W, n_steps))
+    # the page-completing steps with the build inside the step (same results
+    # up to the one page's term in the shares)
+    comp_in = [t for t in completing if t >= W]
+    g_in = capture(torch, in_step_build, comp_in)
+    comp_in_ms = timed(torch, g_in, comp_in) if comp_in else float("nan")
+    comp_in_us = comp_in_ms * 1e3 / len(comp_in) if comp_in else float("nan")
+    del g_in
     timed_bytes = sum(step_bytes(lens[t]) for t in range(W, n_steps))
     ms_step = full_ms / K
     value = timed_bytes / (full_ms / 1e3) / 1e9
@@ -275,7 +306,8 @@ def run_ctx128k(torch, L, synth, dev, W, K, seed):
     comp_us = comp_ms * 1e3 / len(completing) if completing else float("nan")
     amort_us = (15 * steady_us + comp_us) / 16
     log(f"[bench] decode step {ms_step * 1e3:.1f} us over the timed window ({value:.0f} GB/s); "
-        f"steady {steady_us:.1f} us, page-completing {comp_us:.1f} us, 1 in 16 {amort_us:.1f} us")
+        f"steady {steady_us:.1f} us, page-completing {comp_us:.1f} us (build inside the step "
+        f"{comp_in_us:.1f} us), 1 in 16 {amort_us:.1f} us")
 
     step_launches = len(plain) * LAYERS
     step_us = step_ms * 1e3 / step_launches
@@ -285,8 +317,9 @@ def run_ctx128k(torch, L, synth, dev, W, K, seed):
     score_bpl = sum(LAYERS * (lens[t] // B) * H * SLOT_PAYLOAD for t in range(W, n_steps)) / score_launches
     res = dict(
         value=value, ms_step=ms_step, timed_bytes=timed_bytes,
-        steady_us=steady_us, comp_us=comp_us, amort_us=amort_us,
-        page_build_us_per_layer=(comp_us - steady_us) / LAYERS if completing else None,
+        steady_us=steady_us, comp_us=comp_us, amort_us=amort_us, comp_in_us=comp_in_us,
+        amort_in_us=(15 * steady_us + comp_in_us) / 16,
+        page_build_us_per_layer=(comp_in_us - steady_us) / LAYERS if completing else None,
         roofline=roofline("decode_step_kernel<8,4,16> (locks_decode_step: score + select + attend)",
                           "step", step_bpl, step_us),
         score_stage=roofline("score_mfma_kernel<8,4,1> (locks_score_pages)", "score", score_bpl,
@@ -295,7 +328,7 @@ def run_ctx128k(torch, L, synth, dev, W, K, seed):
     log(f"[bench] decode-step kernel {step_us:.2f} us per launch, "
         f"{res['roofline']['achieved']:.0f} GB/s ({res['roofline']['frac']:.1%} of {HBM_PEAK_GBS:.0f}); "
         f"score kernel {score_us:.2f} us per launch ({res['score_stage']['frac']:.1%})")
-    del g_full, g_score, summ, ws, kn, vn
+    del g_full, g_score, summ, summ_all, ws, kn, vn
     return res
 
 
@@ -473,15 +506,17 @@ def oracle_layer0(stack, lens_final, torch):
 
 def check_final_step(final, heads, lens_final):
     """GPU layer-0 outputs of the final step against the oracle (fp64, its own
-    slots): attention within 1e-2 relative L2 per KV head, log-sum-exp within
-    1e-3, no NaN anywhere. Returns (ok, worst rel-L2, worst lse error)."""
+    slots, the deferred-build reading the loop runs): attention within 1e-2
+    relative L2 per KV head, log-sum-exp within 1e-3, no NaN anywhere.
+    Returns (ok, worst rel-L2, worst lse error)."""
     import numpy as np
     from oracle import locks_oracle as O
     if final["any_nan"]:
         return False, float("nan"), float("nan")
     worst, worst_l = 0.0, 0.0
     for h, hd in enumerate(heads):
-        ora = O.decode_head(hd["q"], hd["K"], hd["V"], lens_final, BUDGET, slots=hd["slots"], r=R)
+        ora = O.decode_head(hd["q"], hd["K"], hd["V"], lens_final, BUDGET, slots=hd["slots"], r=R,
+                            deferred=True)
         o = final["out"][h * G:(h + 1) * G]
         e = float(np.linalg.norm(o - ora["out"]) / np.linalg.norm(ora["out"]))
         el = float(np.abs(final["lse"][h * G:(h + 1) * G] - ora["lse"]).max())
@@ -503,7 +538,8 @@ def cpu_baseline(heads, lens_final, seconds):
     per_head = s + kv
 
     def one(hd):
-        O.decode_head(hd["q"], hd["K"], hd["V"], lens_final, BUDGET, slots=hd["slots"], r=R)
+        O.decode_head(hd["q"], hd["K"], hd["V"], lens_final, BUDGET, slots=hd["slots"], r=R,
+                      deferred=True)
 
     limit = threadpool_limits(1) if threadpool_limits else None
     try:
@@ -641,6 +677,8 @@ def main():
             "us_per_step_steady": round(head["steady_us"], 2),
             "us_per_step_page_completing": round(head["comp_us"], 2),
             "us_per_step_amortised_1_in_16": round(head["amort_us"], 2),
+            "us_per_step_page_completing_build_in_step": round(head["comp_in_us"], 2),
+            "us_per_step_amortised_1_in_16_build_in_step": round(head["amort_in_us"], 2),
             "page_build_us_per_layer": None if head["page_build_us_per_layer"] is None
             else round(head["page_build_us_per_layer"], 2),
             "roofline": head["roofline"],

@@ -239,6 +239,9 @@ locks_status locks_sparse_attn(const locks_dims* dims, const void* q, const void
                                float* out, float* lse_out, void* workspace,
                                size_t workspace_bytes, hipStream_t stream);
 
+/* Flags of locks_decode_step / locks_decode_step_noalloc. */
+#define LOCKS_STEP_DEFER_BUILD 1u  /* leave the page the new token completes to locks_build_filled */
+
 /*
  * locks_decode_step -- one whole decode step of one layer, [N] §2 figure 1
  * and §4.4 Algorithm 2 end to end, with the same results as the sequence
@@ -264,6 +267,14 @@ locks_status locks_sparse_attn(const locks_dims* dims, const void* q, const void
  *   NULL step 1 always runs. It must equal seq_lens.
  * sel_pages / sel_count (optional, both or neither): the selection, as
  *   locks_score_select writes it.
+ * flags: 0, or LOCKS_STEP_DEFER_BUILD for the build outside the decode
+ *   critical path ([N] §2): the step then builds nothing; it scores only the
+ *   pages that were full before its token, floor((len - 1) / page_size), so a
+ *   page its token completes is, for this step, the unsummarised recent page
+ *   (selected as always, left out of Z_g). The caller summarises those pages
+ *   with locks_build_filled (same block table and lengths) on any stream,
+ *   ordered after this call and before the next decode step of the layer.
+ *   Other bits: INVALID_ARG.
  * Path: tables of more than 16384 pages, budgets above 2048 pages, and
  *   devices that cannot hold min(H, 8) x nsplit of the kernel's 512-thread
  *   workgroups at once (queried once per device) take separate score, select
@@ -285,8 +296,8 @@ locks_status locks_decode_step(const locks_dims* dims, const void* q, const void
                                const int32_t* seq_lens, const int32_t* seq_lens_host,
                                const int32_t* budgets, int32_t num_seqs, int32_t max_pages,
                                int32_t max_budget, float* out, float* lse_out,
-                               int32_t* sel_pages, int32_t* sel_count, void* workspace,
-                               size_t workspace_bytes, hipStream_t stream);
+                               int32_t* sel_pages, int32_t* sel_count, uint32_t flags,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * locks_decode_step_noalloc -- locks_decode_step for callers that cannot
@@ -314,7 +325,7 @@ locks_status locks_decode_step_noalloc(const locks_dims* dims, const void* q, co
                                        const int32_t* seq_lens_host, const int32_t* budgets,
                                        int32_t num_seqs, int32_t max_pages, int32_t max_budget,
                                        float* out, float* lse_out, int32_t* sel_pages,
-                                       int32_t* sel_count, hipStream_t stream);
+                                       int32_t* sel_count, uint32_t flags, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -13,12 +13,12 @@
 namespace locks {
 hipError_t launch_score(int r, int G, const void* q, const void* summ, const int32_t* table,
                         const int32_t* lens, float* scores, int64_t nb, int S, int H, int MP,
-                        int fill_nan, float2* zpart, const void* knew, const void* vnew,
+                        int flags, float2* zpart, const void* knew, const void* vnew,
                         void* kpool, void* vpool, float* mxout, CoopZero coop,
                         hipStream_t st);
 hipError_t launch_select(int G, const float* scores, const int32_t* lens, const int32_t* budgets,
                          int32_t* sel, int32_t* cnt, float* keybuf, int S, int H, int MP,
-                         int max_budget, hipStream_t st);
+                         int max_budget, int lag, hipStream_t st);
 hipError_t launch_attn(int G, const void* q, const void* kpool, const void* vpool,
                        const int32_t* table, const int32_t* lens, const int32_t* sel,
                        const int32_t* cnt, float* part, float* out, float* lse_out, int64_t nb,
@@ -210,11 +210,11 @@ locks_status locks_score_select(const locks_dims* d, const void* q, const void* 
   float* scores = scores_out ? scores_out : reinterpret_cast<float*>(ws + w.scores);
   const int H = d->num_kv_heads, G = d->group_size;
   hipError_t he = locks::launch_score(d->rank, G, q, summaries, block_table, seq_lens, scores, nb,
-                                      S, H, MP, scores_out ? 1 : 0, nullptr, nullptr, nullptr, nullptr,
+                                      S, H, MP, scores_out ? locks::kScoreFillNan : 0, nullptr, nullptr, nullptr, nullptr,
                                       nullptr, nullptr, locks::CoopZero{}, st);
   if (he != hipSuccess) return LOCKS_ERR_HIP;
   he = locks::launch_select(G, scores, seq_lens, budgets, sel_pages, sel_count,
-                            reinterpret_cast<float*>(ws + w.keys), S, H, MP, KB, st);
+                            reinterpret_cast<float*>(ws + w.keys), S, H, MP, KB, 0, st);
   return hip_status(he);
 }
 
@@ -248,7 +248,7 @@ locks_status locks_select_pages(const locks_dims* d, const float* scores, const 
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   return hip_status(locks::launch_select(d->group_size, scores, seq_lens, budgets, sel_pages,
                                          sel_count, reinterpret_cast<float*>(ws + w.keys), S,
-                                         d->num_kv_heads, MP, KB, st));
+                                         d->num_kv_heads, MP, KB, 0, st));
 }
 
 locks_status locks_sparse_attn(const locks_dims* d, const void* q, const void* k_pool,
@@ -309,15 +309,17 @@ locks_status decode_step_run(const locks_dims* d, const void* q, const void* k_n
                              int64_t nb, const int32_t* block_table, const int32_t* seq_lens,
                              const int32_t* seq_lens_host, const int32_t* budgets, int32_t S,
                              int32_t MP, int32_t KB, float* out, float* lse_out,
-                             int32_t* sel_pages, int32_t* sel_count, const Workspace& w,
-                             uint8_t* ws, bool reset_step, hipStream_t st) {
+                             int32_t* sel_pages, int32_t* sel_count, uint32_t flags,
+                             const Workspace& w, uint8_t* ws, bool reset_step, hipStream_t st) {
   const int H = d->num_kv_heads, G = d->group_size;
+  const bool deferred = (flags & LOCKS_STEP_DEFER_BUILD) != 0;
 
   // Every decision is taken before the first launch, so that a call that
   // returns an error has enqueued nothing.
-  // (i) page build: only when some sequence's new token completes a page
-  bool completes = true;
-  if (seq_lens_host) {
+  // (i) page build: only when some sequence's new token completes a page, and
+  //     never when the caller defers it (the score part then appends)
+  bool completes = !deferred;
+  if (completes && seq_lens_host) {
     completes = false;
     for (int32_t i = 0; i < S; ++i)
       if (seq_lens_host[i] > 0 && seq_lens_host[i] % locks::kPage == 0) completes = true;
@@ -387,19 +389,21 @@ locks_status decode_step_run(const locks_dims* d, const void* q, const void* k_n
     a.vnew = vn;
     a.coop = coop;
     a.r = rfused;
+    a.lag = deferred ? 1 : 0;
     if (a.r == 0) {
       hipError_t he = locks::launch_score(d->rank, G, q, summaries, block_table, seq_lens, scores, nb,
-                                          S, H, MP, 0, zpart, kn, vn, k_pool, v_pool, pmax, coop, st);
+                                          S, H, MP, deferred ? locks::kScoreDeferred : 0, zpart, kn,
+                                          vn, k_pool, v_pool, pmax, coop, st);
       if (he != hipSuccess) return LOCKS_ERR_HIP;
     }
     return hip_status(locks::launch_decode(G, a, st));
   }
   hipError_t he = locks::launch_score(d->rank, G, q, summaries, block_table, seq_lens, scores, nb,
-                                      S, H, MP, 0, zpart, kn, vn, k_pool, v_pool, nullptr,
-                                      locks::CoopZero{}, st);
+                                      S, H, MP, deferred ? locks::kScoreDeferred : 0, zpart, kn, vn,
+                                      k_pool, v_pool, nullptr, locks::CoopZero{}, st);
   if (he != hipSuccess) return LOCKS_ERR_HIP;
   he = locks::launch_select(G, scores, seq_lens, budgets, sel, cnt,
-                            reinterpret_cast<float*>(ws + w.keys), S, H, MP, KB, st);
+                            reinterpret_cast<float*>(ws + w.keys), S, H, MP, KB, deferred ? 1 : 0, st);
   if (he != hipSuccess) return LOCKS_ERR_HIP;
   return hip_status(locks::launch_attn(G, q, k_pool, v_pool, block_table, seq_lens, sel, cnt,
                                        reinterpret_cast<float*>(ws + w.parts), out, lse_out, nb, S,
@@ -438,17 +442,18 @@ locks_status locks_decode_step_noalloc(const locks_dims* d, const void* q, const
                                        const int32_t* seq_lens, const int32_t* seq_lens_host,
                                        const int32_t* budgets, int32_t S, int32_t MP, int32_t KB,
                                        float* out, float* lse_out, int32_t* sel_pages,
-                                       int32_t* sel_count, hipStream_t st) {
+                                       int32_t* sel_count, uint32_t flags, hipStream_t st) {
   locks_status e = decode_step_check(d, q, k_new, v_new, k_pool, v_pool, summaries, nb, block_table,
                                      seq_lens, budgets, S, MP, KB, out, sel_pages, sel_count);
   if (e != LOCKS_OK || S == 0) return e;
+  if (flags & ~(uint32_t)LOCKS_STEP_DEFER_BUILD) return LOCKS_ERR_INVALID_ARG;
   const Workspace w = carve(d, S, MP, KB);
   if (w.total > kScratchBytes) return LOCKS_ERR_WORKSPACE;
   void* ws = scratch_ptr();
   if (!ws) return LOCKS_ERR_HIP;
   return decode_step_run(d, q, k_new, v_new, k_pool, v_pool, summaries, nb, block_table, seq_lens,
-                         seq_lens_host, budgets, S, MP, KB, out, lse_out, sel_pages, sel_count, w,
-                         static_cast<uint8_t*>(ws), true, st);
+                         seq_lens_host, budgets, S, MP, KB, out, lse_out, sel_pages, sel_count,
+                         flags, w, static_cast<uint8_t*>(ws), true, st);
 }
 
 
@@ -457,16 +462,17 @@ locks_status locks_decode_step(const locks_dims* d, const void* q, const void* k
                                int64_t nb, const int32_t* block_table, const int32_t* seq_lens,
                                const int32_t* seq_lens_host, const int32_t* budgets, int32_t S,
                                int32_t MP, int32_t KB, float* out, float* lse_out,
-                               int32_t* sel_pages, int32_t* sel_count, void* workspace,
-                               size_t ws_bytes, hipStream_t st) {
+                               int32_t* sel_pages, int32_t* sel_count, uint32_t flags,
+                               void* workspace, size_t ws_bytes, hipStream_t st) {
   locks_status e = decode_step_check(d, q, k_new, v_new, k_pool, v_pool, summaries, nb, block_table,
                                      seq_lens, budgets, S, MP, KB, out, sel_pages, sel_count);
   if (e != LOCKS_OK || S == 0) return e;
+  if (flags & ~(uint32_t)LOCKS_STEP_DEFER_BUILD) return LOCKS_ERR_INVALID_ARG;
   const Workspace w = carve(d, S, MP, KB);
   if (!workspace || ws_bytes < w.total) return LOCKS_ERR_WORKSPACE;
   return decode_step_run(d, q, k_new, v_new, k_pool, v_pool, summaries, nb, block_table, seq_lens,
-                         seq_lens_host, budgets, S, MP, KB, out, lse_out, sel_pages, sel_count, w,
-                         static_cast<uint8_t*>(workspace), false, st);
+                         seq_lens_host, budgets, S, MP, KB, out, lse_out, sel_pages, sel_count,
+                         flags, w, static_cast<uint8_t*>(workspace), false, st);
 }
 
 }  // extern "C"

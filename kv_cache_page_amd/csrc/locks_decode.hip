@@ -231,7 +231,7 @@ __device__ __forceinline__ void step_score_part(
     float* __restrict__ escore, float* __restrict__ pmax, float2* __restrict__ zpart, int ntiles,
     int64_t num_blocks, int H, int MP, int npairs, const uint16_t* __restrict__ knew,
     const uint16_t* __restrict__ vnew, uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool,
-    CoopZero coop, uint32_t* step) {
+    CoopZero coop, uint32_t* step, int lag) {
   const int bid = blockIdx.x, s = blockIdx.z;
   const int h = bid % H, pair = bid / H;
   const int64_t sh_idx = (int64_t)s * H + h;
@@ -241,8 +241,9 @@ __device__ __forceinline__ void step_score_part(
   const int tile = 2 * pair + sub;
   float zm = -__builtin_inff(), zs = 0.f;
   if (tile < ntiles)
-    score_tile<R, G>(q, summ, table, seq_lens, escore, num_blocks, H, MP, kScorePagesPerWg, 0, knew,
-                     vnew, kpool, vpool, pmax, s, h, tile, wave, tid, zm, zs);
+    score_tile<R, G>(q, summ, table, seq_lens, escore, num_blocks, H, MP, kScorePagesPerWg,
+                     lag ? kScoreDeferred : 0, knew, vnew, kpool, vpool, pmax, s, h, tile, wave,
+                     tid, zm, zs);
   __shared__ float zred[2][4][4][2];
   if (lane < G) {
     zred[sub][wave][lane][0] = zm;
@@ -275,7 +276,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     int slice, int per_wg, uint32_t* __restrict__ mbox, float* __restrict__ out,
     float* __restrict__ lse_out, int32_t* __restrict__ sel_pages, int32_t* __restrict__ sel_count,
     const uint8_t* __restrict__ summ, int npairs, const uint16_t* __restrict__ knew,
-    const uint16_t* __restrict__ vnew, CoopZero coop) {
+    const uint16_t* __restrict__ vnew, CoopZero coop, int lag) {
   constexpr int nsplit = kS;
   constexpr int kTop = kDecThreads / kS;  // top-candidate slots per slice
   static_assert(kTop * kS == kDecThreads, "one top-candidate slot per thread");
@@ -285,7 +286,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
       uint32_t* step = mbox + ((int64_t)blockIdx.z * H + (int)blockIdx.x % H) * coop_mailbox_words(nsplit, G, MP) +
                        coop_zero_words(nsplit, G);
       step_score_part<R, G>(q, summ, table, seq_lens, escore, pmax, zpart, ntiles, num_blocks, H, MP,
-                            npairs, knew, vnew, kpool, vpool, coop, step);
+                            npairs, knew, vnew, kpool, vpool, coop, step, lag);
       return;
     }
   }
@@ -387,7 +388,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
 
   const int len = clampi(len_raw, 0, MP * kPage);
   const int P = (len + kPage - 1) / kPage;
-  const int F = len / kPage;
+  const int F = scored_pages(len, lag);  // summarised pages (pages 0..P-2 are among them)
   const int k = clampi(bud_raw, 2, max_budget);
   const bool sel_all = (P == 0 || k >= P);
   bool in = false;      // this thread's page is in part A
@@ -978,7 +979,8 @@ static void launch_step_rgs(const StepLaunch& a, hipStream_t st) {
                      static_cast<const uint16_t*>(a.q), static_cast<uint16_t*>(a.kpool),
                      static_cast<uint16_t*>(a.vpool), a.table, a.nb, a.H, a.MP, a.KB, a.slice, a.per_wg,
                      a.mbox, a.out, a.lse_out, a.sel, a.cnt, static_cast<const uint8_t*>(a.summ), npairs,
-                     static_cast<const uint16_t*>(a.knew), static_cast<const uint16_t*>(a.vnew), a.coop);
+                     static_cast<const uint16_t*>(a.knew), static_cast<const uint16_t*>(a.vnew), a.coop,
+                     a.lag);
 }
 
 template <int R, int G>

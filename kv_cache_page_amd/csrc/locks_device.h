@@ -10,6 +10,18 @@ constexpr int kHeadDim = 128;
 constexpr int kPage = 16;
 // Pages one score workgroup covers (one Z partial per tile of this many).
 constexpr int kScorePagesPerWg = 128;
+// Flag bits of the score kernels: fill the entries of pages that are not
+// scored with NaN; score only the pages full before the current token (the
+// deferred build: F = (len - 1) / page_size).
+constexpr int kScoreFillNan = 1;
+constexpr int kScoreDeferred = 2;
+
+// Full pages that are summarised (scored) at length len: floor(len / B), or,
+// when the build of a page completed by the current token is deferred,
+// floor((len - 1) / B).
+__device__ __forceinline__ int scored_pages(int len, int lag) {
+  return (len - lag > 0 ? len - lag : 0) / kPage;
+}
 // Exchange counters of the fused decode step, per (sequence, KV head): 4
 // counters, one 128-byte line each, at the start of its mailbox.
 constexpr int kCoopCounters = 4;

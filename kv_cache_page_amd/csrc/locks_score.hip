@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void score_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ summ,
     const int32_t* __restrict__ table, const int32_t* __restrict__ seq_lens,
     float* __restrict__ scores, int64_t num_blocks, int H, int MP, int pages_per_wg,
-    int fill_nan, float2* __restrict__ zpart, const uint16_t* __restrict__ knew,
+    int flags, float2* __restrict__ zpart, const uint16_t* __restrict__ knew,
     const uint16_t* __restrict__ vnew, uint16_t* __restrict__ kpool,
     uint16_t* __restrict__ vpool, float* __restrict__ mxout, CoopZero coop) {
   constexpr SlotLayout L = slot_layout(R);
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void score_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l4 = lane & 3;
   const int len = clampi(seq_lens[s], 0, MP * kPage);
-  const int F = len / kPage;
+  const int F = scored_pages(len, (flags & kScoreDeferred) ? 1 : 0);
   const int j_lo = tile * pages_per_wg;
   if (knew && tile == 0 && threadIdx.x < 2 * (kHeadDim / 8) && len >= 1) {
     // decode-step append of the new token (position len - 1) for this head
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256) void score_kernel(
   }
   const int j_hi = min(j_lo + pages_per_wg, MP);
   float* srow = scores + ((int64_t)s * H + h) * MP * G;
-  if (fill_nan) {
+  if (flags & kScoreFillNan) {
     const int first = max(j_lo, F);
     for (int idx = threadIdx.x; idx < (j_hi - first) * G; idx += blockDim.x)
       srow[(int64_t)first * G + idx] = __builtin_nanf("");
@@ -326,7 +326,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ budgets, int32_t* __restrict__ sel_pages,
     int32_t* __restrict__ sel_count, float* __restrict__ keybuf, int H, int MP,
-    int max_budget) {
+    int max_budget, int lag) {
   extern __shared__ float sh_keys[];
   __shared__ uint32_t bits[kMaxBitmapWords];
   __shared__ uint32_t hist[kBins];
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
   constexpr int nthr = kSelectThreads;
   const int len = clampi(seq_lens[s], 0, MP * kPage);
   const int P = (len + kPage - 1) / kPage;
-  const int F = len / kPage;
+  const int F = scored_pages(len, lag);
   const int k = clampi(budgets[s], 2, max_budget);
   int32_t* out = sel_pages + ((int64_t)s * H + h) * max_budget;
   if (P == 0 || k >= P) {
@@ -550,13 +550,13 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
 template <int R, int G>
 static hipError_t launch_score_rg(const uint16_t* q, const uint8_t* summ, const int32_t* table,
                                   const int32_t* lens, float* scores, int64_t nb, int S, int H,
-                                  int MP, int fill_nan, float2* zpart, const void* knew,
+                                  int MP, int flags, float2* zpart, const void* knew,
                                   const void* vnew, void* kpool, void* vpool, float* mxout,
                                   CoopZero coop, hipStream_t st) {
   const int ppw = kScorePagesPerWg;
   dim3 grid(H, (MP + ppw - 1) / ppw, S);
   hipLaunchKernelGGL((score_kernel<R, G>), grid, dim3(256), 0, st, q, summ, table, lens, scores,
-                     nb, H, MP, ppw, fill_nan, zpart, static_cast<const uint16_t*>(knew),
+                     nb, H, MP, ppw, flags, zpart, static_cast<const uint16_t*>(knew),
                      static_cast<const uint16_t*>(vnew), static_cast<uint16_t*>(kpool),
                      static_cast<uint16_t*>(vpool), mxout, coop);
   return hipGetLastError();
@@ -565,13 +565,13 @@ static hipError_t launch_score_rg(const uint16_t* q, const uint8_t* summ, const 
 template <int G>
 static hipError_t launch_score_g(int r, const uint16_t* q, const uint8_t* summ,
                                  const int32_t* table, const int32_t* lens, float* scores,
-                                 int64_t nb, int S, int H, int MP, int fill_nan, float2* zpart,
+                                 int64_t nb, int S, int H, int MP, int flags, float2* zpart,
                                  const void* knew, const void* vnew, void* kpool, void* vpool,
                                  float* mxout, CoopZero coop, hipStream_t st) {
   switch (r) {
 #define LOCKS_R(RR)                                                                        \
   case RR:                                                                                 \
-    return launch_score_rg<RR, G>(q, summ, table, lens, scores, nb, S, H, MP, fill_nan,   \
+    return launch_score_rg<RR, G>(q, summ, table, lens, scores, nb, S, H, MP, flags,   \
                                   zpart, knew, vnew, kpool, vpool, mxout, coop, st);
     LOCKS_R(1) LOCKS_R(2) LOCKS_R(3) LOCKS_R(4) LOCKS_R(5) LOCKS_R(6) LOCKS_R(7) LOCKS_R(8)
     LOCKS_R(9) LOCKS_R(10) LOCKS_R(11) LOCKS_R(12) LOCKS_R(13) LOCKS_R(14) LOCKS_R(15) LOCKS_R(16)
@@ -584,22 +584,22 @@ static hipError_t launch_score_g(int r, const uint16_t* q, const uint8_t* summ,
 bool score_mfma_supported(int r);
 hipError_t launch_score_mfma(int r, int G, const void* q, const void* summ, const int32_t* table,
                              const int32_t* lens, float* scores, int64_t nb, int S, int H, int MP,
-                             int fill_nan, float2* zpart, const void* knew, const void* vnew,
+                             int flags, float2* zpart, const void* knew, const void* vnew,
                              void* kpool, void* vpool, float* mxout, CoopZero coop,
                              hipStream_t st);
 
 hipError_t launch_score(int r, int G, const void* q, const void* summ, const int32_t* table,
                         const int32_t* lens, float* scores, int64_t nb, int S, int H, int MP,
-                        int fill_nan, float2* zpart, const void* knew, const void* vnew,
+                        int flags, float2* zpart, const void* knew, const void* vnew,
                         void* kpool, void* vpool, float* mxout, CoopZero coop,
                         hipStream_t st) {
   if (score_mfma_supported(r))
-    return launch_score_mfma(r, G, q, summ, table, lens, scores, nb, S, H, MP, fill_nan, zpart,
+    return launch_score_mfma(r, G, q, summ, table, lens, scores, nb, S, H, MP, flags, zpart,
                              knew, vnew, kpool, vpool, mxout, coop, st);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint8_t* ss = static_cast<const uint8_t*>(summ);
   switch (G) {
-#define LOCKS_ARGS qq, ss, table, lens, scores, nb, S, H, MP, fill_nan, zpart, knew, vnew, kpool, vpool, mxout, coop, st
+#define LOCKS_ARGS qq, ss, table, lens, scores, nb, S, H, MP, flags, zpart, knew, vnew, kpool, vpool, mxout, coop, st
     case 1: return launch_score_g<1>(r, LOCKS_ARGS);
     case 2: return launch_score_g<2>(r, LOCKS_ARGS);
     case 4: return launch_score_g<4>(r, LOCKS_ARGS);
@@ -611,25 +611,26 @@ hipError_t launch_score(int r, int G, const void* q, const void* summ, const int
 template <int G>
 static void launch_select_g(dim3 grid, int MP, const float* scores, const int32_t* lens,
                             const int32_t* budgets, int32_t* sel, int32_t* cnt, float* keybuf,
-                            int H, int max_budget, hipStream_t st) {
+                            int H, int max_budget, int lag, hipStream_t st) {
   if (MP <= kSelectLdsPages) {
     hipLaunchKernelGGL((select_kernel<G, true>), grid, dim3(kSelectThreads),
                        (size_t)MP * sizeof(float), st, scores, lens, budgets, sel, cnt, keybuf,
-                       H, MP, max_budget);
+                       H, MP, max_budget, lag);
   } else {
     hipLaunchKernelGGL((select_kernel<G, false>), grid, dim3(kSelectThreads), 0, st, scores, lens,
-                       budgets, sel, cnt, keybuf, H, MP, max_budget);
+                       budgets, sel, cnt, keybuf, H, MP, max_budget, lag);
   }
 }
 
+// lag = 1: only the pages full before the current token are scored (deferred build).
 hipError_t launch_select(int G, const float* scores, const int32_t* lens, const int32_t* budgets,
                          int32_t* sel, int32_t* cnt, float* keybuf, int S, int H, int MP,
-                         int max_budget, hipStream_t st) {
+                         int max_budget, int lag, hipStream_t st) {
   dim3 grid(H, S);
   switch (G) {
-    case 1: launch_select_g<1>(grid, MP, scores, lens, budgets, sel, cnt, keybuf, H, max_budget, st); break;
-    case 2: launch_select_g<2>(grid, MP, scores, lens, budgets, sel, cnt, keybuf, H, max_budget, st); break;
-    case 4: launch_select_g<4>(grid, MP, scores, lens, budgets, sel, cnt, keybuf, H, max_budget, st); break;
+    case 1: launch_select_g<1>(grid, MP, scores, lens, budgets, sel, cnt, keybuf, H, max_budget, lag, st); break;
+    case 2: launch_select_g<2>(grid, MP, scores, lens, budgets, sel, cnt, keybuf, H, max_budget, lag, st); break;
+    case 4: launch_select_g<4>(grid, MP, scores, lens, budgets, sel, cnt, keybuf, H, max_budget, lag, st); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -12,7 +12,7 @@ __global__ __launch_bounds__(256 * TPW) void score_mfma_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ summ,
     const int32_t* __restrict__ table, const int32_t* __restrict__ seq_lens,
     float* __restrict__ scores, int64_t num_blocks, int H, int MP, int pages_per_wg,
-    int fill_nan, float2* __restrict__ zpart, const uint16_t* __restrict__ knew,
+    int flags, float2* __restrict__ zpart, const uint16_t* __restrict__ knew,
     const uint16_t* __restrict__ vnew, uint16_t* __restrict__ kpool,
     uint16_t* __restrict__ vpool, float* __restrict__ mxout, CoopZero coop) {
   const int s = blockIdx.z, h = blockIdx.x;
@@ -23,7 +23,7 @@ __global__ __launch_bounds__(256 * TPW) void score_mfma_kernel(
   const int ntiles = (MP + pages_per_wg - 1) / pages_per_wg;
   float zm = -__builtin_inff(), zs = 0.f;
   if (tile < ntiles)
-    score_tile<R, G>(q, summ, table, seq_lens, scores, num_blocks, H, MP, pages_per_wg, fill_nan,
+    score_tile<R, G>(q, summ, table, seq_lens, scores, num_blocks, H, MP, pages_per_wg, flags,
                      knew, vnew, kpool, vpool, mxout, s, h, tile, wave, tid, zm, zs);
   if (zpart) {
     __shared__ float zred[TPW][4][4][2];
@@ -40,7 +40,7 @@ __global__ __launch_bounds__(256 * TPW) void score_mfma_kernel(
 template <int R, int G>
 static hipError_t launch_r_g(const uint16_t* q, const uint8_t* summ, const int32_t* table,
                              const int32_t* lens, float* scores, int64_t nb, int S, int H, int MP,
-                             int fill_nan, float2* zpart, const void* knew, const void* vnew,
+                             int flags, float2* zpart, const void* knew, const void* vnew,
                              void* kpool, void* vpool, float* mxout, CoopZero coop,
                              hipStream_t st) {
   constexpr int TPW = 1;
@@ -48,7 +48,7 @@ static hipError_t launch_r_g(const uint16_t* q, const uint8_t* summ, const int32
   const int ntiles = (MP + ppw - 1) / ppw;
   dim3 grid(H, (ntiles + TPW - 1) / TPW, S);  // heads first: 8 heads -> one XCD each
   hipLaunchKernelGGL((score_mfma_kernel<R, G, TPW>), grid, dim3(256 * TPW), 0, st, q, summ, table, lens,
-                     scores, nb, H, MP, ppw, fill_nan, zpart, static_cast<const uint16_t*>(knew),
+                     scores, nb, H, MP, ppw, flags, zpart, static_cast<const uint16_t*>(knew),
                      static_cast<const uint16_t*>(vnew), static_cast<uint16_t*>(kpool),
                      static_cast<uint16_t*>(vpool), mxout, coop);
   return hipGetLastError();
@@ -58,12 +58,12 @@ bool score_mfma_supported(int r) { return r == 4 || r == 8 || r == 16; }
 
 hipError_t launch_score_mfma(int r, int G, const void* q, const void* summ, const int32_t* table,
                              const int32_t* lens, float* scores, int64_t nb, int S, int H, int MP,
-                             int fill_nan, float2* zpart, const void* knew, const void* vnew,
+                             int flags, float2* zpart, const void* knew, const void* vnew,
                              void* kpool, void* vpool, float* mxout, CoopZero coop,
                              hipStream_t st) {
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint8_t* ss = static_cast<const uint8_t*>(summ);
-#define LOCKS_ARGS qq, ss, table, lens, scores, nb, S, H, MP, fill_nan, zpart, knew, vnew, kpool, vpool, mxout, coop, st
+#define LOCKS_ARGS qq, ss, table, lens, scores, nb, S, H, MP, flags, zpart, knew, vnew, kpool, vpool, mxout, coop, st
 #define LOCKS_G(RR)                                  \
   switch (G) {                                       \
     case 1: return launch_r_g<RR, 1>(LOCKS_ARGS);    \

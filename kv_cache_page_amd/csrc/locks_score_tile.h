@@ -160,7 +160,7 @@ __device__ __forceinline__ void score_tile(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ summ,
     const int32_t* __restrict__ table, const int32_t* __restrict__ seq_lens,
     float* __restrict__ scores, int64_t num_blocks, int H, int MP, int pages_per_wg,
-    int fill_nan, const uint16_t* __restrict__ knew, const uint16_t* __restrict__ vnew,
+    int flags, const uint16_t* __restrict__ knew, const uint16_t* __restrict__ vnew,
     uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool, float* __restrict__ mxout,
     int s, int h, int tile, int wave, int tid, float& zm, float& zs) {
   static_assert(R == 4 || R == 8 || R == 16, "matrix-core path covers ranks 4, 8, 16");
@@ -196,7 +196,7 @@ __device__ __forceinline__ void score_tile(
   }
   asm volatile("" ::: "memory");
   const int len = clampi(seq_lens[s], 0, MP * kPage);
-  const int F = len / kPage;
+  const int F = scored_pages(len, (flags & kScoreDeferred) ? 1 : 0);
   if (knew && tile == 0 && tid < 2 * (kHeadDim / 8) && len >= 1) {
     // decode-step append of the new token (position len - 1) for this head
     const int blk = table[(int64_t)s * MP + (len - 1) / kPage];
@@ -212,7 +212,7 @@ __device__ __forceinline__ void score_tile(
   }
   const int j_hi = min(j_lo + pages_per_wg, MP);
   float* srow = scores + ((int64_t)s * H + h) * MP * G;
-  if (fill_nan) {
+  if (flags & kScoreFillNan) {
     const int first = max(j_lo, F);
     for (int idx = tid; idx < (j_hi - first) * G; idx += 256)
       reinterpret_cast<uint32_t*>(srow)[(int64_t)first * G + idx] = 0x7FC00000u;  // quiet NaN

@@ -19,6 +19,7 @@ struct StepLaunch {
   const int32_t* table;
   int64_t nb;
   int S, H, MP, KB, nsplit, slice, per_wg;
+  int lag;              // 1: only the pages full before the current token are scored
   uint32_t* mbox;
   float* out;
   float* lse_out;

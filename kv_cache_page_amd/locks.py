@@ -24,6 +24,7 @@ ERR_INVALID_ARG = -1
 ERR_UNSUPPORTED = -2
 ERR_WORKSPACE = -3
 ERR_HIP = -4
+STEP_DEFER_BUILD = 1      # LOCKS_STEP_DEFER_BUILD
 
 ENTRY_POINTS = (
     "locks_status_string", "locks_summary_slot_bytes", "locks_summary_slot_stride",
@@ -80,13 +81,14 @@ _select_pages = _sig("locks_select_pages", ctypes.c_int,
 _sparse_attn = _sig("locks_sparse_attn", ctypes.c_int,
                     [_pd, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp,
                      _vp, _sz, _vp])
+_u32 = ctypes.c_uint32
 _decode_step = _sig("locks_decode_step", ctypes.c_int,
                     [_pd, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32,
-                     _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp])
+                     _i32, _vp, _vp, _vp, _vp, _u32, _vp, _sz, _vp])
 
 _decode_step_noalloc = _sig("locks_decode_step_noalloc", ctypes.c_int,
                             [_pd, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32,
-                             _i32, _i32, _vp, _vp, _vp, _vp, _vp])
+                             _i32, _i32, _vp, _vp, _vp, _vp, _u32, _vp])
 
 
 def status_string(status):
@@ -229,9 +231,10 @@ def sparse_attn(dims, q, k_pool, v_pool, block_table, seq_lens, sel_pages, sel_c
 
 def decode_step(dims, q, k_new, v_new, k_pool, v_pool, summaries, block_table, seq_lens, budgets,
                 max_budget, out, workspace, lse_out=None, sel_pages=None, sel_count=None,
-                seq_lens_host=None, stream=None):
+                seq_lens_host=None, defer_build=False, stream=None):
     """locks_decode_step. seq_lens_host: optional CPU int32 tensor equal to
-    seq_lens (lets the call skip the page-build launch when no page fills)."""
+    seq_lens (lets the call skip the page-build launch when no page fills).
+    defer_build: LOCKS_STEP_DEFER_BUILD (the caller then runs build_filled)."""
     if seq_lens_host is not None:
         if seq_lens_host.device.type != "cpu":
             raise ValueError("seq_lens_host must be a CPU tensor")
@@ -249,6 +252,7 @@ def decode_step(dims, q, k_new, v_new, k_pool, v_pool, summaries, block_table, s
                       _ptr(lse_out, torch.float32, "lse_out"),
                       _ptr(sel_pages, torch.int32, "sel_pages"),
                       _ptr(sel_count, torch.int32, "sel_count"),
+                      STEP_DEFER_BUILD if defer_build else 0,
                       _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
                       _stream(stream))
     _check(st, "locks_decode_step")
@@ -256,7 +260,7 @@ def decode_step(dims, q, k_new, v_new, k_pool, v_pool, summaries, block_table, s
 
 def decode_step_noalloc(dims, q, k_new, v_new, k_pool, v_pool, summaries, block_table, seq_lens,
                         budgets, max_budget, out, lse_out=None, sel_pages=None, sel_count=None,
-                        seq_lens_host=None, stream=None):
+                        seq_lens_host=None, defer_build=False, stream=None):
     """locks_decode_step_noalloc: decode_step on the library's built-in
     per-device scratch (no workspace argument, nothing allocated)."""
     if seq_lens_host is not None:
@@ -273,7 +277,7 @@ def decode_step_noalloc(dims, q, k_new, v_new, k_pool, v_pool, summaries, block_
         _ptr(budgets, torch.int32, "budgets"), seq_lens.numel(), block_table.shape[1], max_budget,
         _ptr(out, torch.float32, "out"), _ptr(lse_out, torch.float32, "lse_out"),
         _ptr(sel_pages, torch.int32, "sel_pages"), _ptr(sel_count, torch.int32, "sel_count"),
-        _stream(stream))
+        STEP_DEFER_BUILD if defer_build else 0, _stream(stream))
     _check(st, "locks_decode_step_noalloc")
 
 

@@ -196,6 +196,8 @@ class LayerStack:
     max_len: int
     B: int = 16
     d: int = 128
+    k_all: torch.Tensor = None  # the one allocation the layers' pools are slices of
+    v_all: torch.Tensor = None
 
 
 def make_layer_stack(layers, max_len, H, G, steps, seed, needle_pages, device="cpu",
@@ -207,6 +209,10 @@ def make_layer_stack(layers, max_len, H, G, steps, seed, needle_pages, device="c
     gc = _gen(seed + 7919, "cpu")
     P = (max_len + B - 1) // B
     table = torch.randperm(P, generator=gc).to(torch.int32).view(1, P)
+    # every layer's pool is a slice of one allocation ([layers * P][H][B][d]),
+    # so block id b of layer l is block l * P + b of the whole
+    k_all = torch.empty(layers * P, H, B, d, dtype=torch.bfloat16, device=device)
+    v_all = torch.empty_like(k_all)
     kps, vps, qs, needles = [], [], [], []
     for l in range(layers):
         g = _gen(seed * 1000 + l, device)
@@ -219,11 +225,14 @@ def make_layer_stack(layers, max_len, H, G, steps, seed, needle_pages, device="c
             slot = int(torch.randint(B, (1,), generator=gc))
             k[int(table[0, j]), h, slot] = NEEDLE_NORM * unit[h]
             needles.append((l, h, j, slot))
-        kps.append(k.to(torch.bfloat16))
-        vps.append(v.to(torch.bfloat16))
+        k_all[l * P:(l + 1) * P] = k
+        v_all[l * P:(l + 1) * P] = v
+        kps.append(k_all[l * P:(l + 1) * P])
+        vps.append(v_all[l * P:(l + 1) * P])
         noise = torch.randn(steps, H, G, d, generator=g, device=device)
         qs.append((q_dir[None, :, None, :] + QUERY_NOISE * noise).reshape(steps, 1, H * G, d))
         del k, v
     q = torch.stack(qs, dim=1).to(torch.bfloat16)        # [steps][layers][1][H*G][d]
     return LayerStack(k_pools=kps, v_pools=vps, q=q, block_table=table.to(device),
-                      needles=needles, H=H, G=G, max_len=max_len, B=B, d=d)
+                      needles=needles, H=H, G=G, max_len=max_len, B=B, d=d, k_all=k_all,
+                      v_all=v_all)

@@ -42,16 +42,18 @@ def oracle_summaries(k_pool, table, seq_lens, H, r, num_blocks):
     return summ
 
 
-def oracle_head(q, k_pool, v_pool, table, seq_lens, budgets, summ, s, h, G, r, mode="quantised"):
+def oracle_head(q, k_pool, v_pool, table, seq_lens, budgets, summ, s, h, G, r, mode="quantised",
+                deferred=False):
     L = int(seq_lens[s])
     Kp, Vp = head_pages(k_pool, v_pool, table, L, s, h)
     qq = np64(q[s, h * G:(h + 1) * G])
-    F = L // B
+    F = (max(L - 1, 0) if deferred else L) // B
     slots = None
     if summ is not None and F > 0:
         blocks = table[s, :F].long().cpu().numpy()
         slots = summ[blocks, h]
-    return O.decode_head(qq, Kp, Vp, L, int(budgets[s]), slots=slots, r=r, mode=mode)
+    return O.decode_head(qq, Kp, Vp, L, int(budgets[s]), slots=slots, r=r, mode=mode,
+                         deferred=deferred)
 
 
 def selection_mismatch(gpu_sel, ora_sel, key, P, tol=1e-5):

@@ -123,12 +123,12 @@ def test_decode_step_rejects_before_launch():
         a = dict(q=fake, k_new=fake, v_new=fake, k_pool=fake, v_pool=fake, summ=fake, nb=40000,
                  table=fake, lens=fake, lens_host=ctypes.cast(host_lens, ctypes.c_void_p),
                  budgets=fake, S=2, MP=17000, KB=64, out=fake, lse=None, sel=None, cnt=None,
-                 ws=fake, ws_bytes=need - 1)
+                 flags=0, ws=fake, ws_bytes=need - 1)
         a.update(kw)
         return L._decode_step(ctypes.byref(d), a["q"], a["k_new"], a["v_new"], a["k_pool"],
                               a["v_pool"], a["summ"], a["nb"], a["table"], a["lens"],
                               a["lens_host"], a["budgets"], a["S"], a["MP"], a["KB"], a["out"],
-                              a["lse"], a["sel"], a["cnt"], a["ws"], a["ws_bytes"], None)
+                              a["lse"], a["sel"], a["cnt"], a["flags"], a["ws"], a["ws_bytes"], None)
 
     assert call() == L.ERR_WORKSPACE                       # one byte short, NULL selection outputs
     assert call(ws=None, ws_bytes=need) == L.ERR_WORKSPACE
@@ -137,4 +137,5 @@ def test_decode_step_rejects_before_launch():
     assert call(k_new=ctypes.c_void_p(264)) == L.ERR_INVALID_ARG   # not 16-byte aligned
     assert call(MP=70000) == L.ERR_UNSUPPORTED
     assert call(KB=1) == L.ERR_INVALID_ARG
+    assert call(flags=2, ws_bytes=need) == L.ERR_INVALID_ARG  # unknown flag bit
     assert call(S=0) == L.OK                                # empty batch: nothing to do

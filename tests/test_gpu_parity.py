@@ -59,7 +59,7 @@ def _run_decode(L, dims, bd, summ_dev, max_budget, scores=True):
                 lse=lse.cpu().numpy())
 
 
-def _check_against_oracle(b, summ, res, r, max_budget, heads=None, score_tol=1e-3):
+def _check_against_oracle(b, summ, res, r, max_budget, heads=None, score_tol=1e-3, deferred=False):
     """Compare one decode step (every or the listed (seq, head)) with the
     oracle fed the same summaries. Returns (max score error, mismatched pages,
     worst attention rel-L2)."""
@@ -70,7 +70,7 @@ def _check_against_oracle(b, summ, res, r, max_budget, heads=None, score_tol=1e-
         Lq = int(b.seq_lens[s])
         P, F = (Lq + 15) // 16, Lq // 16
         ora = Hh.oracle_head(b.q, b.k_pool, b.v_pool, b.block_table, b.seq_lens, b.budgets, summ,
-                             s, h, G, r)
+                             s, h, G, r, deferred=deferred)
         if res["scores"] is not None and F:
             d = np.abs(res["scores"][s, h, :F] - ora["scores"])
             worst_s = max(worst_s, float(d.max()))
@@ -450,7 +450,8 @@ def _step_state(b, r):
     return kp, vp, kn, vn, summ, completed
 
 
-def _run_step(L, dims, b, kp, vp, kn, vn, summ, max_budget, host_lens=True, with_sel=True):
+def _run_step(L, dims, b, kp, vp, kn, vn, summ, max_budget, host_lens=True, with_sel=True,
+              defer_build=False):
     S, H, G = b.num_seqs, b.H, b.G
     kp_d, vp_d = kp.to(DEV), vp.to(DEV)
     summ_d = torch.from_numpy(summ).to(DEV)
@@ -463,7 +464,7 @@ def _run_step(L, dims, b, kp, vp, kn, vn, summ, max_budget, host_lens=True, with
     L.decode_step(dims, b.q.to(DEV), kn.to(DEV), vn.to(DEV), kp_d, vp_d, summ_d,
                   b.block_table.to(DEV), b.seq_lens.to(DEV), b.budgets.to(DEV), max_budget, out,
                   ws, lse_out=lse, sel_pages=sel, sel_count=cnt,
-                  seq_lens_host=b.seq_lens.cpu() if host_lens else None)
+                  seq_lens_host=b.seq_lens.cpu() if host_lens else None, defer_build=defer_build)
     torch.cuda.synchronize()
     res = dict(sel=None if sel is None else sel.cpu().numpy(),
                cnt=None if cnt is None else cnt.cpu().numpy(), scores=None,
@@ -851,3 +852,54 @@ def test_batch32_full_size(L):
     assert frac <= 1e-3
     check(dict(sel=sel.cpu().numpy(), cnt=cnt.cpu().numpy(), out=out.cpu().numpy(),
                lse=lse.cpu().numpy()), "locks_decode_step")
+
+
+@pytest.mark.parametrize("G,r", [(4, 8), (2, 6)])
+def test_decode_step_deferred_build(L, G, r):
+    """LOCKS_STEP_DEFER_BUILD (the build outside the decode critical path):
+    the step appends every token, builds nothing and scores only the pages full
+    before its token (checked against the oracle's deferred reading); then
+    locks_build_filled summarises exactly the pages the tokens completed
+    (code rule against the oracle), and the next step, one token later on the
+    same pools (no page completes), uses them. Rank 6 takes the separate score
+    launch."""
+    _say(f"[gpu] decode step with the build deferred, G={G} r={r}")
+    lens = [16, 17, 32, 40 * 16, 40 * 16 + 1, 300 * 16 + 9, 257 * 16, 33, 64 * 16]
+    budgets = [2, 3, 5, 2, 7, 64, 300, 2, 9]
+    b2 = synth.make_decode_batch([x + 1 for x in lens], 3, G, budgets, seed=260 + G, extra_blocks=11)
+    b1 = synth.DecodeBatch(k_pool=b2.k_pool, v_pool=b2.v_pool, q=b2.q, block_table=b2.block_table,
+                           seq_lens=torch.tensor(lens, dtype=torch.int32), budgets=b2.budgets,
+                           needles=b2.needles, H=b2.H, G=G)
+    kp, vp, kn, vn, summ, completed = _step_state(b1, r)
+    dims = L.Dims(b1.H, G, r)
+    res, kpa, vpa, sa = _run_step(L, dims, b1, kp, vp, kn, vn, summ, 300, defer_build=True)
+    assert torch.equal(kpa, b2.k_pool) and torch.equal(vpa, b2.v_pool)
+    assert np.array_equal(sa, summ)                       # nothing built by the step
+    _, nmis, wo = _check_against_oracle(b1, summ, res, r, 300, deferred=True)
+    _say(f"    deferred step: near-tie swaps {nmis}, worst attn rel-L2 {wo:.2e}")
+    # the caller's build of the completed pages
+    summ_d = torch.from_numpy(sa).to(DEV)
+    L.build_filled(dims, kpa.to(DEV), b1.block_table.to(DEV), b1.seq_lens.to(DEV), summ_d)
+    torch.cuda.synchronize()
+    built = summ_d.cpu().numpy()
+    pairs = [(blk, h) for blk in completed for h in range(b1.H)]
+    keys = np.stack([Hh.np64(b2.k_pool[blk, h]) for blk, h in pairs])
+    frac, _, _ = _compare_codes(np.stack([built[blk, h] for blk, h in pairs]), keys, r)
+    assert frac <= 1e-3
+    for blk in range(b1.num_blocks):
+        if blk not in completed:
+            assert np.array_equal(built[blk], summ[blk])
+    # the next step on the same pools: the token at position len, appended again
+    kn2 = torch.zeros_like(kn)
+    vn2 = torch.zeros_like(vn)
+    for sq, Lq in enumerate(lens):
+        blk, t = int(b2.block_table[sq, Lq // 16]), Lq % 16
+        kn2[sq], vn2[sq] = b2.k_pool[blk, :, t], b2.v_pool[blk, :, t]
+    summ_ora = summ.copy()
+    ora_slots = O.build_slots(keys, r)[0]
+    for i, (blk, h) in enumerate(pairs):
+        summ_ora[blk, h] = ora_slots[i]
+    res2, kpb, _, _ = _run_step(L, dims, b2, kpa, vpa, kn2, vn2, summ_ora, 300, defer_build=True)
+    assert torch.equal(kpb, b2.k_pool)
+    _, nmis2, wo2 = _check_against_oracle(b2, summ_ora, res2, r, 300, deferred=True)
+    _say(f"    next step: near-tie swaps {nmis2}, worst attn rel-L2 {wo2:.2e}")
