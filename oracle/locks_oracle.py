@@ -316,6 +316,39 @@ def attend(q, K, V):
 
 
 # ----------------------------------------------------------------------------
+# Fixed shared sketch ([N] §3.3, Proposition 1): the family of scoring rules
+# that see a page only through the query, its centroid and the sketched keys
+# W^T k_i for one projection W (d x rho) shared by all pages.
+# ----------------------------------------------------------------------------
+
+def shared_sketch_scores(q, K, W):
+    """A member of that family: the rank-rho reconstruction of every key in the
+    shared basis W (orthonormal columns), k_i ~ mu + W W^T (k_i - mu), scored
+    like eq. 4: LSE_i((q . mu + (W^T q) . (W^T (k_i - mu))) / sqrt(d)). It
+    depends on the page only through mu and the sketches W^T k_i.
+    q: (G, d); K: (P, B, d); W: (d, rho). Returns (P, G)."""
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    mu = K.mean(axis=1)                                    # (P, d)
+    sk = K @ W - (mu @ W)[:, None, :]                      # (P, B, rho) = W^T (k_i - mu)
+    a = mu @ q.T                                           # (P, G)
+    inner = np.einsum("pbr,gr->pgb", sk, q @ W)            # (P, G, B)
+    logits = (a[:, :, None] + inner) / math.sqrt(q.shape[1])
+    return logsumexp(logits, axis=2)
+
+
+def blind_direction_pair(K, W, u, c, a=0, b=1):
+    """The construction of Proposition 1: keys K (B, d) of one page, u a unit
+    vector orthogonal to span(W); returns K' with c u added to key a and
+    subtracted from key b (the centroid and every W^T k_i are unchanged)."""
+    Kp = np.array(K, dtype=np.float64, copy=True)
+    Kp[a] += c * u
+    Kp[b] -= c * u
+    return Kp
+
+
+# ----------------------------------------------------------------------------
 # One decode step for one (sequence, KV head)
 # ----------------------------------------------------------------------------
 
