@@ -13,12 +13,15 @@ import math
 import torch
 
 SIGMAS = (3.0, 2.5, 2.0, 1.6, 1.3, 1.0, 0.8, 0.6)
+# a slowly decaying spectrum over all 15 centred directions of a 16-token
+# page (sigma_k = 3 k^-0.5): rank-8 summaries then leave a real tail
+TAIL_SIGMAS = tuple(3.0 * k ** -0.5 for k in range(1, 16))
 NOISE = 0.05
 NEEDLE_NORM = 6.0
 QUERY_NOISE = 0.3
 
 __all__ = [
-    "SIGMAS", "DecodeBatch", "page_keys", "page_values", "gqa_queries",
+    "SIGMAS", "TAIL_SIGMAS", "DecodeBatch", "page_keys", "page_values", "gqa_queries",
     "make_decode_batch", "config_batch", "random_pages", "LayerStack", "make_layer_stack",
 ]
 
@@ -99,14 +102,15 @@ class DecodeBatch:
 
 
 def make_decode_batch(seq_lens, H, G, budgets, seed, needles_per_head=1,
-                      shuffle=True, device="cpu", extra_blocks=0, d=128, B=16):
+                      shuffle=True, device="cpu", extra_blocks=0, d=128, B=16,
+                      sigmas=SIGMAS):
     """Ragged batch of sequences over a shared block pool.
 
     seq_lens: list of token counts (current token included). Blocks of all
     sequences are drawn from one pool (shuffled when `shuffle`), with
     `extra_blocks` unused blocks in the pool. Needles go to uniformly drawn
     logical pages 1..P-2 (never the sink or the recent page) and a uniform
-    slot within the page."""
+    slot within the page. `sigmas` sets the within-page key spectrum."""
     g = _gen(seed, device)
     gc = _gen(seed + 7919, "cpu")          # host-side choices (tables, needles)
     pages = [(L + B - 1) // B for L in seq_lens]
@@ -119,7 +123,7 @@ def make_decode_batch(seq_lens, H, G, budgets, seed, needles_per_head=1,
         table[s, :P] = perm[pos:pos + P].to(torch.int32)
         pos += P
     n_pages = nblk * H
-    k = page_keys(n_pages, g, B, d, device).view(nblk, H, B, d)
+    k = page_keys(n_pages, g, B, d, device, sigmas=sigmas).view(nblk, H, B, d)
     v = page_values(n_pages, g, B, d, device).view(nblk, H, B, d)
     q, q_dir = gqa_queries(len(seq_lens) * H, G, g, d, device)
     needles = []
