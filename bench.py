@@ -32,7 +32,10 @@ Further workloads, each with its own roofline entry under "workloads":
                   shuffled block pool, k = max(8, ceil(P / 16));
   bulk_build      locks_build over the 2,097,152 pages of the 32-layer
                   cache at r = 4, 8 and 16 (pages/s, bytes per page, fp64
-                  ALU roofline).
+                  ALU roofline);
+  offload_ctx128k the 128K step with the K/V pools in pinned host memory
+                  (summaries in HBM): the selected pages cross the host
+                  link (roofline against PCIe 5.0 x16, one direction).
 
 The final timed step's layer-0 outputs are checked against the fp64 oracle
 (and every output for NaN); the run exits non-zero on a mismatch.
@@ -54,6 +57,7 @@ sys.path.insert(0, ROOT)
 LAYERS, H, G, D, B, R, BUDGET, MAX_LEN = 32, 8, 4, 128, 16, 8, 128, 131072
 PAGE_KV_BYTES = 2 * B * D * 2
 HBM_PEAK_GBS = 8000.0
+HOST_LINK_PEAK_GBS = 63.0     # PCIe 5.0 x16, one direction (32 GT/s x 16 lanes, 128b/130b)
 FP64_VALU_PEAK_TFLOPS = 78.6
 METRIC = "decode-step µs and achieved HBM GB/s (summary+selected KV) at 128K ctx, 8 KV heads"
 CSRC = os.path.join(ROOT, "kv_cache_page_amd", "csrc")
@@ -435,6 +439,99 @@ def run_batch32(torch, L, synth, dev, reps=20, seed=3):
 
 
 # ---------------------------------------------------------------------------
+# offload: K/V pools in pinned host memory, summaries in HBM
+# ---------------------------------------------------------------------------
+
+def run_offload(torch, L, synth, dev, layers=4, reps=10, seed=5):
+    """The 128K-context decode step of `layers` layers (independent caches of
+    131072 tokens; the new token starts a page; k = 128) with each layer's K
+    and V pools in pinned, device-mapped host memory: the score and the
+    selection read the summaries in HBM, the attention reads the selected
+    pages across the host link. Also timed: the same caches in HBM, and a
+    DMA copy of one layer's K pool from pinned host memory (the link's
+    practical read rate)."""
+    ln = MAX_LEN + 1
+    dims = L.Dims(H, G, R)
+    log(f"[bench] offload: {layers} layers of a 128K-token cache in pinned host memory")
+    state = []
+    for i in range(layers):
+        b = synth.make_decode_batch([ln], H, G, [BUDGET], seed=seed * 100 + i, needles_per_head=1,
+                                    device=dev)
+        summ = L.alloc_summaries(dims, b.num_blocks, dev)
+        L.build(dims, b.k_pool, b.block_table[0, :ln // B].contiguous(), summ)
+        blk, t = int(b.block_table[0, (ln - 1) // B]), (ln - 1) % B
+        kn = b.k_pool[blk, :, t].clone()[None]
+        vn = b.v_pool[blk, :, t].clone()[None]
+        hk = L.HostPool(b.k_pool.shape)
+        hv = L.HostPool(b.v_pool.shape)
+        hk.host.copy_(b.k_pool.cpu())
+        hv.host.copy_(b.v_pool.cpu())
+        state.append((b, summ, kn, vn, hk, hv))
+    torch.cuda.synchronize()
+    MP = state[0][0].max_pages
+    ws = L.alloc_workspace(dims, 1, MP, BUDGET, dev)
+    outs = {m: torch.empty(layers, 1, H * G, D, device=dev) for m in ("host", "hbm")}
+    host_len = torch.tensor([ln], dtype=torch.int32)
+
+    def step(mode):
+        for i, (b, summ, kn, vn, hk, hv) in enumerate(state):
+            kp, vp = (hk, hv) if mode == "host" else (b.k_pool, b.v_pool)
+            L.decode_step(dims, b.q, kn, vn, kp, vp, summ, b.block_table, b.seq_lens, b.budgets,
+                          BUDGET, outs[mode][i], ws, seq_lens_host=host_len)
+
+    for m in ("host", "hbm"):
+        step(m)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(outs["host"], outs["hbm"]))
+    graphs = capture(torch, step, ["host", "hbm"])
+    us = {}
+    for m in ("host", "hbm"):
+        graphs[m].replay()
+        ms = timed(torch, {i: graphs[m] for i in range(reps)}, range(reps))
+        us[m] = ms * 1e3 / (reps * layers)
+    s_bytes, kv_bytes = head_bytes(ln, BUDGET)
+    link_bytes = H * kv_bytes + H * 2 * D * 2          # selected pages read, new token written
+    # DMA read rate of pinned host memory (one layer's K pool, 268 MB)
+    src = torch.empty(state[0][0].k_pool.shape, dtype=torch.bfloat16, pin_memory=True)
+    dst = torch.empty(src.shape, dtype=torch.bfloat16, device=dev)
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(3):
+        dst.copy_(src, non_blocking=True)
+    e.record()
+    e.synchronize()
+    dma_gbs = 3 * src.numel() * 2 / (a.elapsed_time(e) * 1e-3) / 1e9
+    achieved = link_bytes / (us["host"] * 1e-6) / 1e9
+    nan = bool(torch.isnan(outs["host"]).any())
+    log(f"[bench] offload decode step {us['host']:.1f} us per layer ({achieved:.1f} GB/s over the "
+        f"host link; DMA copy {dma_gbs:.1f} GB/s), HBM pools {us['hbm']:.1f} us; identical "
+        f"outputs: {same}")
+    for (b, summ, kn, vn, hk, hv) in state:
+        hk.free()
+        hv.free()
+    del state, ws, graphs, src, dst
+    return {"workload": f"1 seq, 131072 cached tokens + the new one, {layers} layers (independent "
+                        "caches) stepped in turn, 8 KV heads x 4 q heads, k=128; K/V pools in "
+                        "pinned host memory, summaries in HBM",
+            "us_per_layer_step": round(us["host"], 2), "us_per_layer_step_hbm_pools": round(us["hbm"], 2),
+            "link_bytes_per_layer_step": link_bytes, "hbm_summary_bytes_per_layer_step": H * s_bytes,
+            "host_resident_kv_bytes_per_layer": 2 * state_bytes(ln),
+            "roofline": {"kernel": "decode_step_kernel<8,4,16> (locks_decode_step, host pools)",
+                         "bound": "host link", "achieved": round(achieved, 2),
+                         "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HOST_LINK_PEAK_GBS, 4), "traffic": None,
+                         "dma_copy_gbs": round(dma_gbs, 2)},
+            "identical_to_hbm_pools": same, "any_nan": nan or not same}
+
+
+def state_bytes(ln):
+    """bf16 bytes of one pool (K or V) of one layer holding ln tokens' pages."""
+    return ((ln + B - 1) // B) * H * B * D * 2
+
+
+# ---------------------------------------------------------------------------
 # bulk build at the prefill -> decode boundary, r = 4, 8, 16
 # ---------------------------------------------------------------------------
 
@@ -585,7 +682,7 @@ def main():
                     help="oracle CPU-baseline budget (0 skips it; the final-step check still runs)")
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--only", default="all",
-                    help="comma list of ctx128k, ctx32k, batch32, build (profiling runs)")
+                    help="comma list of ctx128k, ctx32k, batch32, build, offload (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed region, run one elementwise copy that reads 1 GiB "
                          "and writes 1 GiB (the reference for HBM byte counters)")
@@ -600,7 +697,8 @@ def main():
         print("need 0 <= warmup, 1 <= steps, 2 <= warmup + steps <= 256 decode steps",
               file=sys.stderr)
         sys.exit(2)
-    only = set(args.only.split(",")) if args.only != "all" else {"ctx128k", "ctx32k", "batch32", "build"}
+    only = (set(args.only.split(",")) if args.only != "all"
+            else {"ctx128k", "ctx32k", "batch32", "build", "offload"})
 
     import torch
     import synth
@@ -619,6 +717,9 @@ def main():
         torch.cuda.empty_cache()
     if "batch32" in only:
         workloads["batch32_ragged"] = run_batch32(torch, L, synth, dev)
+        torch.cuda.empty_cache()
+    if "offload" in only:
+        workloads["offload_ctx128k"] = run_offload(torch, L, synth, dev)
         torch.cuda.empty_cache()
 
     if args.calibrate_copy:

@@ -327,6 +327,30 @@ locks_status locks_decode_step_noalloc(const locks_dims* dims, const void* q, co
                                        float* out, float* lse_out, int32_t* sel_pages,
                                        int32_t* sel_count, uint32_t flags, hipStream_t stream);
 
+/*
+ * Offload path ([N] §8: the selection never reads keys or values, so the
+ * summaries alone can stay on the accelerator while the whole KV cache lives
+ * in host memory). K and V pools may be pinned, device-mapped host memory:
+ * pass the device pointer that locks_host_pool_alloc returns as k_pool /
+ * v_pool to any entry point above, with the same layout. Scoring and
+ * selection then read only the summaries in device memory; the attention
+ * reads only the selected pages across the host link, the step's append
+ * writes one token per (sequence, KV head) there, and a page build reads
+ * the completed page's keys once. Results are those of device-memory pools.
+ *
+ * locks_host_pool_alloc -- bytes of pinned host memory mapped into the
+ *   current device's address space (page-aligned). host_ptr: the host
+ *   address (fill and read the pool there, ordered with the device work by
+ *   stream synchronisation); device_ptr: the address kernels use. The caller
+ *   owns the memory and frees it with locks_host_pool_free(host_ptr) once no
+ *   enqueued work uses it. Errors: INVALID_ARG (null output, bytes == 0),
+ *   HIP (allocation or mapping failed; both outputs are then NULL).
+ * locks_host_pool_free -- frees what locks_host_pool_alloc returned (NULL:
+ *   no-op). Errors: HIP.
+ */
+locks_status locks_host_pool_alloc(size_t bytes, void** host_ptr, void** device_ptr);
+locks_status locks_host_pool_free(void* host_ptr);
+
 #ifdef __cplusplus
 }
 #endif

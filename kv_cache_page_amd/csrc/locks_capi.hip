@@ -475,4 +475,25 @@ locks_status locks_decode_step(const locks_dims* d, const void* q, const void* k
                          flags, w, static_cast<uint8_t*>(workspace), false, st);
 }
 
+locks_status locks_host_pool_alloc(size_t bytes, void** host_ptr, void** device_ptr) {
+  if (!host_ptr || !device_ptr || bytes == 0) return LOCKS_ERR_INVALID_ARG;
+  *host_ptr = nullptr;
+  *device_ptr = nullptr;
+  void* h = nullptr;
+  if (hipHostMalloc(&h, bytes, hipHostMallocMapped) != hipSuccess || !h) return LOCKS_ERR_HIP;
+  void* dp = nullptr;
+  if (hipHostGetDevicePointer(&dp, h, 0) != hipSuccess || !dp) {
+    (void)hipHostFree(h);
+    return LOCKS_ERR_HIP;
+  }
+  *host_ptr = h;
+  *device_ptr = dp;
+  return LOCKS_OK;
+}
+
+locks_status locks_host_pool_free(void* host_ptr) {
+  if (!host_ptr) return LOCKS_OK;
+  return hip_status(hipHostFree(host_ptr));
+}
+
 }  // extern "C"

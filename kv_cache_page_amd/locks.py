@@ -30,7 +30,8 @@ ENTRY_POINTS = (
     "locks_status_string", "locks_summary_slot_bytes", "locks_summary_slot_stride",
     "locks_workspace_bytes", "locks_build", "locks_build_filled", "locks_append_kv",
     "locks_score_select", "locks_score_pages", "locks_select_pages", "locks_sparse_attn",
-    "locks_decode_step", "locks_decode_step_noalloc",
+    "locks_decode_step", "locks_decode_step_noalloc", "locks_host_pool_alloc",
+    "locks_host_pool_free",
 )
 NOALLOC_SCRATCH_BYTES = 16 << 20   # LOCKS_NOALLOC_SCRATCH_BYTES
 
@@ -91,6 +92,11 @@ _decode_step_noalloc = _sig("locks_decode_step_noalloc", ctypes.c_int,
                              _i32, _i32, _vp, _vp, _vp, _vp, _u32, _vp])
 
 
+_host_alloc = _sig("locks_host_pool_alloc", ctypes.c_int,
+                   [_sz, ctypes.POINTER(_vp), ctypes.POINTER(_vp)])
+_host_free = _sig("locks_host_pool_free", ctypes.c_int, [_vp])
+
+
 def status_string(status):
     return _status_string(int(status)).decode()
 
@@ -111,9 +117,47 @@ def workspace_bytes(dims, num_seqs, max_pages, max_budget):
 # marshalling helpers
 # ---------------------------------------------------------------------------
 
+class HostPool:
+    """A K or V pool in pinned, device-mapped host memory (locks_host_pool_alloc):
+    `host` is a CPU tensor of the given shape over that memory, and entry
+    points given the HostPool pass its device address to the kernels."""
+
+    def __init__(self, shape, dtype=torch.bfloat16):
+        self.shape = torch.Size(shape)
+        self.dtype = dtype
+        nbytes = self.shape.numel() * torch.tensor([], dtype=dtype).element_size()
+        hp, dp = _vp(), _vp()
+        _check(_host_alloc(nbytes, ctypes.byref(hp), ctypes.byref(dp)), "locks_host_pool_alloc")
+        self._host_ptr, self.device_ptr = hp.value, dp.value
+        buf = (ctypes.c_uint8 * nbytes).from_address(self._host_ptr)
+        self.host = torch.frombuffer(buf, dtype=torch.uint8).view(dtype).view(self.shape)
+
+    def is_contiguous(self):
+        return True
+
+    def free(self):
+        """Release the memory (no enqueued work may still use it)."""
+        if self._host_ptr:
+            self.host = None
+            _check(_host_free(self._host_ptr), "locks_host_pool_free")
+            self._host_ptr = self.device_ptr = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
 def _ptr(t, dtype=None, name="tensor"):
     if t is None:
         return None
+    if isinstance(t, HostPool):
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+        if t.device_ptr is None:
+            raise ValueError(f"{name}: host pool already freed")
+        return t.device_ptr
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if dtype is not None and t.dtype != dtype:

@@ -139,3 +139,12 @@ def test_decode_step_rejects_before_launch():
     assert call(KB=1) == L.ERR_INVALID_ARG
     assert call(flags=2, ws_bytes=need) == L.ERR_INVALID_ARG  # unknown flag bit
     assert call(S=0) == L.OK                                # empty batch: nothing to do
+
+
+def test_host_pool_argument_checks():
+    """locks_host_pool_alloc / _free validation (no allocation is attempted)."""
+    hp, dp = ctypes.c_void_p(123), ctypes.c_void_p(456)
+    assert L._host_alloc(0, ctypes.byref(hp), ctypes.byref(dp)) == L.ERR_INVALID_ARG
+    assert L._host_alloc(4096, None, ctypes.byref(dp)) == L.ERR_INVALID_ARG
+    assert L._host_alloc(4096, ctypes.byref(hp), None) == L.ERR_INVALID_ARG
+    assert L._host_free(None) == L.OK
