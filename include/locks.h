@@ -76,7 +76,9 @@ typedef enum {
     LOCKS_ERR_HIP = -4          /* a HIP launch or device query failed       */
 } locks_status;
 
-const char* locks_status_string(locks_status status);
+/* Text for a status code; any int32 is accepted ("unknown status" for values
+ * that are not a locks_status). */
+const char* locks_status_string(int32_t status);
 
 /*
  * Summary slot of one (block, KV head) page -- [N] §4.1 (storage paragraph)

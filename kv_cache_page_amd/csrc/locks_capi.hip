@@ -123,7 +123,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 extern "C" {
 
-const char* locks_status_string(locks_status s) {
+const char* locks_status_string(int32_t s) {
   switch (s) {
     case LOCKS_OK: return "ok";
     case LOCKS_ERR_INVALID_ARG: return "invalid argument";
