@@ -61,6 +61,19 @@ design notes of the repository):
                  token, F' = floor((len - 1) / B): the just-completed page is
                  this step's unsummarised recent page (selected, not in Z_g)
                  and is summarised after the step.
+  R18 basis      the rank x precision ablation of [N] §6 compares int8, int4
+      precision  and int2 bases. A b-bit basis uses the R1 quantiser with
+                 qmax = 2^(b-1) - 1 (127, 7, 1), one scale per column as R2.
+                 Layout of Vq (R4 for int4): int8, one byte per dim in dim
+                 order; int2, four dims per byte in dim order, two's-
+                 complement two-bit fields, lowest bits first. Coefficients
+                 and centroid stay int8.
+  R19 merge      [N] §4.2 names two alternatives to the share average of
+      rules      eq. 5 for the group's single page set: group-max (a page any
+                 query head rates highly) and group-mass (another pooling).
+                 Readings: group-max key_j = max_g m_g(j) on the same
+                 normalised shares; group-mass key_j = sum_g exp(s_jg) /
+                 sum_g Z_g, the pooled unnormalised mass. Selection as R8-R9.
 """
 from __future__ import annotations
 
@@ -70,6 +83,15 @@ import numpy as np
 
 QMAX_INT4 = 7
 QMAX_INT8 = 127
+BASIS_BITS = (2, 4, 8)
+MERGE_RULES = ("share", "max", "mass")
+
+
+def qmax_of(bits):
+    """Reading R18: the symmetric b-bit quantiser's largest code."""
+    if bits not in BASIS_BITS:
+        raise ValueError(f"basis bits must be one of {BASIS_BITS}")
+    return 2 ** (bits - 1) - 1
 ACTIVE_REL = 1e-6
 ACTIVE_FLOOR = 1e-12
 FP16_MAX = 65504.0
@@ -159,10 +181,11 @@ def quantise(x, qmax, axis):
     return codes.astype(np.int64), scale
 
 
-def quantise_summary(summary):
-    """int4 basis with one scale per column, int8 coefficients with one scale
-    per token row c_i, int8 centroid with one scale (readings R1-R3)."""
-    Vq, sV = quantise(summary["V"], QMAX_INT4, axis=1)      # (n, d, r), (n, r)
+def quantise_summary(summary, basis_bits=4):
+    """int4 basis (int8 or int2 in the ablation, reading R18) with one scale per
+    column, int8 coefficients with one scale per token row c_i, int8 centroid
+    with one scale (readings R1-R3)."""
+    Vq, sV = quantise(summary["V"], qmax_of(basis_bits), axis=1)   # (n, d, r), (n, r)
     Cq, sC = quantise(summary["C"], QMAX_INT8, axis=2)      # (n, B, r), (n, B)
     muq, smu = quantise(summary["mu"], QMAX_INT8, axis=1)   # (n, d), (n,)
     return dict(Vq=Vq, sV=sV, Cq=Cq, sC=sC, muq=muq, smu=smu)
@@ -180,10 +203,11 @@ def dequantise(qs):
 # Slot bytes (reading R4)
 # ----------------------------------------------------------------------------
 
-def slot_layout(r, B=16, d=128):
-    """Byte offsets of the summary slot (reading R4)."""
+def slot_layout(r, B=16, d=128, basis_bits=4):
+    """Byte offsets of the summary slot (readings R4, R18)."""
+    qmax_of(basis_bits)
     off_v = 0
-    off_c = off_v + r * (d // 2)
+    off_c = off_v + r * d * basis_bits // 8
     off_mu = off_c + B * r
     off_s = off_mu + d
     payload = off_s + 2 * (r + B + 1)
@@ -197,18 +221,26 @@ def slot_layout(r, B=16, d=128):
 NIBBLE_OF_DIM = np.array([0, 1, 4, 5, 2, 3, 6, 7])
 
 
-def pack_slots(qs, B=16, d=128):
-    """Write slots byte-exactly from codes and scales (reading R4).
+def pack_slots(qs, B=16, d=128, basis_bits=4):
+    """Write slots byte-exactly from codes and scales (readings R4, R18).
     Returns uint8 (n, stride)."""
     n, _, r = qs["Vq"].shape
-    L = slot_layout(r, B, d)
+    L = slot_layout(r, B, d, basis_bits)
     out = np.zeros((n, L["stride"]), dtype=np.uint8)
-    # Vq: (n, d, r) -> per column k, words t, nibble positions
-    cols = np.swapaxes(qs["Vq"], 1, 2).reshape(n, r, d // 8, 8) & 0xF   # dim j of word t
-    nib = np.zeros_like(cols)
-    nib[..., NIBBLE_OF_DIM] = cols                                   # nibble position p
-    packed = (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)  # (n, r, d/8, 4)
-    out[:, L["v"]:L["v"] + r * d // 2] = packed.reshape(n, r * d // 2)
+    vbytes = r * d * basis_bits // 8
+    cols = np.swapaxes(qs["Vq"], 1, 2)                               # (n, r, d): column k, dim
+    if basis_bits == 4:
+        # per column k, words t, nibble positions
+        cols = cols.reshape(n, r, d // 8, 8) & 0xF                   # dim j of word t
+        nib = np.zeros_like(cols)
+        nib[..., NIBBLE_OF_DIM] = cols                               # nibble position p
+        packed = (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)  # (n, r, d/8, 4)
+    elif basis_bits == 8:
+        packed = (cols & 0xFF).astype(np.uint8)
+    else:
+        f = cols.reshape(n, r, d // 4, 4) & 0x3                      # four dims per byte
+        packed = (f[..., 0] | f[..., 1] << 2 | f[..., 2] << 4 | f[..., 3] << 6).astype(np.uint8)
+    out[:, L["v"]:L["v"] + vbytes] = packed.reshape(n, vbytes)
     out[:, L["c"]:L["c"] + B * r] = (qs["Cq"].reshape(n, B * r) & 0xFF).astype(np.uint8)
     out[:, L["mu"]:L["mu"] + d] = (qs["muq"] & 0xFF).astype(np.uint8)
     scales = np.concatenate([qs["sV"], qs["sC"], qs["smu"][:, None]], axis=1).astype("<f2")
@@ -216,17 +248,25 @@ def pack_slots(qs, B=16, d=128):
     return out
 
 
-def unpack_slots(buf, r, B=16, d=128):
-    """Read codes and scales back from slot bytes (reading R4)."""
+def unpack_slots(buf, r, B=16, d=128, basis_bits=4):
+    """Read codes and scales back from slot bytes (readings R4, R18)."""
     buf = np.asarray(buf, dtype=np.uint8)
     n = buf.shape[0]
-    L = slot_layout(r, B, d)
-    packed = buf[:, L["v"]:L["v"] + r * d // 2].reshape(n, r, d // 8, 4).astype(np.int64)
-    nib = np.zeros(packed.shape[:-1] + (8,), dtype=np.int64)
-    nib[..., 0::2] = packed & 0xF
-    nib[..., 1::2] = packed >> 4
-    nib = np.where(nib >= 8, nib - 16, nib)
-    cols = nib[..., NIBBLE_OF_DIM]                                  # dim order
+    L = slot_layout(r, B, d, basis_bits)
+    vb = buf[:, L["v"]:L["v"] + r * d * basis_bits // 8]
+    if basis_bits == 4:
+        packed = vb.reshape(n, r, d // 8, 4).astype(np.int64)
+        nib = np.zeros(packed.shape[:-1] + (8,), dtype=np.int64)
+        nib[..., 0::2] = packed & 0xF
+        nib[..., 1::2] = packed >> 4
+        nib = np.where(nib >= 8, nib - 16, nib)
+        cols = nib[..., NIBBLE_OF_DIM]                              # dim order
+    elif basis_bits == 8:
+        cols = vb.view(np.int8).astype(np.int64)
+    else:
+        packed = vb.reshape(n, r, d // 4).astype(np.int64)
+        f = np.stack([(packed >> (2 * e)) & 0x3 for e in range(4)], axis=-1)
+        cols = np.where(f >= 2, f - 4, f)
     Vq = np.swapaxes(cols.reshape(n, r, d), 1, 2)
     Cq = buf[:, L["c"]:L["c"] + B * r].view(np.int8).astype(np.int64).reshape(n, B, r)
     muq = buf[:, L["mu"]:L["mu"] + d].view(np.int8).astype(np.int64)
@@ -234,12 +274,12 @@ def unpack_slots(buf, r, B=16, d=128):
     return dict(Vq=Vq, sV=sc[:, :r], Cq=Cq, sC=sc[:, r:r + B], muq=muq, smu=sc[:, r + B])
 
 
-def build_slots(keys, r, B=16, d=128):
+def build_slots(keys, r, B=16, d=128, basis_bits=4):
     """Algorithm 1 of [N] §4.3 end to end for full pages keys (n, B, d):
     summary, codes, slot bytes. Returns (slots (n, stride), summary, codes)."""
     s = spectral_summary(keys, r)
-    qs = quantise_summary(s)
-    return pack_slots(qs, B, d), s, qs
+    qs = quantise_summary(s, basis_bits)
+    return pack_slots(qs, B, d, basis_bits), s, qs
 
 
 # ----------------------------------------------------------------------------
@@ -276,15 +316,24 @@ def exact_page_lse(q, K):
     return logsumexp(logits, axis=2)
 
 
-def share_keys(s):
+def share_keys(s, rule="share"):
     """Per-query shares m_g(j) = exp(s_jg) / sum_j' exp(s_j'g) and their group
     average m_bar_j = (1/G) sum_g m_g(j) ([N] §4.2 eq. 5), returned in the log
     domain: key_j = log m_bar_j. s: (F, G) over all summarised pages
-    (reading R7). Returns (key (F,), log Z (G,))."""
+    (reading R7). rule "max" and "mass" are the alternatives of reading R19:
+    log max_g m_g(j), and log (sum_g exp(s_jg) / sum_g Z_g).
+    Returns (key (F,), log Z (G,))."""
     s = np.asarray(s, dtype=np.float64)
     G = s.shape[1]
     logZ = logsumexp(s, axis=0)
-    key = logsumexp(s - logZ[None, :], axis=1) - math.log(G)
+    if rule == "share":
+        key = logsumexp(s - logZ[None, :], axis=1) - math.log(G)
+    elif rule == "max":
+        key = np.max(s - logZ[None, :], axis=1)
+    elif rule == "mass":
+        key = logsumexp(s, axis=1) - logsumexp(logZ, axis=0)
+    else:
+        raise ValueError(f"merge rule must be one of {MERGE_RULES}")
     return key, logZ
 
 
@@ -360,7 +409,8 @@ def n_full_pages(seq_len, B=16):
     return seq_len // B
 
 
-def decode_head(q, Kp, Vp, seq_len, k, slots=None, r=8, mode="quantised", B=16, deferred=False):
+def decode_head(q, Kp, Vp, seq_len, k, slots=None, r=8, mode="quantised", B=16, deferred=False,
+                basis_bits=4, merge="share"):
     """Score -> share -> select -> attend for one (seq, KV head).
 
     q: (G, d). Kp, Vp: (>=P, B, d) logical pages (the tail page may be
@@ -369,6 +419,8 @@ def decode_head(q, Kp, Vp, seq_len, k, slots=None, r=8, mode="quantised", B=16, 
     deployed), "unquantised" from the fp64 summary, "exact" ranks by the
     exact page LSE (the Lemma 1 selector of [N] §3.1). deferred: reading R17,
     only the pages full before the current token are summarised and scored.
+    basis_bits: the stored basis precision (reading R18); merge: the group
+    rule that turns scores into selection keys (reading R19).
     Returns dict(scores (F, G), key (F,), sel (list), out (G, d), lse (G,))."""
     q = np.asarray(q, dtype=np.float64)
     G, d = q.shape
@@ -384,10 +436,10 @@ def decode_head(q, Kp, Vp, seq_len, k, slots=None, r=8, mode="quantised", B=16, 
             scores = page_scores(q, s["mu"], s["V"], s["C"])
         else:
             if slots is None:
-                slots, _, _ = build_slots(Kp[:F], r, B, d)
-            dq = dequantise(unpack_slots(slots[:F], r, B, d))
+                slots, _, _ = build_slots(Kp[:F], r, B, d, basis_bits)
+            dq = dequantise(unpack_slots(slots[:F], r, B, d, basis_bits))
             scores = page_scores(q, dq["mu"], dq["V"], dq["C"])
-        key, _ = share_keys(scores)
+        key, _ = share_keys(scores, merge)
     else:
         scores = np.zeros((0, G))
         key = np.zeros(0)
