@@ -66,7 +66,23 @@ typedef struct {
     int32_t rank;         /* r: kept basis vectors per page, 1..16 */
     int32_t num_kv_heads; /* H_kv >= 1 */
     int32_t group_size;   /* G: query heads per KV head (GQA), 1, 2 or 4 */
+    int32_t basis_bits;   /* stored basis precision: 0 or 4 (int4, the
+                             default), 8 or 2 (the ablation of [N] §6; ranks
+                             4, 8 and 16 only) */
+    int32_t merge_rule;   /* LOCKS_MERGE_*: how the group's query heads pool
+                             their page scores into one key (0: eq. 5) */
 } locks_dims;
+
+/* GQA merge rules ([N] §4.2 and the ablation of [N] §6). With m_g(j) =
+ * exp(s_jg - Z_g) the share of page j for query head g:
+ *   SHARE  key_j = log mean_g m_g(j)                (eq. 5, the default)
+ *   MAX    key_j = log max_g m_g(j)                 (group-max)
+ *   MASS   key_j = log (sum_g exp(s_jg) / sum_g Z_g) (group-mass: the pooled
+ *          unnormalised masses)
+ * The selection rule (sink, recent, top-(k-2) keys) is the same for all. */
+#define LOCKS_MERGE_SHARE 0
+#define LOCKS_MERGE_MAX 1
+#define LOCKS_MERGE_MASS 2
 
 typedef enum {
     LOCKS_OK = 0,
@@ -90,13 +106,19 @@ const char* locks_status_string(int32_t status);
  *                          Each little-endian 32-bit word of a column covers
  *                          dims 8t..8t+7; its four bytes hold the dim pairs
  *                          (0,1), (4,5), (2,3), (6,7), low nibble first.
- *   offset r*d/2      Cq   page_size x r int8, row-major (row i = c_i)
+ *                          With basis_bits 8: r columns x d bytes, int8 in
+ *                          dim order; with 2: r columns x d/4 bytes, four
+ *                          dims per byte in dim order, two's-complement
+ *                          two-bit fields from the lowest bits (codes -1, 0,
+ *                          1). The same quantiser with qmax 127, 7 or 1.
+ *   offset r*d*b/8    Cq   page_size x r int8, row-major (row i = c_i)
  *   next              muq  d int8 (centroid codes in dim order)
  *   next              scales, fp16 little-endian: r basis-column scales,
  *                          page_size coefficient-row scales, 1 centroid scale
  *   then zero padding up to slot_stride (a multiple of 128 bytes, so slots
  *   start on cache lines and share none).
- * Decoded values are code * scale. r = 8: 818 payload bytes, stride 896.
+ * Decoded values are code * scale. r = 8: 818 payload bytes, stride 896
+ * (int8 basis: 1330 and 1408; int2: 562 and 640).
  * The scoring calls take basis-column scales below 8 (the matrix-core path
  * carries V^T q in fp16 parts); locks_build writes at most about 1/7, since
  * its basis columns have unit norm.

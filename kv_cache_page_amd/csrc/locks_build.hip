@@ -77,8 +77,9 @@ __global__ __launch_bounds__(64) void build_kernel(
     const int32_t* __restrict__ ids, int n, const int32_t* __restrict__ table,
     const int32_t* __restrict__ lens, int MP, uint8_t* __restrict__ summ,
     const uint16_t* __restrict__ knew, const uint16_t* __restrict__ vnew,
-    uint16_t* __restrict__ kdst, uint16_t* __restrict__ vdst) {
-  constexpr SlotLayout L = slot_layout(R);
+    uint16_t* __restrict__ kdst, uint16_t* __restrict__ vdst, int bits) {
+  const SlotLayout L = slot_layout(R, bits);
+  const int vq_max = basis_qmax(bits);
   __shared__ float kt[kBuildPages][kPage][kRowPad];
   __shared__ double urow[kBuildPages][kPage][kPage + 1];
   __shared__ double lam_s[kBuildPages][kPage];
@@ -284,17 +285,34 @@ __global__ __launch_bounds__(64) void build_kernel(
     if (i == 0) {
       sig_s[pg][k] = act ? sig * flip : 0.0;  // coefficient multiplier, 0 if inactive
     }
-    const uint16_t sbits = act ? fp16_scale_bits(amax, 7.f) : (uint16_t)0;
+    const uint16_t sbits = act ? fp16_scale_bits(amax, (float)vq_max) : (uint16_t)0;
     const float scale = (float)__builtin_bit_cast(_Float16, sbits);
     int code[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) code[e] = quant_code(v[e] * flip, scale, 7) & 0xF;
-    // bytes carry the dim pairs (0,1), (4,5), (2,3), (6,7), low nibble first
-    const uint32_t word = (uint32_t)(code[0] | code[1] << 4) | (uint32_t)(code[4] | code[5] << 4) << 8 |
-                          (uint32_t)(code[2] | code[3] << 4) << 16 |
-                          (uint32_t)(code[6] | code[7] << 4) << 24;
+    for (int e = 0; e < 8; ++e) code[e] = quant_code(v[e] * flip, scale, vq_max);
     if (sl) {
-      *reinterpret_cast<uint32_t*>(sl + 64 * k + 4 * i) = word;
+      if (bits == 4) {
+        // bytes carry the dim pairs (0,1), (4,5), (2,3), (6,7), low nibble first
+        int c4[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) c4[e] = code[e] & 0xF;
+        const uint32_t word = (uint32_t)(c4[0] | c4[1] << 4) | (uint32_t)(c4[4] | c4[5] << 4) << 8 |
+                              (uint32_t)(c4[2] | c4[3] << 4) << 16 | (uint32_t)(c4[6] | c4[7] << 4) << 24;
+        *reinterpret_cast<uint32_t*>(sl + 64 * k + 4 * i) = word;
+      } else if (bits == 8) {  // one byte per dim, dim order
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lo |= (uint32_t)(code[e] & 0xFF) << (8 * e);
+          hi |= (uint32_t)(code[e + 4] & 0xFF) << (8 * e);
+        }
+        *reinterpret_cast<uint2*>(sl + 128 * k + 8 * i) = make_uint2(lo, hi);
+      } else {  // two bits per dim, dim order from the lowest bits
+        uint32_t h = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h |= (uint32_t)(code[e] & 0x3) << (2 * e);
+        *reinterpret_cast<uint16_t*>(sl + 32 * k + 2 * i) = (uint16_t)h;
+      }
       if (i == 0) *reinterpret_cast<uint16_t*>(sl + L.sv + 2 * k) = sbits;
     }
   }
@@ -370,18 +388,19 @@ template <int R>
 static hipError_t launch_build_r(const uint16_t* kpool, int64_t nb, int H, const int32_t* ids,
                                  int n, const int32_t* table, const int32_t* lens, int MP,
                                  uint8_t* summ, const uint16_t* knew, const uint16_t* vnew,
-                                 uint16_t* kdst, uint16_t* vdst, hipStream_t st) {
+                                 uint16_t* kdst, uint16_t* vdst, int bits, hipStream_t st) {
   const int64_t items = (int64_t)n * H;
   if (items == 0) return hipSuccess;
   const int64_t grid = (items + kBuildPages - 1) / kBuildPages;
   hipLaunchKernelGGL(build_kernel<R>, dim3((unsigned)grid), dim3(64), 0, st, kpool, nb, H, ids, n,
-                     table, lens, MP, summ, knew, vnew, kdst, vdst);
+                     table, lens, MP, summ, knew, vnew, kdst, vdst, bits);
   return hipGetLastError();
 }
 
 hipError_t launch_build_page(int r, const void* kpool, int64_t nb, int H, const int32_t* ids, int n,
                              const int32_t* table, const int32_t* lens, int MP, void* summ,
-                             const void* knew, const void* vnew, void* vpool, hipStream_t st);
+                             const void* knew, const void* vnew, void* vpool, int bits,
+                             hipStream_t st);
 
 // Up to this many pages go to the one-page-per-wave form (shorter time to a
 // summary); larger lists to the 4-pages-per-wave form.
@@ -390,9 +409,11 @@ constexpr int64_t kPageFormMaxItems = 4096;
 // knew/vnew (filled-page mode only, may be null): append the new token too.
 hipError_t launch_build(int r, const void* kpool, int64_t nb, int H, const int32_t* ids, int n,
                         const int32_t* table, const int32_t* lens, int MP, void* summ,
-                        const void* knew, const void* vnew, void* vpool, hipStream_t st) {
+                        const void* knew, const void* vnew, void* vpool, int bits, hipStream_t st) {
+  if (bits != 2 && bits != 4 && bits != 8) return hipErrorInvalidValue;
   if (!ids || (int64_t)n * H <= kPageFormMaxItems)
-    return launch_build_page(r, kpool, nb, H, ids, n, table, lens, MP, summ, knew, vnew, vpool, st);
+    return launch_build_page(r, kpool, nb, H, ids, n, table, lens, MP, summ, knew, vnew, vpool, bits,
+                             st);
   const uint16_t* kp = static_cast<const uint16_t*>(kpool);
   uint8_t* sm = static_cast<uint8_t*>(summ);
   const uint16_t* kn = static_cast<const uint16_t*>(knew);
@@ -402,7 +423,7 @@ hipError_t launch_build(int r, const void* kpool, int64_t nb, int H, const int32
   switch (r) {
 #define LOCKS_R(RR) \
   case RR:          \
-    return launch_build_r<RR>(kp, nb, H, ids, n, table, lens, MP, sm, kn, vn, kd, vd, st);
+    return launch_build_r<RR>(kp, nb, H, ids, n, table, lens, MP, sm, kn, vn, kd, vd, bits, st);
     LOCKS_R(1) LOCKS_R(2) LOCKS_R(3) LOCKS_R(4) LOCKS_R(5) LOCKS_R(6) LOCKS_R(7) LOCKS_R(8)
     LOCKS_R(9) LOCKS_R(10) LOCKS_R(11) LOCKS_R(12) LOCKS_R(13) LOCKS_R(14) LOCKS_R(15) LOCKS_R(16)
 #undef LOCKS_R

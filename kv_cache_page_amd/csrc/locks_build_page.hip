@@ -164,8 +164,9 @@ __global__ __launch_bounds__(64) void build_page_kernel(
     const int32_t* __restrict__ ids, int n, const int32_t* __restrict__ table,
     const int32_t* __restrict__ lens, int MP, uint8_t* __restrict__ summ,
     const uint16_t* __restrict__ knew, const uint16_t* __restrict__ vnew,
-    uint16_t* __restrict__ kdst, uint16_t* __restrict__ vdst) {
-  constexpr SlotLayout L = slot_layout(R);
+    uint16_t* __restrict__ kdst, uint16_t* __restrict__ vdst, int bits) {
+  const SlotLayout L = slot_layout(R, bits);
+  const int vq_max = basis_qmax(bits);
   __shared__ float kt[kPage][kHeadDim + 4];
   __shared__ double g_s[kPage][kPage + 1];
   __shared__ double u_s[kPage][kPage + 1];
@@ -377,15 +378,25 @@ __global__ __launch_bounds__(64) void build_page_kernel(
     const double aval = (l0 <= l1) ? readlane_d(v0, l0) : readlane_d(v1, l1);
     const double flip = (aval < 0.0) ? -1.0 : 1.0;
     if (lane == 0) sig_s[k] = act ? sig * flip : 0.0;
-    const uint16_t sbits = act ? fp16_scale_bits(amax, 7.f) : (uint16_t)0;
+    const uint16_t sbits = act ? fp16_scale_bits(amax, (float)vq_max) : (uint16_t)0;
     const float scale = (float)__builtin_bit_cast(_Float16, sbits);
-    const int code0 = quant_code(v0 * flip, scale, 7) & 0xF;
-    const int code1 = quant_code(v1 * flip, scale, 7) & 0xF;
-    // the 4 pairs of a word: bytes hold the pairs (0,1), (4,5), (2,3), (6,7)
-    const uint32_t byte = (uint32_t)(code0 | (code1 << 4)) << (8 * byte_of_pair);
-    uint32_t word = byte | (uint32_t)__builtin_amdgcn_update_dpp(0, (int)byte, 0xB1, 0xF, 0xF, false);
-    word |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0x4E, 0xF, 0xF, false);
-    if (pq == 0) *reinterpret_cast<uint32_t*>(sl + L.v + 64 * k + 4 * wq) = word;
+    const int qc0 = quant_code(v0 * flip, scale, vq_max);
+    const int qc1 = quant_code(v1 * flip, scale, vq_max);
+    if (bits == 4) {
+      const int code0 = qc0 & 0xF, code1 = qc1 & 0xF;
+      // the 4 pairs of a word: bytes hold the pairs (0,1), (4,5), (2,3), (6,7)
+      const uint32_t byte = (uint32_t)(code0 | (code1 << 4)) << (8 * byte_of_pair);
+      uint32_t word = byte | (uint32_t)__builtin_amdgcn_update_dpp(0, (int)byte, 0xB1, 0xF, 0xF, false);
+      word |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0x4E, 0xF, 0xF, false);
+      if (pq == 0) *reinterpret_cast<uint32_t*>(sl + L.v + 64 * k + 4 * wq) = word;
+    } else if (bits == 8) {  // one byte per dim, dim order
+      *reinterpret_cast<uint16_t*>(sl + L.v + 128 * k + 2 * lane) =
+          (uint16_t)((qc0 & 0xFF) | ((qc1 & 0xFF) << 8));
+    } else {  // two bits per dim: lanes 2b and 2b + 1 share byte b
+      const int nib = (qc0 & 0x3) | ((qc1 & 0x3) << 2);
+      const int other = __builtin_amdgcn_update_dpp(0, nib, 0xB1, 0xF, 0xF, false);  // lane ^ 1
+      if ((lane & 1) == 0) sl[L.v + 32 * k + (lane >> 1)] = (uint8_t)(nib | (other << 4));
+    }
     if (lane == 0) *reinterpret_cast<uint16_t*>(sl + L.sv + 2 * k) = sbits;
   }
   __syncthreads();
@@ -424,17 +435,18 @@ template <int R>
 static hipError_t launch_build_page_r(const uint16_t* kpool, int64_t nb, int H, const int32_t* ids,
                                       int n, const int32_t* table, const int32_t* lens, int MP,
                                       uint8_t* summ, const uint16_t* knew, const uint16_t* vnew,
-                                      uint16_t* kdst, uint16_t* vdst, hipStream_t st) {
+                                      uint16_t* kdst, uint16_t* vdst, int bits, hipStream_t st) {
   const int64_t items = (int64_t)n * H;
   if (items == 0) return hipSuccess;
   hipLaunchKernelGGL(build_page_kernel<R>, dim3((unsigned)items), dim3(64), 0, st, kpool, nb, H, ids,
-                     n, table, lens, MP, summ, knew, vnew, kdst, vdst);
+                     n, table, lens, MP, summ, knew, vnew, kdst, vdst, bits);
   return hipGetLastError();
 }
 
 hipError_t launch_build_page(int r, const void* kpool, int64_t nb, int H, const int32_t* ids, int n,
                              const int32_t* table, const int32_t* lens, int MP, void* summ,
-                             const void* knew, const void* vnew, void* vpool, hipStream_t st) {
+                             const void* knew, const void* vnew, void* vpool, int bits,
+                             hipStream_t st) {
   const uint16_t* kp = static_cast<const uint16_t*>(kpool);
   uint8_t* sm = static_cast<uint8_t*>(summ);
   const uint16_t* kn = static_cast<const uint16_t*>(knew);
@@ -444,7 +456,7 @@ hipError_t launch_build_page(int r, const void* kpool, int64_t nb, int H, const 
   switch (r) {
 #define LOCKS_R(RR) \
   case RR:          \
-    return launch_build_page_r<RR>(kp, nb, H, ids, n, table, lens, MP, sm, kn, vn, kd, vd, st);
+    return launch_build_page_r<RR>(kp, nb, H, ids, n, table, lens, MP, sm, kn, vn, kd, vd, bits, st);
     LOCKS_R(1) LOCKS_R(2) LOCKS_R(3) LOCKS_R(4) LOCKS_R(5) LOCKS_R(6) LOCKS_R(7) LOCKS_R(8)
     LOCKS_R(9) LOCKS_R(10) LOCKS_R(11) LOCKS_R(12) LOCKS_R(13) LOCKS_R(14) LOCKS_R(15) LOCKS_R(16)
 #undef LOCKS_R

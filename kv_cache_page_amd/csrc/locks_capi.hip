@@ -11,21 +11,21 @@
 #include "locks_step.h"
 
 namespace locks {
-hipError_t launch_score(int r, int G, const void* q, const void* summ, const int32_t* table,
-                        const int32_t* lens, float* scores, int64_t nb, int S, int H, int MP,
-                        int flags, float2* zpart, const void* knew, const void* vnew,
-                        void* kpool, void* vpool, float* mxout, CoopZero coop,
+hipError_t launch_score(int r, int bits, int G, const void* q, const void* summ,
+                        const int32_t* table, const int32_t* lens, float* scores, int64_t nb,
+                        int S, int H, int MP, int flags, float2* zpart, const void* knew,
+                        const void* vnew, void* kpool, void* vpool, float* mxout, CoopZero coop,
                         hipStream_t st);
 hipError_t launch_select(int G, const float* scores, const int32_t* lens, const int32_t* budgets,
                          int32_t* sel, int32_t* cnt, float* keybuf, int S, int H, int MP,
-                         int max_budget, int lag, hipStream_t st);
+                         int max_budget, int lag, int rule, hipStream_t st);
 hipError_t launch_attn(int G, const void* q, const void* kpool, const void* vpool,
                        const int32_t* table, const int32_t* lens, const int32_t* sel,
                        const int32_t* cnt, float* part, float* out, float* lse_out, int64_t nb,
                        int S, int H, int MP, int max_budget, int nsplit, int ppw, hipStream_t st);
 hipError_t launch_build(int r, const void* kpool, int64_t nb, int H, const int32_t* ids, int n,
                         const int32_t* table, const int32_t* lens, int MP, void* summ,
-                        const void* knew, const void* vnew, void* vpool, hipStream_t st);
+                        const void* knew, const void* vnew, void* vpool, int bits, hipStream_t st);
 bool decode_shape(int MP, int KB, int* per_wg, int* nsplit, int* slice);
 int64_t decode_mailbox_words(int MP, int KB, int G);
 int64_t decode_mailbox_zero_words(int MP, int KB, int G);
@@ -58,8 +58,17 @@ locks_status check_dims(const locks_dims* d) {
   if (d->head_dim != locks::kHeadDim || d->page_size != locks::kPage) return LOCKS_ERR_UNSUPPORTED;
   if (d->rank > locks::kPage) return LOCKS_ERR_UNSUPPORTED;
   if (d->group_size != 1 && d->group_size != 2 && d->group_size != 4) return LOCKS_ERR_UNSUPPORTED;
+  if (d->basis_bits != 0 && d->basis_bits != 2 && d->basis_bits != 4 && d->basis_bits != 8)
+    return LOCKS_ERR_INVALID_ARG;
+  if (d->merge_rule < LOCKS_MERGE_SHARE || d->merge_rule > LOCKS_MERGE_MASS) return LOCKS_ERR_INVALID_ARG;
+  // the precision ablation's bases (int8, int2) are built and scored at ranks 4, 8 and 16
+  if (d->basis_bits != 0 && d->basis_bits != 4 && d->rank != 4 && d->rank != 8 && d->rank != 16)
+    return LOCKS_ERR_UNSUPPORTED;
   return LOCKS_OK;
 }
+
+// Basis width of the slots (0 means the default int4).
+int bits_of(const locks_dims* d) { return d->basis_bits == 0 ? 4 : d->basis_bits; }
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -136,12 +145,12 @@ const char* locks_status_string(int32_t s) {
 
 size_t locks_summary_slot_bytes(const locks_dims* d) {
   if (check_dims(d) != LOCKS_OK) return 0;
-  return (size_t)locks::slot_layout(d->rank).payload;
+  return (size_t)locks::slot_layout(d->rank, bits_of(d)).payload;
 }
 
 size_t locks_summary_slot_stride(const locks_dims* d) {
   if (check_dims(d) != LOCKS_OK) return 0;
-  return (size_t)locks::slot_layout(d->rank).stride;
+  return (size_t)locks::slot_layout(d->rank, bits_of(d)).stride;
 }
 
 size_t locks_workspace_bytes(const locks_dims* d, int32_t S, int32_t MP, int32_t KB) {
@@ -159,7 +168,7 @@ locks_status locks_build(const locks_dims* d, const void* k_pool, int64_t nb,
   if (!aligned16(k_pool) || !aligned16(summaries)) return LOCKS_ERR_INVALID_ARG;
   return hip_status(locks::launch_build(d->rank, k_pool, nb, d->num_kv_heads, block_ids, n,
                                         nullptr, nullptr, 0, summaries, nullptr, nullptr, nullptr,
-                                        st));
+                                        bits_of(d), st));
 }
 
 locks_status locks_build_filled(const locks_dims* d, const void* k_pool, int64_t nb,
@@ -173,7 +182,7 @@ locks_status locks_build_filled(const locks_dims* d, const void* k_pool, int64_t
   if (!aligned16(k_pool) || !aligned16(summaries)) return LOCKS_ERR_INVALID_ARG;
   return hip_status(locks::launch_build(d->rank, k_pool, nb, d->num_kv_heads, nullptr, S,
                                         block_table, seq_lens, MP, summaries, nullptr, nullptr,
-                                        nullptr, st));
+                                        nullptr, bits_of(d), st));
 }
 
 locks_status locks_append_kv(const locks_dims* d, const void* k_new, const void* v_new,
@@ -209,12 +218,14 @@ locks_status locks_score_select(const locks_dims* d, const void* q, const void* 
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   float* scores = scores_out ? scores_out : reinterpret_cast<float*>(ws + w.scores);
   const int H = d->num_kv_heads, G = d->group_size;
-  hipError_t he = locks::launch_score(d->rank, G, q, summaries, block_table, seq_lens, scores, nb,
-                                      S, H, MP, scores_out ? locks::kScoreFillNan : 0, nullptr, nullptr, nullptr, nullptr,
-                                      nullptr, nullptr, locks::CoopZero{}, st);
+  hipError_t he = locks::launch_score(d->rank, bits_of(d), G, q, summaries, block_table, seq_lens,
+                                      scores, nb, S, H, MP, scores_out ? locks::kScoreFillNan : 0,
+                                      nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                      locks::CoopZero{}, st);
   if (he != hipSuccess) return LOCKS_ERR_HIP;
   he = locks::launch_select(G, scores, seq_lens, budgets, sel_pages, sel_count,
-                            reinterpret_cast<float*>(ws + w.keys), S, H, MP, KB, 0, st);
+                            reinterpret_cast<float*>(ws + w.keys), S, H, MP, KB, 0, d->merge_rule,
+                            st);
   return hip_status(he);
 }
 
@@ -228,9 +239,10 @@ locks_status locks_score_pages(const locks_dims* d, const void* q, const void* s
   if (S == 0) return LOCKS_OK;
   if (!q || !summaries || !block_table || !seq_lens || !scores) return LOCKS_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(summaries)) return LOCKS_ERR_INVALID_ARG;
-  return hip_status(locks::launch_score(d->rank, d->group_size, q, summaries, block_table,
-                                        seq_lens, scores, nb, S, d->num_kv_heads, MP, 0, nullptr,
-                                        nullptr, nullptr, nullptr, nullptr, nullptr, locks::CoopZero{}, st));
+  return hip_status(locks::launch_score(d->rank, bits_of(d), d->group_size, q, summaries,
+                                        block_table, seq_lens, scores, nb, S, d->num_kv_heads, MP,
+                                        0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                        locks::CoopZero{}, st));
 }
 
 locks_status locks_select_pages(const locks_dims* d, const float* scores, const int32_t* seq_lens,
@@ -248,7 +260,7 @@ locks_status locks_select_pages(const locks_dims* d, const float* scores, const 
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   return hip_status(locks::launch_select(d->group_size, scores, seq_lens, budgets, sel_pages,
                                          sel_count, reinterpret_cast<float*>(ws + w.keys), S,
-                                         d->num_kv_heads, MP, KB, 0, st));
+                                         d->num_kv_heads, MP, KB, 0, d->merge_rule, st));
 }
 
 locks_status locks_sparse_attn(const locks_dims* d, const void* q, const void* k_pool,
@@ -311,7 +323,7 @@ locks_status decode_step_run(const locks_dims* d, const void* q, const void* k_n
                              int32_t MP, int32_t KB, float* out, float* lse_out,
                              int32_t* sel_pages, int32_t* sel_count, uint32_t flags,
                              const Workspace& w, uint8_t* ws, bool reset_step, hipStream_t st) {
-  const int H = d->num_kv_heads, G = d->group_size;
+  const int H = d->num_kv_heads, G = d->group_size, bits = bits_of(d);
   const bool deferred = (flags & LOCKS_STEP_DEFER_BUILD) != 0;
 
   // Every decision is taken before the first launch, so that a call that
@@ -329,7 +341,8 @@ locks_status decode_step_run(const locks_dims* d, const void* q, const void* k_n
   //      once; else the separate score, select and attention launches
   int per_wg, nsplit, slice;
   bool fused = locks::decode_shape(MP, KB, &per_wg, &nsplit, &slice);
-  const int rfused = locks::decode_step_fuses_score(d->rank) ? d->rank : 0;
+  // (the matrix-core score part reads int4 bases only)
+  const int rfused = (bits == 4 && locks::decode_step_fuses_score(d->rank)) ? d->rank : 0;
   if (fused) {
     const int HL = H < 8 ? H : 8;
     fused = locks::decode_resident_capacity(rfused, G, nsplit) >= HL * nsplit;
@@ -346,7 +359,7 @@ locks_status decode_step_run(const locks_dims* d, const void* q, const void* k_n
   // 1. append (+ summaries of the pages the new token completes)
   if (completes) {
     hipError_t he = locks::launch_build(d->rank, k_pool, nb, H, nullptr, S, block_table, seq_lens,
-                                        MP, summaries, k_new, v_new, v_pool, st);
+                                        MP, summaries, k_new, v_new, v_pool, bits, st);
     if (he != hipSuccess) return LOCKS_ERR_HIP;
   }
   // 2. scores of all full pages and Z partials (and the append when no page
@@ -390,20 +403,22 @@ locks_status decode_step_run(const locks_dims* d, const void* q, const void* k_n
     a.coop = coop;
     a.r = rfused;
     a.lag = deferred ? 1 : 0;
+    a.rule = d->merge_rule;
     if (a.r == 0) {
-      hipError_t he = locks::launch_score(d->rank, G, q, summaries, block_table, seq_lens, scores, nb,
-                                          S, H, MP, deferred ? locks::kScoreDeferred : 0, zpart, kn,
-                                          vn, k_pool, v_pool, pmax, coop, st);
+      hipError_t he = locks::launch_score(d->rank, bits, G, q, summaries, block_table, seq_lens,
+                                          scores, nb, S, H, MP, deferred ? locks::kScoreDeferred : 0,
+                                          zpart, kn, vn, k_pool, v_pool, pmax, coop, st);
       if (he != hipSuccess) return LOCKS_ERR_HIP;
     }
     return hip_status(locks::launch_decode(G, a, st));
   }
-  hipError_t he = locks::launch_score(d->rank, G, q, summaries, block_table, seq_lens, scores, nb,
-                                      S, H, MP, deferred ? locks::kScoreDeferred : 0, zpart, kn, vn,
-                                      k_pool, v_pool, nullptr, locks::CoopZero{}, st);
+  hipError_t he = locks::launch_score(d->rank, bits, G, q, summaries, block_table, seq_lens, scores,
+                                      nb, S, H, MP, deferred ? locks::kScoreDeferred : 0, zpart, kn,
+                                      vn, k_pool, v_pool, nullptr, locks::CoopZero{}, st);
   if (he != hipSuccess) return LOCKS_ERR_HIP;
   he = locks::launch_select(G, scores, seq_lens, budgets, sel, cnt,
-                            reinterpret_cast<float*>(ws + w.keys), S, H, MP, KB, deferred ? 1 : 0, st);
+                            reinterpret_cast<float*>(ws + w.keys), S, H, MP, KB, deferred ? 1 : 0,
+                            d->merge_rule, st);
   if (he != hipSuccess) return LOCKS_ERR_HIP;
   return hip_status(locks::launch_attn(G, q, k_pool, v_pool, block_table, seq_lens, sel, cnt,
                                        reinterpret_cast<float*>(ws + w.parts), out, lse_out, nb, S,

@@ -276,7 +276,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     int slice, int per_wg, uint32_t* __restrict__ mbox, float* __restrict__ out,
     float* __restrict__ lse_out, int32_t* __restrict__ sel_pages, int32_t* __restrict__ sel_count,
     const uint8_t* __restrict__ summ, int npairs, const uint16_t* __restrict__ knew,
-    const uint16_t* __restrict__ vnew, CoopZero coop, int lag) {
+    const uint16_t* __restrict__ vnew, CoopZero coop, int lag, int rule) {
   constexpr int nsplit = kS;
   constexpr int kTop = kDecThreads / kS;  // top-candidate slots per slice
   static_assert(kTop * kS == kDecThreads, "one top-candidate slot per thread");
@@ -437,15 +437,31 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     for (int g = 0; g < G; ++g)
       wg[g] = (lz[g] == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(fminf(zx - lz[g], 126.f));
     const float log2G = (G == 1) ? 0.f : (G == 2) ? 1.f : 2.f;
-    // ---- 2. key (<= 0) and bin of this thread's page
+    // group-mass: log2 sum_g Z_g
+    float ztot = 0.f;
+#pragma unroll
+    for (int g = 0; g < G; ++g) ztot += (lz[g] == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(lz[g] - zx);
+    ztot = zx + __builtin_amdgcn_logf(ztot);
+    // ---- 2. key (<= 0) and bin of this thread's page: the share average of
+    // eq. 5, or the group-max / group-mass alternatives
     const bool cand = jin && j >= 1 && j <= P - 2;
     float key;
     int bin;
     {
       float t = 0.f;
+      if (rule == kMergeMax) {
 #pragma unroll
-      for (int g = 0; g < G; ++g) t = fmaf(ev[g], wg[g], t);
-      float kj = (mv - zx) + (__builtin_amdgcn_logf(t) - log2G);
+        for (int g = 0; g < G; ++g) t = fmaxf(t, ev[g] * wg[g]);
+      } else if (rule == kMergeMass) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) t += ev[g];
+      } else {
+#pragma unroll
+        for (int g = 0; g < G; ++g) t = fmaf(ev[g], wg[g], t);
+      }
+      float kj = (rule == kMergeMax)    ? (mv - zx) + __builtin_amdgcn_logf(t)
+                 : (rule == kMergeMass) ? mv + __builtin_amdgcn_logf(t) - ztot
+                                        : (mv - zx) + (__builtin_amdgcn_logf(t) - log2G);
       kj = (cand && kj == kj) ? kj : -__builtin_inff();
       key = kj;
       bin = dec_bin(kj);
@@ -980,7 +996,7 @@ static void launch_step_rgs(const StepLaunch& a, hipStream_t st) {
                      static_cast<uint16_t*>(a.vpool), a.table, a.nb, a.H, a.MP, a.KB, a.slice, a.per_wg,
                      a.mbox, a.out, a.lse_out, a.sel, a.cnt, static_cast<const uint8_t*>(a.summ), npairs,
                      static_cast<const uint16_t*>(a.knew), static_cast<const uint16_t*>(a.vnew), a.coop,
-                     a.lag);
+                     a.lag, a.rule);
 }
 
 template <int R, int G>

@@ -63,24 +63,28 @@ constexpr float kLn2 = 0.6931471805599453f;
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 
-// Summary slot byte layout: [Vq r*d/2][Cq B*r][muq d][fp16 scales r+B+1][pad].
-// The stride is a whole number of 128-byte lines, so every slot starts on a
-// line and no two slots (read by the workgroups of different heads, on
-// different XCDs) share one.
+// Summary slot byte layout: [Vq r*d*bits/8][Cq B*r][muq d][fp16 scales r+B+1][pad]
+// (bits = 4 for the int4 basis; 8 and 2 for the precision ablation). The
+// stride is a whole number of 128-byte lines, so every slot starts on a line
+// and no two slots (read by the workgroups of different heads, on different
+// XCDs) share one.
 struct SlotLayout {
   int v, c, mu, sv, sc, smu, payload, stride;
 };
 
-__host__ __device__ constexpr SlotLayout slot_layout(int r) {
+__host__ __device__ constexpr SlotLayout slot_layout(int r, int bits = 4) {
   return SlotLayout{0,
-                    r * (kHeadDim / 2),
-                    r * (kHeadDim / 2) + kPage * r,
-                    r * (kHeadDim / 2) + kPage * r + kHeadDim,
-                    r * (kHeadDim / 2) + kPage * r + kHeadDim + 2 * r,
-                    r * (kHeadDim / 2) + kPage * r + kHeadDim + 2 * (r + kPage),
-                    r * (kHeadDim / 2) + kPage * r + kHeadDim + 2 * (r + kPage + 1),
-                    (r * (kHeadDim / 2) + kPage * r + kHeadDim + 2 * (r + kPage + 1) + 127) / 128 * 128};
+                    r * kHeadDim * bits / 8,
+                    r * kHeadDim * bits / 8 + kPage * r,
+                    r * kHeadDim * bits / 8 + kPage * r + kHeadDim,
+                    r * kHeadDim * bits / 8 + kPage * r + kHeadDim + 2 * r,
+                    r * kHeadDim * bits / 8 + kPage * r + kHeadDim + 2 * (r + kPage),
+                    r * kHeadDim * bits / 8 + kPage * r + kHeadDim + 2 * (r + kPage + 1),
+                    (r * kHeadDim * bits / 8 + kPage * r + kHeadDim + 2 * (r + kPage + 1) + 127) / 128 * 128};
 }
+
+// Largest code of the symmetric b-bit basis quantiser: 2^(b-1) - 1.
+__host__ __device__ constexpr int basis_qmax(int bits) { return (1 << (bits - 1)) - 1; }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

@@ -28,9 +28,11 @@ namespace locks {
 // ---------------------------------------------------------------------------
 // kScorePagesPerWg = 4 waves x 16 pages x 2 batches
 
-template <int R>
+// BITS: the basis width (4; 8 and 2 for the precision ablation). The lane's
+// 32 dims of a basis column take BITS 32-bit words.
+template <int R, int BITS>
 struct SlotRegs {
-  uint4 vq[R];
+  uint32_t vq[R][BITS];
   uint4 mq0, mq1;
   uint32_t cq[R];
   uint16_t sv[R];
@@ -40,14 +42,31 @@ struct SlotRegs {
 
 // Loads the lane's share of one slot. blk < 0 (page outside the range or a
 // block id out of range) loads block 0's slot as a stand-in.
-template <int R>
-__device__ __forceinline__ void load_slot(SlotRegs<R>& d, const uint8_t* __restrict__ summ, int H,
-                                          int h, int blk, int l4) {
-  constexpr SlotLayout L = slot_layout(R);
+template <int R, int BITS>
+__device__ __forceinline__ void load_slot(SlotRegs<R, BITS>& d, const uint8_t* __restrict__ summ,
+                                          int H, int h, int blk, int l4) {
+  constexpr SlotLayout L = slot_layout(R, BITS);
   const uint8_t* slot = static_cast<const uint8_t*>(
       __builtin_assume_aligned(summ + ((int64_t)(blk >= 0 ? blk : 0) * H + h) * L.stride, 16));
 #pragma unroll
-  for (int k = 0; k < R; ++k) d.vq[k] = *reinterpret_cast<const uint4*>(slot + 64 * k + 16 * l4);
+  for (int k = 0; k < R; ++k) {
+    // column k is 16 BITS bytes; the lane's 32 dims are 4 BITS bytes of it
+    const uint8_t* col = slot + 16 * BITS * k + 4 * BITS * l4;
+    if constexpr (BITS == 2) {
+      const uint2 w = *reinterpret_cast<const uint2*>(col);
+      d.vq[k][0] = w.x;
+      d.vq[k][1] = w.y;
+    } else {
+#pragma unroll
+      for (int c = 0; c < BITS / 4; ++c) {
+        const uint4 w = *reinterpret_cast<const uint4*>(col + 16 * c);
+        d.vq[k][4 * c] = w.x;
+        d.vq[k][4 * c + 1] = w.y;
+        d.vq[k][4 * c + 2] = w.z;
+        d.vq[k][4 * c + 3] = w.w;
+      }
+    }
+  }
   d.mq0 = *reinterpret_cast<const uint4*>(slot + L.mu + 32 * l4);
   d.mq1 = *reinterpret_cast<const uint4*>(slot + L.mu + 32 * l4 + 16);
 #pragma unroll
@@ -72,7 +91,7 @@ __device__ __forceinline__ void load_slot(SlotRegs<R>& d, const uint8_t* __restr
 // Otherwise scores receives s_hat in natural-log units.
 // knew/vnew (optional): the workgroup with tile index 0 of each (sequence,
 // head) first appends the new token's key and value for that head.
-template <int R, int G>
+template <int R, int G, int BITS>
 __global__ __launch_bounds__(256) void score_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ summ,
     const int32_t* __restrict__ table, const int32_t* __restrict__ seq_lens,
@@ -80,7 +99,7 @@ __global__ __launch_bounds__(256) void score_kernel(
     int flags, float2* __restrict__ zpart, const uint16_t* __restrict__ knew,
     const uint16_t* __restrict__ vnew, uint16_t* __restrict__ kpool,
     uint16_t* __restrict__ vpool, float* __restrict__ mxout, CoopZero coop) {
-  constexpr SlotLayout L = slot_layout(R);
+  static_assert(BITS == 2 || BITS == 4 || BITS == 8, "basis width");
   constexpr float kTwoM24 = 5.9604644775390625e-08f;  // 2^-24
   zero_coop_mailbox(coop, (int64_t)blockIdx.z * H + blockIdx.x, blockIdx.y, gridDim.y);
   const int s = blockIdx.z, h = blockIdx.x, tile = blockIdx.y;
@@ -114,6 +133,9 @@ __global__ __launch_bounds__(256) void score_kernel(
 
   // ---- queries of the group: lane's 32 dims, power-of-two scaled fp16 pairs
   half2v Q[G][4][4];
+  // int2 basis: the pairs of dims (16 h + e, 16 h + e + 8) that one mask of a
+  // word's two-bit fields yields
+  half2v Q2[BITS == 2 ? G : 1][2][8];
   float vinit[G], minit[G], fscale[G];
   for (int g = 0; g < G; ++g) {
     const uint4* qp = reinterpret_cast<const uint4*>(
@@ -146,7 +168,15 @@ __global__ __launch_bounds__(256) void score_kernel(
       Q[g][t][2] = half2v{(_Float16)(y[4] * up), (_Float16)(y[6] * up)};
       Q[g][t][3] = half2v{(_Float16)(y[5] * up * 0.0625f), (_Float16)(y[7] * up * 0.0625f)};
     }
-    vinit[g] = -8.f * kTwoM24 * qs;
+    if constexpr (BITS == 2) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          Q2[g][hh][e] = half2v{(_Float16)(x[16 * hh + e] * up), (_Float16)(x[16 * hh + e + 8] * up)};
+    }
+    // offset-binary codes: value = code - 8 (int4), - 128 (int8), - 2 (int2)
+    vinit[g] = -(BITS == 4 ? 8.f : BITS == 8 ? 128.f : 2.f) * kTwoM24 * qs;
     minit[g] = -128.f * kTwoM24 * qs;
     // logits in log2 units: 2^(24 - (14 - ex)) * log2(e) / sqrt(d)
     fscale[g] = ldexpf(kLog2e * 0.08838834764831845f, 10 + ex);
@@ -165,16 +195,15 @@ __global__ __launch_bounds__(256) void score_kernel(
     blks[it] = (b >= 0 && b < num_blocks) ? b : -1;
   }
   float zm = -__builtin_inff(), zs = 0.f;  // running LSE of query head l4 over the pages
-  SlotRegs<R> cur, nxt;
-  load_slot<R>(cur, summ, H, h, blks[0], l4);
+  SlotRegs<R, BITS> cur, nxt;
+  load_slot<R, BITS>(cur, summ, H, h, blks[0], l4);
 #pragma unroll
   for (int it = 0; it < kMaxIter; ++it) {
     const int j = jw + 64 * it;
     if (j - (lane >> 2) >= j_end) break;  // wave-uniform
     const bool in = j < j_end;
     const bool ok = blks[it] >= 0;
-    if (it + 1 < kMaxIter) load_slot<R>(nxt, summ, H, h, blks[it + 1 < kMaxIter ? it + 1 : it], l4);
-    const uint4* vq = cur.vq;
+    if (it + 1 < kMaxIter) load_slot<R, BITS>(nxt, summ, H, h, blks[it + 1 < kMaxIter ? it + 1 : it], l4);
     const uint4 mq0 = cur.mq0, mq1 = cur.mq1;
     const uint32_t* cq = cur.cq;
     const uint16_t* sv = cur.sv;
@@ -187,23 +216,56 @@ __global__ __launch_bounds__(256) void score_kernel(
     for (int k = 0; k < R; ++k) {
 #pragma unroll
       for (int g = 0; g < G; ++g) acc[k][g] = vinit[g];
-      const uint32_t words[4] = {vq[k].x, vq[k].y, vq[k].z, vq[k].w};
+      if constexpr (BITS == 4) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint32_t w = words[t] ^ 0x88888888u;
-        const uint32_t w8 = w >> 8;
-        const half2v p0 = __builtin_bit_cast(half2v, w & 0x000F000Fu);
-        const half2v p1 = __builtin_bit_cast(half2v, w & 0x00F000F0u);
-        const half2v p2 = __builtin_bit_cast(half2v, w8 & 0x000F000Fu);
-        const half2v p3 = __builtin_bit_cast(half2v, w8 & 0x00F000F0u);
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t w = cur.vq[k][t] ^ 0x88888888u;
+          const uint32_t w8 = w >> 8;
+          const half2v p0 = __builtin_bit_cast(half2v, w & 0x000F000Fu);
+          const half2v p1 = __builtin_bit_cast(half2v, w & 0x00F000F0u);
+          const half2v p2 = __builtin_bit_cast(half2v, w8 & 0x000F000Fu);
+          const half2v p3 = __builtin_bit_cast(half2v, w8 & 0x00F000F0u);
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float a = acc[k][g];
-          a = __builtin_amdgcn_fdot2(p0, Q[g][t][0], a, false);
-          a = __builtin_amdgcn_fdot2(p1, Q[g][t][1], a, false);
-          a = __builtin_amdgcn_fdot2(p2, Q[g][t][2], a, false);
-          a = __builtin_amdgcn_fdot2(p3, Q[g][t][3], a, false);
-          acc[k][g] = a;
+          for (int g = 0; g < G; ++g) {
+            float a = acc[k][g];
+            a = __builtin_amdgcn_fdot2(p0, Q[g][t][0], a, false);
+            a = __builtin_amdgcn_fdot2(p1, Q[g][t][1], a, false);
+            a = __builtin_amdgcn_fdot2(p2, Q[g][t][2], a, false);
+            a = __builtin_amdgcn_fdot2(p3, Q[g][t][3], a, false);
+            acc[k][g] = a;
+          }
+        }
+      } else if constexpr (BITS == 8) {
+        // bytes as the centroid's: offset binary, even and odd dims of a word
+        float a16[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) a16[g] = 0.f;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const uint32_t w = cur.vq[k][m] ^ 0x80808080u;
+          const half2v e0 = __builtin_bit_cast(half2v, w & 0x00FF00FFu);
+          const half2v e1 = __builtin_bit_cast(half2v, (w >> 8) & 0x00FF00FFu);
+          const int t = m >> 1, o = (m & 1) * 2;
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            acc[k][g] = __builtin_amdgcn_fdot2(e0, Q[g][t][o], acc[k][g], false);
+            a16[g] = __builtin_amdgcn_fdot2(e1, Q[g][t][o + 1], a16[g], false);
+          }
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) acc[k][g] = fmaf(16.f, a16[g], acc[k][g]);
+      } else {
+        // two-bit fields: offset binary after flipping each field's top bit;
+        // mask e yields the fields e and e + 8 of a word
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const uint32_t w = cur.vq[k][hh] ^ 0xAAAAAAAAu;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const half2v p = __builtin_bit_cast(half2v, (w >> (2 * e)) & 0x00030003u);
+#pragma unroll
+            for (int g = 0; g < G; ++g) acc[k][g] = __builtin_amdgcn_fdot2(p, Q2[g][hh][e], acc[k][g], false);
+          }
         }
       }
     }
@@ -326,7 +388,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ budgets, int32_t* __restrict__ sel_pages,
     int32_t* __restrict__ sel_count, float* __restrict__ keybuf, int H, int MP,
-    int max_budget, int lag) {
+    int max_budget, int lag, int rule) {
   extern __shared__ float sh_keys[];
   __shared__ uint32_t bits[kMaxBitmapWords];
   __shared__ uint32_t hist[kBins];
@@ -395,6 +457,12 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
   float logZ[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) logZ[g] = mx[g] + __logf(sm[g]);
+  float logZtot = logZ[0];  // log sum_g Z_g (group-mass)
+#pragma unroll
+  for (int g = 1; g < G; ++g) {
+    const float a = fmaxf(logZtot, logZ[g]), b = fminf(logZtot, logZ[g]);
+    logZtot = a + log1pf(__expf(b - a));
+  }
 
   // ---- 2. keys of the candidates 1..P-2 and their maximum
   const float logG = __logf((float)G);
@@ -405,7 +473,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
       const int j = c0 + u * nthr + tid;
       if (j < 1 || j > P - 2) continue;
       if (!one_chunk) load_scores<G>(sc + (int64_t)j * G, v[u]);
-      const float kj = group_key<G>(v[u], logZ, logG);
+      const float kj = group_key_rule<G>(v[u], logZ, logG, rule, logZtot);
       key[j] = kj;
       kmax = fmaxf(kmax, kj);
     }
@@ -547,7 +615,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
 // ---------------------------------------------------------------------------
 // host-side launchers
 // ---------------------------------------------------------------------------
-template <int R, int G>
+template <int R, int G, int BITS>
 static hipError_t launch_score_rg(const uint16_t* q, const uint8_t* summ, const int32_t* table,
                                   const int32_t* lens, float* scores, int64_t nb, int S, int H,
                                   int MP, int flags, float2* zpart, const void* knew,
@@ -555,7 +623,7 @@ static hipError_t launch_score_rg(const uint16_t* q, const uint8_t* summ, const 
                                   CoopZero coop, hipStream_t st) {
   const int ppw = kScorePagesPerWg;
   dim3 grid(H, (MP + ppw - 1) / ppw, S);
-  hipLaunchKernelGGL((score_kernel<R, G>), grid, dim3(256), 0, st, q, summ, table, lens, scores,
+  hipLaunchKernelGGL((score_kernel<R, G, BITS>), grid, dim3(256), 0, st, q, summ, table, lens, scores,
                      nb, H, MP, ppw, flags, zpart, static_cast<const uint16_t*>(knew),
                      static_cast<const uint16_t*>(vnew), static_cast<uint16_t*>(kpool),
                      static_cast<uint16_t*>(vpool), mxout, coop);
@@ -563,22 +631,36 @@ static hipError_t launch_score_rg(const uint16_t* q, const uint8_t* summ, const 
 }
 
 template <int G>
-static hipError_t launch_score_g(int r, const uint16_t* q, const uint8_t* summ,
+static hipError_t launch_score_g(int r, int bits, const uint16_t* q, const uint8_t* summ,
                                  const int32_t* table, const int32_t* lens, float* scores,
                                  int64_t nb, int S, int H, int MP, int flags, float2* zpart,
                                  const void* knew, const void* vnew, void* kpool, void* vpool,
                                  float* mxout, CoopZero coop, hipStream_t st) {
+#define LOCKS_ARGS q, summ, table, lens, scores, nb, S, H, MP, flags, zpart, knew, vnew, kpool, vpool, mxout, coop, st
+  if (bits != 4) {
+    // the precision ablation: ranks 4, 8 and 16
+#define LOCKS_RB(RR)                                                                   \
+  case RR:                                                                             \
+    return bits == 8 ? launch_score_rg<RR, G, 8>(LOCKS_ARGS)                           \
+                     : bits == 2 ? launch_score_rg<RR, G, 2>(LOCKS_ARGS) : hipErrorInvalidValue;
+    switch (r) {
+      LOCKS_RB(4) LOCKS_RB(8) LOCKS_RB(16)
+      default:
+        return hipErrorInvalidValue;
+    }
+#undef LOCKS_RB
+  }
   switch (r) {
-#define LOCKS_R(RR)                                                                        \
-  case RR:                                                                                 \
-    return launch_score_rg<RR, G>(q, summ, table, lens, scores, nb, S, H, MP, flags,   \
-                                  zpart, knew, vnew, kpool, vpool, mxout, coop, st);
+#define LOCKS_R(RR) \
+  case RR:          \
+    return launch_score_rg<RR, G, 4>(LOCKS_ARGS);
     LOCKS_R(1) LOCKS_R(2) LOCKS_R(3) LOCKS_R(4) LOCKS_R(5) LOCKS_R(6) LOCKS_R(7) LOCKS_R(8)
     LOCKS_R(9) LOCKS_R(10) LOCKS_R(11) LOCKS_R(12) LOCKS_R(13) LOCKS_R(14) LOCKS_R(15) LOCKS_R(16)
 #undef LOCKS_R
     default:
       return hipErrorInvalidValue;
   }
+#undef LOCKS_ARGS
 }
 
 bool score_mfma_supported(int r);
@@ -588,21 +670,22 @@ hipError_t launch_score_mfma(int r, int G, const void* q, const void* summ, cons
                              void* kpool, void* vpool, float* mxout, CoopZero coop,
                              hipStream_t st);
 
-hipError_t launch_score(int r, int G, const void* q, const void* summ, const int32_t* table,
-                        const int32_t* lens, float* scores, int64_t nb, int S, int H, int MP,
-                        int flags, float2* zpart, const void* knew, const void* vnew,
-                        void* kpool, void* vpool, float* mxout, CoopZero coop,
+// bits: the basis width of the slots (4; 8 and 2 go through score_kernel).
+hipError_t launch_score(int r, int bits, int G, const void* q, const void* summ,
+                        const int32_t* table, const int32_t* lens, float* scores, int64_t nb,
+                        int S, int H, int MP, int flags, float2* zpart, const void* knew,
+                        const void* vnew, void* kpool, void* vpool, float* mxout, CoopZero coop,
                         hipStream_t st) {
-  if (score_mfma_supported(r))
+  if (bits == 4 && score_mfma_supported(r))
     return launch_score_mfma(r, G, q, summ, table, lens, scores, nb, S, H, MP, flags, zpart,
                              knew, vnew, kpool, vpool, mxout, coop, st);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint8_t* ss = static_cast<const uint8_t*>(summ);
   switch (G) {
 #define LOCKS_ARGS qq, ss, table, lens, scores, nb, S, H, MP, flags, zpart, knew, vnew, kpool, vpool, mxout, coop, st
-    case 1: return launch_score_g<1>(r, LOCKS_ARGS);
-    case 2: return launch_score_g<2>(r, LOCKS_ARGS);
-    case 4: return launch_score_g<4>(r, LOCKS_ARGS);
+    case 1: return launch_score_g<1>(r, bits, LOCKS_ARGS);
+    case 2: return launch_score_g<2>(r, bits, LOCKS_ARGS);
+    case 4: return launch_score_g<4>(r, bits, LOCKS_ARGS);
 #undef LOCKS_ARGS
     default: return hipErrorInvalidValue;
   }
@@ -611,26 +694,27 @@ hipError_t launch_score(int r, int G, const void* q, const void* summ, const int
 template <int G>
 static void launch_select_g(dim3 grid, int MP, const float* scores, const int32_t* lens,
                             const int32_t* budgets, int32_t* sel, int32_t* cnt, float* keybuf,
-                            int H, int max_budget, int lag, hipStream_t st) {
+                            int H, int max_budget, int lag, int rule, hipStream_t st) {
   if (MP <= kSelectLdsPages) {
     hipLaunchKernelGGL((select_kernel<G, true>), grid, dim3(kSelectThreads),
                        (size_t)MP * sizeof(float), st, scores, lens, budgets, sel, cnt, keybuf,
-                       H, MP, max_budget, lag);
+                       H, MP, max_budget, lag, rule);
   } else {
     hipLaunchKernelGGL((select_kernel<G, false>), grid, dim3(kSelectThreads), 0, st, scores, lens,
-                       budgets, sel, cnt, keybuf, H, MP, max_budget, lag);
+                       budgets, sel, cnt, keybuf, H, MP, max_budget, lag, rule);
   }
 }
 
-// lag = 1: only the pages full before the current token are scored (deferred build).
+// lag = 1: only the pages full before the current token are scored (deferred
+// build). rule: the GQA merge rule (kMergeShare, kMergeMax, kMergeMass).
 hipError_t launch_select(int G, const float* scores, const int32_t* lens, const int32_t* budgets,
                          int32_t* sel, int32_t* cnt, float* keybuf, int S, int H, int MP,
-                         int max_budget, int lag, hipStream_t st) {
+                         int max_budget, int lag, int rule, hipStream_t st) {
   dim3 grid(H, S);
   switch (G) {
-    case 1: launch_select_g<1>(grid, MP, scores, lens, budgets, sel, cnt, keybuf, H, max_budget, lag, st); break;
-    case 2: launch_select_g<2>(grid, MP, scores, lens, budgets, sel, cnt, keybuf, H, max_budget, lag, st); break;
-    case 4: launch_select_g<4>(grid, MP, scores, lens, budgets, sel, cnt, keybuf, H, max_budget, lag, st); break;
+    case 1: launch_select_g<1>(grid, MP, scores, lens, budgets, sel, cnt, keybuf, H, max_budget, lag, rule, st); break;
+    case 2: launch_select_g<2>(grid, MP, scores, lens, budgets, sel, cnt, keybuf, H, max_budget, lag, rule, st); break;
+    case 4: launch_select_g<4>(grid, MP, scores, lens, budgets, sel, cnt, keybuf, H, max_budget, lag, rule, st); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -120,4 +120,29 @@ __device__ __forceinline__ float group_key(const float (&v)[G], const float (&lo
   return (key == key && m != -__builtin_inff()) ? key : -__builtin_inff();
 }
 
+// Merge rules (natural log): 0 = share average (group_key), 1 = group-max
+// log max_g exp(s_g - logZ_g), 2 = group-mass log sum_g exp(s_g) - logZtot
+// with logZtot = log sum_g Z_g.
+constexpr int kMergeShare = 0;
+constexpr int kMergeMax = 1;
+constexpr int kMergeMass = 2;
+template <int G>
+__device__ __forceinline__ float group_key_rule(const float (&v)[G], const float (&logZ)[G],
+                                                float logG, int rule, float logZtot) {
+  if (rule == kMergeShare) return group_key<G>(v, logZ, logG);
+  float m = -__builtin_inff();
+  if (rule == kMergeMax) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) m = fmaxf(m, v[g] - logZ[g]);
+    return (m == m) ? m : -__builtin_inff();
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) m = fmaxf(m, v[g]);
+  float t = 0.f;
+#pragma unroll
+  for (int g = 0; g < G; ++g) t += __expf(v[g] - m);
+  const float key = m + __logf(t) - logZtot;
+  return (key == key && m != -__builtin_inff()) ? key : -__builtin_inff();
+}
+
 }  // namespace locks

@@ -20,6 +20,7 @@ struct StepLaunch {
   int64_t nb;
   int S, H, MP, KB, nsplit, slice, per_wg;
   int lag;              // 1: only the pages full before the current token are scored
+  int rule;             // GQA merge rule of the selection keys (kMergeShare, ...)
   uint32_t* mbox;
   float* out;
   float* lse_out;

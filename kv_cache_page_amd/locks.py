@@ -36,14 +36,25 @@ ENTRY_POINTS = (
 NOALLOC_SCRATCH_BYTES = 16 << 20   # LOCKS_NOALLOC_SCRATCH_BYTES
 
 
+MERGE_SHARE, MERGE_MAX, MERGE_MASS = 0, 1, 2   # LOCKS_MERGE_*
+MERGE_RULES = {"share": MERGE_SHARE, "max": MERGE_MAX, "mass": MERGE_MASS}
+
+
 class Dims(ctypes.Structure):
-    """locks_dims: head_dim, page_size, rank, num_kv_heads, group_size."""
+    """locks_dims: head_dim, page_size, rank, num_kv_heads, group_size,
+    basis_bits (0 = 4), merge_rule (LOCKS_MERGE_*; a name of MERGE_RULES is
+    accepted too)."""
     _fields_ = [("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("rank", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
-                ("group_size", ctypes.c_int32)]
+                ("group_size", ctypes.c_int32), ("basis_bits", ctypes.c_int32),
+                ("merge_rule", ctypes.c_int32)]
 
-    def __init__(self, num_kv_heads, group_size, rank=8, head_dim=128, page_size=16):
-        super().__init__(head_dim, page_size, rank, num_kv_heads, group_size)
+    def __init__(self, num_kv_heads, group_size, rank=8, head_dim=128, page_size=16,
+                 basis_bits=0, merge_rule=MERGE_SHARE):
+        if isinstance(merge_rule, str):
+            merge_rule = MERGE_RULES[merge_rule]
+        super().__init__(head_dim, page_size, rank, num_kv_heads, group_size, basis_bits,
+                         merge_rule)
 
 
 class LocksError(RuntimeError):

@@ -24,10 +24,10 @@ def head_pages(k_pool, v_pool, table, seq_len, s, h):
     return np64(k_pool[blocks, h]), np64(v_pool[blocks, h])
 
 
-def oracle_summaries(k_pool, table, seq_lens, H, r, num_blocks):
+def oracle_summaries(k_pool, table, seq_lens, H, r, num_blocks, basis_bits=4):
     """Oracle-built slots for every full page of every (seq, head), written at
     their physical block positions: uint8 [num_blocks][H][stride]."""
-    stride = O.slot_layout(r)["stride"]
+    stride = O.slot_layout(r, basis_bits=basis_bits)["stride"]
     summ = np.zeros((num_blocks, H, stride), dtype=np.uint8)
     kp = k_pool.detach().to("cpu")
     for s, L in enumerate(seq_lens.tolist()):
@@ -37,13 +37,13 @@ def oracle_summaries(k_pool, table, seq_lens, H, r, num_blocks):
         blocks = table[s, :F].long().cpu()
         for h in range(H):
             keys = kp[blocks, h].double().numpy()
-            slots, _, _ = O.build_slots(keys, r)
+            slots, _, _ = O.build_slots(keys, r, basis_bits=basis_bits)
             summ[blocks.numpy(), h] = slots
     return summ
 
 
 def oracle_head(q, k_pool, v_pool, table, seq_lens, budgets, summ, s, h, G, r, mode="quantised",
-                deferred=False):
+                deferred=False, basis_bits=4, merge="share"):
     L = int(seq_lens[s])
     Kp, Vp = head_pages(k_pool, v_pool, table, L, s, h)
     qq = np64(q[s, h * G:(h + 1) * G])
@@ -53,7 +53,7 @@ def oracle_head(q, k_pool, v_pool, table, seq_lens, budgets, summ, s, h, G, r, m
         blocks = table[s, :F].long().cpu().numpy()
         slots = summ[blocks, h]
     return O.decode_head(qq, Kp, Vp, L, int(budgets[s]), slots=slots, r=r, mode=mode,
-                         deferred=deferred)
+                         deferred=deferred, basis_bits=basis_bits, merge=merge)
 
 
 def selection_mismatch(gpu_sel, ora_sel, key, P, tol=1e-5):

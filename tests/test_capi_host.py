@@ -148,3 +148,20 @@ def test_host_pool_argument_checks():
     assert L._host_alloc(4096, None, ctypes.byref(dp)) == L.ERR_INVALID_ARG
     assert L._host_alloc(4096, ctypes.byref(hp), None) == L.ERR_INVALID_ARG
     assert L._host_free(None) == L.OK
+
+
+def test_basis_width_and_merge_rule_dims():
+    """The precision ablation's slot sizes, and invalid widths and rules."""
+    assert L.slot_bytes(L.Dims(8, 4, 8, basis_bits=8)) == 1330
+    assert L.slot_stride(L.Dims(8, 4, 8, basis_bits=8)) == 1408
+    assert L.slot_bytes(L.Dims(8, 4, 8, basis_bits=2)) == 562
+    assert L.slot_stride(L.Dims(8, 4, 8, basis_bits=2)) == 640
+    assert L.slot_bytes(L.Dims(8, 4, 16, basis_bits=8)) == 16 * 128 + 256 + 128 + 2 * 33
+    assert L.slot_bytes(L.Dims(8, 4, 8, basis_bits=4)) == L.slot_bytes(L.Dims(8, 4, 8)) == 818
+    assert L.slot_bytes(L.Dims(8, 4, 8, basis_bits=3)) == 0
+    assert L.slot_bytes(L.Dims(8, 4, 6, basis_bits=8)) == 0        # ablation ranks 4, 8, 16
+    assert L.slot_bytes(L.Dims(8, 4, 6, basis_bits=4)) > 0
+    for rule in ("share", "max", "mass"):
+        assert L.slot_bytes(L.Dims(8, 4, 8, merge_rule=rule)) == 818
+    assert L.slot_bytes(L.Dims(8, 4, 8, merge_rule=3)) == 0
+    assert L.slot_bytes(L.Dims(8, 4, 8, merge_rule=-1)) == 0

@@ -59,7 +59,8 @@ def _run_decode(L, dims, bd, summ_dev, max_budget, scores=True):
                 lse=lse.cpu().numpy())
 
 
-def _check_against_oracle(b, summ, res, r, max_budget, heads=None, score_tol=1e-3, deferred=False):
+def _check_against_oracle(b, summ, res, r, max_budget, heads=None, score_tol=1e-3, deferred=False,
+                          basis_bits=4, merge="share"):
     """Compare one decode step (every or the listed (seq, head)) with the
     oracle fed the same summaries. Returns (max score error, mismatched pages,
     worst attention rel-L2)."""
@@ -70,7 +71,7 @@ def _check_against_oracle(b, summ, res, r, max_budget, heads=None, score_tol=1e-
         Lq = int(b.seq_lens[s])
         P, F = (Lq + 15) // 16, Lq // 16
         ora = Hh.oracle_head(b.q, b.k_pool, b.v_pool, b.block_table, b.seq_lens, b.budgets, summ,
-                             s, h, G, r, deferred=deferred)
+                             s, h, G, r, deferred=deferred, basis_bits=basis_bits, merge=merge)
         if res["scores"] is not None and F:
             d = np.abs(res["scores"][s, h, :F] - ora["scores"])
             worst_s = max(worst_s, float(d.max()))
@@ -218,13 +219,13 @@ def test_deterministic(L):
 # build
 # ---------------------------------------------------------------------------
 
-def _compare_codes(gpu_slots, keys, r):
+def _compare_codes(gpu_slots, keys, r, basis_bits=4):
     """GPU slots vs the oracle's for the same keys. Returns (fraction of code
     entries that differ, pages excluded as near-degenerate, columns excluded
     as sign-ambiguous)."""
-    ora_slots, summ, _ = O.build_slots(keys, r)
-    g = O.unpack_slots(gpu_slots, r)
-    o = O.unpack_slots(ora_slots, r)
+    ora_slots, summ, _ = O.build_slots(keys, r, basis_bits=basis_bits)
+    g = O.unpack_slots(gpu_slots, r, basis_bits=basis_bits)
+    o = O.unpack_slots(ora_slots, r, basis_bits=basis_bits)
     flag = Hh.gap_flags(summ["lam"], r)
     amb = Hh.sign_ambiguous(summ["V"]) & summ["active"]
     keep = ~flag
@@ -426,7 +427,7 @@ def test_full_size_128k_layer(L):
 # fused decode step (locks_decode_step)
 # ---------------------------------------------------------------------------
 
-def _step_state(b, r):
+def _step_state(b, r, basis_bits=4):
     """Split a batch into the state before its decode step: the token at
     position len - 1 of every sequence removed from the pools (overwritten with
     a constant) and returned as k_new / v_new, and oracle summaries of every
@@ -435,7 +436,8 @@ def _step_state(b, r):
     kn = torch.zeros(S, H, 128, dtype=torch.bfloat16)
     vn = torch.zeros(S, H, 128, dtype=torch.bfloat16)
     kp, vp = b.k_pool.clone(), b.v_pool.clone()
-    summ = Hh.oracle_summaries(b.k_pool, b.block_table, b.seq_lens, H, r, b.num_blocks)
+    summ = Hh.oracle_summaries(b.k_pool, b.block_table, b.seq_lens, H, r, b.num_blocks,
+                               basis_bits=basis_bits)
     completed = []
     for s, Lq in enumerate(b.seq_lens.tolist()):
         if Lq < 1:
@@ -472,7 +474,8 @@ def _run_step(L, dims, b, kp, vp, kn, vn, summ, max_budget, host_lens=True, with
     return res, kp_d.cpu(), vp_d.cpu(), summ_d.cpu().numpy()
 
 
-def _check_step(b, r, kmax, res, kp_after, vp_after, summ_after, summ_before, completed):
+def _check_step(b, r, kmax, res, kp_after, vp_after, summ_after, summ_before, completed,
+                basis_bits=4, merge="share"):
     # the new tokens are in the pools, nothing else moved
     assert torch.equal(kp_after, b.k_pool) and torch.equal(vp_after, b.v_pool)
     # completed pages got GPU-built summaries within the build tolerance; others untouched
@@ -480,16 +483,17 @@ def _check_step(b, r, kmax, res, kp_after, vp_after, summ_after, summ_before, co
     if completed:
         pairs = [(blk, h) for blk in completed for h in range(b.H)]
         keys = np.stack([Hh.np64(b.k_pool[blk, h]) for blk, h in pairs])
-        frac, nflag, namb = _compare_codes(np.stack([summ_after[blk, h] for blk, h in pairs]), keys, r)
+        frac, nflag, namb = _compare_codes(np.stack([summ_after[blk, h] for blk, h in pairs]), keys, r,
+                                           basis_bits=basis_bits)
         assert frac <= 1e-3, frac
-        ora, _, _ = O.build_slots(keys, r)
+        ora, _, _ = O.build_slots(keys, r, basis_bits=basis_bits)
         for i, (blk, h) in enumerate(pairs):
             summ_ora[blk, h] = ora[i]
     for blk in range(b.num_blocks):
         if blk not in completed:
             assert np.array_equal(summ_after[blk], summ_before[blk]), blk
     # score/select/attend against the oracle fed its own summaries
-    return _check_against_oracle(b, summ_ora, res, r, kmax)
+    return _check_against_oracle(b, summ_ora, res, r, kmax, basis_bits=basis_bits, merge=merge)
 
 
 @pytest.mark.parametrize("host_lens", [True, False])
