@@ -163,3 +163,55 @@ def format_report(title, rep):
                  + " | " + " | ".join(f"{c[m][i]:.4f}" for m in ("per_head", "exact", "quantised", "centroid"))
                  + " |")
     return "\n".join(L)
+
+
+# ---------------------------------------------------------------------------
+# the ablation of [N] §6: rank x basis precision, and the GQA merge rule
+# ---------------------------------------------------------------------------
+
+def exact_heads(batch):
+    """Per (sequence, KV head): (q (G, d), exact page LSE (P, G), needle page)
+    for a batch of whole-page sequences of equal length."""
+    lens = batch.seq_lens.cpu().tolist()
+    P = lens[0] // B
+    assert all(L == P * B for L in lens)
+    needles = {(s, h): j for (s, h, j, _) in batch.needles}
+    kp, qs, table, G = batch.k_pool.detach().cpu(), batch.q.detach().cpu(), batch.block_table.cpu(), batch.G
+    out = {}
+    for s in range(len(lens)):
+        for h in range(batch.H):
+            K = kp[table[s, :P].long(), h].double().numpy()
+            q = qs[s, h * G:(h + 1) * G].double().numpy()
+            out[(s, h)] = (q, O.exact_page_lse(q, K), needles.get((s, h)))
+    return out, P
+
+
+def precision_row(heads, P, scores, sels, ks):
+    """One (rank, width) row: median and p99 |s_hat - s| over pages and query
+    heads, carrier retention and mean group coverage at each budget, from the
+    library's scores ((s, h) -> (P, G)) and selections ((s, h) -> {k: pages})."""
+    err = np.concatenate([np.abs(scores[sh] - ex).ravel() for sh, (_, ex, _) in heads.items()])
+    ret = [np.mean([nd in sels[sh][k] for sh, (_, _, nd) in heads.items()]) for k in ks]
+    cov = [np.mean([coverage(ex, sels[sh][k]).mean() for sh, (_, ex, _) in heads.items()]) for k in ks]
+    return dict(eta_p50=float(np.median(err)), eta_p99=float(np.percentile(err, 99)),
+                retention=[float(x) for x in ret], coverage=[float(x) for x in cov])
+
+
+def merge_row(heads, P, sels, ks):
+    """Coverage statistics of one merge rule's selections ((s, h) -> {k:
+    pages}): the mean over query heads, the mean of the worst head of each
+    group, and the 5th percentile over all query heads; None = the per-head
+    oracle (each query head's own exact top-(k-2))."""
+    rows = []
+    for k in ks:
+        per = []
+        for sh, (q, ex, _) in heads.items():
+            if sels is None:
+                c = np.array([coverage(ex, O.select_pages(ex[:, g], P, k))[g] for g in range(ex.shape[1])])
+            else:
+                c = coverage(ex, sels[sh][k])
+            per.append(c)
+        allc = np.concatenate(per)
+        rows.append(dict(mean=float(allc.mean()), worst_head=float(np.mean([c.min() for c in per])),
+                         p5=float(np.percentile(allc, 5))))
+    return rows
