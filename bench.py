@@ -64,7 +64,7 @@ CSRC = os.path.join(ROOT, "kv_cache_page_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 _STEP_SRC = ("locks_decode.hip", ["locks_score_tile.h", "locks_attn_core.h", "locks_select.h",
                                   "locks_step.h", "locks_device.h"])
-_BUILD_SRC = ("locks_build.hip", ["locks_build_common.h", "locks_device.h"])
+_BUILD_SRC = ("locks_build_page.hip", ["locks_build_common.h", "locks_device.h"])
 # (counter summary, source, headers) of every kernel a roofline entry reports on
 KERNELS = {
     "step": (os.path.join(PROFILES, "decode_step_kernel_ctx128k_counters.txt"), *_STEP_SRC),
@@ -72,9 +72,9 @@ KERNELS = {
               "locks_score_mfma.hip", ["locks_score_tile.h", "locks_device.h"]),
     "step32k": (os.path.join(PROFILES, "decode_step_kernel_ctx32k_counters.txt"), *_STEP_SRC),
     "stepb32": (os.path.join(PROFILES, "decode_step_kernel_batch32_counters.txt"), *_STEP_SRC),
-    "build4": (os.path.join(PROFILES, "build_kernel_bulk_r4_counters.txt"), *_BUILD_SRC),
-    "build8": (os.path.join(PROFILES, "build_kernel_bulk_r8_counters.txt"), *_BUILD_SRC),
-    "build16": (os.path.join(PROFILES, "build_kernel_bulk_r16_counters.txt"), *_BUILD_SRC),
+    "build4": (os.path.join(PROFILES, "build_page_kernel_bulk_r4_counters.txt"), *_BUILD_SRC),
+    "build8": (os.path.join(PROFILES, "build_page_kernel_bulk_r8_counters.txt"), *_BUILD_SRC),
+    "build16": (os.path.join(PROFILES, "build_page_kernel_bulk_r16_counters.txt"), *_BUILD_SRC),
 }
 
 
@@ -562,7 +562,7 @@ def run_bulk_build(torch, L, dev, stack):
             "pages": pages, "ms": round(ms, 3), "pages_per_s": round(pps),
             "summary_bytes_per_page": slot_payload(r),
             "summary_frac_of_page_kv": round(slot_payload(r) / PAGE_KV_BYTES, 4),
-            "roofline": {"kernel": f"build_kernel<{r}> (locks_build)", "bound": "alu",
+            "roofline": {"kernel": f"build_page_kernel<{r}> (locks_build)", "bound": "alu",
                          "achieved": round(achieved, 3), "peak": FP64_VALU_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(achieved / FP64_VALU_PEAK_TFLOPS, 4),
                          "traffic": None if traffic is None else round(traffic),

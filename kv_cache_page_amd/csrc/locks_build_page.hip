@@ -1,16 +1,18 @@
-// LOCKS page-summary build, latency form: one 64-lane wave per page (gfx950).
+// LOCKS page-summary build: one 64-lane wave per page (gfx950).
 //
 // [N] = LOCKS reading notes (zhongzhuzhou.org 2026-07-29), §4.1 eq. 2-3 and
 // §4.3 Algorithm 1: centroid mu, deviations D = K - 1 mu^T, Gram D D^T,
 // descending eigendecomposition, basis V = D^T U_r Sigma_r^{-1}, coefficients
-// C = U_r Sigma_r, int4 basis / int8 coefficients / int8 centroid. Same
-// arithmetic rules and slot bytes as the 4-pages-per-wave build kernel (the
-// throughput form used for bulk builds); this form serves the few pages a
-// decode step completes, where the time to one summary is what counts.
+// C = U_r Sigma_r, int4 basis (int8 / int2 for the precision ablation) /
+// int8 coefficients / int8 centroid. Serves every build: the few pages a
+// decode step completes (time to one summary) and whole layers (pages per
+// second: the keys stay in registers, so the kernel needs 9.7 KB of LDS and
+// at most 128 registers, and 16 of its waves fit on a compute unit).
 //
 // Mapping (one wave, lane l):
-//   keys  : lane l loads dims 32 (l % 4) .. +31 of token l / 4 into LDS (fp32,
-//           exact for bf16);
+//   keys  : lane l loads dims 32 (l / 16) .. +31 of token l % 16 (its Gram
+//           operands) and, after the eigensolve, dims 2l, 2l+1 of every
+//           token (its share of the centroid and the basis);
 //   Gram  : K K^T on v_mfma_f64_16x16x4f64, 32 chunks of 4 dims: lane l feeds
 //           K[l % 16][32 (l / 16) + c] as both operands; the result lands as
 //           rows l / 16 + 4 i, column l % 16; centring G = C (K K^T) C;
@@ -22,8 +24,8 @@
 //           scaled to a common exponent) and c = 1/sqrt(1 + t^2) is brought
 //           to fp64 accuracy, so every rotation is orthogonal to fp64
 //           rounding while a visit leaves |a_pq| at about 1e-7 of its value;
-//           sweeps stop at the same off-diagonal criterion as the throughput
-//           form;
+//           sweeps stop when the off-diagonal mass falls below 1e-28 of the
+//           total (at most 12);
 //   basis : lane l owns dims 2l, 2l+1 of every basis column; coefficients:
 //           lane t < 16 owns token row t.
 #include "locks_build_common.h"
@@ -159,7 +161,7 @@ __device__ __forceinline__ double readlane_d(double v, int src) {
 }
 
 template <int R>
-__global__ __launch_bounds__(64) void build_page_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void build_page_kernel(
     const uint16_t* __restrict__ kpool, int64_t num_blocks, int H,
     const int32_t* __restrict__ ids, int n, const int32_t* __restrict__ table,
     const int32_t* __restrict__ lens, int MP, uint8_t* __restrict__ summ,
@@ -167,7 +169,6 @@ __global__ __launch_bounds__(64) void build_page_kernel(
     uint16_t* __restrict__ kdst, uint16_t* __restrict__ vdst, int bits) {
   const SlotLayout L = slot_layout(R, bits);
   const int vq_max = basis_qmax(bits);
-  __shared__ float kt[kPage][kHeadDim + 4];
   __shared__ double g_s[kPage][kPage + 1];
   __shared__ double u_s[kPage][kPage + 1];
   __shared__ double lam_s[kPage];
@@ -178,7 +179,9 @@ __global__ __launch_bounds__(64) void build_page_kernel(
 
   const int lane = threadIdx.x;
   const int64_t item = blockIdx.x;
-  // ---- which page (same selection rules as the throughput form)
+  // ---- which page: block ids[item / H] (all heads), or in filled-page mode
+  // the last page of sequence item / H when its length is a multiple of the
+  // page size (the new token, appended here too, is that page's last key)
   int64_t slot = -1;
   int blk = 0, head = (int)(item % H);
   const uint8_t* last_key = nullptr;
@@ -212,44 +215,39 @@ __global__ __launch_bounds__(64) void build_page_kernel(
   if (slot < 0) return;  // whole wave: nothing to build
   uint8_t* sl = summ + slot * (int64_t)L.stride;
 
-  // ---- keys -> LDS; energy = sum of squares of all keys
+  // ---- keys, straight into registers (no LDS copy): lane (t = lane % 16,
+  // kg = lane / 16) takes dims 32 kg .. 32 kg + 31 of row t, its operands of
+  // the Gram product (and, after the eigensolve, dims 2 lane, 2 lane + 1 of
+  // every row, its share of the centroid and the basis); energy = sum of
+  // squares of all keys
+  const int t = lane & 15, kg = lane >> 4;
+  auto row_of = [&](int tt) -> const uint8_t* {
+    return (last_key && tt == kPage - 1)
+               ? last_key
+               : reinterpret_cast<const uint8_t*>(kpool + (((int64_t)blk * H + head) * kPage + tt) * kHeadDim);
+  };
+  uint4 wg4[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) wg4[e] = *reinterpret_cast<const uint4*>(row_of(t) + 64 * kg + 16 * e);
   double energy = 0.0;
-  {
-    const int t = lane >> 2, qq = lane & 3;
-    const uint8_t* rowp = (last_key && t == kPage - 1)
-                              ? last_key
-                              : reinterpret_cast<const uint8_t*>(
-                                    kpool + (((int64_t)blk * H + head) * kPage + t) * kHeadDim);
-    uint4 w[4];
+  float kv[32];  // dims 32 kg + c, c = 0..31, of row t
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = *reinterpret_cast<const uint4*>(rowp + 64 * qq + 16 * e);
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t ww[4] = {wg4[e].x, wg4[e].y, wg4[e].z, wg4[e].w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t ww[4] = {w[e].x, w[e].y, w[e].z, w[e].w};
-      float f[8];
-#pragma unroll
-      for (int h2 = 0; h2 < 4; ++h2) { f[2 * h2] = bf16_lo(ww[h2]); f[2 * h2 + 1] = bf16_hi(ww[h2]); }
-#pragma unroll
-      for (int h2 = 0; h2 < 8; ++h2) energy = fma((double)f[h2], (double)f[h2], energy);
-      *reinterpret_cast<float4*>(&kt[t][32 * qq + 8 * e]) = make_float4(f[0], f[1], f[2], f[3]);
-      *reinterpret_cast<float4*>(&kt[t][32 * qq + 8 * e + 4]) = make_float4(f[4], f[5], f[6], f[7]);
+    for (int h2 = 0; h2 < 4; ++h2) {
+      kv[8 * e + 2 * h2] = bf16_lo(ww[h2]);
+      kv[8 * e + 2 * h2 + 1] = bf16_hi(ww[h2]);
     }
   }
+#pragma unroll
+  for (int c = 0; c < 32; ++c) energy = fma((double)kv[c], (double)kv[c], energy);
   energy = wave_sum_d(energy);
-  __syncthreads();
 
   // ---- Gram K K^T on the fp64 matrix core: rows l/16 + 4i, column l%16
   double4v mk = {0.0, 0.0, 0.0, 0.0};
-  {
-    const int t = lane & 15, kg = lane >> 4;
 #pragma unroll
-    for (int c8 = 0; c8 < 8; ++c8) {
-      const float4 v = *reinterpret_cast<const float4*>(&kt[t][32 * kg + 4 * c8]);
-      const double vv[4] = {(double)v.x, (double)v.y, (double)v.z, (double)v.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) mk = __builtin_amdgcn_mfma_f64_16x16x4f64(vv[e], vv[e], mk, 0, 0, 0);
-    }
-  }
+  for (int c = 0; c < 32; ++c) mk = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kv[c], (double)kv[c], mk, 0, 0, 0);
   // centring: G = M - rm 1^T - 1 rm^T + mean(rm), rm = row means (M symmetric)
   {
     const int col = lane & 15, rg = lane >> 4;
@@ -331,24 +329,26 @@ __global__ __launch_bounds__(64) void build_page_kernel(
   __syncthreads();
 
   const double thr = fmax(1e-6 * trace, 1e-12 * energy);
+  // the lane's dims of every row (read again: the page was just fetched)
+  uint32_t wc[kPage];
+#pragma unroll
+  for (int tt = 0; tt < kPage; ++tt) wc[tt] = *reinterpret_cast<const uint32_t*>(row_of(tt) + 4 * lane);
   // ---- centroid (dims 2l, 2l+1) and the page's deviations in those dims
   double mu[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) mu[e] = 0.0;
 #pragma unroll
-  for (int t = 0; t < kPage; ++t) {
-    const float2 v = *reinterpret_cast<const float2*>(&kt[t][2 * lane]);
-    mu[0] += (double)v.x;
-    mu[1] += (double)v.y;
+  for (int tt = 0; tt < kPage; ++tt) {
+    mu[0] += (double)bf16_lo(wc[tt]);
+    mu[1] += (double)bf16_hi(wc[tt]);
   }
   mu[0] *= (1.0 / kPage);
   mu[1] *= (1.0 / kPage);
   double dv[kPage][2];
 #pragma unroll
-  for (int t = 0; t < kPage; ++t) {
-    const float2 v = *reinterpret_cast<const float2*>(&kt[t][2 * lane]);
-    dv[t][0] = (double)v.x - mu[0];
-    dv[t][1] = (double)v.y - mu[1];
+  for (int tt = 0; tt < kPage; ++tt) {
+    dv[tt][0] = (double)bf16_lo(wc[tt]) - mu[0];
+    dv[tt][1] = (double)bf16_hi(wc[tt]) - mu[1];
   }
 
   // ---- basis columns: v_k = D^T u_k / sigma_k, canonical sign, int4 codes
