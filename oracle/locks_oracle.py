@@ -74,6 +74,10 @@ design notes of the repository):
                  Readings: group-max key_j = max_g m_g(j) on the same
                  normalised shares; group-mass key_j = sum_g exp(s_jg) /
                  sum_g Z_g, the pooled unnormalised mass. Selection as R8-R9.
+                 Per-head, the "per-head oracle" that [N] §4.2 and the §6
+                 ablation compare against (G selections per group): query
+                 head g takes its own sink/recent/top-(k-2) by its own share
+                 m_g(j) and attends only its own pages.
 """
 from __future__ import annotations
 
@@ -84,7 +88,7 @@ import numpy as np
 QMAX_INT4 = 7
 QMAX_INT8 = 127
 BASIS_BITS = (2, 4, 8)
-MERGE_RULES = ("share", "max", "mass")
+MERGE_RULES = ("share", "max", "mass", "per_head")
 
 
 def qmax_of(bits):
@@ -321,8 +325,9 @@ def share_keys(s, rule="share"):
     average m_bar_j = (1/G) sum_g m_g(j) ([N] §4.2 eq. 5), returned in the log
     domain: key_j = log m_bar_j. s: (F, G) over all summarised pages
     (reading R7). rule "max" and "mass" are the alternatives of reading R19:
-    log max_g m_g(j), and log (sum_g exp(s_jg) / sum_g Z_g).
-    Returns (key (F,), log Z (G,))."""
+    log max_g m_g(j), and log (sum_g exp(s_jg) / sum_g Z_g); "per_head" keeps
+    every query head's own log share log m_g(j).
+    Returns (key (F,) -- (F, G) for "per_head" --, log Z (G,))."""
     s = np.asarray(s, dtype=np.float64)
     G = s.shape[1]
     logZ = logsumexp(s, axis=0)
@@ -332,6 +337,8 @@ def share_keys(s, rule="share"):
         key = np.max(s - logZ[None, :], axis=1)
     elif rule == "mass":
         key = logsumexp(s, axis=1) - logsumexp(logZ, axis=0)
+    elif rule == "per_head":
+        key = s - logZ[None, :]
     else:
         raise ValueError(f"merge rule must be one of {MERGE_RULES}")
     return key, logZ
@@ -421,7 +428,9 @@ def decode_head(q, Kp, Vp, seq_len, k, slots=None, r=8, mode="quantised", B=16, 
     only the pages full before the current token are summarised and scored.
     basis_bits: the stored basis precision (reading R18); merge: the group
     rule that turns scores into selection keys (reading R19).
-    Returns dict(scores (F, G), key (F,), sel (list), out (G, d), lse (G,))."""
+    Returns dict(scores (F, G), key (F,), sel (list), out (G, d), lse (G,));
+    with merge "per_head", key is (F, G) and sel holds one list per query
+    head, whose output attends only that head's own pages."""
     q = np.asarray(q, dtype=np.float64)
     G, d = q.shape
     P = n_pages(seq_len, B)
@@ -442,14 +451,23 @@ def decode_head(q, Kp, Vp, seq_len, k, slots=None, r=8, mode="quantised", B=16, 
         key, _ = share_keys(scores, merge)
     else:
         scores = np.zeros((0, G))
-        key = np.zeros(0)
-    sel = select_pages(key, P, k)
-    toks_k, toks_v = [], []
-    for j in sel:
-        m = B if j < P - 1 else seq_len - B * (P - 1)
-        toks_k.append(Kp[j, :m]); toks_v.append(Vp[j, :m])
-    if sel:
-        out, lse = attend(q, np.concatenate(toks_k), np.concatenate(toks_v))
+        key = np.zeros((0, G)) if merge == "per_head" else np.zeros(0)
+
+    def attend_pages(qq, sel):
+        toks_k, toks_v = [], []
+        for j in sel:
+            m = B if j < P - 1 else seq_len - B * (P - 1)
+            toks_k.append(Kp[j, :m]); toks_v.append(Vp[j, :m])
+        if not sel:
+            return np.zeros((qq.shape[0], d)), np.full(qq.shape[0], -np.inf)
+        return attend(qq, np.concatenate(toks_k), np.concatenate(toks_v))
+
+    if merge == "per_head":
+        sel = [select_pages(key[:, g], P, k) for g in range(G)]
+        per = [attend_pages(q[g:g + 1], sel[g]) for g in range(G)]
+        out = np.concatenate([o for o, _ in per])
+        lse = np.concatenate([l for _, l in per])
     else:
-        out, lse = np.zeros((G, d)), np.full(G, -np.inf)
+        sel = select_pages(key, P, k)
+        out, lse = attend_pages(q, sel)
     return dict(scores=scores, key=key, sel=sel, out=out, lse=lse)

@@ -159,3 +159,69 @@ def test_precision_ablation_ordering():
     assert 3 * i4 < i2 < cen
     assert err(16, 4) > 0.8 * i4                  # int4: little gain from r = 8 to 16
     assert err(16) < 1e-12 < err(16, 8)           # unquantised exact at full rank, int8 not
+
+
+# ---------------------------------------------------------------------------
+# per-head selection (reading R19: the per-head oracle of [N] §4.2 and §6)
+# ---------------------------------------------------------------------------
+
+def _small_head(G, seed, P=9, tail=5):
+    rng = np.random.default_rng(seed)
+    K = rng.normal(size=(P, 16, 128))
+    V = rng.normal(size=(P, 16, 128))
+    q = rng.normal(size=(G, 128)) * 0.4
+    return q, K, V, 16 * (P - 1) + tail
+
+
+def test_per_head_with_one_query_head_is_the_share_rule():
+    q, K, V, ln = _small_head(1, 21)
+    a = O.decode_head(q, K, V, ln, 5, merge="share")
+    b = O.decode_head(q, K, V, ln, 5, merge="per_head")
+    assert b["sel"] == [a["sel"]]
+    np.testing.assert_array_equal(b["out"], a["out"])
+    np.testing.assert_array_equal(b["lse"], a["lse"])
+
+
+def test_per_head_rows_are_single_query_decodes():
+    """Query head g's selection and output are those of a decode of query g
+    alone: the per-head path pairs every query with its own page set."""
+    q, K, V, ln = _small_head(4, 22)
+    slots = O.build_slots(K[:8], 8)[0]
+    ph = O.decode_head(q, K, V, ln, 4, slots=slots, merge="per_head")
+    assert len(ph["sel"]) == 4 and len({tuple(s) for s in ph["sel"]}) > 1  # the heads disagree
+    for g in range(4):
+        one = O.decode_head(q[g:g + 1], K, V, ln, 4, slots=slots, merge="share")
+        assert ph["sel"][g] == one["sel"]
+        np.testing.assert_array_equal(ph["out"][g], one["out"][0])
+        np.testing.assert_array_equal(ph["lse"][g], one["lse"][0])
+
+
+def test_per_head_maximises_each_heads_own_coverage():
+    """Brute force over every k-set with the sink and the recent page: query
+    head g's own selection has the largest coverage sum_{j in S} m_g(j) that
+    any such set reaches (Corollary 3 with G = 1), so it covers at least as
+    much of head g as the group's shared selection does."""
+    import itertools
+    rng = np.random.default_rng(7)
+    P, k, G = 9, 4, 4
+    s = rng.normal(size=(P, G)) * 1.5
+    key, logZ = O.share_keys(s, "per_head")
+    m = np.exp(key)                                   # m_g(j)
+    shared = O.select_pages(O.share_keys(s, "share")[0], P, k)
+    best = [max(sum(m[j, g] for j in (0, P - 1) + c)
+                for c in itertools.combinations(range(1, P - 1), k - 2)) for g in range(G)]
+    for g in range(G):
+        own = O.select_pages(key[:, g], P, k)
+        cov = m[own, g].sum()
+        assert abs(cov - best[g]) < 1e-12
+        assert cov >= m[shared, g].sum() - 1e-12
+    np.testing.assert_allclose(m.sum(axis=0), 1.0, atol=1e-12)
+
+
+def test_per_head_with_identical_query_heads_matches_the_shared_set():
+    q, K, V, ln = _small_head(1, 23)
+    q4 = np.repeat(q, 4, axis=0)
+    ph = O.decode_head(q4, K, V, ln, 5, merge="per_head")
+    sh = O.decode_head(q4, K, V, ln, 5, merge="share")
+    assert all(sel == sh["sel"] for sel in ph["sel"])
+    np.testing.assert_allclose(ph["out"], sh["out"], atol=1e-12)
