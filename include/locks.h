@@ -79,10 +79,26 @@ typedef struct {
  *   MAX    key_j = log max_g m_g(j)                 (group-max)
  *   MASS   key_j = log (sum_g exp(s_jg) / sum_g Z_g) (group-mass: the pooled
  *          unnormalised masses)
- * The selection rule (sink, recent, top-(k-2) keys) is the same for all. */
+ * The selection rule (sink, recent, top-(k-2) keys) is the same for all.
+ *   PER_HEAD  no pooling: every query head selects its own sink, recent and
+ *          top-(k-2) pages by its own share m_g(j) and attends only those
+ *          (the per-head oracle that [N] §4.2 and §6 compare the shared rule
+ *          against, G selections per group). Every entry point except
+ *          locks_build, locks_build_filled and locks_append_kv then treats
+ *          each query head as a KV head of its own: num_kv_heads x group_size
+ *          heads of one query head each, head h reading the summaries and
+ *          K/V of KV head h / group_size. Arrays with a KV-head axis take
+ *          num_kv_heads x group_size rows: sel_pages
+ *          [S][H_kv G][max_budget], sel_count [S][H_kv G], page scores
+ *          [S][H_kv G][max_pages] (query head h_kv G + g in row h_kv G + g);
+ *          the workspace sizes follow (locks_workspace_bytes with the same
+ *          dims). q, out and lse_out keep their layouts. Each page summary is
+ *          read once per query head, so the score stage reads G times the
+ *          bytes of the shared rules. */
 #define LOCKS_MERGE_SHARE 0
 #define LOCKS_MERGE_MAX 1
 #define LOCKS_MERGE_MASS 2
+#define LOCKS_MERGE_PER_HEAD 3
 
 typedef enum {
     LOCKS_OK = 0,

@@ -24,7 +24,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_kernel(
     const uint16_t* __restrict__ vpool, const int32_t* __restrict__ table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel,
     const int32_t* __restrict__ cnt, float* __restrict__ part, int64_t num_blocks, int H,
-    int MP, int max_budget, int nsplit, int ppw) {
+    int MP, int max_budget, int nsplit, int ppw, int hdiv) {
   __shared__ float sh_acc[kAttnWaves][G][kHeadDim];
   __shared__ float sh_ml[kAttnWaves][G][2];
 
@@ -51,7 +51,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_kernel(
       if (j < 0 || j >= P) return;
       const int blk = table[(int64_t)s * MP + j];
       if (blk < 0 || blk >= num_blocks) return;
-      off = ((int64_t)blk * H + h) * (kPage * kHeadDim);
+      off = ((int64_t)blk * (H / hdiv) + h / hdiv) * (kPage * kHeadDim);  // the pools' head (score_head_div)
       nv = (j == P - 1) ? len - kPage * (P - 1) : kPage;
     };
     attn_wave_pages<kAttnChunk>(acc, qw, kpool, vpool, min(kAttnChunk, mine - c0), page_at,
@@ -119,7 +119,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
 hipError_t launch_attn(int G, const void* q, const void* kpool, const void* vpool,
                        const int32_t* table, const int32_t* lens, const int32_t* sel,
                        const int32_t* cnt, float* part, float* out, float* lse_out, int64_t nb,
-                       int S, int H, int MP, int max_budget, int nsplit, int ppw, hipStream_t st) {
+                       int S, int H, int MP, int max_budget, int nsplit, int ppw, int hdiv,
+                       hipStream_t st) {
+  if (hdiv < 1 || H % hdiv != 0) return hipErrorInvalidValue;
   dim3 grid(H, nsplit, S), mgrid(H, S);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint16_t* kk = static_cast<const uint16_t*>(kpool);
@@ -128,7 +130,7 @@ hipError_t launch_attn(int G, const void* q, const void* kpool, const void* vpoo
 #define LOCKS_G(GG)                                                                               \
   case GG:                                                                                        \
     hipLaunchKernelGGL(attn_kernel<GG>, grid, dim3(64 * kAttnWaves), 0, st, qq, kk, vv, table,   \
-                       lens, sel, cnt, part, nb, H, MP, max_budget, nsplit, ppw);                 \
+                       lens, sel, cnt, part, nb, H, MP, max_budget, nsplit, ppw, hdiv);           \
     hipLaunchKernelGGL(attn_merge_kernel<GG>, mgrid, dim3(256), 0, st, cnt, part, out, lse_out,  \
                        H, max_budget, nsplit, ppw);                                               \
     break;

@@ -22,7 +22,8 @@ hipError_t launch_select(int G, const float* scores, const int32_t* lens, const 
 hipError_t launch_attn(int G, const void* q, const void* kpool, const void* vpool,
                        const int32_t* table, const int32_t* lens, const int32_t* sel,
                        const int32_t* cnt, float* part, float* out, float* lse_out, int64_t nb,
-                       int S, int H, int MP, int max_budget, int nsplit, int ppw, hipStream_t st);
+                       int S, int H, int MP, int max_budget, int nsplit, int ppw, int hdiv,
+                       hipStream_t st);
 hipError_t launch_build(int r, const void* kpool, int64_t nb, int H, const int32_t* ids, int n,
                         const int32_t* table, const int32_t* lens, int MP, void* summ,
                         const void* knew, const void* vnew, void* vpool, int bits, hipStream_t st);
@@ -60,7 +61,8 @@ locks_status check_dims(const locks_dims* d) {
   if (d->group_size != 1 && d->group_size != 2 && d->group_size != 4) return LOCKS_ERR_UNSUPPORTED;
   if (d->basis_bits != 0 && d->basis_bits != 2 && d->basis_bits != 4 && d->basis_bits != 8)
     return LOCKS_ERR_INVALID_ARG;
-  if (d->merge_rule < LOCKS_MERGE_SHARE || d->merge_rule > LOCKS_MERGE_MASS) return LOCKS_ERR_INVALID_ARG;
+  if (d->merge_rule < LOCKS_MERGE_SHARE || d->merge_rule > LOCKS_MERGE_PER_HEAD) return LOCKS_ERR_INVALID_ARG;
+  if (d->merge_rule == LOCKS_MERGE_PER_HEAD && d->num_kv_heads > INT32_MAX / 4) return LOCKS_ERR_UNSUPPORTED;
   // the precision ablation's bases (int8, int2) are built and scored at ranks 4, 8 and 16
   if (d->basis_bits != 0 && d->basis_bits != 4 && d->rank != 4 && d->rank != 8 && d->rank != 16)
     return LOCKS_ERR_UNSUPPORTED;
@@ -69,6 +71,32 @@ locks_status check_dims(const locks_dims* d) {
 
 // Basis width of the slots (0 means the default int4).
 int bits_of(const locks_dims* d) { return d->basis_bits == 0 ? 4 : d->basis_bits; }
+
+// The dims the score, selection and attention launches run on. With
+// LOCKS_MERGE_PER_HEAD every query head is a group of its own: the view has
+// num_kv_heads x group_size heads of group 1 under the share rule (which, for
+// one query head, keys each page by that head's own share), and view head h
+// reads the summaries and K/V of KV head h / group_size (hdiv, the kernels'
+// head divisor). The build and append launches keep the KV heads.
+struct HeadView {
+  locks_dims v;
+  int hdiv;
+};
+HeadView view_of(const locks_dims* d) {
+  HeadView r{*d, 1};
+  if (d->merge_rule == LOCKS_MERGE_PER_HEAD) {
+    r.v.num_kv_heads = d->num_kv_heads * d->group_size;
+    r.v.group_size = 1;
+    r.v.merge_rule = LOCKS_MERGE_SHARE;
+    r.hdiv = d->group_size;
+  }
+  return r;
+}
+
+// Score-kernel flags that carry the view's head divisor.
+int head_div_flags(const HeadView& hv) {
+  return hv.hdiv > 1 ? hv.hdiv << locks::kScoreHeadDivShift : 0;
+}
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -155,7 +183,8 @@ size_t locks_summary_slot_stride(const locks_dims* d) {
 
 size_t locks_workspace_bytes(const locks_dims* d, int32_t S, int32_t MP, int32_t KB) {
   if (check_dims(d) != LOCKS_OK || check_batch(S, MP, KB, 1) != LOCKS_OK) return 0;
-  return carve(d, S, MP, KB).total;
+  const HeadView hv = view_of(d);
+  return carve(&hv.v, S, MP, KB).total;
 }
 
 locks_status locks_build(const locks_dims* d, const void* k_pool, int64_t nb,
@@ -213,18 +242,20 @@ locks_status locks_score_select(const locks_dims* d, const void* q, const void* 
   if (!q || !summaries || !block_table || !seq_lens || !budgets || !sel_pages || !sel_count)
     return LOCKS_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(summaries)) return LOCKS_ERR_INVALID_ARG;
-  const Workspace w = carve(d, S, MP, KB);
+  const HeadView hv = view_of(d);
+  const Workspace w = carve(&hv.v, S, MP, KB);
   if (!workspace || ws_bytes < w.total) return LOCKS_ERR_WORKSPACE;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   float* scores = scores_out ? scores_out : reinterpret_cast<float*>(ws + w.scores);
-  const int H = d->num_kv_heads, G = d->group_size;
+  const int H = hv.v.num_kv_heads, G = hv.v.group_size;
   hipError_t he = locks::launch_score(d->rank, bits_of(d), G, q, summaries, block_table, seq_lens,
-                                      scores, nb, S, H, MP, scores_out ? locks::kScoreFillNan : 0,
+                                      scores, nb, S, H, MP,
+                                      (scores_out ? locks::kScoreFillNan : 0) | head_div_flags(hv),
                                       nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                                       locks::CoopZero{}, st);
   if (he != hipSuccess) return LOCKS_ERR_HIP;
   he = locks::launch_select(G, scores, seq_lens, budgets, sel_pages, sel_count,
-                            reinterpret_cast<float*>(ws + w.keys), S, H, MP, KB, 0, d->merge_rule,
+                            reinterpret_cast<float*>(ws + w.keys), S, H, MP, KB, 0, hv.v.merge_rule,
                             st);
   return hip_status(he);
 }
@@ -239,10 +270,11 @@ locks_status locks_score_pages(const locks_dims* d, const void* q, const void* s
   if (S == 0) return LOCKS_OK;
   if (!q || !summaries || !block_table || !seq_lens || !scores) return LOCKS_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(summaries)) return LOCKS_ERR_INVALID_ARG;
-  return hip_status(locks::launch_score(d->rank, bits_of(d), d->group_size, q, summaries,
-                                        block_table, seq_lens, scores, nb, S, d->num_kv_heads, MP,
-                                        0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
-                                        locks::CoopZero{}, st));
+  const HeadView hv = view_of(d);
+  return hip_status(locks::launch_score(d->rank, bits_of(d), hv.v.group_size, q, summaries,
+                                        block_table, seq_lens, scores, nb, S, hv.v.num_kv_heads, MP,
+                                        head_div_flags(hv), nullptr, nullptr, nullptr, nullptr,
+                                        nullptr, nullptr, locks::CoopZero{}, st));
 }
 
 locks_status locks_select_pages(const locks_dims* d, const float* scores, const int32_t* seq_lens,
@@ -255,12 +287,13 @@ locks_status locks_select_pages(const locks_dims* d, const float* scores, const 
   if (e != LOCKS_OK) return e;
   if (S == 0) return LOCKS_OK;
   if (!scores || !seq_lens || !budgets || !sel_pages || !sel_count) return LOCKS_ERR_INVALID_ARG;
-  const Workspace w = carve(d, S, MP, KB);
+  const HeadView hv = view_of(d);
+  const Workspace w = carve(&hv.v, S, MP, KB);
   if (!workspace || ws_bytes < w.total) return LOCKS_ERR_WORKSPACE;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  return hip_status(locks::launch_select(d->group_size, scores, seq_lens, budgets, sel_pages,
+  return hip_status(locks::launch_select(hv.v.group_size, scores, seq_lens, budgets, sel_pages,
                                          sel_count, reinterpret_cast<float*>(ws + w.keys), S,
-                                         d->num_kv_heads, MP, KB, 0, d->merge_rule, st));
+                                         hv.v.num_kv_heads, MP, KB, 0, hv.v.merge_rule, st));
 }
 
 locks_status locks_sparse_attn(const locks_dims* d, const void* q, const void* k_pool,
@@ -277,13 +310,14 @@ locks_status locks_sparse_attn(const locks_dims* d, const void* q, const void* k
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !sel_pages || !sel_count || !out)
     return LOCKS_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool)) return LOCKS_ERR_INVALID_ARG;
-  const Workspace w = carve(d, S, MP, KB);
+  const HeadView hv = view_of(d);
+  const Workspace w = carve(&hv.v, S, MP, KB);
   if (!workspace || ws_bytes < w.total) return LOCKS_ERR_WORKSPACE;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   return hip_status(locks::launch_attn(
-      d->group_size, q, k_pool, v_pool, block_table, seq_lens, sel_pages, sel_count,
-      reinterpret_cast<float*>(ws + w.parts), out, lse_out, nb, S, d->num_kv_heads, MP, KB,
-      w.nsplit, attn_pages_per_wave(KB), st));
+      hv.v.group_size, q, k_pool, v_pool, block_table, seq_lens, sel_pages, sel_count,
+      reinterpret_cast<float*>(ws + w.parts), out, lse_out, nb, S, hv.v.num_kv_heads, MP, KB,
+      w.nsplit, attn_pages_per_wave(KB), hv.hdiv, st));
 }
 
 }  // extern "C"
@@ -323,8 +357,12 @@ locks_status decode_step_run(const locks_dims* d, const void* q, const void* k_n
                              int32_t MP, int32_t KB, float* out, float* lse_out,
                              int32_t* sel_pages, int32_t* sel_count, uint32_t flags,
                              const Workspace& w, uint8_t* ws, bool reset_step, hipStream_t st) {
-  const int H = d->num_kv_heads, G = d->group_size, bits = bits_of(d);
+  // (H, G: the view's heads for the score, selection and attention launches;
+  // the build and append launches run on the Hk KV heads)
+  const HeadView hv = view_of(d);
+  const int H = hv.v.num_kv_heads, G = hv.v.group_size, Hk = d->num_kv_heads, bits = bits_of(d);
   const bool deferred = (flags & LOCKS_STEP_DEFER_BUILD) != 0;
+  const int sflags = (deferred ? locks::kScoreDeferred : 0) | head_div_flags(hv);
 
   // Every decision is taken before the first launch, so that a call that
   // returns an error has enqueued nothing.
@@ -358,7 +396,7 @@ locks_status decode_step_run(const locks_dims* d, const void* q, const void* k_n
   }
   // 1. append (+ summaries of the pages the new token completes)
   if (completes) {
-    hipError_t he = locks::launch_build(d->rank, k_pool, nb, H, nullptr, S, block_table, seq_lens,
+    hipError_t he = locks::launch_build(d->rank, k_pool, nb, Hk, nullptr, S, block_table, seq_lens,
                                         MP, summaries, k_new, v_new, v_pool, bits, st);
     if (he != hipSuccess) return LOCKS_ERR_HIP;
   }
@@ -403,26 +441,27 @@ locks_status decode_step_run(const locks_dims* d, const void* q, const void* k_n
     a.coop = coop;
     a.r = rfused;
     a.lag = deferred ? 1 : 0;
-    a.rule = d->merge_rule;
+    a.rule = hv.v.merge_rule;
+    a.hdiv = hv.hdiv;
     if (a.r == 0) {
       hipError_t he = locks::launch_score(d->rank, bits, G, q, summaries, block_table, seq_lens,
-                                          scores, nb, S, H, MP, deferred ? locks::kScoreDeferred : 0,
-                                          zpart, kn, vn, k_pool, v_pool, pmax, coop, st);
+                                          scores, nb, S, H, MP, sflags, zpart, kn, vn, k_pool,
+                                          v_pool, pmax, coop, st);
       if (he != hipSuccess) return LOCKS_ERR_HIP;
     }
     return hip_status(locks::launch_decode(G, a, st));
   }
   hipError_t he = locks::launch_score(d->rank, bits, G, q, summaries, block_table, seq_lens, scores,
-                                      nb, S, H, MP, deferred ? locks::kScoreDeferred : 0, zpart, kn,
-                                      vn, k_pool, v_pool, nullptr, locks::CoopZero{}, st);
+                                      nb, S, H, MP, sflags, zpart, kn, vn, k_pool, v_pool, nullptr,
+                                      locks::CoopZero{}, st);
   if (he != hipSuccess) return LOCKS_ERR_HIP;
   he = locks::launch_select(G, scores, seq_lens, budgets, sel, cnt,
                             reinterpret_cast<float*>(ws + w.keys), S, H, MP, KB, deferred ? 1 : 0,
-                            d->merge_rule, st);
+                            hv.v.merge_rule, st);
   if (he != hipSuccess) return LOCKS_ERR_HIP;
   return hip_status(locks::launch_attn(G, q, k_pool, v_pool, block_table, seq_lens, sel, cnt,
                                        reinterpret_cast<float*>(ws + w.parts), out, lse_out, nb, S,
-                                       H, MP, KB, w.nsplit, attn_pages_per_wave(KB), st));
+                                       H, MP, KB, w.nsplit, attn_pages_per_wave(KB), hv.hdiv, st));
 }
 
 // Built-in scratch of locks_decode_step_noalloc, one per device (each GPU the
@@ -462,7 +501,8 @@ locks_status locks_decode_step_noalloc(const locks_dims* d, const void* q, const
                                      seq_lens, budgets, S, MP, KB, out, sel_pages, sel_count);
   if (e != LOCKS_OK || S == 0) return e;
   if (flags & ~(uint32_t)LOCKS_STEP_DEFER_BUILD) return LOCKS_ERR_INVALID_ARG;
-  const Workspace w = carve(d, S, MP, KB);
+  const HeadView hv = view_of(d);
+  const Workspace w = carve(&hv.v, S, MP, KB);
   if (w.total > kScratchBytes) return LOCKS_ERR_WORKSPACE;
   void* ws = scratch_ptr();
   if (!ws) return LOCKS_ERR_HIP;
@@ -483,7 +523,8 @@ locks_status locks_decode_step(const locks_dims* d, const void* q, const void* k
                                      seq_lens, budgets, S, MP, KB, out, sel_pages, sel_count);
   if (e != LOCKS_OK || S == 0) return e;
   if (flags & ~(uint32_t)LOCKS_STEP_DEFER_BUILD) return LOCKS_ERR_INVALID_ARG;
-  const Workspace w = carve(d, S, MP, KB);
+  const HeadView hv = view_of(d);
+  const Workspace w = carve(&hv.v, S, MP, KB);
   if (!workspace || ws_bytes < w.total) return LOCKS_ERR_WORKSPACE;
   return decode_step_run(d, q, k_new, v_new, k_pool, v_pool, summaries, nb, block_table, seq_lens,
                          seq_lens_host, budgets, S, MP, KB, out, lse_out, sel_pages, sel_count,

@@ -231,7 +231,7 @@ __device__ __forceinline__ void step_score_part(
     float* __restrict__ escore, float* __restrict__ pmax, float2* __restrict__ zpart, int ntiles,
     int64_t num_blocks, int H, int MP, int npairs, const uint16_t* __restrict__ knew,
     const uint16_t* __restrict__ vnew, uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool,
-    CoopZero coop, uint32_t* step, int lag) {
+    CoopZero coop, uint32_t* step, int lag, int hdiv) {
   const int bid = blockIdx.x, s = blockIdx.z;
   const int h = bid % H, pair = bid / H;
   const int64_t sh_idx = (int64_t)s * H + h;
@@ -242,7 +242,7 @@ __device__ __forceinline__ void step_score_part(
   float zm = -__builtin_inff(), zs = 0.f;
   if (tile < ntiles)
     score_tile<R, G>(q, summ, table, seq_lens, escore, num_blocks, H, MP, kScorePagesPerWg,
-                     lag ? kScoreDeferred : 0, knew, vnew, kpool, vpool, pmax, s, h, tile, wave,
+                     (lag ? kScoreDeferred : 0) | (hdiv << kScoreHeadDivShift), knew, vnew, kpool, vpool, pmax, s, h, tile, wave,
                      tid, zm, zs);
   __shared__ float zred[2][4][4][2];
   if (lane < G) {
@@ -276,7 +276,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     int slice, int per_wg, uint32_t* __restrict__ mbox, float* __restrict__ out,
     float* __restrict__ lse_out, int32_t* __restrict__ sel_pages, int32_t* __restrict__ sel_count,
     const uint8_t* __restrict__ summ, int npairs, const uint16_t* __restrict__ knew,
-    const uint16_t* __restrict__ vnew, CoopZero coop, int lag, int rule) {
+    const uint16_t* __restrict__ vnew, CoopZero coop, int lag, int rule, int hdiv) {
   constexpr int nsplit = kS;
   constexpr int kTop = kDecThreads / kS;  // top-candidate slots per slice
   static_assert(kTop * kS == kDecThreads, "one top-candidate slot per thread");
@@ -286,7 +286,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
       uint32_t* step = mbox + ((int64_t)blockIdx.z * H + (int)blockIdx.x % H) * coop_mailbox_words(nsplit, G, MP) +
                        coop_zero_words(nsplit, G);
       step_score_part<R, G>(q, summ, table, seq_lens, escore, pmax, zpart, ntiles, num_blocks, H, MP,
-                            npairs, knew, vnew, kpool, vpool, coop, step, lag);
+                            npairs, knew, vnew, kpool, vpool, coop, step, lag, hdiv);
       return;
     }
   }
@@ -321,6 +321,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
   if (h >= H) return;  // padding of the last head row
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t sh_idx = (int64_t)s * H + h;
+  const int hd = h / hdiv, Hd = H / hdiv;  // the pools' head of this head (score_head_div)
   uint32_t* mb = mbox + sh_idx * coop_mailbox_words(nsplit, G, MP);
   uint32_t* ctr = mb;                                            // [kCoopCounters][kCoopCtrWords]
   uint32_t* mb_hist = ctr + kCoopCounters * kCoopCtrWords;       // [nsplit][512], count + 1
@@ -673,7 +674,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
   if (wave < nc) {
     const int pj = cs_page[wave], blk = cs_blk[wave];
     const bool valid = blk >= 0 && blk < num_blocks;  // candidates are full pages
-    attn_load_page(bspec, kpool, vpool, valid ? ((int64_t)blk * H + h) * (kPage * kHeadDim) : 0, lane);
+    attn_load_page(bspec, kpool, vpool, valid ? ((int64_t)blk * Hd + hd) * (kPage * kHeadDim) : 0, lane);
   }
   if (fast_b && wave == kDecWaves - 1) {
     // lane e < ct holds candidate e; rank by key (lower page first on ties)
@@ -725,7 +726,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     }
   }
   // ---- attention over part A (or the positions)
-  attn_list(acc, qw, kpool, vpool, att_page, att_blk, wave, kDecWaves, natt, P, len, H, h,
+  attn_list(acc, qw, kpool, vpool, att_page, att_blk, wave, kDecWaves, natt, P, len, Hd, hd,
                num_blocks, lane);
   if (!sel_all && ok && part_bin && !fast_b) {
     // membership `mem` of candidate t (page `page`), called by every thread
@@ -827,7 +828,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
   const int bbefore = sh_int[5];
   if (fast_b) ok = sh_u[1] != 0u;
   if (ok && wave < nc && cs_mem[wave]) attn_page(acc, bspec, qw, kPage, lane);
-  attn_list(acc, qw, kpool, vpool, b_page, b_blk, wave, kDecWaves, sh_int[4], P, len, H, h,
+  attn_list(acc, qw, kpool, vpool, b_page, b_blk, wave, kDecWaves, sh_int[4], P, len, Hd, hd,
                num_blocks, lane);
   attn_wave_to_lds<G>(acc, sh_acc[wave], sh_ml[wave], lane);
   __syncthreads();
@@ -996,7 +997,7 @@ static void launch_step_rgs(const StepLaunch& a, hipStream_t st) {
                      static_cast<uint16_t*>(a.vpool), a.table, a.nb, a.H, a.MP, a.KB, a.slice, a.per_wg,
                      a.mbox, a.out, a.lse_out, a.sel, a.cnt, static_cast<const uint8_t*>(a.summ), npairs,
                      static_cast<const uint16_t*>(a.knew), static_cast<const uint16_t*>(a.vnew), a.coop,
-                     a.lag, a.rule);
+                     a.lag, a.rule, a.hdiv > 0 ? a.hdiv : 1);
 }
 
 template <int R, int G>

@@ -15,6 +15,15 @@ constexpr int kScorePagesPerWg = 128;
 // deferred build: F = (len - 1) / page_size).
 constexpr int kScoreFillNan = 1;
 constexpr int kScoreDeferred = 2;
+// Bits 8..15 of the score flags: a head divisor (0 reads as 1). Head h of H
+// then reads the slots of, and appends the new K/V row to, head h / div of
+// H / div in the pools, while its query, outputs and workspace rows stay its
+// own: with div = G every query head of a group is a head of its own.
+constexpr int kScoreHeadDivShift = 8;
+__host__ __device__ inline int score_head_div(int flags) {
+  const int v = (flags >> kScoreHeadDivShift) & 0xFF;
+  return v ? v : 1;
+}
 
 // Full pages that are summarised (scored) at length len: floor(len / B), or,
 // when the build of a page completed by the current token is deferred,

@@ -108,13 +108,15 @@ __global__ __launch_bounds__(256) void score_kernel(
   const int len = clampi(seq_lens[s], 0, MP * kPage);
   const int F = scored_pages(len, (flags & kScoreDeferred) ? 1 : 0);
   const int j_lo = tile * pages_per_wg;
-  if (knew && tile == 0 && threadIdx.x < 2 * (kHeadDim / 8) && len >= 1) {
+  // the pools' head of this head (score_head_div)
+  const int hdiv = score_head_div(flags), hd = h / hdiv, Hd = H / hdiv;
+  if (knew && tile == 0 && h % hdiv == 0 && threadIdx.x < 2 * (kHeadDim / 8) && len >= 1) {
     // decode-step append of the new token (position len - 1) for this head
     const int blk = table[(int64_t)s * MP + (len - 1) / kPage];
     if (blk >= 0 && blk < num_blocks) {
       const int c = threadIdx.x % (kHeadDim / 8);
-      const int64_t src = ((int64_t)s * H + h) * kHeadDim + 8 * c;
-      const int64_t dst = (((int64_t)blk * H + h) * kPage + (len - 1) % kPage) * kHeadDim + 8 * c;
+      const int64_t src = ((int64_t)s * Hd + hd) * kHeadDim + 8 * c;
+      const int64_t dst = (((int64_t)blk * Hd + hd) * kPage + (len - 1) % kPage) * kHeadDim + 8 * c;
       if (threadIdx.x < kHeadDim / 8)
         *reinterpret_cast<uint4*>(kpool + dst) = *reinterpret_cast<const uint4*>(knew + src);
       else
@@ -196,14 +198,14 @@ __global__ __launch_bounds__(256) void score_kernel(
   }
   float zm = -__builtin_inff(), zs = 0.f;  // running LSE of query head l4 over the pages
   SlotRegs<R, BITS> cur, nxt;
-  load_slot<R, BITS>(cur, summ, H, h, blks[0], l4);
+  load_slot<R, BITS>(cur, summ, Hd, hd, blks[0], l4);
 #pragma unroll
   for (int it = 0; it < kMaxIter; ++it) {
     const int j = jw + 64 * it;
     if (j - (lane >> 2) >= j_end) break;  // wave-uniform
     const bool in = j < j_end;
     const bool ok = blks[it] >= 0;
-    if (it + 1 < kMaxIter) load_slot<R, BITS>(nxt, summ, H, h, blks[it + 1 < kMaxIter ? it + 1 : it], l4);
+    if (it + 1 < kMaxIter) load_slot<R, BITS>(nxt, summ, Hd, hd, blks[it + 1 < kMaxIter ? it + 1 : it], l4);
     const uint4 mq0 = cur.mq0, mq1 = cur.mq1;
     const uint32_t* cq = cur.cq;
     const uint16_t* sv = cur.sv;

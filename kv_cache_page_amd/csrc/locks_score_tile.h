@@ -197,13 +197,15 @@ __device__ __forceinline__ void score_tile(
   asm volatile("" ::: "memory");
   const int len = clampi(seq_lens[s], 0, MP * kPage);
   const int F = scored_pages(len, (flags & kScoreDeferred) ? 1 : 0);
-  if (knew && tile == 0 && tid < 2 * (kHeadDim / 8) && len >= 1) {
+  // the pools' head of this head (score_head_div)
+  const int hdiv = score_head_div(flags), hd = h / hdiv, Hd = H / hdiv;
+  if (knew && tile == 0 && h % hdiv == 0 && tid < 2 * (kHeadDim / 8) && len >= 1) {
     // decode-step append of the new token (position len - 1) for this head
     const int blk = table[(int64_t)s * MP + (len - 1) / kPage];
     if (blk >= 0 && blk < num_blocks) {
       const int c = tid % (kHeadDim / 8);
-      const int64_t src = ((int64_t)s * H + h) * kHeadDim + 8 * c;
-      const int64_t dst = (((int64_t)blk * H + h) * kPage + (len - 1) % kPage) * kHeadDim + 8 * c;
+      const int64_t src = ((int64_t)s * Hd + hd) * kHeadDim + 8 * c;
+      const int64_t dst = (((int64_t)blk * Hd + hd) * kPage + (len - 1) % kPage) * kHeadDim + 8 * c;
       if (tid < kHeadDim / 8)
         st_agent(reinterpret_cast<uint4*>(kpool + dst), *reinterpret_cast<const uint4*>(knew + src));
       else
@@ -234,8 +236,8 @@ __device__ __forceinline__ void score_tile(
   }
 
   // slot of block b for this head: summ_h + b * (H * stride), one 32 x 32 -> 64 multiply-add
-  const uint8_t* summ_h = summ + (size_t)h * L.stride;
-  const uint32_t hs = (uint32_t)H * (uint32_t)L.stride;
+  const uint8_t* summ_h = summ + (size_t)hd * L.stride;
+  const uint32_t hs = (uint32_t)Hd * (uint32_t)L.stride;
   auto slot_ptr = [&](int b) -> const uint8_t* {
     return summ_h + (uint64_t)(uint32_t)(b < 0 ? 0 : b) * hs;
   };

@@ -21,6 +21,7 @@ struct StepLaunch {
   int S, H, MP, KB, nsplit, slice, per_wg;
   int lag;              // 1: only the pages full before the current token are scored
   int rule;             // GQA merge rule of the selection keys (kMergeShare, ...)
+  int hdiv;             // head divisor of the K/V and summary pools (score_head_div; 0 or 1: none)
   uint32_t* mbox;
   float* out;
   float* lse_out;

@@ -36,8 +36,9 @@ ENTRY_POINTS = (
 NOALLOC_SCRATCH_BYTES = 16 << 20   # LOCKS_NOALLOC_SCRATCH_BYTES
 
 
-MERGE_SHARE, MERGE_MAX, MERGE_MASS = 0, 1, 2   # LOCKS_MERGE_*
-MERGE_RULES = {"share": MERGE_SHARE, "max": MERGE_MAX, "mass": MERGE_MASS}
+MERGE_SHARE, MERGE_MAX, MERGE_MASS, MERGE_PER_HEAD = 0, 1, 2, 3   # LOCKS_MERGE_*
+MERGE_RULES = {"share": MERGE_SHARE, "max": MERGE_MAX, "mass": MERGE_MASS,
+               "per_head": MERGE_PER_HEAD}
 
 
 class Dims(ctypes.Structure):
@@ -336,6 +337,14 @@ def decode_step_noalloc(dims, q, k_new, v_new, k_pool, v_pool, summaries, block_
     _check(st, "locks_decode_step_noalloc")
 
 
+def selection_heads(dims):
+    """Rows of the per-head arrays (sel_pages, sel_count, page scores): the KV
+    heads, or every query head under LOCKS_MERGE_PER_HEAD."""
+    if dims.merge_rule == MERGE_PER_HEAD:
+        return dims.num_kv_heads * dims.group_size
+    return dims.num_kv_heads
+
+
 class Decoder:
     """Holds the per-layer output buffers and workspace of one decode step and
     calls score_select then sparse_attn on the current stream."""
@@ -343,8 +352,9 @@ class Decoder:
     def __init__(self, dims, num_seqs, max_pages, max_budget, device):
         self.dims, self.max_budget = dims, max_budget
         H, G = dims.num_kv_heads, dims.group_size
-        self.sel = torch.empty(num_seqs, H, max_budget, dtype=torch.int32, device=device)
-        self.cnt = torch.empty(num_seqs, H, dtype=torch.int32, device=device)
+        self.sel = torch.empty(num_seqs, selection_heads(dims), max_budget, dtype=torch.int32,
+                               device=device)
+        self.cnt = torch.empty(num_seqs, selection_heads(dims), dtype=torch.int32, device=device)
         self.out = torch.empty(num_seqs, H * G, dims.head_dim, dtype=torch.float32, device=device)
         self.lse = torch.empty(num_seqs, H * G, dtype=torch.float32, device=device)
         self.ws = alloc_workspace(dims, num_seqs, max_pages, max_budget, device)

@@ -199,15 +199,18 @@ def precision_row(heads, P, scores, sels, ks):
 
 def merge_row(heads, P, sels, ks):
     """Coverage statistics of one merge rule's selections ((s, h) -> {k:
-    pages}): the mean over query heads, the mean of the worst head of each
-    group, and the 5th percentile over all query heads; None = the per-head
-    oracle (each query head's own exact top-(k-2))."""
+    pages}, or {k: [pages of query head g]} for per-head selections): the
+    mean over query heads, the mean of the worst head of each group, and the
+    5th percentile over all query heads; None = the per-head oracle (each
+    query head's own exact top-(k-2))."""
     rows = []
     for k in ks:
         per = []
         for sh, (q, ex, _) in heads.items():
             if sels is None:
                 c = np.array([coverage(ex, O.select_pages(ex[:, g], P, k))[g] for g in range(ex.shape[1])])
+            elif sels[sh][k] and isinstance(sels[sh][k][0], list):
+                c = np.array([coverage(ex, sel)[g] for g, sel in enumerate(sels[sh][k])])
             else:
                 c = coverage(ex, sels[sh][k])
             per.append(c)

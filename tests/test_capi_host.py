@@ -161,7 +161,22 @@ def test_basis_width_and_merge_rule_dims():
     assert L.slot_bytes(L.Dims(8, 4, 8, basis_bits=3)) == 0
     assert L.slot_bytes(L.Dims(8, 4, 6, basis_bits=8)) == 0        # ablation ranks 4, 8, 16
     assert L.slot_bytes(L.Dims(8, 4, 6, basis_bits=4)) > 0
-    for rule in ("share", "max", "mass"):
+    for rule in ("share", "max", "mass", "per_head"):
         assert L.slot_bytes(L.Dims(8, 4, 8, merge_rule=rule)) == 818
-    assert L.slot_bytes(L.Dims(8, 4, 8, merge_rule=3)) == 0
+    assert L.slot_bytes(L.Dims(8, 4, 8, merge_rule=4)) == 0
     assert L.slot_bytes(L.Dims(8, 4, 8, merge_rule=-1)) == 0
+
+
+def test_per_head_rule_sizes_its_arrays_by_query_head():
+    """LOCKS_MERGE_PER_HEAD: the workspace is that of num_kv_heads x
+    group_size heads of one query head each (the selection rows and the
+    mailboxes grow by G, the page scores stay the same size)."""
+    H, G, MP, KB = 8, 4, 2048, 64
+    shared = L.Dims(H, G, 8)
+    per = L.Dims(H, G, 8, merge_rule="per_head")
+    view = L.Dims(H * G, 1, 8)
+    assert L.workspace_bytes(per, 2, MP, KB) == L.workspace_bytes(view, 2, MP, KB)
+    assert L.workspace_bytes(per, 2, MP, KB) > L.workspace_bytes(shared, 2, MP, KB)
+    assert L.selection_heads(per) == H * G and L.selection_heads(shared) == H
+    # more KV heads than a view of int32 heads can hold
+    assert L.workspace_bytes(L.Dims(2 ** 30, 4, 8, merge_rule="per_head"), 1, MP, KB) == 0
