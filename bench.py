@@ -35,7 +35,10 @@ Further workloads, each with its own roofline entry under "workloads":
                   ALU roofline);
   offload_ctx128k the 128K step with the K/V pools in pinned host memory
                   (summaries in HBM): the selected pages cross the host
-                  link (roofline against PCIe 5.0 x16, one direction).
+                  link (roofline against PCIe 5.0 x16, one direction);
+  rank_sweep_ctx128k  one 128K layer's decode step at r = 4, 8 and 16
+                  (490 / 818 / 1474 summary bytes per page), over 8
+                  replicas of the summaries taken in turn.
 
 The final timed step's layer-0 outputs are checked against the fp64 oracle
 (and every output for NaN); the run exits non-zero on a mismatch.
@@ -154,7 +157,7 @@ def traffic_from_counters(which):
 
 def roofline(kernel, which, bytes_per_launch, us_per_launch):
     achieved = bytes_per_launch / (us_per_launch * 1e-6) / 1e9
-    traffic = traffic_from_counters(which)
+    traffic = traffic_from_counters(which) if which else None
     return {"kernel": kernel, "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None if traffic is None else round(traffic),
@@ -383,6 +386,63 @@ def run_ctx32k(torch, L, synth, dev, replicas=32, reps=20):
             "us_per_step": round(us, 3), "bytes_per_step": bpl,
             "roofline": roofline("decode_step_kernel<8,4,8> (locks_decode_step)", "step32k", bpl, us),
             "any_nan": nan}
+
+
+# ---------------------------------------------------------------------------
+# rank sweep of the decode step at 128K context
+# ---------------------------------------------------------------------------
+
+def run_rank_sweep(torch, L, synth, dev, ranks=(4, 8, 16), replicas=8, reps=20):
+    """One 128K-token layer (8191 full pages + 1 token, k = 128) through the
+    fused decode step at each rank: the summaries of every rank built from the
+    same keys, `replicas` copies of them stepped in turn (8 x 30..100 MB, so
+    every launch streams its summaries from HBM; the K/V pool is shared)."""
+    ln = 131072 - B + 1
+    k = BUDGET
+    log(f"[bench] rank sweep: 128K-token layer, r in {ranks}, {replicas} summary replicas each")
+    b = synth.make_decode_batch([ln], H, G, [k], seed=1100, device=dev)
+    blk, t = int(b.block_table[0, (ln - 1) // B]), (ln - 1) % B
+    kn = b.k_pool[blk, :, t].clone()[None]
+    vn = b.v_pool[blk, :, t].clone()[None]
+    full = b.block_table[0, :ln // B].contiguous()
+    out = torch.empty(1, H * G, D, device=dev)
+    host = torch.tensor([ln], dtype=torch.int32)
+    res = {}
+    for r in ranks:
+        dims = L.Dims(H, G, r)
+        summs = []
+        for _ in range(replicas):
+            summ = L.alloc_summaries(dims, b.num_blocks, dev)
+            L.build(dims, b.k_pool, full, summ)
+            summs.append(summ)
+        ws = L.alloc_workspace(dims, 1, b.max_pages, k, dev)
+
+        def rotate(_):
+            for summ in summs:
+                L.decode_step(dims, b.q, kn, vn, b.k_pool, b.v_pool, summ, b.block_table,
+                              b.seq_lens, b.budgets, k, out, ws, seq_lens_host=host)
+
+        rotate(0)
+        torch.cuda.synchronize()
+        g = capture(torch, rotate, [0])
+        g[0].replay()
+        ms = timed(torch, {i: g[0] for i in range(reps)}, range(reps))
+        us = ms * 1e3 / (reps * replicas)
+        F = ln // B
+        kv = (k - 1) * PAGE_KV_BYTES + (ln - B * (F)) * (PAGE_KV_BYTES // B)
+        bpl = H * (F * slot_payload(r) + kv)
+        res[f"r{r}"] = {"us_per_step": round(us, 3), "bytes_per_step": bpl,
+                        "summary_bytes_per_page": slot_payload(r),
+                        "roofline": roofline(f"decode_step_kernel<{r},4,16> (locks_decode_step)",
+                                             "step" if r == R else None, bpl, us),
+                        "any_nan": bool(torch.isnan(out).any())}
+        log(f"[bench] rank sweep r={r}: decode step {us:.2f} us per launch ({bpl / us / 1e3:.0f} GB/s)")
+        del summs, ws, g
+        torch.cuda.empty_cache()
+    del b
+    res["workload"] = ("1 seq, 131056 cached tokens + the new one (8191 full pages), 1 layer, 8 KV heads "
+                       f"x 4 q heads, k=128; summaries at each rank, {replicas} replicas stepped in turn")
+    return res
 
 
 # ---------------------------------------------------------------------------
@@ -682,7 +742,7 @@ def main():
                     help="oracle CPU-baseline budget (0 skips it; the final-step check still runs)")
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--only", default="all",
-                    help="comma list of ctx128k, ctx32k, batch32, build, offload (profiling runs)")
+                    help="comma list of ctx128k, ctx32k, batch32, build, offload, ranks (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed region, run one elementwise copy that reads 1 GiB "
                          "and writes 1 GiB (the reference for HBM byte counters)")
@@ -698,7 +758,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     only = (set(args.only.split(",")) if args.only != "all"
-            else {"ctx128k", "ctx32k", "batch32", "build", "offload"})
+            else {"ctx128k", "ctx32k", "batch32", "build", "offload", "ranks"})
 
     import torch
     import synth
@@ -717,6 +777,9 @@ def main():
         torch.cuda.empty_cache()
     if "batch32" in only:
         workloads["batch32_ragged"] = run_batch32(torch, L, synth, dev)
+        torch.cuda.empty_cache()
+    if "ranks" in only:
+        workloads["rank_sweep_ctx128k"] = run_rank_sweep(torch, L, synth, dev)
         torch.cuda.empty_cache()
     if "offload" in only:
         workloads["offload_ctx128k"] = run_offload(torch, L, synth, dev)

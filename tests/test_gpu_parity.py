@@ -689,14 +689,16 @@ def test_decode_steps_in_sequence_see_the_appended_tokens(L, H, r):
         _say(f"    step {i} (length {Lq}): near-tie swaps {nmis}, worst attn rel-L2 {wo:.2e}")
 
 
-def test_decode_step_full_size_128k(L):
+@pytest.mark.parametrize("r", [8, 4, 16])
+def test_decode_step_full_size_128k(L, r):
     """One layer of the 128K-token, 8-KV-head workload through the fused entry
-    point at its real shape (one step after the bulk build)."""
-    _say("[gpu] decode step, full-size 128K layer")
+    point at its real shape (one step after the bulk build), at the rank of
+    the headline and at the two other ranks the decode step is timed at."""
+    _say(f"[gpu] decode step, full-size 128K layer, r={r}")
     b = synth.config_batch("ctx128k")
-    kp, vp, kn, vn, summ, completed = _step_state(b, 8)
-    res, kpa, vpa, sa = _run_step(L, L.Dims(b.H, b.G, 8), b, kp, vp, kn, vn, summ, 128)
-    ws, nmis, wo = _check_step(b, 8, 128, res, kpa, vpa, sa, summ, completed)
+    kp, vp, kn, vn, summ, completed = _step_state(b, r)
+    res, kpa, vpa, sa = _run_step(L, L.Dims(b.H, b.G, r), b, kp, vp, kn, vn, summ, 128)
+    ws, nmis, wo = _check_step(b, r, 128, res, kpa, vpa, sa, summ, completed)
     _say(f"    near-tie swaps {nmis}, worst attn rel-L2 {wo:.2e}")
 
 
