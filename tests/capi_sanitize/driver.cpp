@@ -48,6 +48,14 @@ int main() {
     std::fprintf(stderr, "FAIL: workspace size for INT_MAX sequences: %zu\n", big);
     ++g_fail;
   }
+  // per-head selection: the workspace of one query head per KV head-like row
+  locks_dims dph{128, 16, 8, 8, 4, 0, LOCKS_MERGE_PER_HEAD};
+  locks_dims dview{128, 16, 8, 32, 1, 0, LOCKS_MERGE_SHARE};
+  locks_dims dbadrule{128, 16, 8, 8, 4, 0, LOCKS_MERGE_PER_HEAD + 1};
+  locks_dims dhuge{128, 16, 8, INT_MAX / 2, 4, 0, LOCKS_MERGE_PER_HEAD};
+  EXPECT_EQ(locks_workspace_bytes(&dph, 2, 2048, 64), locks_workspace_bytes(&dview, 2, 2048, 64));
+  EXPECT_EQ(locks_workspace_bytes(&dbadrule, 2, 2048, 64), 0);
+  EXPECT_EQ(locks_workspace_bytes(&dhuge, 1, 2048, 64), 0);
   for (int32_t s = -5; s <= 1; ++s)
     if (!locks_status_string(s) || !std::strlen(locks_status_string(s))) ++g_fail;
   if (std::strcmp(locks_status_string(INT_MIN), "unknown status") != 0) ++g_fail;
