@@ -306,6 +306,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
   __shared__ int sh_cbase[kS + 1];  // crossing-bin candidates before slice y
   __shared__ int sh_waves[16];
   __shared__ int sh_wa[kDecWaves], sh_wc[kDecWaves], sh_wt[kDecWaves];
+  __shared__ uint32_t sh_vote[kDecWaves];  // exchange 1: a wave still missing data
   __shared__ int sh_nocov;  // some slice's top candidates stop before the crossing bin
   __shared__ int sh_int[8];
   __shared__ uint32_t sh_u[2];
@@ -521,7 +522,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     }
     // every slice's count of bin tid (kept in registers) and top-candidate
     // slot tid (slice tid / kTop)
-    uint32_t hy[kS];
+    uint32_t hy[kS] = {};
     uint64_t tv = 0ull;
     {
       uint32_t pending = ok ? 1u : 0u;  // a workgroup that already failed does not wait
@@ -536,16 +537,25 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
         pending |= ((tv >> 32) == 0ull) ? 1u : 0u;
         if (pending) __builtin_amdgcn_s_sleep(1);
       }
-      ok = __syncthreads_and(pending == 0u) && ok;
+      // the summed histogram and every wave's vote on "all arrived" share one
+      // barrier (the counts are only used when the vote passes)
+      const uint64_t miss = __ballot(pending != 0u);
       uint32_t t = 0u;
 #pragma unroll
       for (int y = 0; y < kS; ++y) {
-        hy[y] = ok ? hy[y] - 1u : 0u;
+        hy[y] -= 1u;
         t += hy[y];
       }
       hist[tid] = t;
+      if (lane == 0) sh_vote[wave] = miss != 0ull ? 1u : 0u;
     }
     __syncthreads();
+    {
+      uint32_t any = 0u;
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) any |= sh_vote[w];
+      ok = ok && any == 0u;
+    }
     if (ok) {
       // ---- crossing bin: every wave scans the histogram itself (lane l
       // holds bins 8l .. 8l+7), so no broadcast is needed
