@@ -346,7 +346,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
   if (tid < G * kHeadDim / 8) sh_q[tid] = reinterpret_cast<const uint4*>(q + sh_idx * G * kHeadDim)[tid];
   for (int i = tid; i < kHistCopies * (kBins + 1); i += kDecThreads) (&histc[0][0])[i] = 0u;
   if (tid < kDecThreads / 32) slice_bits[tid] = 0u;
-  if (tid == 0) sh_nocov = 0;
+  if (tid == 0) {
+    sh_nocov = 0;
+    sh_int[4] = 0;  // part B: members of this slice and of the slices before it
+    sh_int[5] = 0;
+    sh_u[1] = 1u;   // the fast ranking received every candidate
+  }
   my_blk[tid] = bk;
   bool ok = !poisoned;  // false after a timed-out wait (here or in an earlier launch)
   if constexpr (R > 0) {
@@ -469,7 +474,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
       bin = dec_bin(kj);
     }
     // ---- 3. slice histogram (candidates only), published; exchange 1
-    __syncthreads();
+    // (the zeroed copies are visible here: in a fused launch the barrier of
+    // the flags wait came after the zeroing)
+    if constexpr (R == 0) __syncthreads();
     if (cand) atomicAdd(&histc[lane & (kHistCopies - 1)][bin], 1u);
     __syncthreads();
     {
@@ -623,8 +630,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
       if (lds_b && te) {  // the candidate list, in slice and page order
         const int pos = preT + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(balT >> 32),
                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)balT, 0u));
+        const uint32_t pg = (uint32_t)(tv >> 32) - 1u;
         cand_key[pos] = tkey;
-        cand_page[pos] = (uint32_t)(tv >> 32) - 1u;
+        cand_page[pos] = pg;
+        // this slice's first candidates, loaded ahead by wave kc (part 5)
+        const int kc = pos - sh_cbase[x];
+        if (kc >= 0 && kc < kDecWaves && kc < sh_cbase[x + 1] - sh_cbase[x]) {
+          cs_page[kc] = (int)pg;
+          cs_blk[kc] = my_blk[clampi((int)pg - x * slice, 0, kDecThreads - 1)];
+        }
       }
       if (in) {
         const int pos = preA + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(balA >> 32),
@@ -669,13 +683,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
   // the others already attend part A; larger bins by the whole workgroup after.
   const int cb_lo = part_bin ? sh_cbase[x] : 0, cb_hi = part_bin ? sh_cbase[x + 1] : 0;
   const bool fast_b = !sel_all && ok && part_bin && ct <= 64;
-  if (tid == 0) { sh_int[4] = 0; sh_int[5] = 0; sh_u[1] = 1u; }
-  if (lds_b && tid < min(cb_hi - cb_lo, kDecWaves)) {
-    const int pj = (int)cand_page[cb_lo + tid];
-    cs_page[tid] = pj;
-    cs_blk[tid] = my_blk[clampi(pj - x * slice, 0, kDecThreads - 1)];
-  }
-  __syncthreads();
   attn_load_q<G>(qw, reinterpret_cast<const uint16_t*>(sh_q), lane);
   // the K/V of the slice's first crossing-bin candidates load now (wave k
   // takes candidate k) and are attended if ranking makes them members
