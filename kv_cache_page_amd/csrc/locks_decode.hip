@@ -224,6 +224,15 @@ __device__ __forceinline__ void attn_list(AttnAcc& acc, const AttnQ& qw,
 // reads from it (score outputs, Z partials, the appended K/V row, mailbox
 // zeros) is written with agent-scope stores, which reach memory before the
 // flag, so the two may run on different XCDs.
+// Decode workgroups of a head that hold pages (or, when every page is
+// selected, positions) of a sequence of P pages: the others leave at once
+// and the exchanges and the merge run over these only (at least one, which
+// writes the outputs of an empty sequence).
+__device__ __forceinline__ int decode_wgs_needed(int P, bool sel_all, int slice, int per_wg, int nsplit) {
+  const int a = sel_all ? (P + per_wg - 1) / per_wg : (P + slice - 1) / slice;
+  return min(max(a, 1), nsplit);
+}
+
 template <int R, int G>
 __device__ __forceinline__ void step_score_part(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ summ,
@@ -339,6 +348,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
   const bool poisoned = ld_coh(mb_step + 1) == kPoison;
   const int len_raw = seq_lens[s];
   const int bud_raw = budgets[s];
+  const int len = clampi(len_raw, 0, MP * kPage);
+  const int P = (len + kPage - 1) / kPage;
+  const int k = clampi(bud_raw, 2, max_budget);
+  const bool sel_all = (P == 0 || k >= P);
+  // the head's workgroups with pages of this sequence (the others have
+  // nothing to attend or publish: they leave below, before the flags wait and
+  // without touching the mailbox, once the loads here are all issued)
+  const int act = decode_wgs_needed(P, sel_all, slice, per_wg, nsplit);
   const int j = x * slice + tid;  // this thread's page
   const bool jin = tid < slice && j < MP;
   const int jj = jin ? j : 0;
@@ -353,6 +370,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     sh_u[1] = 1u;   // the fast ranking received every candidate
   }
   my_blk[tid] = bk;
+  if (x >= act) return;
   bool ok = !poisoned;  // false after a timed-out wait (here or in an earlier launch)
   if constexpr (R > 0) {
     // ---- wait (bounded) for the head's score workgroups of this epoch
@@ -393,11 +411,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
   load_scores<G>(escore + (sh_idx * MP + jj) * G, ev);
   const float mv = pmax[sh_idx * MP + jj];
 
-  const int len = clampi(len_raw, 0, MP * kPage);
-  const int P = (len + kPage - 1) / kPage;
   const int F = scored_pages(len, lag);  // summarised pages (pages 0..P-2 are among them)
-  const int k = clampi(bud_raw, 2, max_budget);
-  const bool sel_all = (P == 0 || k >= P);
   bool in = false;      // this thread's page is in part A
   int natt = 0;         // pages in att_page (part A, or the positions when every page is selected)
   int tbin = -1, need = 0, ct = 0;
@@ -537,10 +551,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
         pending = 0u;
 #pragma unroll
         for (int y = 0; y < kS; ++y) {
-          hy[y] = ld_coh(&mb_hist[y * kBins + tid]);
+          // (an absent slice reads as empty; its load is kept unconditional:
+          // the mailbox holds every slice's words, zeroed in this step)
+          const uint32_t w = ld_coh(&mb_hist[y * kBins + tid]);
+          hy[y] = (y < act) ? w : 1u;
           pending |= (hy[y] == 0u) ? 1u : 0u;
         }
-        tv = ld_coh64(&mb_top[tid]);
+        // (the top list of an absent slice: empty, cut off at no bin)
+        const uint64_t tw = ld_coh64(&mb_top[tid]);
+        tv = (tid / kTop < act) ? tw : (tid % kTop == kTop - 1) ? ((1ull << 32) | (uint32_t)kBins) : kTopEmpty;
         pending |= ((tv >> 32) == 0ull) ? 1u : 0u;
         if (pending) __builtin_amdgcn_s_sleep(1);
       }
@@ -794,7 +813,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
       // large crossing bin: counted barrier, then an exact 8-bit radix select
       // on the order-preserving key bits over the published candidates
       coop_arrive(&ctr[1 * kCoopCtrWords], &sh_u[0]);
-      ok = coop_wait(&ctr[1 * kCoopCtrWords], (uint32_t)nsplit, &sh_u[1]);
+      ok = coop_wait(&ctr[1 * kCoopCtrWords], (uint32_t)act, &sh_u[1]);
       if (ok) {
         uint32_t prefix = 0u;
         int needr = need;
@@ -891,7 +910,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
       __syncthreads();
       if (wave == 0) {
         uint32_t a = 1u;
-        if (lane < nsplit && ok) {
+        if (lane < act && ok) {
           for (int it = 0; it < kSpinMax; ++it) {
             a = ld_coh(&mb_acnt[lane]);
             if (a != 0u) break;
@@ -923,22 +942,27 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     }
   }
 
-  // ---- the merge, spread over the head's workgroups: workgroup x takes the
-  // elements [x kE, (x + 1) kE) of the G x 128 outputs; thread e of them waits
-  // (bounded) for the nsplit partials of its element and combines them in
-  // split order
-  constexpr int kE = G * kHeadDim / kS;
-  static_assert(kE * kS == G * kHeadDim, "whole elements per workgroup");
-  if (tid >= kE) return;
-  const int g = (x * kE + tid) / kHeadDim, d = (x * kE + tid) % kHeadDim;
+  // ---- the merge, spread over the head's act workgroups: workgroup x takes
+  // the elements [x N / act, (x + 1) N / act) of the N = G x 128 outputs (at
+  // least one each, as N >= act); the thread of element e waits (bounded) for
+  // the act partials of it and combines them in split order (an absent
+  // split: empty)
+  constexpr int kN = G * kHeadDim;
+  const int e = x * kN / act + tid;
+  if (e >= (x + 1) * kN / act) return;
+  const int g = e / kHeadDim, d = e % kHeadDim;
   uint64_t po[kS], pl[kS];
   bool got = false;
+  constexpr uint64_t kEmptyLse = (1ull << 32) | 0xFF800000u;  // tagged -inf
   for (int it = 0; it < kSpinMax; ++it) {
     uint32_t miss = 0u;
 #pragma unroll
     for (int y = 0; y < kS; ++y) {
-      po[y] = ld_coh64(&mb_po[(y * G + g) * kHeadDim + d]);
-      pl[y] = ld_coh64(&mb_pl[y * G + g]);
+      // (unconditional loads: the mailbox holds every split's words)
+      const uint64_t wo = ld_coh64(&mb_po[(y * G + g) * kHeadDim + d]);
+      const uint64_t wl = ld_coh64(&mb_pl[y * G + g]);
+      po[y] = (y < act) ? wo : (1ull << 32);
+      pl[y] = (y < act) ? wl : kEmptyLse;
     }
 #pragma unroll
     for (int y = 0; y < kS; ++y) miss |= (uint32_t)((po[y] >> 32) == 0ull) | (uint32_t)((pl[y] >> 32) == 0ull);
@@ -971,7 +995,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     lse_out[sh_idx * G + g] = some ? (M + __builtin_amdgcn_logf(W)) * kLn2 : -__builtin_inff();
   // every workgroup of the head has read the epoch (each published a partial
   // after reading it), so the next step's launch may use the next one
-  if (R > 0 && x == nsplit - 1 && tid == 0) st_coh(mb_step, epoch + 1u);
+  if (R > 0 && x == act - 1 && tid == 0) st_coh(mb_step, epoch + 1u);
 }
 
 // Launch shape for a table of MP pages and a budget of KB pages: false when
