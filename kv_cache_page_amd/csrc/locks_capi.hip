@@ -33,6 +33,7 @@ int64_t decode_mailbox_zero_words(int MP, int KB, int G);
 hipError_t launch_decode(int G, const StepLaunch& a, hipStream_t st);
 bool decode_step_fuses_score(int r);
 int decode_resident_capacity(int r, int G, int nsplit);
+int step_score_tiles(int MP, int nsplit);
 hipError_t launch_step_reset(uint32_t* mbox, int64_t sh, int MP, int KB, int G, hipStream_t st);
 hipError_t launch_append(const void* knew, const void* vnew, void* kpool, void* vpool, int64_t nb,
                          const int32_t* table, const int32_t* lens, int S, int H, int MP,
@@ -128,8 +129,10 @@ Workspace carve(const locks_dims* d, int32_t S, int32_t MP, int32_t KB) {
   off = align_up(off + sh * MP * d->group_size * sizeof(float));
   w.pmax = off;
   off = align_up(off + sh * MP * sizeof(float));
-  w.zpart = off;  // (the fused decode step pads it to 64 bytes per tile, tiles rounded up to even)
-  off = align_up(off + sh * (size_t)((w.ntiles + 1) / 2 * 2) * 64);
+  w.zpart = off;  // (the fused decode step pads it to 64 bytes per tile, tiles rounded up to even,
+                  // and may cut the table into smaller tiles)
+  const int zt = fused ? std::max(w.ntiles, locks::step_score_tiles(MP, ns_f)) : w.ntiles;
+  off = align_up(off + sh * (size_t)((zt + 1) / 2 * 2) * 64);
   w.keys = off;
   off = align_up(off + sh * MP * sizeof(uint32_t));
   w.parts = off;

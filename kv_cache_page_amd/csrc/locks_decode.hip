@@ -117,6 +117,12 @@ __host__ __device__ inline int64_t coop_zero_words(int nsplit, int G) {
 constexpr int kStepWords = 128;
 constexpr uint32_t kPoison = 0x504F4953u;  // not a value a zeroed or stale-filled workspace holds by chance
 constexpr int kMaxScorePairs = 64;  // one polling lane each
+// Pages per score tile in a fused launch with nsplit selection workgroups per
+// head: 32 for the smallest split count (tables of at most 8 x 512 pages), so
+// that a short table still spreads its summary reads over enough compute
+// units (a workgroup's reads are bounded by the loads it keeps in flight,
+// not by the memory's bandwidth); 128 otherwise.
+__host__ __device__ constexpr int step_tile_pages(int nsplit) { return nsplit <= 8 ? 32 : 128; }
 __host__ __device__ inline int64_t coop_mailbox_words(int nsplit, int G, int MP) {
   return (coop_zero_words(nsplit, G) + kStepWords + 2LL * MP + 31) / 32 * 32;
 }
@@ -233,7 +239,7 @@ __device__ __forceinline__ int decode_wgs_needed(int P, bool sel_all, int slice,
   return min(max(a, 1), nsplit);
 }
 
-template <int R, int G>
+template <int R, int G, int TP>
 __device__ __forceinline__ void step_score_part(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ summ,
     const int32_t* __restrict__ table, const int32_t* __restrict__ seq_lens,
@@ -250,7 +256,7 @@ __device__ __forceinline__ void step_score_part(
   const int tile = 2 * pair + sub;
   float zm = -__builtin_inff(), zs = 0.f;
   if (tile < ntiles)
-    score_tile<R, G>(q, summ, table, seq_lens, escore, num_blocks, H, MP, kScorePagesPerWg,
+    score_tile<R, G, TP>(q, summ, table, seq_lens, escore, num_blocks, H, MP,
                      (lag ? kScoreDeferred : 0) | (hdiv << kScoreHeadDivShift), knew, vnew, kpool, vpool, pmax, s, h, tile, wave,
                      tid, zm, zs);
   __shared__ float zred[2][4][4][2];
@@ -294,7 +300,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     if ((int)blockIdx.x < n_score) {
       uint32_t* step = mbox + ((int64_t)blockIdx.z * H + (int)blockIdx.x % H) * coop_mailbox_words(nsplit, G, MP) +
                        coop_zero_words(nsplit, G);
-      step_score_part<R, G>(q, summ, table, seq_lens, escore, pmax, zpart, ntiles, num_blocks, H, MP,
+      step_score_part<R, G, step_tile_pages(kS)>(q, summ, table, seq_lens, escore, pmax, zpart, ntiles, num_blocks, H, MP,
                             npairs, knew, vnew, kpool, vpool, coop, step, lag, hdiv);
       return;
     }
@@ -399,7 +405,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
   // from before the launch).
   const float2* zp = zpart + ((R > 0) ? sh_idx * 2 * npairs * 8 : sh_idx * ntiles * G);
   const int zstride = (R > 0) ? 8 : G;  // float2 per tile
-  constexpr int kZl = (kDecMaxSplits * kDecThreads + 64 * kScorePagesPerWg - 1) / (64 * kScorePagesPerWg);
+  constexpr int kTP = (R > 0) ? step_tile_pages(kS) : kScorePagesPerWg;  // pages per tile
+  // the table holds at most kS x 512 pages (decode_shape)
+  constexpr int kZl = (kS * kDecThreads + 64 * kTP - 1) / (64 * kTP);
   float2 zl[kZl][G];  // tile partials t = lane + 64 c
 #pragma unroll
   for (int c = 0; c < kZl; ++c) {
@@ -434,7 +442,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
   } else {
     // From here P >= 3, k < P and pages 0..P-2 are full (F >= P-1).
     // ---- 1. log2 Z_g over the F full pages (tiles beyond F hold nothing)
-    const int ntu = (F + kScorePagesPerWg - 1) / kScorePagesPerWg;
+    const int ntu = (F + kTP - 1) / kTP;
     float lz[G], zx = -__builtin_inff();
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -1015,6 +1023,13 @@ bool decode_shape(int MP, int KB, int* per_wg, int* nsplit, int* slice) {
 
 int decode_max_splits() { return kDecMaxSplits; }
 
+// Score tiles of a fused launch over MP pages with nsplit selection
+// workgroups per head (the kernel is instantiated for nsplit 8, 16, 32).
+int step_score_tiles(int MP, int nsplit) {
+  const int ns = nsplit <= 8 ? 8 : nsplit <= 16 ? 16 : 32;
+  return (MP + step_tile_pages(ns) - 1) / step_tile_pages(ns);
+}
+
 int64_t decode_mailbox_words(int MP, int KB, int G) {
   int pw, ns, sl;
   if (!decode_shape(MP, KB, &pw, &ns, &sl)) return 0;
@@ -1029,11 +1044,12 @@ int64_t decode_mailbox_zero_words(int MP, int KB, int G) {
 template <int R, int G, int kS>
 static void launch_step_rgs(const StepLaunch& a, hipStream_t st) {
   const int HL = a.H < 8 ? a.H : 8;
-  const int npairs = (a.ntiles + 1) / 2;
+  const int ntiles = R > 0 ? step_score_tiles(a.MP, kS) : a.ntiles;
+  const int npairs = (ntiles + 1) / 2;
   const int n_score = R > 0 ? a.H * npairs : 0;
   const int n_dec = HL * kS * ((a.H + HL - 1) / HL);
   hipLaunchKernelGGL((decode_step_kernel<R, G, kS>), dim3(n_score + n_dec, 1, a.S), dim3(kDecThreads), 0, st,
-                     a.escore, a.pmax, a.zpart, a.ntiles, a.lens, a.budgets,
+                     a.escore, a.pmax, a.zpart, ntiles, a.lens, a.budgets,
                      static_cast<const uint16_t*>(a.q), static_cast<uint16_t*>(a.kpool),
                      static_cast<uint16_t*>(a.vpool), a.table, a.nb, a.H, a.MP, a.KB, a.slice, a.per_wg,
                      a.mbox, a.out, a.lse_out, a.sel, a.cnt, static_cast<const uint8_t*>(a.summ), npairs,
@@ -1130,7 +1146,7 @@ int decode_resident_capacity(int r, int G, int nsplit) {
 }
 
 hipError_t launch_decode(int G, const StepLaunch& a, hipStream_t st) {
-  if (a.r != 0 && (a.ntiles + 1) / 2 > kMaxScorePairs) return hipErrorInvalidValue;
+  if (a.r != 0 && (step_score_tiles(a.MP, a.nsplit) + 1) / 2 > kMaxScorePairs) return hipErrorInvalidValue;
   switch (G) {
     case 1: return launch_step_g<1>(a, st);
     case 2: return launch_step_g<2>(a, st);

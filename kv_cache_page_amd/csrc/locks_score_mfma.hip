@@ -11,7 +11,7 @@ template <int R, int G, int TPW>
 __global__ __launch_bounds__(256 * TPW) void score_mfma_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ summ,
     const int32_t* __restrict__ table, const int32_t* __restrict__ seq_lens,
-    float* __restrict__ scores, int64_t num_blocks, int H, int MP, int pages_per_wg,
+    float* __restrict__ scores, int64_t num_blocks, int H, int MP,
     int flags, float2* __restrict__ zpart, const uint16_t* __restrict__ knew,
     const uint16_t* __restrict__ vnew, uint16_t* __restrict__ kpool,
     uint16_t* __restrict__ vpool, float* __restrict__ mxout, CoopZero coop) {
@@ -20,10 +20,10 @@ __global__ __launch_bounds__(256 * TPW) void score_mfma_kernel(
   const int sub = (TPW == 1) ? 0 : (int)(threadIdx.x >> 8);
   const int tile = blockIdx.y * TPW + sub;
   const int tid = threadIdx.x & 255, wave = tid >> 6, lane = tid & 63;
-  const int ntiles = (MP + pages_per_wg - 1) / pages_per_wg;
+  const int ntiles = (MP + kScorePagesPerWg - 1) / kScorePagesPerWg;
   float zm = -__builtin_inff(), zs = 0.f;
   if (tile < ntiles)
-    score_tile<R, G>(q, summ, table, seq_lens, scores, num_blocks, H, MP, pages_per_wg, flags,
+    score_tile<R, G>(q, summ, table, seq_lens, scores, num_blocks, H, MP, flags,
                      knew, vnew, kpool, vpool, mxout, s, h, tile, wave, tid, zm, zs);
   if (zpart) {
     __shared__ float zred[TPW][4][4][2];
@@ -44,11 +44,10 @@ static hipError_t launch_r_g(const uint16_t* q, const uint8_t* summ, const int32
                              void* kpool, void* vpool, float* mxout, CoopZero coop,
                              hipStream_t st) {
   constexpr int TPW = 1;
-  const int ppw = kScorePagesPerWg;
-  const int ntiles = (MP + ppw - 1) / ppw;
+  const int ntiles = (MP + kScorePagesPerWg - 1) / kScorePagesPerWg;
   dim3 grid(H, (ntiles + TPW - 1) / TPW, S);  // heads first: 8 heads -> one XCD each
   hipLaunchKernelGGL((score_mfma_kernel<R, G, TPW>), grid, dim3(256 * TPW), 0, st, q, summ, table, lens,
-                     scores, nb, H, MP, ppw, flags, zpart, static_cast<const uint16_t*>(knew),
+                     scores, nb, H, MP, flags, zpart, static_cast<const uint16_t*>(knew),
                      static_cast<const uint16_t*>(vnew), static_cast<uint16_t*>(kpool),
                      static_cast<uint16_t*>(vpool), mxout, coop);
   return hipGetLastError();

@@ -153,27 +153,29 @@ __device__ __forceinline__ void split_hi_lo2(float w0, float s0, float w1, float
   lo = __builtin_bit_cast(uint32_t, l);
 }
 
-// One 128-page tile, by 4 waves (wave = 0..3, tid = 64 wave + lane). Leaves
-// the wave's Z partial of query gq = lane % 4 in (zm, zs) of lanes 0..3.
-template <int R, int G>
+// One tile of TP pages (128, or 32 in a fused decode step over a short
+// table), by 4 waves (wave = 0..3, tid = 64 wave + lane). Leaves the wave's Z
+// partial of query gq = lane % 4 in (zm, zs) of lanes 0..3.
+template <int R, int G, int TP = kScorePagesPerWg>
 __device__ __forceinline__ void score_tile(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ summ,
     const int32_t* __restrict__ table, const int32_t* __restrict__ seq_lens,
-    float* __restrict__ scores, int64_t num_blocks, int H, int MP, int pages_per_wg,
+    float* __restrict__ scores, int64_t num_blocks, int H, int MP,
     int flags, const uint16_t* __restrict__ knew, const uint16_t* __restrict__ vnew,
     uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool, float* __restrict__ mxout,
     int s, int h, int tile, int wave, int tid, float& zm, float& zs) {
   static_assert(R == 4 || R == 8 || R == 16, "matrix-core path covers ranks 4, 8, 16");
+  static_assert(TP == 32 || TP == 64 || TP == 128, "a wave takes 8 pages or whole 16-page halves");
   constexpr SlotLayout L = slot_layout(R);
   constexpr int NHR = R / 4;
   constexpr float kTwoM24 = 5.9604644775390625e-08f;  // 2^-24
-  constexpr int kWavePages = kScorePagesPerWg / 4;    // pages per wave
+  constexpr int kWavePages = TP / 4;                  // pages per wave
   constexpr int kHalves = (kWavePages + 15) / 16;     // 16-page halves (centroid MFMAs)
   constexpr int kGroups = kWavePages / 4;             // 4-page groups per wave
   const int lane = tid & 63;
   const int r16 = lane & 15, q16 = lane >> 4;
   const int gq = r16 & 3;  // this lane's query (B column r16 carries query r16 % 4)
-  const int j_lo = tile * pages_per_wg;
+  const int j_lo = tile * TP;
   const int P0 = j_lo + kWavePages * wave;  // this wave's first page
   // block ids of the pages P0 + 16 u + r16, read together with the length
   int traw[kHalves];
@@ -212,7 +214,7 @@ __device__ __forceinline__ void score_tile(
         st_agent(reinterpret_cast<uint4*>(vpool + dst), *reinterpret_cast<const uint4*>(vnew + src));
     }
   }
-  const int j_hi = min(j_lo + pages_per_wg, MP);
+  const int j_hi = min(j_lo + TP, MP);
   float* srow = scores + ((int64_t)s * H + h) * MP * G;
   if (flags & kScoreFillNan) {
     const int first = max(j_lo, F);
@@ -222,16 +224,17 @@ __device__ __forceinline__ void score_tile(
   if (j_lo >= F) return;
   const int j_end = min(j_hi, F);
 
-  // ---- live block ids (-1: page past the end or id out of range); the slot
-  // addresses each role needs come by lane permutes. vbits[u] bit i: page
-  // P0 + 16 u + i is live.
+  // ---- live block ids (-1: page past the end, of the next wave (8-page
+  // waves fill half a 16-page half) or id out of range); the slot addresses
+  // each role needs come by lane permutes. vbits[u] bit i: page P0 + 16 u + i
+  // is live.
   int bo[kHalves];
   uint32_t vbits[kHalves];
 #pragma unroll
   for (int u = 0; u < kHalves; ++u) {
     const int j = P0 + 16 * u + r16;
     const int b = traw[u];
-    bo[u] = (j < j_end && b >= 0 && b < num_blocks) ? b : -1;
+    bo[u] = (j < j_end && 16 * u + r16 < kWavePages && b >= 0 && b < num_blocks) ? b : -1;
     vbits[u] = (uint32_t)__ballot(bo[u] >= 0) & 0xFFFFu;
   }
 

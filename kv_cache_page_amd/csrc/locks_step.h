@@ -9,8 +9,8 @@ namespace locks {
 struct StepLaunch {
   float* escore;        // per page and query e = 2^(s - m) (decode layout)
   float* pmax;          // per page m = max_g s (base 2)
-  float2* zpart;        // per 128-page tile and query, base-2 (max, sum)
-  int ntiles;
+  float2* zpart;        // per score tile and query, base-2 (max, sum)
+  int ntiles;           // 128-page tiles (a fused launch with a score part sets its own)
   const int32_t* lens;
   const int32_t* budgets;
   const void* q;
