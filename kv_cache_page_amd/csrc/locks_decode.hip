@@ -246,8 +246,7 @@ __device__ __forceinline__ void step_score_part(
     float* __restrict__ escore, float* __restrict__ pmax, float2* __restrict__ zpart, int ntiles,
     int64_t num_blocks, int H, int MP, int npairs, const uint16_t* __restrict__ knew,
     const uint16_t* __restrict__ vnew, uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool,
-    CoopZero coop, uint32_t* step, int lag, int hdiv) {
-  const int bid = blockIdx.x, s = blockIdx.z;
+    CoopZero coop, uint32_t* step, int lag, int hdiv, int bid, int s) {
   const int h = bid % H, pair = bid / H;
   const int64_t sh_idx = (int64_t)s * H + h;
   const uint32_t E = ld_coh(step);
@@ -281,7 +280,14 @@ __device__ __forceinline__ void step_score_part(
 // R > 0: one fused launch per step, the score workgroups first (H x npairs,
 // heads first), then the decode workgroups, which wait for their head's
 // score workgroups. R = 0: the decode workgroups alone, after a separate
-// score kernel.
+// score kernel. Grid row z holds sequence z's score workgroups, then the
+// decode workgroups of sequence z - dshift. With several sequences and a
+// score part, dshift = 1 (S + 1 rows): the dispatcher starts workgroups in
+// row order, so a sequence's decode workgroups start after the next
+// sequence's score workgroups, when their own scores are about done, instead
+// of holding compute units that the next score reads wait for. Each
+// workgroup still waits only for earlier ones (its sequence's score
+// workgroups) and its own contiguous decode group.
 template <int R, int G, int kS>
 __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     float* __restrict__ escore, float* __restrict__ pmax, float2* __restrict__ zpart, int ntiles,
@@ -291,17 +297,19 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     int slice, int per_wg, uint32_t* __restrict__ mbox, float* __restrict__ out,
     float* __restrict__ lse_out, int32_t* __restrict__ sel_pages, int32_t* __restrict__ sel_count,
     const uint8_t* __restrict__ summ, int npairs, const uint16_t* __restrict__ knew,
-    const uint16_t* __restrict__ vnew, CoopZero coop, int lag, int rule, int hdiv) {
+    const uint16_t* __restrict__ vnew, CoopZero coop, int lag, int rule, int hdiv, int dshift) {
   constexpr int nsplit = kS;
   constexpr int kTop = kDecThreads / kS;  // top-candidate slots per slice
   static_assert(kTop * kS == kDecThreads, "one top-candidate slot per thread");
   const int n_score = (R > 0) ? H * npairs : 0;
   if constexpr (R > 0) {
     if ((int)blockIdx.x < n_score) {
+      // (the score part of the extra last row, dshift = 1, is empty)
+      if ((int)blockIdx.z >= (int)gridDim.z - dshift) return;
       uint32_t* step = mbox + ((int64_t)blockIdx.z * H + (int)blockIdx.x % H) * coop_mailbox_words(nsplit, G, MP) +
                        coop_zero_words(nsplit, G);
       step_score_part<R, G, step_tile_pages(kS)>(q, summ, table, seq_lens, escore, pmax, zpart, ntiles, num_blocks, H, MP,
-                            npairs, knew, vnew, kpool, vpool, coop, step, lag, hdiv);
+                            npairs, knew, vnew, kpool, vpool, coop, step, lag, hdiv, (int)blockIdx.x, (int)blockIdx.z);
       return;
     }
   }
@@ -333,7 +341,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
   const int HL = H < 8 ? H : 8;
   const int bid = (int)blockIdx.x - n_score;
   const int hr = bid / (HL * nsplit), rr = bid % (HL * nsplit);
-  const int h = hr * HL + rr % HL, x = rr / HL, s = blockIdx.z;
+  const int h = hr * HL + rr % HL, x = rr / HL, s = (int)blockIdx.z - dshift;
+  if (s < 0) return;  // the decode part of the first row, dshift = 1, is empty
   if (h >= H) return;  // padding of the last head row
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t sh_idx = (int64_t)s * H + h;
@@ -1048,13 +1057,14 @@ static void launch_step_rgs(const StepLaunch& a, hipStream_t st) {
   const int npairs = (ntiles + 1) / 2;
   const int n_score = R > 0 ? a.H * npairs : 0;
   const int n_dec = HL * kS * ((a.H + HL - 1) / HL);
-  hipLaunchKernelGGL((decode_step_kernel<R, G, kS>), dim3(n_score + n_dec, 1, a.S), dim3(kDecThreads), 0, st,
+  const int dshift = (R > 0 && a.S > 1) ? 1 : 0;
+  hipLaunchKernelGGL((decode_step_kernel<R, G, kS>), dim3(n_score + n_dec, 1, (unsigned)a.S + (unsigned)dshift), dim3(kDecThreads), 0, st,
                      a.escore, a.pmax, a.zpart, ntiles, a.lens, a.budgets,
                      static_cast<const uint16_t*>(a.q), static_cast<uint16_t*>(a.kpool),
                      static_cast<uint16_t*>(a.vpool), a.table, a.nb, a.H, a.MP, a.KB, a.slice, a.per_wg,
                      a.mbox, a.out, a.lse_out, a.sel, a.cnt, static_cast<const uint8_t*>(a.summ), npairs,
                      static_cast<const uint16_t*>(a.knew), static_cast<const uint16_t*>(a.vnew), a.coop,
-                     a.lag, a.rule, a.hdiv > 0 ? a.hdiv : 1);
+                     a.lag, a.rule, a.hdiv > 0 ? a.hdiv : 1, dshift);
 }
 
 template <int R, int G>
