@@ -97,14 +97,15 @@ __device__ __forceinline__ int dec_bin(float key) {
 // the score kernel: the counters [kCoopCounters][kCoopCtrWords], slice
 // histograms [nsplit][512], part-A counts [32], fast candidates [512], the
 // slices' top candidates [nsplit][512 / nsplit] and the split partials
-// [nsplit][G][128] and their log-sums [nsplit][G] (the last four 64-bit).
+// [nsplit][G][128] (the last three 64-bit; a partial word carries its
+// split's log-sum, see the merge).
 // Not zeroed: the large-bin candidates (key bits, page) [MP] each.
 __host__ __device__ inline int64_t coop_part_offset(int nsplit) {
   return (int64_t)kCoopCounters * kCoopCtrWords + (int64_t)nsplit * kBins + kDecMaxSplits + 2 * kFastCand +
          2 * kDecThreads;
 }
 __host__ __device__ inline int64_t coop_zero_words(int nsplit, int G) {
-  return coop_part_offset(nsplit) + 2LL * nsplit * G * (kHeadDim + 1);
+  return coop_part_offset(nsplit) + 2LL * nsplit * G * kHeadDim;
 }
 // After the zeroed words: the step region (not zeroed) of a fused launch,
 // [0] the epoch (see step_tag), [1] the poison word and [32 ..) one
@@ -887,10 +888,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
   __syncthreads();
 
   // ---- the workgroup's partial, normalised: thread (g, d) combines the 8
-  // wave partials into o = acc / l and lse = m + log2 l, published as tagged
-  // words (value | 1 << 32) that the merging workgroups poll
-  uint64_t* mb_po = mb_part(mb, nsplit);            // [nsplit][G][128]
-  uint64_t* mb_pl = mb_po + nsplit * G * kHeadDim;  // [nsplit][G]
+  // wave partials into o = acc / l and lse = m + log2 l and publishes both in
+  // one word, o | ~bits(lse) << 32, that the merging workgroups poll: the
+  // complemented log-sum is never 0 (the one float whose complement is 0, a
+  // NaN, is stored as the canonical NaN), so a zeroed word reads as absent,
+  // and one load per split brings the value and its weight together
+  uint64_t* mb_po = mb_part(mb, nsplit);  // [nsplit][G][128]
   if (tid < G * kHeadDim) {
     const int g = tid / kHeadDim, d = tid % kHeadDim;
     float M = -__builtin_inff();
@@ -905,12 +908,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     }
     float o = L > 0.f ? a / L : 0.f;
     if (!ok) o = __builtin_nanf("");
-    constexpr uint64_t kTag = 1ull << 32;
-    st_coh64(&mb_po[(x * G + g) * kHeadDim + d], kTag | __float_as_uint(o));
-    if (d == 0) {
-      const float lse = L > 0.f ? M + __builtin_amdgcn_logf(L) : -__builtin_inff();
-      st_coh64(&mb_pl[x * G + g], kTag | __float_as_uint(lse));
-    }
+    const float lse = L > 0.f ? M + __builtin_amdgcn_logf(L) : -__builtin_inff();
+    uint32_t lb = __float_as_uint(lse);
+    if (lb == 0xFFFFFFFFu) lb = 0x7FC00000u;
+    st_coh64(&mb_po[(x * G + g) * kHeadDim + d], ((uint64_t)(~lb) << 32) | __float_as_uint(o));
   }
 
   // ---- selection output: every workgroup writes its slice's selected pages
@@ -968,21 +969,19 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
   const int e = x * kN / act + tid;
   if (e >= (x + 1) * kN / act) return;
   const int g = e / kHeadDim, d = e % kHeadDim;
-  uint64_t po[kS], pl[kS];
+  uint64_t po[kS];
   bool got = false;
-  constexpr uint64_t kEmptyLse = (1ull << 32) | 0xFF800000u;  // tagged -inf
+  constexpr uint64_t kEmpty = (uint64_t)(~0xFF800000u) << 32;  // o = 0, lse = -inf
   for (int it = 0; it < kSpinMax; ++it) {
     uint32_t miss = 0u;
 #pragma unroll
     for (int y = 0; y < kS; ++y) {
       // (unconditional loads: the mailbox holds every split's words)
       const uint64_t wo = ld_coh64(&mb_po[(y * G + g) * kHeadDim + d]);
-      const uint64_t wl = ld_coh64(&mb_pl[y * G + g]);
-      po[y] = (y < act) ? wo : (1ull << 32);
-      pl[y] = (y < act) ? wl : kEmptyLse;
+      po[y] = (y < act) ? wo : kEmpty;
     }
 #pragma unroll
-    for (int y = 0; y < kS; ++y) miss |= (uint32_t)((po[y] >> 32) == 0ull) | (uint32_t)((pl[y] >> 32) == 0ull);
+    for (int y = 0; y < kS; ++y) miss |= (uint32_t)((po[y] >> 32) == 0ull);
     if (miss == 0u) {
       got = true;
       break;
@@ -993,11 +992,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
   // split order
   float M = -__builtin_inff();
 #pragma unroll
-  for (int y = 0; y < kS; ++y) M = fmaxf(M, __uint_as_float((uint32_t)pl[y]));
+  for (int y = 0; y < kS; ++y) M = fmaxf(M, __uint_as_float(~(uint32_t)(po[y] >> 32)));
   float W = 0.f, a = 0.f;
 #pragma unroll
   for (int y = 0; y < kS; ++y) {
-    const float ly = __uint_as_float((uint32_t)pl[y]);
+    const float ly = __uint_as_float(~(uint32_t)(po[y] >> 32));
     const float f = (ly == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(ly - M);
     W += f;
     a = fmaf(__uint_as_float((uint32_t)po[y]), f, a);
