@@ -250,7 +250,8 @@ __device__ __forceinline__ void step_score_part(
     CoopZero coop, uint32_t* step, int lag, int hdiv, int bid, int s) {
   const int h = bid % H, pair = bid / H;
   const int64_t sh_idx = (int64_t)s * H + h;
-  const uint32_t E = ld_coh(step);
+  uint32_t E = 0u;  // the head's epoch, read and used by thread 0 only
+  if (threadIdx.x == 0) E = ld_coh(step);
   zero_coop_mailbox(coop, sh_idx, pair, npairs);
   const int sub = threadIdx.x >> 8, tid = threadIdx.x & 255, wave = tid >> 6, lane = tid & 63;
   const int tile = 2 * pair + sub;
@@ -360,8 +361,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
 
   // ---- loads that need no score output first: length, budget, the block id
   // of this thread's page (clamped, so the loads are unconditional), queries
-  const uint32_t epoch = (R > 0) ? ld_coh(mb_step) : 0u;
-  const bool poisoned = ld_coh(mb_step + 1) == kPoison;
+  // (the epoch and the poison word, adjacent, by one lane per wave: every
+  // workgroup of the head reads them, and one request per wave keeps their
+  // line from being a hot spot)
+  uint64_t epw = 0ull;
+  if (lane == 0) epw = ld_coh64(reinterpret_cast<const uint64_t*>(mb_step));
+  epw = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(epw >> 32)) << 32) |
+        (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)epw);
+  const uint32_t epoch = (R > 0) ? (uint32_t)epw : 0u;
+  const bool poisoned = (uint32_t)(epw >> 32) == kPoison;
   const int len_raw = seq_lens[s];
   const int bud_raw = budgets[s];
   const int len = clampi(len_raw, 0, MP * kPage);
