@@ -124,11 +124,13 @@ Workspace carve(const locks_dims* d, int32_t S, int32_t MP, int32_t KB) {
   w.ntiles = (MP + locks::kScorePagesPerWg - 1) / locks::kScorePagesPerWg;
   int per_f, ns_f, slice_f;
   const bool fused = locks::decode_shape(MP, KB, &per_f, &ns_f, &slice_f);
+  // (a fused decode step's score outputs have rows of MP rounded up to 32 pages)
+  const size_t rowp = fused ? (size_t)locks::step_row_pages(MP) : (size_t)MP;
   size_t off = 0;
   w.scores = off;
-  off = align_up(off + sh * MP * d->group_size * sizeof(float));
+  off = align_up(off + sh * rowp * d->group_size * sizeof(float));
   w.pmax = off;
-  off = align_up(off + sh * MP * sizeof(float));
+  off = align_up(off + sh * rowp * sizeof(float));
   w.zpart = off;  // (the fused decode step pads it to 64 bytes per tile, tiles rounded up to even,
                   // and may cut the table into smaller tiles)
   const int zt = fused ? std::max(w.ntiles, locks::step_score_tiles(MP, ns_f)) : w.ntiles;

@@ -257,7 +257,7 @@ __device__ __forceinline__ void step_score_part(
   const int tile = 2 * pair + sub;
   float zm = -__builtin_inff(), zs = 0.f;
   if (tile < ntiles)
-    score_tile<R, G, TP>(q, summ, table, seq_lens, escore, num_blocks, H, MP,
+    score_tile<R, G, TP>(q, summ, table, seq_lens, escore, num_blocks, H, MP, step_row_pages(MP),
                      (lag ? kScoreDeferred : 0) | (hdiv << kScoreHeadDivShift), knew, vnew, kpool, vpool, pmax, s, h, tile, wave,
                      tid, zm, zs);
   __shared__ float zred[2][4][4][2];
@@ -434,8 +434,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     for (int g = 0; g < G; ++g) zl[c][g] = zp[t * zstride + g];
   }
   float ev[G];
-  load_scores<G>(escore + (sh_idx * MP + jj) * G, ev);
-  const float mv = pmax[sh_idx * MP + jj];
+  const int rowp = (R > 0) ? step_row_pages(MP) : MP;  // score output row length
+  load_scores<G>(escore + (sh_idx * rowp + jj) * G, ev);
+  const float mv = pmax[sh_idx * rowp + jj];
 
   const int F = scored_pages(len, lag);  // summarised pages (pages 0..P-2 are among them)
   bool in = false;      // this thread's page is in part A

@@ -23,7 +23,7 @@ __global__ __launch_bounds__(256 * TPW) void score_mfma_kernel(
   const int ntiles = (MP + kScorePagesPerWg - 1) / kScorePagesPerWg;
   float zm = -__builtin_inff(), zs = 0.f;
   if (tile < ntiles)
-    score_tile<R, G>(q, summ, table, seq_lens, scores, num_blocks, H, MP, flags,
+    score_tile<R, G>(q, summ, table, seq_lens, scores, num_blocks, H, MP, MP, flags,
                      knew, vnew, kpool, vpool, mxout, s, h, tile, wave, tid, zm, zs);
   if (zpart) {
     __shared__ float zred[TPW][4][4][2];

@@ -160,7 +160,7 @@ template <int R, int G, int TP = kScorePagesPerWg>
 __device__ __forceinline__ void score_tile(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ summ,
     const int32_t* __restrict__ table, const int32_t* __restrict__ seq_lens,
-    float* __restrict__ scores, int64_t num_blocks, int H, int MP,
+    float* __restrict__ scores, int64_t num_blocks, int H, int MP, int rowp,
     int flags, const uint16_t* __restrict__ knew, const uint16_t* __restrict__ vnew,
     uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool, float* __restrict__ mxout,
     int s, int h, int tile, int wave, int tid, float& zm, float& zs) {
@@ -215,7 +215,9 @@ __device__ __forceinline__ void score_tile(
     }
   }
   const int j_hi = min(j_lo + TP, MP);
-  float* srow = scores + ((int64_t)s * H + h) * MP * G;
+  // output rows of rowp >= MP pages (a fused decode step rounds them up so
+  // that every tile writes whole 128-byte lines)
+  float* srow = scores + ((int64_t)s * H + h) * rowp * G;
   if (flags & kScoreFillNan) {
     const int first = max(j_lo, F);
     for (int idx = tid; idx < (j_hi - first) * G; idx += 256)
@@ -461,7 +463,7 @@ __device__ __forceinline__ void score_tile(
       // (coherent stores: in a fused decode step, other workgroups of the same
       // launch read them)
       if (writer && gq < G) st_agent(&srow[(int64_t)jp * G + gq], ev);
-      if (writer && gq == 0) st_agent(&mxout[((int64_t)s * H + h) * MP + jp], mx);
+      if (writer && gq == 0) st_agent(&mxout[((int64_t)s * H + h) * rowp + jp], mx);
     } else if (writer && gq < G) {
       srow[(int64_t)jp * G + gq] = out2 * kLn2;
     }

@@ -6,6 +6,11 @@
 
 namespace locks {
 
+// Row length in pages of a fused launch's score outputs (e per page and query,
+// page maxima): MP rounded up to 32, so that each tile's outputs fill whole
+// 128-byte lines of their own for any table width.
+__host__ __device__ constexpr int step_row_pages(int MP) { return (MP + 31) / 32 * 32; }
+
 struct StepLaunch {
   float* escore;        // per page and query e = 2^(s - m) (decode layout)
   float* pmax;          // per page m = max_g s (base 2)
