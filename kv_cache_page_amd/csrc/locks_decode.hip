@@ -235,6 +235,13 @@ __device__ __forceinline__ void attn_list(AttnAcc& acc, const AttnQ& qw,
 // selected, positions) of a sequence of P pages: the others leave at once
 // and the exchanges and the merge run over these only (at least one, which
 // writes the outputs of an empty sequence).
+// Score pairs (two tiles of TP pages) that hold scored pages of a sequence
+// of len tokens: at least one (it appends the new token and sets a flag).
+__device__ __forceinline__ int step_pairs_needed(int len, int lag, int TP, int npairs) {
+  const int tiles = (scored_pages(len, lag) + TP - 1) / TP;
+  return min(max((tiles + 1) / 2, 1), npairs);
+}
+
 __device__ __forceinline__ int decode_wgs_needed(int P, bool sel_all, int slice, int per_wg, int nsplit) {
   const int a = sel_all ? (P + per_wg - 1) / per_wg : (P + slice - 1) / slice;
   return min(max(a, 1), nsplit);
@@ -247,12 +254,21 @@ __device__ __forceinline__ void step_score_part(
     float* __restrict__ escore, float* __restrict__ pmax, float2* __restrict__ zpart, int ntiles,
     int64_t num_blocks, int H, int MP, int npairs, const uint16_t* __restrict__ knew,
     const uint16_t* __restrict__ vnew, uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool,
-    CoopZero coop, uint32_t* step, int lag, int hdiv, int bid, int s) {
+    CoopZero coop, uint32_t* step, int lag, int hdiv, int bid, int s, bool trim) {
   const int h = bid % H, pair = bid / H;
   const int64_t sh_idx = (int64_t)s * H + h;
+  // With trim (a launch over several sequences, sized by the longest), the
+  // pairs past this sequence's scored pages leave at once: the selection
+  // workgroups wait only for the flags of the first npz pairs, which zero
+  // the mailbox among themselves.
+  int npz = npairs;
+  if (trim) {
+    npz = step_pairs_needed(clampi(seq_lens[s], 0, MP * kPage), lag, TP, npairs);
+    if (pair >= npz) return;
+  }
   uint32_t E = 0u;  // the head's epoch, read and used by thread 0 only
   if (threadIdx.x == 0) E = ld_coh(step);
-  zero_coop_mailbox(coop, sh_idx, pair, npairs);
+  zero_coop_mailbox(coop, sh_idx, pair, npz);
   const int sub = threadIdx.x >> 8, tid = threadIdx.x & 255, wave = tid >> 6, lane = tid & 63;
   const int tile = 2 * pair + sub;
   float zm = -__builtin_inff(), zs = 0.f;
@@ -311,7 +327,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
       uint32_t* step = mbox + ((int64_t)blockIdx.z * H + (int)blockIdx.x % H) * coop_mailbox_words(nsplit, G, MP) +
                        coop_zero_words(nsplit, G);
       step_score_part<R, G, step_tile_pages(kS)>(q, summ, table, seq_lens, escore, pmax, zpart, ntiles, num_blocks, H, MP,
-                            npairs, knew, vnew, kpool, vpool, coop, step, lag, hdiv, (int)blockIdx.x, (int)blockIdx.z);
+                            npairs, knew, vnew, kpool, vpool, coop, step, lag, hdiv, (int)blockIdx.x, (int)blockIdx.z,
+                            dshift != 0);
       return;
     }
   }
@@ -380,6 +397,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
   // nothing to attend or publish: they leave below, before the flags wait and
   // without touching the mailbox, once the loads here are all issued)
   const int act = decode_wgs_needed(P, sel_all, slice, per_wg, nsplit);
+  // (over several sequences, a workgroup without pages leaves before any
+  // other load: short sequences leave many of them)
+  if (dshift && x >= act) return;
   const int j = x * slice + tid;  // this thread's page
   const bool jin = tid < slice && j < MP;
   const int jj = jin ? j : 0;
@@ -398,11 +418,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
   bool ok = !poisoned;  // false after a timed-out wait (here or in an earlier launch)
   if constexpr (R > 0) {
     // ---- wait (bounded) for the head's score workgroups of this epoch
+    // the score pairs of this sequence that set a flag (all of them unless
+    // the launch trims them, as the score part does)
+    const int npz = dshift ? step_pairs_needed(len, lag, step_tile_pages(kS), npairs) : npairs;
     if (wave == 0 && !poisoned) {
       const uint32_t want = step_tag(epoch);
       uint32_t done = 0u;
       for (int it = 0; it < kSpinMax; ++it) {
-        const uint32_t v = (lane < npairs) ? ld_coh(&mb_step[32 + lane]) : want;
+        const uint32_t v = (lane < npz) ? ld_coh(&mb_step[32 + lane]) : want;
         if (__ballot(v != want) == 0ull) {
           done = 1u;
           break;
