@@ -511,6 +511,24 @@ def test_decode_step_ragged(L, host_lens):
     _say(f"    near-tie swaps {nmis}, worst attn rel-L2 {wo:.2e}")
 
 
+def test_decode_step_ragged_wide_table(L):
+    """One fused launch over sequences of very different lengths in a table of
+    4201 pages (16 selection workgroups per head, 128-page score tiles): an
+    empty sequence, one shorter than a page, one that completes a page, and
+    medium and long ones. The launch trims the score pairs and selection
+    workgroups past each sequence's pages; every (sequence, head) is checked
+    against the oracle."""
+    _say("[gpu] decode step, ragged batch over a 4201-page table")
+    lens = [0, 5, 16 * 16, 600 * 16 + 7, 4200 * 16 + 3]
+    budgets = [2, 3, 9, 40, 200]
+    b = synth.make_decode_batch(lens, 4, 4, budgets, seed=151, extra_blocks=5)
+    kp, vp, kn, vn, summ, completed = _step_state(b, 8)
+    dims = L.Dims(b.H, b.G, 8)
+    res, kpa, vpa, sa = _run_step(L, dims, b, kp, vp, kn, vn, summ, 200)
+    ws, nmis, wo = _check_step(b, 8, 200, res, kpa, vpa, sa, summ, completed)
+    _say(f"    near-tie swaps {nmis}, worst attn rel-L2 {wo:.2e}")
+
+
 @pytest.mark.parametrize("G,r", [(1, 4), (2, 16)])
 def test_decode_step_group_sizes(L, G, r):
     _say(f"[gpu] decode step G={G} r={r}")
