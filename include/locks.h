@@ -292,9 +292,9 @@ locks_status locks_sparse_attn(const locks_dims* dims, const void* q, const void
  *   1. only when a sequence's new token completes a page: append every new
  *      token and build the summaries of the completed pages (their last key
  *      is taken from k_new);
- *   2. score every full page, keeping per 128-page tile the (max, sum exp)
- *      of the scores for Z_g (and append the new tokens when step 1 did not
- *      run), then select S and attend: the attention workgroups of a
+ *   2. score every full page, keeping per tile of pages (128, or 32 when the
+ *      table is short) the (max, sum exp) of the scores for Z_g (and append
+ *      the new tokens when step 1 did not run), then select S and attend: the attention workgroups of a
  *      (sequence, KV head) wait for its score workgroups, share the selection
  *      (each selects within its own slice of the pages and they exchange
  *      histograms and candidates through the workspace), attend their own

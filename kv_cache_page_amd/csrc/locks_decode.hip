@@ -1,5 +1,8 @@
-// LOCKS decode step, second kernel: page selection, sparse attention over the
-// selected pages and the merge of the split partials, in one launch (gfx950).
+// LOCKS decode step in one launch (gfx950): for ranks 4, 8 and 16 the page
+// scores (score workgroups first in the grid, the tile code of the score
+// kernel), then page selection, sparse attention over the selected pages and
+// the merge of the split partials; for other ranks the same selection and
+// attention after a separate score kernel.
 //
 // [N] = LOCKS reading notes (zhongzhuzhou.org 2026-07-29): §4.4 Algorithm 2
 // (query-aware selection of the sink page, the most recent page and the
@@ -14,8 +17,9 @@
 // owns the page slice [x * slice, (x + 1) * slice) (slice <= 512, one page
 // per thread), selects within it and attends its own selected pages. They
 // exchange data through a per-(sequence, head) mailbox in the workspace whose
-// slots carry their own "written" tag (the score kernel of the same step
-// zeroes them), so a reader waits for exactly the data it needs:
+// slots carry their own "written" tag (the score workgroups or the score
+// kernel of the same step zero them), so a reader waits for exactly the data
+// it needs:
 //   1. slice histograms of the key bins (count + 1 per bin), each with the
 //      slice's top candidates (key, page + 1) up to a cut-off bin: every
 //      workgroup sums the histograms, finds the crossing bin t of the
@@ -24,9 +28,10 @@
 //      when every cut-off lies beyond t, else published by each slice. Every
 //      workgroup ranks them (part B) while its part-A pages are already being
 //      attended, then attends its slice's part-B members;
-//   3. the workgroup partials, normalised (o = acc / l, lse = m + log2 l) and
-//      tagged per element: each workgroup polls those of its 1/nsplit share
-//      of the output elements and merges them in split order.
+//   3. the workgroup partials, normalised (o = acc / l, lse = m + log2 l),
+//      one word per element that carries o and the complemented bits of the
+//      log-sum (its tag): each workgroup polls those of its 1/nsplit share of
+//      the output elements and merges them in split order.
 // Mailbox accesses are agent-scope relaxed atomics (coherent across the XCDs
 // without cache write-back or invalidation); a tagged 64-bit slot is written
 // and read whole, so its value is valid once its tag is. Waits poll with a
@@ -42,9 +47,10 @@
 // candidates (degenerate keys) goes through a counted barrier instead and an
 // exact 8-bit radix select on the order-preserving key bits.
 //
-// Inputs from the score kernel (decode layout): per page j and query g,
+// Inputs from the score part (decode layout): per page j and query g,
 // e_jg = 2^(s_jg - m_j) with m_j = max_g s_jg (base-2 scores), and m_j; per
-// 128-page tile and query, the base-2 (max, sum) of the scores.
+// score tile (128 pages, or 32 in a fused launch with 8 splits) and query,
+// the base-2 (max, sum) of the scores.
 //
 // Selection, in base-2 units:
 //   1. log2 Z_g from the tile partials (every wave reduces them by itself);
