@@ -100,7 +100,7 @@ __device__ __forceinline__ int dec_bin(float key) {
 }
 
 // Mailbox words of one (sequence, KV head) and G queries per head. Zeroed by
-// the score kernel: the counters [kCoopCounters][kCoopCtrWords], slice
+// the score part of the step (score workgroups or the score kernel): the counters [kCoopCounters][kCoopCtrWords], slice
 // histograms [nsplit][512], part-A counts [32], fast candidates [512], the
 // slices' top candidates [nsplit][512 / nsplit] and the split partials
 // [nsplit][G][128] (the last three 64-bit; a partial word carries its
@@ -229,6 +229,22 @@ __device__ __forceinline__ void attn_list(AttnAcc& acc, const AttnQ& qw,
   }
 }
 
+// Score pairs (two tiles of TP pages) that hold scored pages of a sequence
+// of len tokens: at least one (it appends the new token and sets a flag).
+__device__ __forceinline__ int step_pairs_needed(int len, int lag, int TP, int npairs) {
+  const int tiles = (scored_pages(len, lag) + TP - 1) / TP;
+  return min(max((tiles + 1) / 2, 1), npairs);
+}
+
+// Decode workgroups of a head that hold pages (or, when every page is
+// selected, positions) of a sequence of P pages: the others leave at once
+// and the exchanges and the merge run over these only (at least one, which
+// writes the outputs of an empty sequence).
+__device__ __forceinline__ int decode_wgs_needed(int P, bool sel_all, int slice, int per_wg, int nsplit) {
+  const int a = sel_all ? (P + per_wg - 1) / per_wg : (P + slice - 1) / slice;
+  return min(max(a, 1), nsplit);
+}
+
 // The score part of a fused launch: workgroup (h, pair) scores the tiles
 // 2 pair and 2 pair + 1 of head h (waves 0-3 and 4-7), writes the decode-layout
 // outputs and the tiles' Z partials, zeroes its share of the head's mailbox,
@@ -237,22 +253,6 @@ __device__ __forceinline__ void attn_list(AttnAcc& acc, const AttnQ& qw,
 // reads from it (score outputs, Z partials, the appended K/V row, mailbox
 // zeros) is written with agent-scope stores, which reach memory before the
 // flag, so the two may run on different XCDs.
-// Decode workgroups of a head that hold pages (or, when every page is
-// selected, positions) of a sequence of P pages: the others leave at once
-// and the exchanges and the merge run over these only (at least one, which
-// writes the outputs of an empty sequence).
-// Score pairs (two tiles of TP pages) that hold scored pages of a sequence
-// of len tokens: at least one (it appends the new token and sets a flag).
-__device__ __forceinline__ int step_pairs_needed(int len, int lag, int TP, int npairs) {
-  const int tiles = (scored_pages(len, lag) + TP - 1) / TP;
-  return min(max((tiles + 1) / 2, 1), npairs);
-}
-
-__device__ __forceinline__ int decode_wgs_needed(int P, bool sel_all, int slice, int per_wg, int nsplit) {
-  const int a = sel_all ? (P + per_wg - 1) / per_wg : (P + slice - 1) / slice;
-  return min(max(a, 1), nsplit);
-}
-
 template <int R, int G, int TP>
 __device__ __forceinline__ void step_score_part(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ summ,
