@@ -648,6 +648,75 @@ def test_decode_step_repeat_is_bitwise_stable(L):
         assert np.array_equal(o, outs[0][0]) and np.array_equal(l, outs[0][1])
 
 
+def test_decode_step_graph_replays(L):
+    """The single-launch decode step captured in a HIP graph and replayed:
+    with the outputs reset by eager work and the stream synchronised between
+    replays, and an eager call on the same workspace in between, every replay
+    gives the eager call's outputs and selection bit for bit (the head
+    epochs in the workspace advance with every launch, captured or not);
+    the eager result matches the oracle. No length completes a page, so the
+    step is one launch."""
+    _say("[gpu] decode step captured in a HIP graph, 4 replays")
+    lens = [600 * 16 + 5, 33 * 16 + 9, 2000 * 16 + 1]
+    budgets = [40, 8, 64]
+    b = synth.make_decode_batch(lens, 4, 4, budgets, seed=171, extra_blocks=3)
+    kp, vp, kn, vn, summ, completed = _step_state(b, 8)
+    assert not completed
+    dims = L.Dims(b.H, b.G, 8)
+    S, H, G, kb = b.num_seqs, b.H, b.G, 64
+    kp_d, vp_d, summ_d = kp.to(DEV), vp.to(DEV), torch.from_numpy(summ).to(DEV)
+    q_d, kn_d, vn_d = b.q.to(DEV), kn.to(DEV), vn.to(DEV)
+    tab, lens_d, bud = b.block_table.to(DEV), b.seq_lens.to(DEV), b.budgets.to(DEV)
+    host = b.seq_lens.cpu()
+    ws = L.alloc_workspace(dims, S, b.max_pages, kb, DEV)
+    ws.zero_()
+
+    def bufs():
+        return (torch.empty(S, H * G, 128, device=DEV), torch.empty(S, H * G, device=DEV),
+                torch.empty(S, H, kb, dtype=torch.int32, device=DEV),
+                torch.empty(S, H, dtype=torch.int32, device=DEV))
+
+    def reset(t):
+        t[0].fill_(float("nan"))
+        t[1].fill_(float("nan"))
+        t[2].fill_(-9)
+        t[3].fill_(-9)
+
+    def step(t):
+        L.decode_step(dims, q_d, kn_d, vn_d, kp_d, vp_d, summ_d, tab, lens_d, bud, kb, t[0], ws,
+                      lse_out=t[1], sel_pages=t[2], sel_count=t[3], seq_lens_host=host)
+
+    eager = bufs()
+    reset(eager)
+    step(eager)
+    torch.cuda.synchronize()
+    res = dict(sel=eager[2].cpu().numpy(), cnt=eager[3].cpu().numpy(), scores=None,
+               out=eager[0].cpu().numpy(), lse=eager[1].cpu().numpy())
+    assert torch.equal(kp_d.cpu(), b.k_pool) and torch.equal(vp_d.cpu(), b.v_pool)
+    _check_against_oracle(b, summ, res, 8, kb)
+
+    static = bufs()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(static)
+    torch.cuda.synchronize()
+    other = bufs()
+    for rep in range(4):
+        reset(static)
+        torch.cuda.synchronize()
+        if rep == 2:  # an eager step on the same workspace between replays
+            reset(other)
+            step(other)
+            torch.cuda.synchronize()
+            for a, e in zip(other, eager):
+                assert torch.equal(a, e), "eager step between replays"
+        g.replay()
+        torch.cuda.synchronize()
+        for a, e in zip(static, eager):
+            assert torch.equal(a, e), f"replay {rep}"
+    _say("    4 replays bit-identical to the eager step")
+
+
 @pytest.mark.parametrize("H,r", [(8, 8), (3, 8), (3, 6)])
 def test_decode_steps_in_sequence_see_the_appended_tokens(L, H, r):
     """Three decode steps in a row on the same device pools and workspace, each
