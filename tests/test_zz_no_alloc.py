@@ -101,3 +101,48 @@ def test_noalloc_rejects_oversize_shape(L):
                               torch.full((32,), 512, dtype=torch.int32, device=DEV), 512,
                               torch.zeros(32, 32, 128, device=DEV))
     assert e.value.status == L.ERR_WORKSPACE
+
+
+def test_noalloc_graph_replays(L):
+    """locks_decode_step_noalloc captured in a HIP graph (the kind of caller it
+    is for) and replayed three times, with the outputs reset by eager work and
+    the stream synchronised between replays: every replay equals the eager
+    locks_decode_step on its own workspace, bit for bit (outputs, log-sum-exps,
+    selections, pools, summaries). No length completes a page."""
+    lens, H, budgets = [700 * 16 + 3, 90 * 16 + 11], 8, [64, 16]
+    print(f"[gpu] no-alloc decode step in a HIP graph: lengths {lens}, {H} KV heads", flush=True)
+    dims, b, kp, vp, kn, vn, summ = _inputs(L, lens, H, budgets, 303)
+    kmax = max(budgets)
+    ws = L.alloc_workspace(dims, b.num_seqs, b.max_pages, kmax, DEV)
+    ref = _step(L, L.decode_step, dims, b, kp, vp, kn, vn, summ, kmax, ws=ws)
+    S, G = b.num_seqs, b.G
+    kp2, vp2, summ2 = kp.clone(), vp.clone(), summ.clone()
+    q, tab = b.q.to(DEV), b.block_table.to(DEV)
+    lens_d, bud = b.seq_lens.to(DEV), b.budgets.to(DEV)
+    host = b.seq_lens.cpu()
+    out = torch.empty(S, H * G, 128, device=DEV)
+    lse = torch.empty(S, H * G, device=DEV)
+    sel = torch.empty(S, H, kmax, dtype=torch.int32, device=DEV)
+    cnt = torch.empty(S, H, dtype=torch.int32, device=DEV)
+
+    def step():
+        L.decode_step_noalloc(dims, q, kn, vn, kp2, vp2, summ2, tab, lens_d, bud, kmax, out,
+                              lse_out=lse, sel_pages=sel, sel_count=cnt, seq_lens_host=host)
+
+    step()  # the per-device set-up happens outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        sel.fill_(-9)
+        cnt.fill_(-9)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [x.cpu() for x in (out, lse, sel, cnt, kp2, vp2, summ2)]
+        for name, a, c in zip(("out", "lse", "sel", "cnt", "k_pool", "v_pool", "summaries"), ref, got):
+            assert torch.equal(a, c), (rep, name)
