@@ -281,8 +281,10 @@ __device__ __forceinline__ void score_tile(
   // Issues are unconditional (a group past the end reads block 0's slot,
   // which exists): a load behind a branch makes the compiler's wait counts
   // assume the worst case, and every group would then wait for all loads.
+  // (the first kDepth - 1 groups, or every group of a wave that has fewer)
+  constexpr int kFirst = (kDepth - 1 < kGroups) ? kDepth - 1 : kGroups;
 #pragma unroll
-  for (int gi = 0; gi < kDepth - 1; ++gi) issue(gi, buf[gi]);
+  for (int gi = 0; gi < kFirst; ++gi) issue(gi, buf[gi]);
   __builtin_amdgcn_sched_barrier(0);  // keep the first issues ahead of the query-operand work
   // ---- query operands, power-of-two scaled into fp16 (built while the slot
   // loads are in flight)
