@@ -529,8 +529,10 @@ def test_decode_step_ragged_wide_table(L):
     _say(f"    near-tie swaps {nmis}, worst attn rel-L2 {wo:.2e}")
 
 
-@pytest.mark.parametrize("G,r", [(1, 4), (2, 16)])
+@pytest.mark.parametrize("G,r", [(1, 4), (2, 16), (4, 4), (4, 16)])
 def test_decode_step_group_sizes(L, G, r):
+    """Group sizes and ranks through the single launch over a short table
+    (8 selection workgroups per head, 32-page score tiles)."""
     _say(f"[gpu] decode step G={G} r={r}")
     b = synth.make_decode_batch([70 * 16, 33 * 16 + 5, 129 * 16 + 1], 2, G, [9, 40, 17],
                                 seed=160 + G)
