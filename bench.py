@@ -75,6 +75,8 @@ KERNELS = {
               "locks_score_mfma.hip", ["locks_score_tile.h", "locks_device.h"]),
     "step32k": (os.path.join(PROFILES, "decode_step_kernel_ctx32k_counters.txt"), *_STEP_SRC),
     "stepb32": (os.path.join(PROFILES, "decode_step_kernel_batch32_counters.txt"), *_STEP_SRC),
+    "step_r4": (os.path.join(PROFILES, "decode_step_kernel_r4_ctx128k_counters.txt"), *_STEP_SRC),
+    "step_r16": (os.path.join(PROFILES, "decode_step_kernel_r16_ctx128k_counters.txt"), *_STEP_SRC),
     "build4": (os.path.join(PROFILES, "build_page_kernel_bulk_r4_counters.txt"), *_BUILD_SRC),
     "build8": (os.path.join(PROFILES, "build_page_kernel_bulk_r8_counters.txt"), *_BUILD_SRC),
     "build16": (os.path.join(PROFILES, "build_page_kernel_bulk_r16_counters.txt"), *_BUILD_SRC),
@@ -434,7 +436,7 @@ def run_rank_sweep(torch, L, synth, dev, ranks=(4, 8, 16), replicas=8, reps=20):
         res[f"r{r}"] = {"us_per_step": round(us, 3), "bytes_per_step": bpl,
                         "summary_bytes_per_page": slot_payload(r),
                         "roofline": roofline(f"decode_step_kernel<{r},4,16> (locks_decode_step)",
-                                             "step" if r == R else None, bpl, us),
+                                             "step" if r == R else f"step_r{r}", bpl, us),
                         "any_nan": bool(torch.isnan(out).any())}
         log(f"[bench] rank sweep r={r}: decode step {us:.2f} us per launch ({bpl / us / 1e3:.0f} GB/s)")
         del summs, ws, g
